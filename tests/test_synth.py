@@ -1,0 +1,67 @@
+"""The seeded input generators: published SplitMix64 outputs, determinism, distributions."""
+import numpy as np
+import torch
+
+import moe_synth as synth
+
+
+def test_splitmix64_published_first_outputs():
+    # SplitMix64 seeded with 0 starts 0xe220a8397b1dcdaf, 0x6e789e6aa1b965f4 (Vigna's reference generator).
+    assert synth.splitmix64_py(0, 0) == 0xE220A8397B1DCDAF
+    assert synth.splitmix64_py(0, 1) == 0x6E789E6AA1B965F4
+
+
+def test_torch_words_match_python_definition():
+    for key in (0, 1, 0xFFFFFFFFFFFFFFFF, synth.derive_key(3, 4, 5)):
+        for start in (0, 12345, 10**10):
+            got = synth.splitmix64_words(key, start, 64).tolist()
+            want = [synth._signed(synth.splitmix64_py(key, start + i)) for i in range(64)]
+            assert got == want
+
+
+def test_code_bytes_little_endian_words():
+    key = synth.derive_key(9)
+    out = torch.empty(16, dtype=torch.uint8)
+    synth.fill_code_bytes(out, key)
+    w0 = synth.splitmix64_py(key, 0)
+    assert out[:8].tolist() == [(w0 >> (8 * j)) & 0xFF for j in range(8)]
+
+
+def test_expert_slices_match_whole_layer():
+    wl = synth.WORKLOADS["tiny"]
+    full = synth.layer_weights(wl, 0)
+    for mat in synth.MATRICES:
+        for g in (0, 3, wl.experts):
+            c, s = synth.expert_matrix(wl, 0, mat, g)
+            assert torch.equal(c, full[mat][0][g]) and torch.equal(s, full[mat][1][g])
+
+
+def test_distributions():
+    wl = synth.WORKLOADS["tiny"]
+    full = synth.layer_weights(wl, 0)
+    codes = full["gate"][0].numpy().reshape(-1)
+    nib = np.concatenate([codes & 15, codes >> 4])
+    hist = np.bincount(nib, minlength=16) / nib.size
+    assert np.all(np.abs(hist - 1 / 16) < 0.01)
+    sc = full["down"][1].numpy().reshape(-1)
+    assert sc.min() == 123 and sc.max() == 127
+    assert np.all(np.abs(np.bincount(sc - 123, minlength=5) / sc.size - 0.2) < 0.03)
+    wr = synth.router_weights(synth.WORKLOADS["decode_t8"])
+    assert abs(wr.std() - 0.02) < 2e-4 and abs(wr.mean()) < 2e-4
+
+
+def test_determinism_and_distinct_streams():
+    a = synth.tokens("decode_t8", layer=0, step=0)
+    b = synth.tokens("decode_t8", layer=0, step=0)
+    c = synth.tokens("decode_t8", layer=1, step=0)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    c1, _ = synth.expert_matrix("decode_t8", 0, "gate", 5)
+    c2, _ = synth.expert_matrix("decode_t8", 1, "gate", 5)
+    assert not torch.equal(c1, c2)
+
+
+def test_bf16_rounding_is_nearest_even():
+    f = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -2.5, 1 + 2 ** -7 + 2 ** -9], np.float32)
+    bits = synth.f32_to_bf16_bits(f)
+    # 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> even (1+2^-6); 1+2^-7+2^-9 rounds to 1+2^-7
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F80, 0xC020, 0x3F81]
