@@ -1,0 +1,352 @@
+// C ABI of the MoE layer: validation, workspace carve-up, path choice, kernel enqueue.
+// Nothing here synchronises the host with the device.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+struct moe_layer {
+  moe_layer_desc desc;
+  moe::Dims dims;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+constexpr int kMaxTokens = 1 << 20;
+constexpr int kGemvMaxTokens = 32;  // AUTO: GEMV up to this many tokens, grouped GEMM above
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace layout for T tokens; assigns pointers when base != nullptr.  Returns bytes.
+size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return p;
+  };
+  const size_t tk = (size_t)T * d.K;
+  const size_t rows = (size_t)T * (d.K + d.S);
+  const size_t C = ((size_t)T + moe::kChunk - 1) / moe::kChunk;
+  const size_t gnz = std::min<size_t>(d.E, tk) + d.S;
+  const size_t mt_bound = (rows + gnz * (moe::kGemmBM - 1)) / moe::kGemmBM + 1;
+  moe::CallBufs t{};
+  t.logits = reinterpret_cast<float*>(take((size_t)T * d.E * 4));
+  t.idx = reinterpret_cast<int32_t*>(take(tk * 4));
+  t.w = reinterpret_cast<float*>(take(tk * 4));
+  t.counts = reinterpret_cast<int32_t*>(take((size_t)d.E * 4));
+  t.offsets = reinterpret_cast<int32_t*>(take((size_t)(d.E + 1) * 4));
+  t.perm = reinterpret_cast<int32_t*>(take(tk * 4));
+  t.gmask = reinterpret_cast<uint64_t*>(take(C * d.E * 8));
+  t.cbase = reinterpret_cast<int32_t*>(take(C * d.E * 4));
+  t.grp_row0 = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
+  t.grp_rows = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
+  t.act = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
+  t.info = reinterpret_cast<int32_t*>(take(16));
+  t.mt_group = reinterpret_cast<int32_t*>(take(mt_bound * 4));
+  t.mt_row0 = reinterpret_cast<int32_t*>(take(mt_bound * 4));
+  t.h = take(rows * d.I * 4);
+  t.staging = reinterpret_cast<float*>(take(rows * d.H * 4));
+  if (b) *b = t;
+  return off;
+}
+
+int mt_bound_of(const moe::Dims& d, int T) {
+  const size_t tk = (size_t)T * d.K;
+  const size_t rows = (size_t)T * (d.K + d.S);
+  const size_t gnz = std::min<size_t>(d.E, tk) + d.S;
+  return (int)((rows + gnz * (moe::kGemmBM - 1)) / moe::kGemmBM + 1);
+}
+
+int max_active_of(const moe::Dims& d, int T) {
+  return (int)(std::min<size_t>(d.E, (size_t)T * d.K) + d.S);
+}
+
+struct DeviceGuard {
+  int old = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old) != hipSuccess) old = -1;
+    if (old != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (old >= 0) (void)hipSetDevice(old);
+  }
+};
+
+// ---- kernel timing -------------------------------------------------------------------
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct TimingAcc {
+  const char* name;
+  int64_t launches = 0;
+  double ms = 0;
+};
+std::mutex g_tmu;
+bool g_tenabled = false;
+std::vector<TimingRec> g_trecs;
+std::vector<hipEvent_t> g_tpool;
+std::map<std::string, TimingAcc> g_tacc;
+
+hipEvent_t take_event() {
+  if (!g_tpool.empty()) {
+    hipEvent_t e = g_tpool.back();
+    g_tpool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drain_timing_locked() {
+  for (auto& r : g_trecs) {
+    float ms = 0.f;
+    if (r.b && hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      auto& acc = g_tacc[r.name];
+      acc.name = r.name;
+      acc.launches += 1;
+      acc.ms += ms;
+    }
+    if (r.a) g_tpool.push_back(r.a);
+    if (r.b) g_tpool.push_back(r.b);
+  }
+  g_trecs.clear();
+}
+
+}  // namespace
+
+namespace moe {
+
+int timing_begin(const char* name, hipStream_t s) {
+  if (!g_tenabled) return -1;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  TimingRec r{name, take_event(), take_event()};
+  if (!r.a || !r.b) return -1;
+  (void)hipEventRecord(r.a, s);
+  g_trecs.push_back(r);
+  return (int)g_trecs.size() - 1;
+}
+
+void timing_end(int token, hipStream_t s) {
+  if (token < 0) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (token < (int)g_trecs.size()) (void)hipEventRecord(g_trecs[token].b, s);
+}
+
+}  // namespace moe
+
+// =====================================================================================
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported device or configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_ALLOC: return "allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_device_supported(int32_t device, char* name, int32_t cap) {
+  auto put = [&](const char* s) {
+    if (name && cap > 0) {
+      strncpy(name, s, (size_t)cap - 1);
+      name[cap - 1] = '\0';
+    }
+  };
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    put("no HIP device");
+    return 0;
+  }
+  if (device < 0 || device >= n) {
+    put("device ordinal out of range");
+    return 0;
+  }
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) {
+    (void)hipGetLastError();
+    put("hipGetDeviceProperties failed");
+    return 0;
+  }
+  put(p.gcnArchName);
+  return strncmp(p.gcnArchName, "gfx950", 6) == 0 && (p.gcnArchName[6] == '\0' || p.gcnArchName[6] == ':');
+}
+
+int32_t moe_layer_create(const moe_layer_desc* d, moe_layer** out) {
+  if (out) *out = nullptr;
+  if (!d || !out) return fail(MOE_ERR_INVALID, "moe_layer_create: NULL descriptor or output pointer");
+  if (d->abi_version != MOE_ABI_VERSION)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_create: ABI version %d, library is %d", d->abi_version,
+                MOE_ABI_VERSION);
+  if (d->hidden < 32 || d->hidden > 8192 || d->hidden % 32)
+    return fail(MOE_ERR_INVALID, "hidden=%d must be a multiple of 32 in [32, 8192]", d->hidden);
+  if (d->inter < 32 || d->inter > 8192 || d->inter % 32)
+    return fail(MOE_ERR_INVALID, "inter=%d must be a multiple of 32 in [32, 8192]", d->inter);
+  if (d->n_experts < 1 || d->n_experts > 1024)
+    return fail(MOE_ERR_INVALID, "n_experts=%d must be in [1, 1024]", d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID, "top_k=%d must be in [1, n_experts=%d]", d->top_k, d->n_experts);
+  if (d->n_shared != 0 && d->n_shared != 1) return fail(MOE_ERR_INVALID, "n_shared=%d must be 0 or 1", d->n_shared);
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GEMM) return fail(MOE_ERR_INVALID, "path=%d unknown", d->path);
+  if (!d->w_router || !d->gate_codes || !d->gate_scales || !d->up_codes || !d->up_scales || !d->down_codes ||
+      !d->down_scales)
+    return fail(MOE_ERR_INVALID, "moe_layer_create: a weight pointer is NULL");
+  if (!aligned16(d->w_router) || !aligned16(d->gate_codes) || !aligned16(d->up_codes) ||
+      !aligned16(d->down_codes))
+    return fail(MOE_ERR_INVALID, "router weights and code arrays must be 16-byte aligned");
+  char arch[64];
+  if (!moe_device_supported(d->device, arch, sizeof(arch)))
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is not a supported gfx950 (%s)", d->device, arch);
+  moe_layer* L = new (std::nothrow) moe_layer;
+  if (!L) return fail(MOE_ERR_ALLOC, "moe_layer_create: out of host memory");
+  L->desc = *d;
+  L->dims = moe::Dims{d->hidden, d->n_experts, d->top_k, d->n_shared, d->inter, d->n_experts + d->n_shared};
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer* layer) { delete layer; }
+
+uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens) {
+  if (!layer || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+  return carve(layer->dims, std::max(max_tokens, 1), nullptr, nullptr);
+}
+
+static int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void* ws, uint64_t ws_bytes,
+                          const char* what) {
+  if (!L) return fail(MOE_ERR_INVALID, "%s: NULL layer", what);
+  if (T < 0 || T > kMaxTokens) return fail(MOE_ERR_INVALID, "%s: tokens=%d out of [0, %d]", what, T, kMaxTokens);
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_ERR_INVALID, "%s: NULL input", what);
+  if (reinterpret_cast<uintptr_t>(x) & 15u) return fail(MOE_ERR_INVALID, "%s: x must be 16-byte aligned", what);
+  const uint64_t need = carve(L->dims, T, nullptr, nullptr);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %p/%llu bytes, need %llu bytes aligned to 256", what, ws,
+                (unsigned long long)ws_bytes, (unsigned long long)need);
+  return MOE_OK;
+}
+
+static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s) {
+  const moe::Dims& d = L->dims;
+  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b.logits, T, s);
+  if (e == hipSuccess) e = T <= moe::kChunk ? moe::launch_route_small(d, b, T, s) : moe::launch_route_chunked(d, b, T, s);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+static void use_route_out(moe::CallBufs& b, const moe_route_out* r) {
+  b.idx = r->idx;
+  b.w = r->weight;
+  b.counts = r->counts;
+  b.offsets = r->offsets;
+  b.perm = r->perm;
+}
+
+static bool route_ok(const moe_route_out* r) {
+  return r && r->idx && r->weight && r->counts && r->offsets && r->perm;
+}
+
+int32_t moe_route(const moe_layer* L, const uint16_t* x, int32_t T, const moe_route_out* route, void* ws,
+                  uint64_t ws_bytes, void* stream) {
+  int32_t st = check_call(L, x, T, ws, ws_bytes, "moe_route");
+  if (st != MOE_OK || T == 0) return st;
+  if (!route_ok(route)) return fail(MOE_ERR_INVALID, "moe_route: every route_out buffer is required");
+  DeviceGuard dg(L->desc.device);
+  if (!dg.ok) return fail(MOE_ERR_HIP, "moe_route: hipSetDevice(%d) failed", L->desc.device);
+  moe::CallBufs b;
+  carve(L->dims, T, static_cast<char*>(ws), &b);
+  use_route_out(b, route);
+  return enqueue_route(L, x, T, b, static_cast<hipStream_t>(stream));
+}
+
+int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
+                    void* ws, uint64_t ws_bytes, void* stream) {
+  int32_t st = check_call(L, x, T, ws, ws_bytes, "moe_forward");
+  if (st != MOE_OK || T == 0) return st;
+  if (!y) return fail(MOE_ERR_INVALID, "moe_forward: NULL output");
+  if (reinterpret_cast<uintptr_t>(y) & 15u) return fail(MOE_ERR_INVALID, "moe_forward: y must be 16-byte aligned");
+  if (route && !route_ok(route)) return fail(MOE_ERR_INVALID, "moe_forward: route_out given with a NULL buffer");
+  DeviceGuard dg(L->desc.device);
+  if (!dg.ok) return fail(MOE_ERR_HIP, "moe_forward: hipSetDevice(%d) failed", L->desc.device);
+  const moe::Dims& d = L->dims;
+  moe::CallBufs b;
+  carve(d, T, static_cast<char*>(ws), &b);
+  if (route) use_route_out(b, route);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_route(L, x, T, b, s);
+  if (st != MOE_OK) return st;
+  const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
+  hipError_t e;
+  if (gemv) {
+    const int na = max_active_of(d, T);
+    e = moe::launch_gemv_gateup(d, L->desc, x, b, T, na, s);
+    if (e == hipSuccess) e = moe::launch_gemv_down(d, L->desc, b, T, na, s);
+  } else {
+    const int mb = mt_bound_of(d, T);
+    e = moe::launch_gemm_gateup(d, L->desc, x, b, T, mb, s);
+    if (e == hipSuccess) e = moe::launch_gemm_down(d, L->desc, b, T, mb, s);
+  }
+  if (e == hipSuccess) e = moe::launch_combine(d, b, y, T, s);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_forward: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int32_t moe_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_tenabled = on != 0;
+  return MOE_OK;
+}
+
+int32_t moe_timing_read(const char** names, int64_t* launches, double* total_ms, int32_t cap) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  drain_timing_locked();
+  int32_t i = 0;
+  for (auto& kv : g_tacc) {
+    if (i < cap) {
+      if (names) names[i] = kv.second.name;
+      if (launches) launches[i] = kv.second.launches;
+      if (total_ms) total_ms[i] = kv.second.ms;
+    }
+    ++i;
+  }
+  return i;
+}
+
+void moe_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  drain_timing_locked();
+  g_tacc.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal declarations shared by the HIP sources of the MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;        // tokens per routing chunk (one bit per token in a 64-bit mask)
+constexpr int kGemmBM = 64;       // grouped-GEMM rows per M-tile
+constexpr int kGemmBN = 64;       // grouped-GEMM output columns per workgroup
+
+// e8m0 scale byte -> float32 with bit pattern s << 23 (s = 0 gives +0, s = 255 gives +inf).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
+// Eight e2m1 codes (one dword; byte q holds elements 2q and 2q+1) -> four bf16 pairs / four
+// fp32 pairs, each value multiplied by `scale` by the gfx950 scaled FP4 converts.
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t v, float scale, bf16x2 out[4]) {
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+}
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float scale, f32x2 out[4]) {
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 1);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 2);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 3);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Token of grouped row r: routed rows carry t*k+j in perm; the shared expert's rows
+// (r >= T*k) are the tokens in order.
+__device__ __forceinline__ int row_token(const int32_t* perm, int r, int tk, int k) {
+  return r < tk ? perm[r] / k : r - tk;
+}
+
+struct Dims {
+  int H, E, K, S, I, G;  // hidden, experts, top-k, shared, inter, groups = E + S
+};
+
+// Device buffers of one call, carved from the workspace (and the caller's route buffers).
+struct CallBufs {
+  float* logits;      // [T][E]
+  int32_t* idx;       // [T][k]
+  float* w;           // [T][k]
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* perm;      // [T*k]
+  uint64_t* gmask;    // [C][E] per-chunk token masks
+  int32_t* cbase;     // [C][E] rows of expert e in chunks before c
+  int32_t* grp_row0;  // [G] first grouped row of group g
+  int32_t* grp_rows;  // [G] rows of group g
+  int32_t* act;       // [G] groups with rows, ascending, shared last
+  int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles
+  int32_t* mt_group;  // [mt_bound]
+  int32_t* mt_row0;   // [mt_bound]
+  void* h;            // [T(k+S)][I] fp32 (GEMV path) or bf16 (GEMM path)
+  float* staging;     // [T(k+S)][H] weighted expert outputs, slot-indexed
+};
+
+// ---- kernel timing hooks (api.hip) --------------------------------------------------
+int timing_begin(const char* name, hipStream_t s);
+void timing_end(int token, hipStream_t s);
+
+// ---- launchers (return hipGetLastError of the launch) ---------------------------------
+hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
+                                float* logits, int T, hipStream_t s);
+hipError_t launch_route_small(const Dims& d, const CallBufs& b, int T, hipStream_t s);
+hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
+
+hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
+                              int T, int max_act, hipStream_t s);
+hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
+                            hipStream_t s);
+hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
+                              int T, int mt_bound, hipStream_t s);
+hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
+                            hipStream_t s);
+hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,157 @@
+"""Python face of the C ABI: torch tensors in, device pointers and sizes out.
+
+Every step of the layer runs in the HIP library; this module only checks tensor
+shapes/dtypes, allocates outputs and the workspace with torch, and passes pointers
+and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_PATHS = {"auto": _lib.MOE_PATH_AUTO, "gemv": _lib.MOE_PATH_GEMV, "gemm": _lib.MOE_PATH_GEMM}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def device_supported(device: int = 0):
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(64)
+    ok = lib.moe_device_supported(device, buf, 64)
+    return bool(ok), buf.value.decode()
+
+
+class MoeLayer:
+    """One routed FP4-expert MoE layer over borrowed device weights.
+
+    ``gate``/``up``/``down`` are (codes, scales) uint8 CUDA tensors shaped
+    [E+S][N][K/2] and [E+S][N][K/32]; the library keeps only their pointers, so
+    this object holds references to keep them alive.
+    """
+
+    def __init__(self, w_router: torch.Tensor, gate, up, down, top_k: int, n_shared: int = 1,
+                 router_bias: Optional[torch.Tensor] = None, path: str = "auto"):
+        self.lib = _lib.load()
+        e, h = w_router.shape
+        g, inter, hk = gate[0].shape
+        if g != e + n_shared or hk * 2 != h:
+            raise ValueError(f"gate codes {tuple(gate[0].shape)} do not match E={e}, S={n_shared}, H={h}")
+        for name, (c, s), n, k in (("gate", gate, inter, h), ("up", up, inter, h), ("down", down, h, inter)):
+            if tuple(c.shape) != (g, n, k // 2) or tuple(s.shape) != (g, n, k // 32):
+                raise ValueError(f"{name} weights: codes {tuple(c.shape)} / scales {tuple(s.shape)}, "
+                                 f"expected {(g, n, k // 2)} / {(g, n, k // 32)}")
+            if c.dtype != torch.uint8 or s.dtype != torch.uint8 or not c.is_cuda or not s.is_cuda:
+                raise ValueError(f"{name} weights must be uint8 CUDA tensors")
+            if not c.is_contiguous() or not s.is_contiguous():
+                raise ValueError(f"{name} weights must be contiguous")
+        if w_router.dtype != torch.float32 or not w_router.is_cuda or not w_router.is_contiguous():
+            raise ValueError("w_router must be a contiguous float32 CUDA tensor")
+        if router_bias is not None and (router_bias.dtype != torch.float32 or router_bias.numel() != e
+                                        or not router_bias.is_cuda):
+            raise ValueError("router_bias must be a float32 CUDA tensor of E values")
+        self.hidden, self.n_experts, self.top_k, self.n_shared, self.inter = h, e, top_k, n_shared, inter
+        self.device = w_router.device
+        self._keep = (w_router, gate, up, down, router_bias)
+        desc = _lib.LayerDesc(
+            abi_version=_lib.MOE_ABI_VERSION, hidden=h, n_experts=e, top_k=top_k, n_shared=n_shared,
+            inter=inter, path=_PATHS[path], device=w_router.device.index or 0,
+            w_router=_ptr(w_router), router_bias=_ptr(router_bias),
+            gate_codes=_ptr(gate[0]), gate_scales=_ptr(gate[1]), up_codes=_ptr(up[0]),
+            up_scales=_ptr(up[1]), down_codes=_ptr(down[0]), down_scales=_ptr(down[1]))
+        handle = ctypes.c_void_p()
+        _lib.check(self.lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(handle)), self.lib)
+        self._h = handle
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.moe_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -------------------------------------------------------------------------------
+    def workspace_bytes(self, max_tokens: int) -> int:
+        return int(self.lib.moe_workspace_bytes(self._h, max_tokens))
+
+    def workspace(self, max_tokens: int) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(max_tokens), dtype=torch.uint8, device=self.device)
+
+    def route_buffers(self, tokens: int) -> dict:
+        d, k, e = self.device, self.top_k, self.n_experts
+        return dict(idx=torch.empty((tokens, k), dtype=torch.int32, device=d),
+                    weight=torch.empty((tokens, k), dtype=torch.float32, device=d),
+                    counts=torch.empty(e, dtype=torch.int32, device=d),
+                    offsets=torch.empty(e + 1, dtype=torch.int32, device=d),
+                    perm=torch.empty(tokens * k, dtype=torch.int32, device=d))
+
+    @staticmethod
+    def _route_struct(r: dict) -> _lib.RouteOut:
+        return _lib.RouteOut(idx=_ptr(r["idx"]), weight=_ptr(r["weight"]), counts=_ptr(r["counts"]),
+                             offsets=_ptr(r["offsets"]), perm=_ptr(r["perm"]))
+
+    def _check_x(self, x: torch.Tensor) -> int:
+        if x.dim() != 2 or x.shape[1] != self.hidden or x.element_size() != 2 or not x.is_cuda:
+            raise ValueError(f"x must be a [T][{self.hidden}] bf16 CUDA tensor")
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous")
+        return x.shape[0]
+
+    def route(self, x: torch.Tensor, workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+              stream=None) -> dict:
+        t = self._check_x(x)
+        out = out if out is not None else self.route_buffers(t)
+        ws = workspace if workspace is not None else self.workspace(t)
+        rs = self._route_struct(out)
+        _lib.check(self.lib.moe_route(self._h, _ptr(x), t, ctypes.byref(rs), _ptr(ws), ws.numel(),
+                                      _stream_handle(stream)), self.lib)
+        return out
+
+    def forward(self, x: torch.Tensor, workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                route: Optional[dict] = None, stream=None) -> torch.Tensor:
+        t = self._check_x(x)
+        if y is None:
+            y = torch.empty((t, self.hidden), dtype=torch.float32, device=self.device)
+        ws = workspace if workspace is not None else self.workspace(t)
+        rs = self._route_struct(route) if route is not None else None
+        _lib.check(self.lib.moe_forward(self._h, _ptr(x), t, _ptr(y), ctypes.byref(rs) if rs is not None else None,
+                                        _ptr(ws), ws.numel(), _stream_handle(stream)), self.lib)
+        return y
+
+    __call__ = forward
+
+
+# ---- kernel timing ---------------------------------------------------------------------
+
+def timing_enable(on: bool = True):
+    _lib.load().moe_timing_enable(1 if on else 0)
+
+
+def timing_reset():
+    _lib.load().moe_timing_reset()
+
+
+def timing_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last reset (waits for the recorded events)."""
+    lib = _lib.load()
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    launches = (ctypes.c_int64 * cap)()
+    ms = (ctypes.c_double * cap)()
+    n = lib.moe_timing_read(names, launches, ms, cap)
+    return {names[i].decode(): (int(launches[i]), float(ms[i])) for i in range(min(n, cap))}

@@ -1,0 +1,158 @@
+/*
+ * moe.h -- C ABI of the routed FP4-expert MoE layer for AMD Instinct MI355X (gfx950).
+ *
+ * The header includes only <stdint.h> and the caller drives the library, never the
+ * other way round: the same shape as the kernel tier on "DeepSeek V4: the CUDA
+ * kernels, as a tier rather than an engine" (PR #772, "Why it works as a tier").
+ * The caller owns device memory and streams; the library enqueues kernels.
+ *
+ * The layer (for T tokens of width H, E routed experts, top-k, S shared experts, expert
+ * width I):
+ *   1. router scores   l[t,e] = sum_h x[t,h] * w_router[e,h] + router_bias[e]   (fp32)
+ *   2. top-k per token (score descending, ties to the lower expert index) and weights
+ *      w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected scores
+ *   3. rows grouped by expert: counts[e], offsets[e] (exclusive scan, offsets[E] = T*k),
+ *      perm[r] = t*k + j for the pair at grouped row r, ascending token within an expert
+ *   4. per expert, SwiGLU with FP4 weights dequantised on the fly:
+ *      h = silu(x Wg^T) * (x Wu^T),  y_e = h Wd^T
+ *   5. the shared expert (S = 1) on every token with weight 1
+ *   6. y[t] = y_shared[t] + sum_j w[t,j] * y_{idx[t,j]}[t]
+ * Steps 1-3 follow "feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine"
+ * (PR #1055, "What it is": prefill routes on the device into expert-grouped GEMM rows;
+ * decode fuses routed and shared experts).  Step 4's format follows "Add DeepSeek V4 Flash
+ * CPU inference with NVMe expert streaming" (PR #165): FP4 E2M1 values with one UE8M0
+ * scale per group of 32 along the reduction axis.
+ *
+ * Weight layout (device memory, row-major, group g in [0, E+S); the shared expert is
+ * group E):
+ *   gate_codes, up_codes   uint8 [E+S][I][H/2]   low nibble = element 2i, high = 2i+1
+ *   gate_scales, up_scales uint8 [E+S][I][H/32]  scale j covers elements 32j..32j+31
+ *   down_codes             uint8 [E+S][H][I/2]
+ *   down_scales            uint8 [E+S][H][I/32]
+ * An e8m0 byte s means the float32 with bit pattern s << 23 (s = 0 is +0, s = 255 is
+ * +inf), as "DeepSeek V4: the CUDA kernels, as a tier rather than an engine" (PR #772)
+ * describes for the MXFP4 decode.
+ *
+ * Errors: every entry point returns a status (MOE_OK = 0).  Argument errors are reported
+ * before anything is enqueued; launch errors are read back with hipGetLastError right after
+ * the launches; a device fault surfaces at the caller's next synchronisation.  No C++
+ * exception crosses this boundary.  moe_last_error() gives a message for the calling
+ * thread's last failure, so a caller can log the reason and fall back (the per-stage
+ * fallback convention of PR #1055).
+ */
+#ifndef MOE_FP4_MOE_H
+#define MOE_FP4_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* NULL pointer, bad size, inconsistent descriptor */
+  MOE_ERR_UNSUPPORTED = 2,  /* no device, device is not gfx950, ABI version mismatch */
+  MOE_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_ALLOC = 5         /* the library could not allocate its own small metadata */
+};
+
+/* Execution path for the expert products.  AUTO picks by token count: the FP4 GEMV
+ * kernels (decode: HBM-bound, few rows per expert) or the FP4 grouped GEMM on bf16
+ * MFMA (prefill).  The two others force one path (A/B testing, the kill-switch pattern
+ * of PR #165's AVX2 series). */
+enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
+
+/* Layer description.  All pointers are device pointers on `device`.  The library BORROWS
+ * them: the caller keeps them alive and unchanged until moe_layer_destroy. */
+typedef struct moe_layer_desc {
+  int32_t abi_version;   /* must be MOE_ABI_VERSION */
+  int32_t hidden;        /* H: multiple of 32, 32..8192 */
+  int32_t n_experts;     /* E: 1..1024 */
+  int32_t top_k;         /* k: 1..E */
+  int32_t n_shared;      /* S: 0 or 1 */
+  int32_t inter;         /* I: multiple of 32, 32..8192 */
+  int32_t path;          /* enum moe_path */
+  int32_t device;        /* HIP device ordinal holding the weights */
+  const float* w_router;       /* fp32 [E][H] */
+  const float* router_bias;    /* fp32 [E], or NULL for no bias */
+  const uint8_t* gate_codes;   /* see layout above */
+  const uint8_t* gate_scales;
+  const uint8_t* up_codes;
+  const uint8_t* up_scales;
+  const uint8_t* down_codes;
+  const uint8_t* down_scales;
+} moe_layer_desc;
+
+/* Routing results (device pointers), written by moe_route / moe_forward. */
+typedef struct moe_route_out {
+  int32_t* idx;      /* [T][k] expert of slot j of token t, score-descending */
+  float* weight;     /* [T][k] renormalised softmax weight of that slot */
+  int32_t* counts;   /* [E] rows per expert */
+  int32_t* offsets;  /* [E+1] exclusive scan of counts; offsets[E] = T*k */
+  int32_t* perm;     /* [T*k] t*k+j at grouped row r, ascending t within an expert */
+} moe_route_out;
+
+typedef struct moe_layer moe_layer;
+
+/* MOE_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+/* 1 if HIP device `device` is a gfx950 the library was built for, else 0.  Writes the
+ * device's architecture name (or a reason) into name[0..cap-1], NUL-terminated, when
+ * name is not NULL and cap > 0. */
+int32_t moe_device_supported(int32_t device, char* name, int32_t cap);
+
+/* Validate `desc`, check the device, and create a layer.  On success *out is a new layer
+ * (destroy with moe_layer_destroy); on failure *out is NULL and nothing is leaked.
+ * Enqueues no work.  A layer is immutable after creation: concurrent calls on different
+ * streams are safe when each uses its own workspace. */
+int32_t moe_layer_create(const moe_layer_desc* desc, moe_layer** out);
+
+/* Free the layer's own metadata (never the borrowed weights).  NULL is a no-op.  The
+ * caller must have synchronised every stream that used the layer. */
+void moe_layer_destroy(moe_layer* layer);
+
+/* Bytes of device workspace one call with up to max_tokens tokens needs (0 on bad
+ * arguments).  The caller allocates and owns it; it must be 256-byte aligned. */
+uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens);
+
+/* Steps 1-3 for x (bf16 bit patterns, device, [T][H]) into `route` (all five pointers
+ * required).  Asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ * T = 0 is a no-op.  No host synchronisation. */
+int32_t moe_route(const moe_layer* layer, const uint16_t* x, int32_t tokens,
+                  const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
+                  void* stream);
+
+/* The whole layer: y (fp32, device, [T][H]; must not overlap x or the workspace) for x
+ * (bf16 bit patterns, device, [T][H]).  If `route` is not NULL its five buffers receive
+ * the routing (as moe_route); if NULL the routing stays in the workspace.  Asynchronous
+ * on `stream`; T = 0 is a no-op; no host synchronisation. */
+int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, float* y,
+                    const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
+                    void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(int32_t status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* ---- kernel timing (measurement support) ------------------------------------------
+ * While enabled, every kernel the library launches is bracketed by a pair of HIP events
+ * recorded on the stream it runs on.  moe_timing_read waits for those events and returns,
+ * per kernel name, the launch count and summed duration since the last reset.  Process
+ * wide; not meant to be toggled while other threads call the library. */
+int32_t moe_timing_enable(int32_t on);
+/* Number of distinct kernel names recorded; fills up to `cap` entries. names[i] points to
+ * static strings. */
+int32_t moe_timing_read(const char** names, int64_t* launches, double* total_ms, int32_t cap);
+void moe_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP4_MOE_H */

@@ -1,0 +1,107 @@
+"""Helpers for the GPU parity tests: build layers on the device, run them, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import moe_synth as synth
+import oracle
+
+REL_L2_TOL = 5e-3          # relative L2 error of y
+MAX_ABS_OVER_RMS_TOL = 2e-2  # max |dy| relative to rms(y_ref)
+WEIGHT_TOL = 2e-6          # routing weights (fp32 softmax vs fp64)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def require_gpu():
+    import fp4_routed_expert_moe_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    m.load_library()
+    ok, arch = m.device_supported(0)
+    assert ok, f"device 0 is {arch}, not gfx950"
+
+
+def stack_groups(groups, device="cuda"):
+    """List of per-group dicts (numpy codes/scales) -> dict mat -> (codes, scales) device tensors."""
+    out = {}
+    for mat in synth.MATRICES:
+        c = np.stack([g[mat][0] for g in groups])
+        s = np.stack([g[mat][1] for g in groups])
+        out[mat] = (torch.from_numpy(c).to(device).contiguous(), torch.from_numpy(s).to(device).contiguous())
+    return out
+
+
+def make_layer(w_router, weights, top_k, n_shared, bias=None, path="auto"):
+    from fp4_routed_expert_moe_amd import MoeLayer
+    wr = torch.from_numpy(np.ascontiguousarray(w_router, dtype=np.float32)).cuda()
+    b = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32)).cuda()
+    return MoeLayer(wr, weights["gate"], weights["up"], weights["down"], top_k, n_shared, b, path)
+
+
+def x_to_device(x_bits):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+
+
+def run_layer(layer, x_bits, workspace=None):
+    x = x_to_device(x_bits)
+    route = layer.route_buffers(x.shape[0])
+    y = layer.forward(x, workspace=workspace, route=route)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in route.items()}
+    out["y"] = y.cpu().numpy()
+    return out
+
+
+def check_routing(got, ref):
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["perm"], ref["perm"])
+    np.testing.assert_allclose(got["weight"], ref["w"], rtol=0, atol=WEIGHT_TOL)
+
+
+def output_error(y, y_ref):
+    y = np.asarray(y, dtype=np.float64)
+    d = y - y_ref
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    nref = float(np.linalg.norm(y_ref))
+    return dict(rel_l2=float(np.linalg.norm(d)) / nref if nref else float(np.linalg.norm(d)),
+                max_abs=float(np.abs(d).max()) if d.size else 0.0, rms_ref=rms,
+                max_over_rms=float(np.abs(d).max()) / rms if rms else float(np.abs(d).max()),
+                max_ref=float(np.abs(y_ref).max()) if d.size else 0.0)
+
+
+def check_outputs(y, y_ref, what=""):
+    if y_ref.size == 0:
+        return {}
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    e = output_error(y, y_ref)
+    say(f"  {what}: rel_l2={e['rel_l2']:.3e} max_abs={e['max_abs']:.3e} "
+        f"max/rms={e['max_over_rms']:.3e} rms_ref={e['rms_ref']:.3e}")
+    if e["rms_ref"] == 0:
+        assert e["max_abs"] == 0
+        return e
+    assert e["rel_l2"] <= REL_L2_TOL, e
+    assert e["max_over_rms"] <= MAX_ABS_OVER_RMS_TOL, e
+    return e
+
+
+def oracle_routing(x_bits, w_router, bias, top_k):
+    logits = oracle.router_logits(x_bits, w_router, bias)
+    idx, w, _ = oracle.select_experts(logits, top_k)
+    counts, offsets, perm = oracle.group_rows(idx, np.asarray(w_router).shape[0])
+    return dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm)
+
+
+def check_device_weights(wl, layer, weights, groups):
+    """Device-generated weights equal the host generator's bytes for the given groups."""
+    for g in groups:
+        for mat in synth.MATRICES:
+            c, s = synth.expert_matrix(wl, layer, mat, g)
+            assert torch.equal(weights[mat][0][g].cpu(), c), (mat, g)
+            assert torch.equal(weights[mat][1][g].cpu(), s), (mat, g)

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP layer against the float64 oracle on the same seeded inputs.
+
+Routing (idx, counts, offsets, perm) must match bit for bit; weights within 2e-6; outputs
+within rel-L2 5e-3 and max|dy| <= 2e-2 * rms(y_ref).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as synth
+import oracle
+from helpers import random_experts, screened_tokens, identity_experts
+from gpu_util import (check_device_weights, check_outputs, check_routing, make_layer, oracle_routing,
+                      require_gpu, run_layer, say, stack_groups, x_to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _random_case(seed, hidden, experts, top_k, shared, inter, tokens, bias=False, scale_lo=123, scale_hi=127):
+    rng = np.random.default_rng(seed)
+    groups = random_experts(rng, hidden, inter, experts + shared, scale_lo, scale_hi)
+    wr = (0.02 * rng.standard_normal((experts, hidden))).astype(np.float32)
+    b = (rng.standard_normal(experts)).astype(np.float32) if bias else None
+    wl = synth.custom_workload(f"case{seed}", hidden, experts, top_k, shared, inter, tokens)
+    x = screened_tokens(wl, wr, b)
+    return groups, wr, b, x
+
+
+def _check_case(groups, wr, b, x, top_k, shared, paths=("gemv", "gemm"), what=""):
+    ref = oracle.moe_forward(x, wr, b, groups, top_k, shared)
+    weights = stack_groups(groups)
+    outs = {}
+    for path in paths:
+        layer = make_layer(wr, weights, top_k, shared, b, path)
+        got = run_layer(layer, x)
+        check_routing(got, ref)
+        check_outputs(got["y"], ref["y"], f"{what} path={path}")
+        outs[path] = got
+    return outs
+
+
+# ------------------------------------------------------------------------------- tiny
+
+
+def test_tiny_workload_both_paths():
+    wl = synth.WORKLOADS["tiny"]
+    weights = synth.layer_weights(wl, 0, device="cuda")
+    check_device_weights(wl, 0, weights, range(wl.groups))
+    wr = synth.router_weights(wl)
+    x = screened_tokens(wl, wr, None)
+    ref = oracle.moe_forward(x, wr, None, synth.LazyExperts(wl, 0, cache=wl.groups), wl.top_k, wl.shared)
+    for path in ("auto", "gemv", "gemm"):
+        got = run_layer(make_layer(wr, weights, wl.top_k, wl.shared, None, path), x)
+        check_routing(got, ref)
+        check_outputs(got["y"], ref["y"], f"tiny path={path}")
+
+
+def test_identity_experts_closed_form_on_gpu():
+    hidden, inter, experts, k = 128, 64, 6, 2
+    rng = np.random.default_rng(0)
+    sigma = [g + 1 for g in range(experts)] + [0]
+    groups = identity_experts(hidden, inter, experts, 1, sigma)
+    wr = (0.3 * rng.standard_normal((experts, hidden))).astype(np.float32)
+    wl = synth.custom_workload("ident", hidden, experts, k, 1, inter, 5)
+    x = screened_tokens(wl, wr, None)
+    _check_case(groups, wr, None, x, k, 1, what="identity")
+
+
+@pytest.mark.parametrize("case", [
+    # (seed, H, E, k, S, I, T)  multi-tile, ragged tails, several routing chunks
+    (1, 512, 16, 4, 1, 256, 100),
+    (2, 256, 32, 6, 1, 128, 129),
+    (3, 96, 5, 2, 1, 32, 7),        # H, I not multiples of 64; E < 64
+    (4, 1024, 64, 8, 0, 512, 33),   # no shared expert
+    (5, 288, 70, 3, 1, 160, 65),    # E not a multiple of 64
+])
+def test_random_shapes_both_paths(case):
+    seed, hidden, experts, k, shared, inter, tokens = case
+    groups, wr, b, x = _random_case(seed, hidden, experts, k, shared, inter, tokens, bias=seed % 2 == 0)
+    _check_case(groups, wr, b, x, k, shared, what=f"case{case}")
+
+
+def test_top_k_equals_all_experts():
+    groups, wr, b, x = _random_case(6, 128, 8, 8, 1, 64, 20)
+    _check_case(groups, wr, b, x, 8, 1, what="k=E")
+
+
+def test_every_token_on_one_expert():
+    rng = np.random.default_rng(8)
+    hidden, experts, k, inter, tokens = 256, 16, 2, 128, 150
+    groups = random_experts(rng, hidden, inter, experts + 1)
+    wr = (0.02 * rng.standard_normal((experts, hidden))).astype(np.float32)
+    b = np.zeros(experts, np.float32)
+    b[11] = 50.0                                     # expert 11 always first
+    wl = synth.custom_workload("onehot", hidden, experts, k, 1, inter, tokens)
+    x = screened_tokens(wl, wr, b)
+    outs = _check_case(groups, wr, b, x, k, 1, what="hot expert")
+    assert outs["gemm"]["counts"][11] == tokens
+
+
+def test_zero_and_extreme_scales():
+    # s=0 blocks contribute exactly zero; scales far from 1 stay exact in bf16/fp32
+    groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=112, scale_hi=134)
+    for g in groups[::2]:
+        g["gate"][1][:, 0] = 0
+        g["down"][1][5, :] = 0
+    _check_case(groups, wr, b, x, 2, 1, what="scales")
+
+
+def test_single_token_and_batch_equals_single():
+    groups, wr, b, x = _random_case(10, 512, 32, 4, 1, 256, 12)
+    weights = stack_groups(groups)
+    for path in ("gemv", "gemm"):
+        layer = make_layer(wr, weights, 4, 1, b, path)
+        full = run_layer(layer, x)
+        for t in (0, 5, 11):
+            one = run_layer(layer, x[t:t + 1])
+            np.testing.assert_array_equal(one["idx"][0], full["idx"][t])
+            np.testing.assert_array_equal(one["y"][0], full["y"][t])
+
+
+def test_zero_tokens_is_a_noop():
+    groups, wr, b, x = _random_case(11, 128, 8, 2, 1, 64, 4)
+    layer = make_layer(wr, stack_groups(groups), 2, 1, b)
+    y = torch.full((0, 128), 7.0, device="cuda")
+    out = layer.forward(torch.empty((0, 128), dtype=torch.int16, device="cuda"), y=y,
+                        workspace=layer.workspace(1))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+
+
+def test_route_call_matches_forward_routing():
+    groups, wr, b, x = _random_case(12, 256, 32, 6, 1, 128, 200)
+    layer = make_layer(wr, stack_groups(groups), 6, 1, b)
+    xd = x_to_device(x)
+    r1 = layer.route(xd)
+    r2 = layer.route_buffers(xd.shape[0])
+    layer.forward(xd, route=r2)
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_deterministic_repeat():
+    groups, wr, b, x = _random_case(13, 512, 16, 4, 1, 256, 80)
+    layer = make_layer(wr, stack_groups(groups), 4, 1, b, "gemm")
+    a = run_layer(layer, x)
+    c = run_layer(layer, x)
+    np.testing.assert_array_equal(a["y"], c["y"])
+
+
+def test_workspace_errors():
+    from fp4_routed_expert_moe_amd import MoeError
+    groups, wr, b, x = _random_case(14, 128, 8, 2, 1, 64, 10)
+    layer = make_layer(wr, stack_groups(groups), 2, 1, b)
+    xd = x_to_device(x)
+    small = torch.empty(layer.workspace_bytes(10) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(MoeError) as ei:
+        layer.forward(xd, workspace=small)
+    assert ei.value.status == 3
+    assert layer.workspace_bytes(10) <= layer.workspace_bytes(11)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+
+def _full_size(name, sample_tokens, layer_index=0, bias=True):
+    wl = synth.WORKLOADS[name]
+    say(f"[{name}] generating weights on the GPU")
+    weights = synth.layer_weights(wl, layer_index, device="cuda")
+    torch.cuda.synchronize()
+    check_device_weights(wl, layer_index, weights, [0, 97, wl.experts])
+    wr = synth.router_weights(wl, layer_index)
+    b = synth.router_bias(wl)
+    x = screened_tokens(wl, wr, b, layer=layer_index)
+    layer = make_layer(wr, weights, wl.top_k, wl.shared, b)
+    say(f"[{name}] GPU forward T={x.shape[0]}")
+    got = run_layer(layer, x)
+    ref_route = oracle_routing(x, wr, b, wl.top_k)
+    check_routing(got, ref_route)
+    sample = np.linspace(0, x.shape[0] - 1, min(sample_tokens, x.shape[0])).astype(int)
+    say(f"[{name}] oracle on {len(sample)} sampled tokens")
+    ref = oracle.moe_forward(x[sample], wr, b, synth.LazyExperts(wl, layer_index, cache=4), wl.top_k, wl.shared)
+    check_outputs(got["y"][sample], ref["y"], name)
+    return got, layer, x
+
+
+def test_decode_batch_full_size():
+    _full_size("decode_t8", 8)
+
+
+def test_prefill_512_full_size():
+    _full_size("prefill_t512", 6)
+
+
+def test_prefill_4096_zipf_full_size():
+    got, _, _ = _full_size("prefill_t4096_zipf", 6)
+    assert got["counts"].max() > 0.10 * got["idx"].size
+
+
+def test_stacked_decode_16_layers():
+    wl = synth.WORKLOADS["stacked_decode_16l"]
+    layers, routers = [], []
+    for l in range(wl.layers):
+        weights = synth.layer_weights(wl, l, device="cuda")
+        wr = synth.router_weights(wl, l)
+        layers.append((make_layer(wr, weights, wl.top_k, wl.shared), weights))
+        routers.append(wr)
+    torch.cuda.synchronize()
+    check_device_weights(wl, 15, layers[15][1], [3])
+    say("[stacked] 16 layers resident")
+    steps = wl.steps
+    xs = {}
+    ws = layers[0][0].workspace(1)
+    ys, routes = {}, {}
+    for s in range(steps):
+        for l in range(wl.layers):
+            x = screened_tokens(wl, routers[l], None, layer=l, step=s)
+            xs[(s, l)] = x
+            layer = layers[l][0]
+            r = layer.route_buffers(1)
+            ys[(s, l)] = layer.forward(x_to_device(x), workspace=ws, route=r)
+            routes[(s, l)] = r
+        if s % 64 == 0:
+            say(f"[stacked] step {s}")
+    torch.cuda.synchronize()
+    for (s, l), r in routes.items():
+        ref = oracle_routing(xs[(s, l)], routers[l], None, wl.top_k)
+        got = {k: v.cpu().numpy() for k, v in r.items()}
+        check_routing(got, ref)
+    for (s, l) in [(0, 0), (17, 5), (128, 9), (255, 15)]:
+        ref = oracle.moe_forward(xs[(s, l)], routers[l], None, synth.LazyExperts(wl, l, cache=2), wl.top_k,
+                                 wl.shared)
+        check_outputs(ys[(s, l)].cpu().numpy(), ref["y"], f"stacked step={s} layer={l}")
