@@ -63,7 +63,9 @@ def main():
     nl = max(1, min(args.layers, wl.layers if wl.layers > 1 else args.layers))
     layers, keep = [], []
     for l in range(nl):
-        w = synth.layer_weights(wl, l, device=dev)
+        raw = synth.layer_weights(wl, l, device=dev)          # checkpoint layout
+        w = {m: moe.pack_fp4(*raw[m]) for m in synth.MATRICES}  # kernel layout, packed once
+        del raw
         wr = torch.from_numpy(synth.router_weights(wl, l)).to(dev)
         b = synth.router_bias(wl)
         bt = None if b is None else torch.from_numpy(b).to(dev)

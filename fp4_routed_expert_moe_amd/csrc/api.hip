@@ -322,6 +322,29 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   return MOE_OK;
 }
 
+int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
+                     int32_t groups, int32_t rows, int32_t cols, void* stream) {
+  if (!codes_in || !scales_in || !codes_out || !scales_out)
+    return fail(MOE_ERR_INVALID, "moe_pack_fp4: NULL pointer");
+  if (groups < 1 || rows < 1 || cols < 32 || cols % 32)
+    return fail(MOE_ERR_INVALID, "moe_pack_fp4: groups=%d rows=%d cols=%d (cols must be a positive multiple of 32)",
+                groups, rows, cols);
+  if (!aligned16(codes_in) || !aligned16(codes_out))
+    return fail(MOE_ERR_INVALID, "moe_pack_fp4: code arrays must be 16-byte aligned");
+  const size_t cb = (size_t)groups * rows * (cols / 2), sb = (size_t)groups * rows * (cols / 32);
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+  };
+  if (overlap(codes_in, cb, codes_out, cb) || overlap(scales_in, sb, scales_out, sb))
+    return fail(MOE_ERR_INVALID, "moe_pack_fp4: output overlaps input");
+  const hipError_t e = moe::launch_pack(codes_in, scales_in, codes_out, scales_out, groups, rows, cols,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_pack_fp4: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 int32_t moe_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_tenabled = on != 0;

@@ -13,6 +13,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
+// Read-only views in the constant address space: uniform loads through them become scalar
+// loads (SGPRs), which is how a value shared by every lane of a wave is best fetched.
+typedef const __attribute__((address_space(4))) uint32_t c_u32;
+typedef const __attribute__((address_space(4))) float c_f32;
+
 constexpr int kWave = 64;
 constexpr int kChunk = 64;        // tokens per routing chunk (one bit per token in a 64-bit mask)
 constexpr int kGemmBM = 64;       // grouped-GEMM rows per M-tile
@@ -87,6 +92,8 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
                               int T, int mt_bound, hipStream_t s);
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s);
+hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
+                       int groups, int N, int K, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s);
 
 }  // namespace moe

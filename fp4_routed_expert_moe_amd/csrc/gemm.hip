@@ -10,7 +10,9 @@
 // * Weights never touch LDS: the 16x16x32 bf16 MFMA's B operand for one lane is 8
 //   consecutive K values of one weight row, i.e. 4 bytes of e2m1 codes plus that row's e8m0
 //   scale, so each lane loads one dword and converts it with the gfx950 scaled FP4->bf16
-//   converts.  Every dequantised product is exact (e2m1 * 2^(s-127) has 2 significant bits).
+//   converts.  In the block-interleaved kernel layout (pack.hip) a wave's 64 dwords are 256
+//   contiguous bytes.  Every dequantised product is exact (e2m1 * 2^(s-127) has 2
+//   significant bits).
 // * Epilogues: SwiGLU into bf16 h (gate/up); weight * y into the slot-indexed staging rows
 //   (down).
 #include "common.h"
@@ -21,11 +23,13 @@ constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64, LDA = BK + 8;  // LDS row pit
 
 __device__ __forceinline__ float silu_g(float g) { return g / (1.0f + expf(-g)); }
 
-// 8 consecutive K values (k % 8 == 0) of one weight row as scaled bf16.
-__device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* __restrict__ codes_row,
-                                              const uint8_t* __restrict__ scales_row, int k) {
-  const uint32_t c = *reinterpret_cast<const uint32_t*>(codes_row + (k >> 1));
-  const float s = e8m0_to_f32(scales_row[k >> 5]);
+// 8 consecutive K values (k % 8 == 0) of one weight row as scaled bf16.  codes_col/scales_col
+// point at block 0 of the row in the kernel layout; block kb is N chunks further.
+__device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* __restrict__ codes_col,
+                                              const uint8_t* __restrict__ scales_col, size_t N, int k) {
+  const size_t kb = (size_t)(k >> 5);
+  const uint32_t c = *reinterpret_cast<const uint32_t*>(codes_col + kb * N * 16 + ((k & 31) >> 1));
+  const float s = e8m0_to_f32(scales_col[kb * N]);
   bf16x2 p[4];
   fp4x8_to_bf16(c, s, p);
   bf16x8 r;
@@ -48,19 +52,19 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(
     const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint16_t* __restrict__ hout,
     int T, int k, int H, int I) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  const int mt = blockIdx.y;
+  const int mt = blockIdx.x;
   if (mt >= info[1]) return;
   const int g = mt_group[mt], m0 = mt_row0[mt];
   const int rows = grp_rows[g], row0 = grp_row0[g];
   const int tk = T * k;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ncol = blockIdx.x * BN + wave * 16 + (lane & 15);
+  const int ncol = blockIdx.y * BN + wave * 16 + (lane & 15);
   const bool col_ok = ncol < I;
-  const size_t wrow = (size_t)g * I + (col_ok ? ncol : I - 1);
-  const uint8_t* gcr = gc + wrow * (H >> 1);
-  const uint8_t* gsr = gs + wrow * (H >> 5);
-  const uint8_t* ucr = uc + wrow * (H >> 1);
-  const uint8_t* usr = us + wrow * (H >> 5);
+  const size_t col = (size_t)g * (H >> 5) * I + (col_ok ? ncol : I - 1);
+  const uint8_t* gcr = gc + col * 16;
+  const uint8_t* gsr = gs + col;
+  const uint8_t* ucr = uc + col * 16;
+  const uint8_t* usr = us + col;
   // activation loader: 64 rows x 4 segments of 16 bf16
   const int arow = tid >> 2, aseg = tid & 3;
   const bool a_ok = m0 + arow < rows;
@@ -83,8 +87,8 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       if (k0 + kk < H) {
-        const bf16x8 bg = load_b_frag(gcr, gsr, k0 + kk + kq);
-        const bf16x8 bu = load_b_frag(ucr, usr, k0 + kk + kq);
+        const bf16x8 bg = load_b_frag(gcr, gsr, I, k0 + kk + kq);
+        const bf16x8 bu = load_b_frag(ucr, usr, I, k0 + kk + kq);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[(ms * 16 + (lane & 15)) * LDA + kk + kq]);
@@ -117,17 +121,17 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(
     const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ grp_row0,
     const int32_t* __restrict__ grp_rows, float* __restrict__ staging, int T, int k, int H, int I) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  const int mt = blockIdx.y;
+  const int mt = blockIdx.x;
   if (mt >= info[1]) return;
   const int g = mt_group[mt], m0 = mt_row0[mt];
   const int rows = grp_rows[g], row0 = grp_row0[g];
   const int tk = T * k;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ncol = blockIdx.x * BN + wave * 16 + (lane & 15);
+  const int ncol = blockIdx.y * BN + wave * 16 + (lane & 15);
   const bool col_ok = ncol < H;
-  const size_t wrow = (size_t)g * H + (col_ok ? ncol : H - 1);
-  const uint8_t* dcr = dc + wrow * (I >> 1);
-  const uint8_t* dsr = ds + wrow * (I >> 5);
+  const size_t col = (size_t)g * (I >> 5) * H + (col_ok ? ncol : H - 1);
+  const uint8_t* dcr = dc + col * 16;
+  const uint8_t* dsr = ds + col;
   const int arow = tid >> 2, aseg = tid & 3;
   const bool a_ok = m0 + arow < rows;
   const uint16_t* asrc = hin + (size_t)(row0 + (a_ok ? m0 + arow : 0)) * I + aseg * 16;
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       if (k0 + kk < I) {
-        const bf16x8 bd = load_b_frag(dcr, dsr, k0 + kk + kq);
+        const bf16x8 bd = load_b_frag(dcr, dsr, H, k0 + kk + kq);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[(ms * 16 + (lane & 15)) * LDA + kk + kq]);
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int mt_bound, hipStream_t s) {
-  dim3 grid((d.I + BN - 1) / BN, mt_bound);
+  dim3 grid(mt_bound, (d.I + BN - 1) / BN);
   const int tk = timing_begin("gemm_gateup", s);
   gemm_gateup_kernel<<<grid, 256, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
                                           b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows,
@@ -187,7 +191,7 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
 
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s) {
-  dim3 grid((d.H + BN - 1) / BN, mt_bound);
+  dim3 grid(mt_bound, (d.H + BN - 1) / BN);
   const int tk = timing_begin("gemm_down", s);
   gemm_down_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(b.h), w.down_codes, w.down_scales, b.perm,
                                         b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, b.staging, T,

@@ -3,126 +3,106 @@
 //
 // "feat(dsv4): DeepSeek V4 Flash support -- CUDA/VRAM expert tiering ..." (PR #1031) makes a
 // custom FP4 expert-grouped matvec the default GPU expert path, and "Add DeepSeek V4 Flash
-// CPU inference with NVMe expert streaming" (PR #165, the NEON rows16 comment) pairs gate
-// and up in one "dual" pass.  Here one workgroup owns a tile of output rows of one active
-// group: gate and up rows are read together so SwiGLU happens in registers.
+// CPU inference with NVMe expert streaming" (PR #165, the NEON rows16 comment) computes one
+// weight row per vector lane with the columns ascending, and pairs gate and up in one "dual"
+// pass.  The gfx950 version keeps both ideas:
 //
-// Mapping: thread (rsub, b) owns 32-element block b of the reduction axis for the rows
-// n = n_base + rsub + rpi*i.  Each thread loads 16 contiguous code bytes per row (a wave
-// reads 1 KiB contiguous per row), dequantises in registers with the gfx950 FP4 converts,
-// and keeps its slice of the activations in registers across all rows.  The e8m0 scale is
-// a power of two, so the 32-element partial sum is scaled once (exact).  Partial sums over
-// blocks are reduced through LDS.
+// * One lane owns one output row (gate and up rows n together, so SwiGLU stays in
+//   registers); a workgroup owns 64 rows of one active group.  Weights are in the
+//   block-interleaved kernel layout (pack.hip), so the 64 lanes' 16-byte loads of one block
+//   are one contiguous KiB.
+// * The reduction axis is split over the workgroup's 4 waves; each lane walks its row's
+//   32-element blocks in ascending order, 16 code bytes per load, several blocks in flight.
+// * The activations are the same for every lane, so they are read with scalar loads into
+//   SGPRs and used directly as the shared operand of v_dot2 / v_fma.
+// * e2m1 codes are converted with the gfx950 scaled converts, the e8m0 scale applied inside
+//   the convert (exact: the scale is a power of two).
+// * The 4 wave partials are added in a fixed order through LDS, so a token's result does not
+//   depend on which other tokens share its expert.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kGemvRI = 4;   // row iterations per workgroup
-constexpr int kGateTT = 4;   // tokens per pass, gate/up
-constexpr int kDownTT = 2;   // tokens per pass, down (fp32 activations in registers)
+constexpr int kSplit = 4;     // waves per workgroup = slices of the reduction axis
+constexpr int kGateTT = 4;    // tokens per pass, gate/up (bf16 activations: 16 SGPRs per block)
+constexpr int kDownTT = 2;    // tokens per pass, down (fp32 activations: 32 SGPRs per block)
+constexpr int kUnroll = 4;    // 32-element blocks in flight per lane
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
-__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// Threads per reduction task (a power of two <= 64) so that tasks * P <= 256.
-__device__ __forceinline__ int reduce_lanes(int tasks) {
-  int p = 1;
-  while (p < 64 && p * 2 * tasks <= 256) p <<= 1;
-  return p;
-}
-
 // ------------------------------------------------------------------------------------
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n])   (fp32 h)
 // ------------------------------------------------------------------------------------
 template <int NT>
-__device__ __forceinline__ void gateup_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ gc,
-                                            const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uc,
-                                            const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
-                                            float* __restrict__ hout, float* red, int r_first, int tk, int k,
-                                            int H, int I, size_t grow, int n_base, int rpi, int KB, int rsub,
-                                            int b, bool on) {
-  const int tid = threadIdx.x;
-  uint4 xr[NT][4];
+__device__ __forceinline__ void gateup_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ gcr,
+                                            const uint8_t* __restrict__ gsr, const uint8_t* __restrict__ ucr,
+                                            const uint8_t* __restrict__ usr, const int32_t* __restrict__ perm,
+                                            float* __restrict__ hout, float (*red)[2 * kGateTT][64], int r_first,
+                                            int tk, int k, int H, int I, int n, bool nok, int kb0, int kb1) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  c_u32* xrow[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int t = row_token(perm, r_first + tt, tk, k);
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + b * 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[tt][q] = on ? src[q] : make_uint4(0, 0, 0, 0);
+    xrow[tt] = (c_u32*)(x + (size_t)t * H);
   }
-  uint4 cg[kGemvRI], cu[kGemvRI];
-  uint32_t sg[kGemvRI], su[kGemvRI];
+  float ag[NT], au[NT];
 #pragma unroll
-  for (int i = 0; i < kGemvRI; ++i) {
-    const int n = n_base + rsub + rpi * i;
-    if (on && n < I) {
-      const size_t row = grow + n;
-      cg[i] = *reinterpret_cast<const uint4*>(gc + row * (H >> 1) + b * 16);
-      cu[i] = *reinterpret_cast<const uint4*>(uc + row * (H >> 1) + b * 16);
-      sg[i] = gs[row * KB + b];
-      su[i] = us[row * KB + b];
-    } else {
-      cg[i] = cu[i] = make_uint4(0, 0, 0, 0);
-      sg[i] = su[i] = 0;
+  for (int tt = 0; tt < NT; ++tt) ag[tt] = au[tt] = 0.f;
+  for (int kb = kb0; kb < kb1; kb += kUnroll) {
+    uint4 cg[kUnroll], cu[kUnroll];
+    float sg[kUnroll], su[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int b = min(kb + u, kb1 - 1);  // tail: re-read the last block, contribution skipped
+      cg[u] = *reinterpret_cast<const uint4*>(gcr + (size_t)b * I * 16);
+      cu[u] = *reinterpret_cast<const uint4*>(ucr + (size_t)b * I * 16);
+      sg[u] = e8m0_to_f32(gsr[(size_t)b * I]);
+      su[u] = e8m0_to_f32(usr[(size_t)b * I]);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kGemvRI; ++i) {
-    float ag[NT], au[NT];
+    for (int u = 0; u < kUnroll; ++u) {
+      if (kb + u < kb1) {
+        const uint32_t cgw[4] = {cg[u].x, cg[u].y, cg[u].z, cg[u].w};
+        const uint32_t cuw[4] = {cu[u].x, cu[u].y, cu[u].z, cu[u].w};
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) ag[tt] = au[tt] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          bf16x2 wg[4], wu[4];
+          fp4x8_to_bf16(cgw[q], sg[u], wg);
+          fp4x8_to_bf16(cuw[q], su[u], wu);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x2 wg[4], wu[4];
-      fp4x8_to_bf16(u4get(cg[i], q), 1.0f, wg);
-      fp4x8_to_bf16(u4get(cu[i], q), 1.0f, wu);
+          for (int tt = 0; tt < NT; ++tt) {
+            c_u32* xp = xrow[tt] + (size_t)(kb + u) * 16 + 4 * q;
 #pragma unroll
-      for (int sel = 0; sel < 4; ++sel) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const bf16x2 xp = as_bf16x2(u4get(xr[tt][q], sel));
-          ag[tt] = __builtin_amdgcn_fdot2_f32_bf16(wg[sel], xp, ag[tt], false);
-          au[tt] = __builtin_amdgcn_fdot2_f32_bf16(wu[sel], xp, au[tt], false);
+            for (int s = 0; s < 4; ++s) {
+              const bf16x2 xv = as_bf16x2(xp[s]);
+              ag[tt] = __builtin_amdgcn_fdot2_f32_bf16(wg[s], xv, ag[tt], false);
+              au[tt] = __builtin_amdgcn_fdot2_f32_bf16(wu[s], xv, au[tt], false);
+            }
+          }
         }
       }
     }
-    const float scg = e8m0_to_f32(sg[i]), scu = e8m0_to_f32(su[i]);
+  }
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      red[((i * NT + tt) * 2 + 0) * 256 + tid] = ag[tt] * scg;
-      red[((i * NT + tt) * 2 + 1) * 256 + tid] = au[tt] * scu;
-    }
+  for (int tt = 0; tt < NT; ++tt) {
+    red[wave][2 * tt][lane] = ag[tt];
+    red[wave][2 * tt + 1][lane] = au[tt];
   }
   __syncthreads();
-  const int tasks = kGemvRI * rpi * NT;
-  const int P = reduce_lanes(tasks);
-  for (int base = 0; base < tasks * P; base += 256) {
-    const int id = base + tid;
-    const int task = id / P, p = id - (id / P) * P;
-    const bool ok = task < tasks;
-    float s_g = 0.f, s_u = 0.f;
-    int n = 0, tt = 0;
-    if (ok) {
-      tt = task % NT;
-      const int r2 = task / NT;
-      const int rs = r2 % rpi, i = r2 / rpi;
-      n = n_base + rs + rpi * i;
-      const float* rg = red + ((i * NT + tt) * 2) * 256 + rs * KB;
-      for (int bb = p; bb < KB; bb += P) {
-        s_g += rg[bb];
-        s_u += rg[256 + bb];
+  if (wave == 0 && nok) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      float g = red[0][2 * tt][lane], u = red[0][2 * tt + 1][lane];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) {
+        g += red[w][2 * tt][lane];
+        u += red[w][2 * tt + 1][lane];
       }
+      hout[(size_t)(r_first + tt) * I + n] = silu_f(g) * u;
     }
-    for (int m = 1; m < P; m <<= 1) {
-      s_g += __shfl_xor(s_g, m, 64);
-      s_u += __shfl_xor(s_u, m, 64);
-    }
-    if (ok && p == 0 && n < I) hout[(size_t)(r_first + tt) * I + n] = silu_f(s_g) * s_u;
   }
   __syncthreads();
 }
@@ -132,25 +112,29 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
     const int32_t* __restrict__ grp_rows, float* __restrict__ hout, int T, int k, int H, int I) {
-  __shared__ float red[kGemvRI * kGateTT * 2 * 256];
+  __shared__ float red[kSplit][2 * kGateTT][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
   const int rows = grp_rows[g], row0 = grp_row0[g];
+  // readfirstlane: the wave index is uniform, and the compiler must know it for scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 64 + lane;
+  const bool nok = n < I;
   const int KB = H >> 5;
-  const int rpi = 256 / KB;
-  const int tid = threadIdx.x;
-  const int rsub = tid / KB, b = tid - rsub * KB;
-  const bool on = rsub < rpi;
-  const int n_base = blockIdx.x * rpi * kGemvRI;
+  const int kb0 = wave * KB / kSplit, kb1 = (wave + 1) * KB / kSplit;
+  // kernel layout: block kb of row n of group g at ((g*KB + kb)*I + n) 16-byte chunks
+  const size_t col = (size_t)g * KB * I + (nok ? n : I - 1);
+  const uint8_t* gcr = gc + col * 16;
+  const uint8_t* ucr = uc + col * 16;
+  const uint8_t* gsr = gs + col;
+  const uint8_t* usr = us + col;
   const int tk = T * k;
-  const size_t grow = (size_t)g * I;
   for (int c0 = 0; c0 < rows; c0 += kGateTT) {
-    const int nt = min(kGateTT, rows - c0);
-    switch (nt) {
-      case 1: gateup_pass<1>(x, gc, gs, uc, us, perm, hout, red, row0 + c0, tk, k, H, I, grow, n_base, rpi, KB, rsub, b, on); break;
-      case 2: gateup_pass<2>(x, gc, gs, uc, us, perm, hout, red, row0 + c0, tk, k, H, I, grow, n_base, rpi, KB, rsub, b, on); break;
-      case 3: gateup_pass<3>(x, gc, gs, uc, us, perm, hout, red, row0 + c0, tk, k, H, I, grow, n_base, rpi, KB, rsub, b, on); break;
-      default: gateup_pass<4>(x, gc, gs, uc, us, perm, hout, red, row0 + c0, tk, k, H, I, grow, n_base, rpi, KB, rsub, b, on); break;
+    switch (min(kGateTT, rows - c0)) {
+      case 1: gateup_pass<1>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
+      case 2: gateup_pass<2>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
+      case 3: gateup_pass<3>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
+      default: gateup_pass<4>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
     }
   }
 }
@@ -159,79 +143,54 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 // down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n])    (fp32 h, fp32 FMA)
 // ------------------------------------------------------------------------------------
 template <int NT>
-__device__ __forceinline__ void down_pass(const float* __restrict__ hin, const uint8_t* __restrict__ dc,
-                                          const uint8_t* __restrict__ ds, const int32_t* __restrict__ perm,
-                                          const float* __restrict__ wts, float* __restrict__ staging, float* red,
-                                          int r_first, int tk, int H, int I, size_t grow, int n_base, int rpi,
-                                          int KB, int rsub, int b, bool on) {
-  const int tid = threadIdx.x;
-  float4 xr[NT][8];
+__device__ __forceinline__ void down_pass(const float* __restrict__ hin, const uint8_t* __restrict__ dcr,
+                                          const uint8_t* __restrict__ dsr, const int32_t* __restrict__ perm,
+                                          const float* __restrict__ wts, float* __restrict__ staging,
+                                          float (*red)[kDownTT][64], int r_first, int tk, int H, int I, int n,
+                                          bool nok, int kb0, int kb1) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float a[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const float4* src = reinterpret_cast<const float4*>(hin + (size_t)(r_first + tt) * I + b * 32);
+  for (int tt = 0; tt < NT; ++tt) a[tt] = 0.f;
+  for (int kb = kb0; kb < kb1; kb += kUnroll) {
+    uint4 cd[kUnroll];
+    float sd[kUnroll];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xr[tt][q] = on ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  uint4 cd[kGemvRI];
-  uint32_t sd[kGemvRI];
-#pragma unroll
-  for (int i = 0; i < kGemvRI; ++i) {
-    const int n = n_base + rsub + rpi * i;
-    if (on && n < H) {
-      const size_t row = grow + n;
-      cd[i] = *reinterpret_cast<const uint4*>(dc + row * (I >> 1) + b * 16);
-      sd[i] = ds[row * KB + b];
-    } else {
-      cd[i] = make_uint4(0, 0, 0, 0);
-      sd[i] = 0;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int b = min(kb + u, kb1 - 1);
+      cd[u] = *reinterpret_cast<const uint4*>(dcr + (size_t)b * H * 16);
+      sd[u] = e8m0_to_f32(dsr[(size_t)b * H]);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kGemvRI; ++i) {
-    float a[NT];
+    for (int u = 0; u < kUnroll; ++u) {
+      if (kb + u < kb1) {
+        const uint32_t cw[4] = {cd[u].x, cd[u].y, cd[u].z, cd[u].w};
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) a[tt] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          f32x2 wv[4];
+          fp4x8_to_f32(cw[q], sd[u], wv);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x2 wq[4];
-      fp4x8_to_f32(u4get(cd[i], q), 1.0f, wq);
+          for (int tt = 0; tt < NT; ++tt) {
+            c_f32* hp = (c_f32*)(hin + (size_t)(r_first + tt) * I + (size_t)(kb + u) * 32 + 8 * q);
 #pragma unroll
-      for (int sel = 0; sel < 4; ++sel) {
-        const f32x2 wv = wq[sel];
-        // elements 8q + 2sel and 8q + 2sel + 1
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const float4 xv = xr[tt][2 * q + (sel >> 1)];
-          const float x0 = (sel & 1) ? xv.z : xv.x;
-          const float x1 = (sel & 1) ? xv.w : xv.y;
-          a[tt] = fmaf(wv.x, x0, a[tt]);
-          a[tt] = fmaf(wv.y, x1, a[tt]);
+            for (int s = 0; s < 4; ++s) {
+              a[tt] = fmaf(wv[s].x, hp[2 * s], a[tt]);
+              a[tt] = fmaf(wv[s].y, hp[2 * s + 1], a[tt]);
+            }
+          }
         }
       }
     }
-    const float sc = e8m0_to_f32(sd[i]);
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) red[(i * NT + tt) * 256 + tid] = a[tt] * sc;
   }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) red[wave][tt][lane] = a[tt];
   __syncthreads();
-  const int tasks = kGemvRI * rpi * NT;
-  const int P = reduce_lanes(tasks);
-  for (int base = 0; base < tasks * P; base += 256) {
-    const int id = base + tid;
-    const int task = id / P, p = id - (id / P) * P;
-    const bool ok = task < tasks;
-    float s = 0.f;
-    int n = 0, tt = 0;
-    if (ok) {
-      tt = task % NT;
-      const int r2 = task / NT;
-      const int rs = r2 % rpi, i = r2 / rpi;
-      n = n_base + rs + rpi * i;
-      const float* rr = red + (i * NT + tt) * 256 + rs * KB;
-      for (int bb = p; bb < KB; bb += P) s += rr[bb];
-    }
-    for (int m = 1; m < P; m <<= 1) s += __shfl_xor(s, m, 64);
-    if (ok && p == 0 && n < H) {
+  if (wave == 0 && nok) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      float s = red[0][tt][lane];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) s += red[w][tt][lane];
       const int r = r_first + tt;
       const int slot = r < tk ? perm[r] : r;
       const float wt = r < tk ? wts[slot] : 1.0f;
@@ -246,48 +205,47 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
     const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
     float* __restrict__ staging, int T, int k, int H, int I) {
-  __shared__ float red[kGemvRI * kDownTT * 256];
+  __shared__ float red[kSplit][kDownTT][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
   const int rows = grp_rows[g], row0 = grp_row0[g];
+  // readfirstlane: the wave index is uniform, and the compiler must know it for scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 64 + lane;
+  const bool nok = n < H;
   const int KB = I >> 5;
-  const int rpi = 256 / KB;
-  const int tid = threadIdx.x;
-  const int rsub = tid / KB, b = tid - rsub * KB;
-  const bool on = rsub < rpi;
-  const int n_base = blockIdx.x * rpi * kGemvRI;
+  const int kb0 = wave * KB / kSplit, kb1 = (wave + 1) * KB / kSplit;
+  const size_t col = (size_t)g * KB * H + (nok ? n : H - 1);
+  const uint8_t* dcr = dc + col * 16;
+  const uint8_t* dsr = ds + col;
   const int tk = T * k;
-  const size_t grow = (size_t)g * H;
   for (int c0 = 0; c0 < rows; c0 += kDownTT) {
     if (rows - c0 >= 2)
-      down_pass<2>(hin, dc, ds, perm, wts, staging, red, row0 + c0, tk, H, I, grow, n_base, rpi, KB, rsub, b, on);
+      down_pass<2>(hin, dcr, dsr, perm, wts, staging, red, row0 + c0, tk, H, I, n, nok, kb0, kb1);
     else
-      down_pass<1>(hin, dc, ds, perm, wts, staging, red, row0 + c0, tk, H, I, grow, n_base, rpi, KB, rsub, b, on);
+      down_pass<1>(hin, dcr, dsr, perm, wts, staging, red, row0 + c0, tk, H, I, n, nok, kb0, kb1);
   }
 }
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int max_act, hipStream_t s) {
-  const int rpi = 256 / (d.H >> 5);
-  const int nr = rpi * kGemvRI;
-  dim3 grid((d.I + nr - 1) / nr, max_act);
+  dim3 grid((d.I + 63) / 64, max_act);
   const int tk = timing_begin("gemv_gateup", s);
-  gemv_gateup_kernel<<<grid, 256, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.act,
-                                          b.info, b.grp_row0, b.grp_rows, static_cast<float*>(b.h), T, d.K, d.H,
-                                          d.I);
+  gemv_gateup_kernel<<<grid, 64 * kSplit, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
+                                                  b.act, b.info, b.grp_row0, b.grp_rows, static_cast<float*>(b.h),
+                                                  T, d.K, d.H, d.I);
   timing_end(tk, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
                             hipStream_t s) {
-  const int rpi = 256 / (d.I >> 5);
-  const int nr = rpi * kGemvRI;
-  dim3 grid((d.H + nr - 1) / nr, max_act);
+  dim3 grid((d.H + 63) / 64, max_act);
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<<<grid, 256, 0, s>>>(static_cast<const float*>(b.h), w.down_codes, w.down_scales, b.perm, b.w,
-                                        b.act, b.info, b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H, d.I);
+  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const float*>(b.h), w.down_codes, w.down_scales, b.perm,
+                                                b.w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H,
+                                                d.I);
   timing_end(tk, s);
   return hipGetLastError();
 }

@@ -1,0 +1,78 @@
+// One-time repack of FP4 expert weights from the checkpoint layout into the layout the
+// kernels stream.
+//
+// Checkpoint layout (row-major, per group g):   codes [N][K/2],       scales [N][K/32]
+// Kernel layout (block-interleaved, per group):  codes [K/32][N][16],  scales [K/32][N]
+//
+// In the kernel layout the 16 code bytes of block kb of rows n, n+1, ... are adjacent, so a
+// wave whose lanes own consecutive rows reads 1 KiB contiguous per instruction, and the
+// scales of those rows are 64 contiguous bytes.  "Add DeepSeek V4 Flash CPU inference with
+// NVMe expert streaming" (PR #165) repacks pinned experts the same way for its SIMD kernels
+// (16 rows interleaved per vector lane, packed once per expert).
+//
+// Each workgroup transposes a tile of 64 rows x 64 blocks through LDS, reading and writing
+// whole 16-byte chunks with consecutive threads on consecutive addresses.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kPackTile = 64;
+
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint4* __restrict__ in, uint4* __restrict__ out,
+                                                         int N, int KB, int ntiles) {
+  __shared__ uint4 tile[kPackTile][kPackTile + 1];
+  const int g = blockIdx.x / ntiles;
+  const int n0 = (blockIdx.x - g * ntiles) * kPackTile;
+  const int kb0 = blockIdx.y * kPackTile;
+  const size_t gin = (size_t)g * N * KB;
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int r = i / kPackTile, c = i % kPackTile;  // c fastest: contiguous chunks of one row
+    const int n = n0 + r, kb = kb0 + c;
+    if (n < N && kb < KB) tile[r][c] = in[gin + (size_t)n * KB + kb];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int c = i / kPackTile, r = i % kPackTile;  // r fastest: contiguous rows of one block
+    const int n = n0 + r, kb = kb0 + c;
+    if (n < N && kb < KB) out[gin + (size_t)kb * N + n] = tile[r][c];
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                          int N, int KB, int ntiles) {
+  __shared__ uint8_t tile[kPackTile][kPackTile + 4];
+  const int g = blockIdx.x / ntiles;
+  const int n0 = (blockIdx.x - g * ntiles) * kPackTile;
+  const int kb0 = blockIdx.y * kPackTile;
+  const size_t gin = (size_t)g * N * KB;
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int r = i / kPackTile, c = i % kPackTile;
+    const int n = n0 + r, kb = kb0 + c;
+    if (n < N && kb < KB) tile[r][c] = in[gin + (size_t)n * KB + kb];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int c = i / kPackTile, r = i % kPackTile;
+    const int n = n0 + r, kb = kb0 + c;
+    if (n < N && kb < KB) out[gin + (size_t)kb * N + n] = tile[r][c];
+  }
+}
+
+hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
+                       int groups, int N, int K, hipStream_t s) {
+  const int KB = K / 32;
+  const int ntiles = (N + kPackTile - 1) / kPackTile;
+  dim3 grid(ntiles * groups, (KB + kPackTile - 1) / kPackTile);
+  int tk = timing_begin("pack_codes", s);
+  pack_codes_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4*>(codes_in), reinterpret_cast<uint4*>(codes_out),
+                                         N, KB, ntiles);
+  timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tk = timing_begin("pack_scales", s);
+  pack_scales_kernel<<<grid, 256, 0, s>>>(scales_in, scales_out, N, KB, ntiles);
+  timing_end(tk, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -13,7 +13,9 @@ namespace moe {
 
 // ------------------------------------------------------------------------------------
 // Router scores l[t][e] = x[t] . W_r[e] + b[e]  (fp32 accumulate, bf16 activations).
-// One wave per expert row; the row streams once from HBM per token tile of kRouterTT.
+// One workgroup per (expert, tile of kRouterTT tokens): the 256 threads split the hidden
+// axis (8 values each per step), partial sums are reduced across each wave and then the
+// 4 waves in a fixed order, so a score does not depend on the other tokens of the batch.
 // ------------------------------------------------------------------------------------
 constexpr int kRouterTT = 8;
 
@@ -22,16 +24,16 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T, int E,
                                                             int H) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
+  __shared__ float part[4][kRouterTT];
+  const int e = blockIdx.x;
   const int t0 = blockIdx.y * kRouterTT;
-  if (e >= E) return;  // whole wave leaves; no block barrier below
   const int nt = min(kRouterTT, T - t0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float acc[kRouterTT];
 #pragma unroll
   for (int i = 0; i < kRouterTT; ++i) acc[i] = 0.f;
   const float* wrow = wr + (size_t)e * H;
-  for (int h = lane * 8; h < H; h += 64 * 8) {  // H % 32 == 0, so h + 8 <= H
+  for (int h = tid * 8; h < H; h += 256 * 8) {  // H % 32 == 0, so h + 8 <= H
     const float4 w0 = *reinterpret_cast<const float4*>(wrow + h);
     const float4 w1 = *reinterpret_cast<const float4*>(wrow + h + 4);
 #pragma unroll
@@ -51,13 +53,17 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       }
     }
   }
-  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
   for (int i = 0; i < kRouterTT; ++i) {
     float v = acc[i];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0 && i < nt) logits[(size_t)(t0 + i) * E + e] = v + b;
+    if (lane == 0) part[wave][i] = v;
+  }
+  __syncthreads();
+  if (tid < nt) {
+    const float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    logits[(size_t)(t0 + tid) * E + e] = v + (bias ? bias[e] : 0.f);
   }
 }
 
@@ -87,22 +93,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-constexpr int kMaxQ = 16;  // E <= 1024 = 16 scores per lane
-
-// Writes idx[0..k), w[0..k) of the token and sets bit `tbit` of mask[e] for each pick.
+// Writes idx[0..k), w[0..k) of the token and sets bit `tbit` of mask[e] for each pick;
+// also copies the picks to sel (LDS) when sel is not NULL.  Q = scores per lane (E <= 64*Q).
+template <int Q>
 __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lane,
                            int32_t* __restrict__ idx_out, float* __restrict__ w_out, uint64_t* mask,
-                           int tbit) {
-  uint64_t key[kMaxQ];
+                           int tbit, int32_t* sel) {
+  uint64_t key[Q];
+  float val[Q];
 #pragma unroll
-  for (int q = 0; q < kMaxQ; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int e = lane + 64 * q;
-    key[q] = e < E ? rank_key(lrow[e], e) : 0ull;
+    val[q] = e < E ? lrow[e] : 0.f;
+    key[q] = e < E ? rank_key(val[q], e) : 0ull;
   }
-  int selE[kMaxQ];
-  float selV[kMaxQ];
+  int selE[Q];
+  float selV[Q];
 #pragma unroll
-  for (int q = 0; q < kMaxQ; ++q) {
+  for (int q = 0; q < Q; ++q) {
     selE[q] = 0;
     selV[q] = 0.f;
   }
@@ -110,31 +118,38 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lan
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0ull;
 #pragma unroll
-    for (int q = 0; q < kMaxQ; ++q) best = key[q] > best ? key[q] : best;
+    for (int q = 0; q < Q; ++q) best = key[q] > best ? key[q] : best;
     best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const float v = lrow[e];
+    const int e = __builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu - (uint32_t)best));
+    float mine = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (q == (e >> 6)) mine = val[q];
+    const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine), e & 63));
     if (j == 0) vtop = v;
     if ((e & 63) == lane) {
 #pragma unroll
-      for (int q = 0; q < kMaxQ; ++q)
+      for (int q = 0; q < Q; ++q)
         if (q == (e >> 6)) key[q] = 0ull;
     }
     if ((j & 63) == lane) {
 #pragma unroll
-      for (int q = 0; q < kMaxQ; ++q)
+      for (int q = 0; q < Q; ++q)
         if (q == (j >> 6)) {
           selE[q] = e;
           selV[q] = v;
         }
     }
-    if (lane == 0) atomicOr(reinterpret_cast<unsigned long long*>(&mask[e]), 1ull << tbit);
+    if (lane == 0) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[e]), 1ull << tbit);
+      if (sel) sel[j] = e;
+    }
   }
   // softmax over the k picked scores; xor-butterfly sums are identical on every lane
-  float p[kMaxQ];
+  float p[Q];
   float s = 0.f;
 #pragma unroll
-  for (int q = 0; q < kMaxQ; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int j = lane + 64 * q;
     p[q] = 0.f;
     if (j < k) {
@@ -145,13 +160,28 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lan
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
 #pragma unroll
-  for (int q = 0; q < kMaxQ; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int j = lane + 64 * q;
     if (j < k) {
       idx_out[j] = selE[q];
       w_out[j] = p[q] / s;
     }
   }
+}
+
+// Calls topk_token with the smallest Q >= ceil(E/64) among 1, 2, 4, 8, 16.
+__device__ __forceinline__ void topk_any(int E, const float* lrow, int k, int lane, int32_t* idx_out,
+                                         float* w_out, uint64_t* mask, int tbit, int32_t* sel) {
+  if (E <= 64)
+    topk_token<1>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+  else if (E <= 128)
+    topk_token<2>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+  else if (E <= 256)
+    topk_token<4>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+  else if (E <= 512)
+    topk_token<8>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+  else
+    topk_token<16>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
 }
 
 // ------------------------------------------------------------------------------------
@@ -228,15 +258,20 @@ __device__ int build_tables(int cnt, int T, int E, int k, int S, const CallBufs&
 // ------------------------------------------------------------------------------------
 // Small batches (T <= 64): top-k, tables and scatter in one 1024-thread workgroup.
 // ------------------------------------------------------------------------------------
+constexpr int kSmallSel = 4096;  // picks kept in LDS by the one-workgroup route (T*k)
+
 __global__ __launch_bounds__(1024) void route_small_kernel(CallBufs b, int T, int E, int k, int S) {
   __shared__ uint64_t mask[1024];
   __shared__ int offs[1024];
+  __shared__ int32_t sel[kSmallSel];
   __shared__ int lds16[16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool in_lds = T * k <= kSmallSel;
   if (tid < E) mask[tid] = 0ull;
   __syncthreads();
   for (int t = wave; t < T; t += 16)
-    topk_token(b.logits + (size_t)t * E, E, k, lane, b.idx + (size_t)t * k, b.w + (size_t)t * k, mask, t);
+    topk_any(E, b.logits + (size_t)t * E, k, lane, b.idx + (size_t)t * k, b.w + (size_t)t * k, mask, t,
+             in_lds ? sel + t * k : nullptr);
   __syncthreads();
   const int cnt = tid < E ? __popcll(mask[tid]) : 0;
   const int off = build_tables(cnt, T, E, k, S, b, lds16);
@@ -245,7 +280,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(CallBufs b, int T, in
   if (tid < T) {
     const uint64_t below = (1ull << tid) - 1ull;
     for (int j = 0; j < k; ++j) {
-      const int e = b.idx[tid * k + j];
+      const int e = in_lds ? sel[tid * k + j] : b.idx[tid * k + j];
       b.perm[offs[e] + __popcll(mask[e] & below)] = tid * k + j;
     }
   }
@@ -266,7 +301,7 @@ __global__ __launch_bounds__(256) void topk_chunk_kernel(const float* __restrict
   for (int i = wave; i < kChunk; i += 4) {
     const int t = c * kChunk + i;
     if (t >= T) break;
-    topk_token(logits + (size_t)t * E, E, k, lane, idx + (size_t)t * k, w + (size_t)t * k, mask, i);
+    topk_any(E, logits + (size_t)t * E, k, lane, idx + (size_t)t * k, w + (size_t)t * k, mask, i, nullptr);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) gmask[(size_t)c * E + e] = mask[e];
@@ -299,7 +334,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 float* logits, int T, hipStream_t s) {
-  dim3 grid((d.E + 3) / 4, (T + kRouterTT - 1) / kRouterTT);
+  dim3 grid(d.E, (T + kRouterTT - 1) / kRouterTT);
   const int tk = timing_begin("router_logits", s);
   router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, bias, logits, T, d.E, d.H);
   timing_end(tk, s);

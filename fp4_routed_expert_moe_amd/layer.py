@@ -33,25 +33,43 @@ def device_supported(device: int = 0):
     return bool(ok), buf.value.decode()
 
 
+def pack_fp4(codes: torch.Tensor, scales: torch.Tensor, stream=None):
+    """Checkpoint layout (codes [G][N][K/2], scales [G][N][K/32]) -> kernel layout
+    (codes [G][K/32][N][16], scales [G][K/32][N]), by the library's pack kernel."""
+    lib = _lib.load()
+    g, n, half_k = codes.shape
+    k = 2 * half_k
+    if tuple(scales.shape) != (g, n, k // 32) or codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("pack_fp4 wants uint8 codes [G][N][K/2] and scales [G][N][K/32]")
+    if not (codes.is_cuda and scales.is_cuda and codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("pack_fp4 wants contiguous CUDA tensors")
+    out_c = torch.empty((g, k // 32, n, 16), dtype=torch.uint8, device=codes.device)
+    out_s = torch.empty((g, k // 32, n), dtype=torch.uint8, device=codes.device)
+    _lib.check(lib.moe_pack_fp4(_ptr(codes), _ptr(scales), _ptr(out_c), _ptr(out_s), g, n, k,
+                                _stream_handle(stream)), lib)
+    return out_c, out_s
+
+
 class MoeLayer:
     """One routed FP4-expert MoE layer over borrowed device weights.
 
-    ``gate``/``up``/``down`` are (codes, scales) uint8 CUDA tensors shaped
-    [E+S][N][K/2] and [E+S][N][K/32]; the library keeps only their pointers, so
-    this object holds references to keep them alive.
+    ``gate``/``up``/``down`` are (codes, scales) uint8 CUDA tensors in the kernel
+    layout: codes [E+S][K/32][N][16], scales [E+S][K/32][N] (see ``pack_fp4``);
+    the library keeps only their pointers, so this object holds references to
+    keep them alive.
     """
 
     def __init__(self, w_router: torch.Tensor, gate, up, down, top_k: int, n_shared: int = 1,
                  router_bias: Optional[torch.Tensor] = None, path: str = "auto"):
         self.lib = _lib.load()
         e, h = w_router.shape
-        g, inter, hk = gate[0].shape
-        if g != e + n_shared or hk * 2 != h:
+        g, hb, inter, sixteen = gate[0].shape
+        if g != e + n_shared or hb * 32 != h or sixteen != 16:
             raise ValueError(f"gate codes {tuple(gate[0].shape)} do not match E={e}, S={n_shared}, H={h}")
         for name, (c, s), n, k in (("gate", gate, inter, h), ("up", up, inter, h), ("down", down, h, inter)):
-            if tuple(c.shape) != (g, n, k // 2) or tuple(s.shape) != (g, n, k // 32):
+            if tuple(c.shape) != (g, k // 32, n, 16) or tuple(s.shape) != (g, k // 32, n):
                 raise ValueError(f"{name} weights: codes {tuple(c.shape)} / scales {tuple(s.shape)}, "
-                                 f"expected {(g, n, k // 2)} / {(g, n, k // 32)}")
+                                 f"expected {(g, k // 32, n, 16)} / {(g, k // 32, n)} (kernel layout)")
             if c.dtype != torch.uint8 or s.dtype != torch.uint8 or not c.is_cuda or not s.is_cuda:
                 raise ValueError(f"{name} weights must be uint8 CUDA tensors")
             if not c.is_contiguous() or not s.is_contiguous():

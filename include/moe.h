@@ -23,15 +23,18 @@
  * CPU inference with NVMe expert streaming" (PR #165): FP4 E2M1 values with one UE8M0
  * scale per group of 32 along the reduction axis.
  *
- * Weight layout (device memory, row-major, group g in [0, E+S); the shared expert is
- * group E):
- *   gate_codes, up_codes   uint8 [E+S][I][H/2]   low nibble = element 2i, high = 2i+1
- *   gate_scales, up_scales uint8 [E+S][I][H/32]  scale j covers elements 32j..32j+31
- *   down_codes             uint8 [E+S][H][I/2]
- *   down_scales            uint8 [E+S][H][I/32]
- * An e8m0 byte s means the float32 with bit pattern s << 23 (s = 0 is +0, s = 255 is
- * +inf), as "DeepSeek V4: the CUDA kernels, as a tier rather than an engine" (PR #772)
- * describes for the MXFP4 decode.
+ * Weight layouts.  Group g in [0, E+S); the shared expert is group E.  A matrix has N output
+ * rows and a reduction axis of K values (gate/up: N = I, K = H; down: N = H, K = I); e2m1
+ * codes pack two values per byte (low nibble = even element) and one e8m0 scale covers 32
+ * consecutive values of a row.  An e8m0 byte s means the float32 with bit pattern s << 23
+ * (s = 0 is +0, s = 255 is +inf), as "DeepSeek V4: the CUDA kernels, as a tier rather than an
+ * engine" (PR #772) describes for the MXFP4 decode.
+ *   checkpoint layout (row-major):   codes uint8 [E+S][N][K/2],       scales uint8 [E+S][N][K/32]
+ *   kernel layout (block-interleaved): codes uint8 [E+S][K/32][N][16], scales uint8 [E+S][K/32][N]
+ * In the kernel layout the 16 code bytes of block kb of consecutive rows are adjacent, which
+ * is what the decode kernels stream (one lane per row, one contiguous KiB per wave load).
+ * moe_pack_fp4 converts the first into the second once, at load time; the layer reads the
+ * kernel layout only.
  *
  * Errors: every entry point returns a status (MOE_OK = 0).  Argument errors are reported
  * before anything is enqueued; launch errors are read back with hipGetLastError right after
@@ -79,12 +82,12 @@ typedef struct moe_layer_desc {
   int32_t device;        /* HIP device ordinal holding the weights */
   const float* w_router;       /* fp32 [E][H] */
   const float* router_bias;    /* fp32 [E], or NULL for no bias */
-  const uint8_t* gate_codes;   /* see layout above */
-  const uint8_t* gate_scales;
-  const uint8_t* up_codes;
-  const uint8_t* up_scales;
-  const uint8_t* down_codes;
-  const uint8_t* down_scales;
+  const uint8_t* gate_codes;   /* kernel layout (see above): [E+S][H/32][I][16] */
+  const uint8_t* gate_scales;  /* [E+S][H/32][I] */
+  const uint8_t* up_codes;     /* [E+S][H/32][I][16] */
+  const uint8_t* up_scales;    /* [E+S][H/32][I] */
+  const uint8_t* down_codes;   /* [E+S][I/32][H][16] */
+  const uint8_t* down_scales;  /* [E+S][I/32][H] */
 } moe_layer_desc;
 
 /* Routing results (device pointers), written by moe_route / moe_forward. */
@@ -134,6 +137,14 @@ int32_t moe_route(const moe_layer* layer, const uint16_t* x, int32_t tokens,
 int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, float* y,
                     const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
                     void* stream);
+
+/* Repack `groups` FP4 matrices of `rows` x `cols` (cols = reduction axis, multiple of 32)
+ * from the checkpoint layout into the kernel layout (device pointers; codes 16-byte aligned;
+ * outputs must not overlap inputs).  Asynchronous on `stream` (a hipStream_t, NULL = default
+ * stream) of the current device.  "Add DeepSeek V4 Flash CPU inference with NVMe expert
+ * streaming" (PR #165) likewise repacks each expert once into its kernels' interleaved layout. */
+int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out,
+                     uint8_t* scales_out, int32_t groups, int32_t rows, int32_t cols, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(int32_t status);

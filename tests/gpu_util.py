@@ -36,11 +36,20 @@ def stack_groups(groups, device="cuda"):
     return out
 
 
-def make_layer(w_router, weights, top_k, n_shared, bias=None, path="auto"):
+def pack_weights(weights):
+    """Checkpoint-layout device weights -> kernel layout, through the library's pack call."""
+    from fp4_routed_expert_moe_amd import pack_fp4
+    return {mat: pack_fp4(*weights[mat]) for mat in synth.MATRICES}
+
+
+def make_layer(w_router, weights, top_k, n_shared, bias=None, path="auto", packed=None):
+    """Layer over checkpoint-layout device weights (packed here unless `packed` is given)."""
     from fp4_routed_expert_moe_amd import MoeLayer
     wr = torch.from_numpy(np.ascontiguousarray(w_router, dtype=np.float32)).cuda()
     b = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32)).cuda()
-    return MoeLayer(wr, weights["gate"], weights["up"], weights["down"], top_k, n_shared, b, path)
+    pk = packed if packed is not None else pack_weights(weights)
+    layer = MoeLayer(wr, pk["gate"], pk["up"], pk["down"], top_k, n_shared, b, path)
+    return layer
 
 
 def x_to_device(x_bits):

