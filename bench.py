@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--batches", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = one batch (capped at 8 tokens)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB before the steps (a known-size "
+                        "reference for hardware byte counters)")
     return p.parse_args()
 
 
@@ -80,6 +83,14 @@ def main():
 
     def step(s):
         layers[s % nl].forward(xs[s % nb], workspace=ws, y=y)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # active experts of every (layer, batch) pair a step can meet (outside the timed region)
     period = int(np.lcm(nl, nb))

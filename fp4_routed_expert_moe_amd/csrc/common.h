@@ -41,6 +41,16 @@ __device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float scale, f32x2 out[
   out[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 3);
 }
 
+// Eight e2m1 codes -> one bf16x8 MFMA operand (value i from nibble i), times `scale`.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
+  bf16x2 p[4];
+  fp4x8_to_bf16(v, scale, p);
+  bf16x8 r;
+  r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
+  r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
+  return r;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 

@@ -30,12 +30,7 @@ __device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* __restrict__ codes_
   const size_t kb = (size_t)(k >> 5);
   const uint32_t c = *reinterpret_cast<const uint32_t*>(codes_col + kb * N * 16 + ((k & 31) >> 1));
   const float s = e8m0_to_f32(scales_col[kb * N]);
-  bf16x2 p[4];
-  fp4x8_to_bf16(c, s, p);
-  bf16x8 r;
-  r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
-  r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
-  return r;
+  return fp4x8_to_bf16x8(c, s);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

@@ -3,249 +3,277 @@
 //
 // "feat(dsv4): DeepSeek V4 Flash support -- CUDA/VRAM expert tiering ..." (PR #1031) makes a
 // custom FP4 expert-grouped matvec the default GPU expert path, and "Add DeepSeek V4 Flash
-// CPU inference with NVMe expert streaming" (PR #165, the NEON rows16 comment) computes one
-// weight row per vector lane with the columns ascending, and pairs gate and up in one "dual"
-// pass.  The gfx950 version keeps both ideas:
+// CPU inference with NVMe expert streaming" (PR #165, the NEON rows16 comment) pairs gate
+// and up in one "dual" pass over interleaved rows.  On gfx950 the products go to the matrix
+// cores, so the vector ALU only converts FP4 to bf16 (one convert per code byte):
 //
-// * One lane owns one output row (gate and up rows n together, so SwiGLU stays in
-//   registers); a workgroup owns 64 rows of one active group.  Weights are in the
-//   block-interleaved kernel layout (pack.hip), so the 64 lanes' 16-byte loads of one block
-//   are one contiguous KiB.
-// * The reduction axis is split over the workgroup's 4 waves; each lane walks its row's
-//   32-element blocks in ascending order, 16 code bytes per load, several blocks in flight.
-// * The activations are the same for every lane, so they are read with scalar loads into
-//   SGPRs and used directly as the shared operand of v_dot2 / v_fma.
-// * e2m1 codes are converted with the gfx950 scaled converts, the e8m0 scale applied inside
-//   the convert (exact: the scale is a power of two).
-// * The 4 wave partials are added in a fixed order through LDS, so a token's result does not
-//   depend on which other tokens share its expert.
+// * Gate and up row n are produced by the same lane, so SwiGLU stays in registers; the
+//   tokens of one group are the MFMA's M side, up to 16 per pass -- one pass for every group
+//   in decode, whatever its token count.
+// * Lane (n, q) loads one whole 16-byte block (32 values) of row n from the block-interleaved
+//   kernel layout (a wave reads 4 x 256 contiguous bytes) and feeds it to four
+//   16x16x32 bf16 MFMAs, eight values each.  The activation lanes (m, q) supply the same
+//   K values of token m, so each MFMA sums one 8-value slice of four blocks; over the four
+//   MFMAs every K value is met once.  Each lane scales by its own block's e8m0 inside the
+//   convert (exact: a power of two).
+// * Products bf16 x bf16 are exact in fp32 and accumulate in fp32.  h leaves gate/up as a
+//   bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi), 16 significant bits), and the down
+//   projection runs one MFMA on each, so h is not rounded to 8 bits.
+// * A token's result depends only on its own activations: the K order and the order in
+//   which the wave partials are added are fixed, so batch composition never changes a bit.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kSplit = 4;     // waves per workgroup = slices of the reduction axis
-constexpr int kGateTT = 4;    // tokens per pass, gate/up (bf16 activations: 16 SGPRs per block)
-constexpr int kDownTT = 2;    // tokens per pass, down (fp32 activations: 32 SGPRs per block)
-constexpr int kUnroll = 4;    // 32-element blocks in flight per lane
+constexpr int kSkM = 16;  // tokens per pass (MFMA M)
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// ------------------------------------------------------------------------------------
-// gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n])   (fp32 h)
-// ------------------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ void gateup_pass(const uint16_t* __restrict__ x, const uint8_t* __restrict__ gcr,
-                                            const uint8_t* __restrict__ gsr, const uint8_t* __restrict__ ucr,
-                                            const uint8_t* __restrict__ usr, const int32_t* __restrict__ perm,
-                                            float* __restrict__ hout, float (*red)[2 * kGateTT][64], int r_first,
-                                            int tk, int k, int H, int I, int n, bool nok, int kb0, int kb1) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  c_u32* xrow[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int t = row_token(perm, r_first + tt, tk, k);
-    xrow[tt] = (c_u32*)(x + (size_t)t * H);
-  }
-  float ag[NT], au[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) ag[tt] = au[tt] = 0.f;
-  for (int kb = kb0; kb < kb1; kb += kUnroll) {
-    uint4 cg[kUnroll], cu[kUnroll];
-    float sg[kUnroll], su[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int b = min(kb + u, kb1 - 1);  // tail: re-read the last block, contribution skipped
-      cg[u] = *reinterpret_cast<const uint4*>(gcr + (size_t)b * I * 16);
-      cu[u] = *reinterpret_cast<const uint4*>(ucr + (size_t)b * I * 16);
-      sg[u] = e8m0_to_f32(gsr[(size_t)b * I]);
-      su[u] = e8m0_to_f32(usr[(size_t)b * I]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (kb + u < kb1) {
-        const uint32_t cgw[4] = {cg[u].x, cg[u].y, cg[u].z, cg[u].w};
-        const uint32_t cuw[4] = {cu[u].x, cu[u].y, cu[u].z, cu[u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x2 wg[4], wu[4];
-          fp4x8_to_bf16(cgw[q], sg[u], wg);
-          fp4x8_to_bf16(cuw[q], su[u], wu);
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt) {
-            c_u32* xp = xrow[tt] + (size_t)(kb + u) * 16 + 4 * q;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const bf16x2 xv = as_bf16x2(xp[s]);
-              ag[tt] = __builtin_amdgcn_fdot2_f32_bf16(wg[s], xv, ag[tt], false);
-              au[tt] = __builtin_amdgcn_fdot2_f32_bf16(wu[s], xv, au[tt], false);
-            }
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    red[wave][2 * tt][lane] = ag[tt];
-    red[wave][2 * tt + 1][lane] = au[tt];
-  }
-  __syncthreads();
-  if (wave == 0 && nok) {
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      float g = red[0][2 * tt][lane], u = red[0][2 * tt + 1][lane];
-#pragma unroll
-      for (int w = 1; w < kSplit; ++w) {
-        g += red[w][2 * tt][lane];
-        u += red[w][2 * tt + 1][lane];
-      }
-      hout[(size_t)(r_first + tt) * I + n] = silu_f(g) * u;
-    }
-  }
-  __syncthreads();
+__device__ __forceinline__ uint32_t u4w(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ------------------------------------------------------------------------------------
+// Work split: a workgroup owns 64 rows of one group; its 4 waves take one quarter of the
+// reduction axis each and stream all 64 rows (4 MFMA column tiles sharing one activation
+// operand), reading 4 contiguous KiB per matrix per step.  The quarters are added through
+// LDS in a fixed order, wave w finishing column tile w.
+// ------------------------------------------------------------------------------------
+constexpr int kTiles = 4;   // 16-row MFMA column tiles per wave
+constexpr int kSplit = 4;   // waves per workgroup = reduction-axis quarters
+
+// One step of the gate/up stream: 4 blocks (lane q takes block kb + q) of the
+// wave's kTiles column tiles, both matrices, plus the matching activation slice.
+struct GateUpStage {
+  uint4 cg[kTiles], cu[kTiles], xa[4];
+  float sg[kTiles], su[kTiles];
+};
+
+__device__ __forceinline__ void load_gateup(GateUpStage& st, const uint8_t* __restrict__ gc,
+                                            const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uc,
+                                            const uint8_t* __restrict__ us, const uint16_t* __restrict__ xr,
+                                            const size_t* col, int kb, int kb_hi, int I, int q, bool mok) {
+  const int blk = kb + q;
+  const bool bok = blk < kb_hi;
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    st.cg[j] = st.cu[j] = make_uint4(0, 0, 0, 0);
+    st.sg[j] = st.su[j] = 0.f;
+    if (bok) {
+      const size_t c = col[j] + (size_t)blk * I;
+      st.cg[j] = *reinterpret_cast<const uint4*>(gc + c * 16);
+      st.cu[j] = *reinterpret_cast<const uint4*>(uc + c * 16);
+      st.sg[j] = e8m0_to_f32(gs[c]);
+      st.su[j] = e8m0_to_f32(us[c]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) st.xa[s] = make_uint4(0, 0, 0, 0);
+  if (bok && mok) {
+    const uint4* xp = reinterpret_cast<const uint4*>(xr + (size_t)blk * 32);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st.xa[s] = xp[s];
+  }
+}
+
+struct DownStage {
+  uint4 cd[kTiles], ha[4], la[4];
+  float sd[kTiles];
+};
+
+__device__ __forceinline__ void load_down(DownStage& st, const uint8_t* __restrict__ dc,
+                                          const uint8_t* __restrict__ ds, const uint16_t* __restrict__ hhi,
+                                          const uint16_t* __restrict__ hlo, size_t hrow, const size_t* col, int kb,
+                                          int kb_hi, int H, int q, bool mok) {
+  const int blk = kb + q;
+  const bool bok = blk < kb_hi;
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    st.cd[j] = make_uint4(0, 0, 0, 0);
+    st.sd[j] = 0.f;
+    if (bok) {
+      const size_t c = col[j] + (size_t)blk * H;
+      st.cd[j] = *reinterpret_cast<const uint4*>(dc + c * 16);
+      st.sd[j] = e8m0_to_f32(ds[c]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) st.ha[s] = st.la[s] = make_uint4(0, 0, 0, 0);
+  if (bok && mok) {
+    const uint4* hp = reinterpret_cast<const uint4*>(hhi + hrow + (size_t)blk * 32);
+    const uint4* lp = reinterpret_cast<const uint4*>(hlo + hrow + (size_t)blk * 32);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      st.ha[s] = hp[s];
+      st.la[s] = lp[s];
+    }
+  }
+}
+
+// gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), stored as bf16 hi + lo
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, float* __restrict__ hout, int T, int k, int H, int I) {
-  __shared__ float red[kSplit][2 * kGateTT][64];
+    const int32_t* __restrict__ grp_rows, uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo, int T, int k,
+    int H, int I) {
+  __shared__ f32x4 red[kSplit][kTiles][2][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
   const int rows = grp_rows[g], row0 = grp_row0[g];
-  // readfirstlane: the wave index is uniform, and the compiler must know it for scalar loads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 64 + lane;
-  const bool nok = n < I;
-  const int KB = H >> 5;
-  const int kb0 = wave * KB / kSplit, kb1 = (wave + 1) * KB / kSplit;
-  // kernel layout: block kb of row n of group g at ((g*KB + kb)*I + n) 16-byte chunks
-  const size_t col = (size_t)g * KB * I + (nok ? n : I - 1);
-  const uint8_t* gcr = gc + col * 16;
-  const uint8_t* ucr = uc + col * 16;
-  const uint8_t* gsr = gs + col;
-  const uint8_t* usr = us + col;
-  const int tk = T * k;
-  for (int c0 = 0; c0 < rows; c0 += kGateTT) {
-    switch (min(kGateTT, rows - c0)) {
-      case 1: gateup_pass<1>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
-      case 2: gateup_pass<2>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
-      case 3: gateup_pass<3>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
-      default: gateup_pass<4>(x, gcr, gsr, ucr, usr, perm, hout, red, row0 + c0, tk, k, H, I, n, nok, kb0, kb1); break;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------
-// down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n])    (fp32 h, fp32 FMA)
-// ------------------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ void down_pass(const float* __restrict__ hin, const uint8_t* __restrict__ dcr,
-                                          const uint8_t* __restrict__ dsr, const int32_t* __restrict__ perm,
-                                          const float* __restrict__ wts, float* __restrict__ staging,
-                                          float (*red)[kDownTT][64], int r_first, int tk, int H, int I, int n,
-                                          bool nok, int kb0, int kb1) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float a[NT];
+  const int m = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * (16 * kTiles);
+  const int KB = H >> 5;
+  const int kb_lo = wave * KB / kSplit, kb_hi = (wave + 1) * KB / kSplit;
+  const size_t gbase = (size_t)g * KB * I;
+  size_t col[kTiles];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) a[tt] = 0.f;
-  for (int kb = kb0; kb < kb1; kb += kUnroll) {
-    uint4 cd[kUnroll];
-    float sd[kUnroll];
+  for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, I - 1);
+  const int tk = T * k;
+  for (int c0 = 0; c0 < rows; c0 += kSkM) {
+    const int nt = min(kSkM, rows - c0);
+    const bool mok = m < nt;
+    const uint16_t* xr = x + (size_t)(mok ? row_token(perm, row0 + c0 + m, tk, k) : 0) * H;
+    f32x4 ag[kTiles], au[kTiles];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int b = min(kb + u, kb1 - 1);
-      cd[u] = *reinterpret_cast<const uint4*>(dcr + (size_t)b * H * 16);
-      sd[u] = e8m0_to_f32(dsr[(size_t)b * H]);
-    }
+    for (int j = 0; j < kTiles; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = kb_lo; kb < kb_hi; kb += 4) {
+      GateUpStage cur;
+      load_gateup(cur, gc, gs, uc, us, xr, col, kb, kb_hi, I, q, mok);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (kb + u < kb1) {
-        const uint32_t cw[4] = {cd[u].x, cd[u].y, cd[u].z, cd[u].w};
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = as_bf16x8(cur.xa[s]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x2 wv[4];
-          fp4x8_to_f32(cw[q], sd[u], wv);
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt) {
-            c_f32* hp = (c_f32*)(hin + (size_t)(r_first + tt) * I + (size_t)(kb + u) * 32 + 8 * q);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              a[tt] = fmaf(wv[s].x, hp[2 * s], a[tt]);
-              a[tt] = fmaf(wv[s].y, hp[2 * s + 1], a[tt]);
-            }
-          }
+        for (int j = 0; j < kTiles; ++j) {
+          ag[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16x8(u4w(cur.cg[j], s), cur.sg[j]), ag[j], 0,
+                                                          0, 0);
+          au[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16x8(u4w(cur.cu[j], s), cur.su[j]), au[j], 0,
+                                                          0, 0);
         }
       }
     }
-  }
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) red[wave][tt][lane] = a[tt];
-  __syncthreads();
-  if (wave == 0 && nok) {
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      float s = red[0][tt][lane];
-#pragma unroll
-      for (int w = 1; w < kSplit; ++w) s += red[w][tt][lane];
-      const int r = r_first + tt;
-      const int slot = r < tk ? perm[r] : r;
-      const float wt = r < tk ? wts[slot] : 1.0f;
-      staging[(size_t)slot * H + n] = s * wt;
+    for (int j = 0; j < kTiles; ++j) {
+      red[wave][j][0][lane] = ag[j];
+      red[wave][j][1][lane] = au[j];
     }
+    __syncthreads();
+    {
+      const int j = wave;  // wave w finishes column tile w
+      f32x4 gsum = red[0][j][0][lane], usum = red[0][j][1][lane];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) {
+        gsum += red[w][j][0][lane];
+        usum += red[w][j][1][lane];
+      }
+      const int n = n0 + 16 * j + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * q + i;  // lane (n, q) holds tokens 4q .. 4q+3 of row n
+        if (n < I && tok < nt) {
+          const float hv = silu_f(gsum[i]) * usum[i];
+          const uint16_t hi = bf16_bits(hv);
+          const size_t o = (size_t)(row0 + c0 + tok) * I + n;
+          hhi[o] = hi;
+          hlo[o] = bf16_bits(hv - bf16_val(hi));
+        }
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
+// down:  staging[slot(r)][n] = weight(r) * ((h_hi + h_lo)_r . Wd[n])
 __global__ __launch_bounds__(256) void gemv_down_kernel(
-    const float* __restrict__ hin, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
-    const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ act,
-    const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
-    float* __restrict__ staging, int T, int k, int H, int I) {
-  __shared__ float red[kSplit][kDownTT][64];
+    const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo, const uint8_t* __restrict__ dc,
+    const uint8_t* __restrict__ ds, const int32_t* __restrict__ perm, const float* __restrict__ wts,
+    const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
+    const int32_t* __restrict__ grp_rows, float* __restrict__ staging, int T, int k, int H, int I) {
+  __shared__ f32x4 red[kSplit][kTiles][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
   const int rows = grp_rows[g], row0 = grp_row0[g];
-  // readfirstlane: the wave index is uniform, and the compiler must know it for scalar loads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 64 + lane;
-  const bool nok = n < H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * (16 * kTiles);
   const int KB = I >> 5;
-  const int kb0 = wave * KB / kSplit, kb1 = (wave + 1) * KB / kSplit;
-  const size_t col = (size_t)g * KB * H + (nok ? n : H - 1);
-  const uint8_t* dcr = dc + col * 16;
-  const uint8_t* dsr = ds + col;
+  const int kb_lo = wave * KB / kSplit, kb_hi = (wave + 1) * KB / kSplit;
+  const size_t gbase = (size_t)g * KB * H;
+  size_t col[kTiles];
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, H - 1);
   const int tk = T * k;
-  for (int c0 = 0; c0 < rows; c0 += kDownTT) {
-    if (rows - c0 >= 2)
-      down_pass<2>(hin, dcr, dsr, perm, wts, staging, red, row0 + c0, tk, H, I, n, nok, kb0, kb1);
-    else
-      down_pass<1>(hin, dcr, dsr, perm, wts, staging, red, row0 + c0, tk, H, I, n, nok, kb0, kb1);
+  for (int c0 = 0; c0 < rows; c0 += kSkM) {
+    const int nt = min(kSkM, rows - c0);
+    const bool mok = m < nt;
+    const size_t hrow = (size_t)(row0 + c0 + (mok ? m : 0)) * I;
+    f32x4 acc[kTiles];
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = kb_lo; kb < kb_hi; kb += 4) {
+      DownStage cur;
+      load_down(cur, dc, ds, hhi, hlo, hrow, col, kb, kb_hi, H, q, mok);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int j = 0; j < kTiles; ++j) {
+          const bf16x8 b = fp4x8_to_bf16x8(u4w(cur.cd[j], s), cur.sd[j]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ha[s]), b, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.la[s]), b, acc[j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    {
+      const int j = wave;
+      f32x4 sum = red[0][j][lane];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) sum += red[w][j][lane];
+      const int n = n0 + 16 * j + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * q + i;
+        if (n < H && tok < nt) {
+          const int r = row0 + c0 + tok;
+          const int slot = r < tk ? perm[r] : r;
+          const float wt = r < tk ? wts[slot] : 1.0f;
+          staging[(size_t)slot * H + n] = sum[i] * wt;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int max_act, hipStream_t s) {
-  dim3 grid((d.I + 63) / 64, max_act);
+  dim3 grid((d.I + 16 * kTiles - 1) / (16 * kTiles), max_act);
+  uint16_t* hhi = static_cast<uint16_t*>(b.h);
+  uint16_t* hlo = hhi + (size_t)T * (d.K + d.S) * d.I;
   const int tk = timing_begin("gemv_gateup", s);
   gemv_gateup_kernel<<<grid, 64 * kSplit, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
-                                                  b.act, b.info, b.grp_row0, b.grp_rows, static_cast<float*>(b.h),
-                                                  T, d.K, d.H, d.I);
+                                                  b.act, b.info, b.grp_row0, b.grp_rows, hhi, hlo, T, d.K, d.H, d.I);
   timing_end(tk, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
                             hipStream_t s) {
-  dim3 grid((d.H + 63) / 64, max_act);
+  dim3 grid((d.H + 16 * kTiles - 1) / (16 * kTiles), max_act);
+  const uint16_t* hhi = static_cast<const uint16_t*>(b.h);
+  const uint16_t* hlo = hhi + (size_t)T * (d.K + d.S) * d.I;
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const float*>(b.h), w.down_codes, w.down_scales, b.perm,
-                                                b.w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H,
-                                                d.I);
+  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(hhi, hlo, w.down_codes, w.down_scales, b.perm, b.w, b.act, b.info,
+                                                b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H, d.I);
   timing_end(tk, s);
   return hipGetLastError();
 }
