@@ -56,11 +56,14 @@ class RouteOut(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load (once) and type the C ABI.  Raises if the library was not built."""
+def load(path: str = None) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library was not built.
+
+    ``MOE_LIB`` in the environment names another build of the same library (A/B runs)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MOE_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is missing; run fp4_routed_expert_moe_amd/build.py "
                            "(or __graft_entry__.build()) first")

@@ -65,6 +65,7 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   t.mt_group = reinterpret_cast<int32_t*>(take(mt_bound * 4));
   t.mt_row0 = reinterpret_cast<int32_t*>(take(mt_bound * 4));
   t.h = take(rows * d.I * 4);
+  t.xq = reinterpret_cast<uint8_t*>(take((size_t)T * d.H * 2 + (size_t)T * (d.H / 32)));
   t.staging = reinterpret_cast<float*>(take(rows * d.H * 4));
   if (b) *b = t;
   return off;
@@ -257,9 +258,13 @@ static int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void
   return MOE_OK;
 }
 
-static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s) {
+// Routing; when quantize_x is set the router kernel also writes the FP8 activation terms
+// the GEMV path reads.
+static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
+                             bool quantize_x) {
   const moe::Dims& d = L->dims;
-  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b.logits, T, s);
+  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b.logits, T,
+                                           quantize_x ? b.xq : nullptr, s);
   if (e == hipSuccess) e = T <= moe::kChunk ? moe::launch_route_small(d, b, T, s) : moe::launch_route_chunked(d, b, T, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -287,7 +292,7 @@ int32_t moe_route(const moe_layer* L, const uint16_t* x, int32_t T, const moe_ro
   moe::CallBufs b;
   carve(L->dims, T, static_cast<char*>(ws), &b);
   use_route_out(b, route);
-  return enqueue_route(L, x, T, b, static_cast<hipStream_t>(stream));
+  return enqueue_route(L, x, T, b, static_cast<hipStream_t>(stream), false);
 }
 
 int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
@@ -304,9 +309,9 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   carve(d, T, static_cast<char*>(ws), &b);
   if (route) use_route_out(b, route);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = enqueue_route(L, x, T, b, s);
-  if (st != MOE_OK) return st;
   const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
+  st = enqueue_route(L, x, T, b, s, gemv);
+  if (st != MOE_OK) return st;
   hipError_t e;
   if (gemv) {
     const int na = max_active_of(d, T);

@@ -51,6 +51,34 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
   return r;
 }
 
+// ---- exact FP8 (e4m3) term splits for the block-scaled MFMA ------------------------
+// A 32-value block v is written as S * (t0 + t1/16 + t2/256 + ...), each t an e4m3 value, with
+// S = 2^(s-127) a power of two chosen from the block's largest magnitude so that |v/S| < 256
+// (e4m3 saturates at 448 and the converts round to nearest even).  Term i carries e8m0 scale
+// s - 4i.  Each term keeps 4 significant bits of what the previous terms left, so two terms
+// hold a bf16 value exactly and three terms hold 12 significant bits of an fp32 value
+// (values below 2^-14 of the block maximum keep fewer).
+__device__ __forceinline__ int fp8_block_scale(float amax) {
+  if (!(amax > 0.f)) return 127;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  return max(e - 7, 9);
+}
+__device__ __forceinline__ float fp8_inv_scale(int s) { return __uint_as_float((uint32_t)(254 - s) << 23); }
+
+// Four values -> one dword of e4m3 bytes (value i in byte i).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return (uint32_t)p;
+}
+// One value -> its e4m3 byte, and back.
+__device__ __forceinline__ uint32_t fp8_of(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
@@ -80,7 +108,8 @@ struct CallBufs {
   int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles
   int32_t* mt_group;  // [mt_bound]
   int32_t* mt_row0;   // [mt_bound]
-  void* h;            // [T(k+S)][I] fp32 (GEMV path) or bf16 (GEMM path)
+  void* h;            // GEMV path: h as FP8 terms + scales (see gemv.hip); GEMM path: bf16 [T(k+S)][I]
+  uint8_t* xq;        // GEMV path: x as 2 FP8 terms [2][T][H] then e8m0 scales [T][H/32]
   float* staging;     // [T(k+S)][H] weighted expert outputs, slot-indexed
 };
 
@@ -90,7 +119,7 @@ void timing_end(int token, hipStream_t s);
 
 // ---- launchers (return hipGetLastError of the launch) ---------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                float* logits, int T, hipStream_t s);
+                                float* logits, int T, uint8_t* xq, hipStream_t s);
 hipError_t launch_route_small(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 

@@ -4,124 +4,70 @@
 // "feat(dsv4): DeepSeek V4 Flash support -- CUDA/VRAM expert tiering ..." (PR #1031) makes a
 // custom FP4 expert-grouped matvec the default GPU expert path, and "Add DeepSeek V4 Flash
 // CPU inference with NVMe expert streaming" (PR #165, the NEON rows16 comment) pairs gate
-// and up in one "dual" pass over interleaved rows.  On gfx950 the products go to the matrix
-// cores, so the vector ALU only converts FP4 to bf16 (one convert per code byte):
+// and up in one "dual" pass over interleaved rows.  On gfx950 the products run on the
+// block-scaled matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4), which take the e2m1 codes
+// and their e8m0 scales exactly as stored: no convert touches the weights.
 //
-// * Gate and up row n are produced by the same lane, so SwiGLU stays in registers; the
-//   tokens of one group are the MFMA's M side, up to 16 per pass -- one pass for every group
-//   in decode, whatever its token count.
-// * Lane (n, q) loads one whole 16-byte block (32 values) of row n from the block-interleaved
-//   kernel layout (a wave reads 4 x 256 contiguous bytes) and feeds it to four
-//   16x16x32 bf16 MFMAs, eight values each.  The activation lanes (m, q) supply the same
-//   K values of token m, so each MFMA sums one 8-value slice of four blocks; over the four
-//   MFMAs every K value is met once.  Each lane scales by its own block's e8m0 inside the
-//   convert (exact: a power of two).
-// * Products bf16 x bf16 are exact in fp32 and accumulate in fp32.  h leaves gate/up as a
-//   bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi), 16 significant bits), and the down
-//   projection runs one MFMA on each, so h is not rounded to 8 bits.
-// * A token's result depends only on its own activations: the K order and the order in
-//   which the wave partials are added are fixed, so batch composition never changes a bit.
+// * B (weights, FP4): lane (n, q) holds block kb+q of row n -- one 16-byte chunk of the
+//   block-interleaved kernel layout (a wave reads 4 x 256 contiguous bytes per column tile)
+//   -- and that block's scale byte.
+// * A (activations, FP8 e4m3): lane (m, q) holds 16 values at K offset 16q and 16 at 64+16q
+//   of the 128-value step for token m, plus the scale of block kb+q.  Activations arrive as
+//   exact FP8 term splits (x: 2 terms = all 8 bf16 bits; h: 3 terms = 12 bits), one MFMA
+//   per term, all accumulating in fp32.
+// * A wave owns 64 rows (4 column tiles of 16 sharing the activation operand) and one
+//   quarter of the reduction axis; the 4 quarters are added through LDS in a fixed order.
+//   Gate and up row n meet in the same lane, so SwiGLU stays in registers.  The tokens of
+//   a group are the MFMA's M side, up to 16 per pass: one pass per group in decode.
+// * A token's result depends only on its own activations (fixed K and reduction order), so
+//   batch composition never changes a bit of it.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kSkM = 16;  // tokens per pass (MFMA M)
+constexpr int kSkM = 16;    // tokens per pass (MFMA M)
+#ifndef MOE_GEMV_TILES
+#define MOE_GEMV_TILES 4
+#endif
+#ifndef MOE_GEMV_SPLIT
+#define MOE_GEMV_SPLIT 4
+#endif
+constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (even)
+constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ uint32_t u4w(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+__device__ __forceinline__ i32x8 fp4_operand(const uint4& c) {
+  return i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};  // FP4 reads the low 4 dwords
+}
+__device__ __forceinline__ i32x8 fp8_operand(const uint4& lo, const uint4& hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// acc += A(fp8, scale sa) x B(fp4, scale sb)
+__device__ __forceinline__ f32x4 mma_f8f4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
+}
+
+// Loads the FP8 activation operand of term `t` for lane (m, q) at step kb: K values
+// kb*32 + 16q .. +16 (block kb + q/2) and kb*32 + 64 + 16q .. +16 (block kb + 2 + q/2).
+__device__ __forceinline__ i32x8 load_act(const uint8_t* __restrict__ row, int kb, int q, bool ok1, bool ok2) {
+  const uint8_t* p = row + (size_t)kb * 32 + 16 * q;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  return fp8_operand(ok1 ? ld16(p) : z, ok2 ? ld16(p + 64) : z);
+}
 
 // ------------------------------------------------------------------------------------
-// Work split: a workgroup owns 64 rows of one group; its 4 waves take one quarter of the
-// reduction axis each and stream all 64 rows (4 MFMA column tiles sharing one activation
-// operand), reading 4 contiguous KiB per matrix per step.  The quarters are added through
-// LDS in a fixed order, wave w finishing column tile w.
+// gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
+// (h8 = [3][rows][I] bytes, hs = [rows][I/32] e8m0).
 // ------------------------------------------------------------------------------------
-constexpr int kTiles = 4;   // 16-row MFMA column tiles per wave
-constexpr int kSplit = 4;   // waves per workgroup = reduction-axis quarters
-
-// One step of the gate/up stream: 4 blocks (lane q takes block kb + q) of the
-// wave's kTiles column tiles, both matrices, plus the matching activation slice.
-struct GateUpStage {
-  uint4 cg[kTiles], cu[kTiles], xa[4];
-  float sg[kTiles], su[kTiles];
-};
-
-__device__ __forceinline__ void load_gateup(GateUpStage& st, const uint8_t* __restrict__ gc,
-                                            const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uc,
-                                            const uint8_t* __restrict__ us, const uint16_t* __restrict__ xr,
-                                            const size_t* col, int kb, int kb_hi, int I, int q, bool mok) {
-  const int blk = kb + q;
-  const bool bok = blk < kb_hi;
-#pragma unroll
-  for (int j = 0; j < kTiles; ++j) {
-    st.cg[j] = st.cu[j] = make_uint4(0, 0, 0, 0);
-    st.sg[j] = st.su[j] = 0.f;
-    if (bok) {
-      const size_t c = col[j] + (size_t)blk * I;
-      st.cg[j] = *reinterpret_cast<const uint4*>(gc + c * 16);
-      st.cu[j] = *reinterpret_cast<const uint4*>(uc + c * 16);
-      st.sg[j] = e8m0_to_f32(gs[c]);
-      st.su[j] = e8m0_to_f32(us[c]);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) st.xa[s] = make_uint4(0, 0, 0, 0);
-  if (bok && mok) {
-    const uint4* xp = reinterpret_cast<const uint4*>(xr + (size_t)blk * 32);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) st.xa[s] = xp[s];
-  }
-}
-
-struct DownStage {
-  uint4 cd[kTiles], ha[4], la[4];
-  float sd[kTiles];
-};
-
-__device__ __forceinline__ void load_down(DownStage& st, const uint8_t* __restrict__ dc,
-                                          const uint8_t* __restrict__ ds, const uint16_t* __restrict__ hhi,
-                                          const uint16_t* __restrict__ hlo, size_t hrow, const size_t* col, int kb,
-                                          int kb_hi, int H, int q, bool mok) {
-  const int blk = kb + q;
-  const bool bok = blk < kb_hi;
-#pragma unroll
-  for (int j = 0; j < kTiles; ++j) {
-    st.cd[j] = make_uint4(0, 0, 0, 0);
-    st.sd[j] = 0.f;
-    if (bok) {
-      const size_t c = col[j] + (size_t)blk * H;
-      st.cd[j] = *reinterpret_cast<const uint4*>(dc + c * 16);
-      st.sd[j] = e8m0_to_f32(ds[c]);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) st.ha[s] = st.la[s] = make_uint4(0, 0, 0, 0);
-  if (bok && mok) {
-    const uint4* hp = reinterpret_cast<const uint4*>(hhi + hrow + (size_t)blk * 32);
-    const uint4* lp = reinterpret_cast<const uint4*>(hlo + hrow + (size_t)blk * 32);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      st.ha[s] = hp[s];
-      st.la[s] = lp[s];
-    }
-  }
-}
-
-// gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), stored as bf16 hi + lo
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo, int T, int k,
-    int H, int I) {
+    const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, int T, int k, int H, int I, int R) {
   __shared__ f32x4 red[kSplit][kTiles][2][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
@@ -135,27 +81,46 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   size_t col[kTiles];
 #pragma unroll
   for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, I - 1);
+  const uint8_t* x_hi = xq;
+  const uint8_t* x_lo = xq + (size_t)T * H;
+  const uint8_t* x_sc = xq + (size_t)2 * T * H;
+  uint8_t* hs = h8 + (size_t)3 * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
     const bool mok = m < nt;
-    const uint16_t* xr = x + (size_t)(mok ? row_token(perm, row0 + c0 + m, tk, k) : 0) * H;
+    const int tok = mok ? row_token(perm, row0 + c0 + m, tk, k) : 0;
     f32x4 ag[kTiles], au[kTiles];
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int kb = kb_lo; kb < kb_hi; kb += 4) {
-      GateUpStage cur;
-      load_gateup(cur, gc, gs, uc, us, xr, col, kb, kb_hi, I, q, mok);
+      const int blk = kb + q;
+      const bool bok = blk < kb_hi;
+      uint4 cg[kTiles], cu[kTiles];
+      int sg[kTiles], su[kTiles];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = as_bf16x8(cur.xa[s]);
-#pragma unroll
-        for (int j = 0; j < kTiles; ++j) {
-          ag[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16x8(u4w(cur.cg[j], s), cur.sg[j]), ag[j], 0,
-                                                          0, 0);
-          au[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16x8(u4w(cur.cu[j], s), cur.su[j]), au[j], 0,
-                                                          0, 0);
+      for (int j = 0; j < kTiles; ++j) {
+        cg[j] = cu[j] = make_uint4(0, 0, 0, 0);
+        sg[j] = su[j] = 127;
+        if (bok) {
+          const size_t c = col[j] + (size_t)blk * I;
+          cg[j] = ld16(gc + c * 16);
+          cu[j] = ld16(uc + c * 16);
+          sg[j] = gs[c];
+          su[j] = us[c];
         }
+      }
+      const bool ok1 = mok && kb + (q >> 1) < kb_hi, ok2 = mok && kb + 2 + (q >> 1) < kb_hi;
+      const i32x8 a0 = load_act(x_hi + (size_t)tok * H, kb, q, ok1, ok2);
+      const i32x8 a1 = load_act(x_lo + (size_t)tok * H, kb, q, ok1, ok2);
+      const int sx = (bok && mok) ? x_sc[(size_t)tok * KB + blk] : 127;
+#pragma unroll
+      for (int j = 0; j < kTiles; ++j) {
+        const i32x8 bg = fp4_operand(cg[j]), bu = fp4_operand(cu[j]);
+        ag[j] = mma_f8f4(a0, bg, ag[j], sx, sg[j]);
+        au[j] = mma_f8f4(a0, bu, au[j], sx, su[j]);
+        ag[j] = mma_f8f4(a1, bg, ag[j], sx - 4, sg[j]);
+        au[j] = mma_f8f4(a1, bu, au[j], sx - 4, su[j]);
       }
     }
 #pragma unroll
@@ -164,24 +129,48 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
       red[wave][j][1][lane] = au[j];
     }
     __syncthreads();
-    {
-      const int j = wave;  // wave w finishes column tile w
-      f32x4 gsum = red[0][j][0][lane], usum = red[0][j][1][lane];
+    if (wave < kTiles / 2) {
+      // wave p finishes column tiles 2p and 2p+1 = one 32-column block of h
+      const int p = wave;
+      float hv[2][4];
 #pragma unroll
-      for (int w = 1; w < kSplit; ++w) {
-        gsum += red[w][j][0][lane];
-        usum += red[w][j][1][lane];
+      for (int c = 0; c < 2; ++c) {
+        const int j = 2 * p + c;
+        f32x4 gsum = red[0][j][0][lane], usum = red[0][j][1][lane];
+#pragma unroll
+        for (int w = 1; w < kSplit; ++w) {
+          gsum += red[w][j][0][lane];
+          usum += red[w][j][1][lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[c][i] = silu_f(gsum[i]) * usum[i];
       }
-      const int n = n0 + 16 * j + m;
+      const int nb = n0 + 32 * p;  // first column of the block
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * q + i;  // lane (n, q) holds tokens 4q .. 4q+3 of row n
-        if (n < I && tok < nt) {
-          const float hv = silu_f(gsum[i]) * usum[i];
-          const uint16_t hi = bf16_bits(hv);
-          const size_t o = (size_t)(row0 + c0 + tok) * I + n;
-          hhi[o] = hi;
-          hlo[o] = bf16_bits(hv - bf16_val(hi));
+        // lanes with the same q hold the same 4 tokens: reduce |h| over the 32 columns
+        float a = fmaxf(fabsf(hv[0][i]), fabsf(hv[1][i]));
+#pragma unroll
+        for (int msk = 1; msk < 16; msk <<= 1) a = fmaxf(a, __shfl_xor(a, msk, 64));
+        const int sc = fp8_block_scale(a);
+        const float inv = fp8_inv_scale(sc);
+        const int tok_i = 4 * q + i;
+        if (nb < I && tok_i < nt) {
+          const size_t r = (size_t)(row0 + c0 + tok_i);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float v = hv[c][i] * inv;
+            const uint32_t t0 = fp8_of(v);
+            v = (v - f32_of_fp8(t0)) * 16.f;
+            const uint32_t t1 = fp8_of(v);
+            v = (v - f32_of_fp8(t1)) * 16.f;
+            const uint32_t t2 = fp8_of(v);
+            const size_t o = r * I + nb + 16 * c + m;
+            h8[o] = (uint8_t)t0;
+            h8[(size_t)R * I + o] = (uint8_t)t1;
+            h8[(size_t)2 * R * I + o] = (uint8_t)t2;
+          }
+          if (m == 0) hs[r * (I >> 5) + (nb >> 5)] = (uint8_t)sc;
         }
       }
     }
@@ -189,12 +178,14 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   }
 }
 
-// down:  staging[slot(r)][n] = weight(r) * ((h_hi + h_lo)_r . Wd[n])
+// ------------------------------------------------------------------------------------
+// down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms
+// ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemv_down_kernel(
-    const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo, const uint8_t* __restrict__ dc,
-    const uint8_t* __restrict__ ds, const int32_t* __restrict__ perm, const float* __restrict__ wts,
-    const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, float* __restrict__ staging, int T, int k, int H, int I) {
+    const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
+    const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ act,
+    const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
+    float* __restrict__ staging, int T, int k, int H, int I, int R) {
   __shared__ f32x4 red[kSplit][kTiles][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = act[blockIdx.y];
@@ -208,43 +199,62 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   size_t col[kTiles];
 #pragma unroll
   for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, H - 1);
+  const uint8_t* hs = h8 + (size_t)3 * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
     const bool mok = m < nt;
-    const size_t hrow = (size_t)(row0 + c0 + (mok ? m : 0)) * I;
+    const size_t r = (size_t)(row0 + c0 + (mok ? m : 0));
+    const uint8_t* t0row = h8 + r * I;
+    const uint8_t* t1row = t0row + (size_t)R * I;
+    const uint8_t* t2row = t1row + (size_t)R * I;
     f32x4 acc[kTiles];
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int kb = kb_lo; kb < kb_hi; kb += 4) {
-      DownStage cur;
-      load_down(cur, dc, ds, hhi, hlo, hrow, col, kb, kb_hi, H, q, mok);
+      const int blk = kb + q;
+      const bool bok = blk < kb_hi;
+      uint4 cd[kTiles];
+      int sd[kTiles];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int j = 0; j < kTiles; ++j) {
-          const bf16x8 b = fp4x8_to_bf16x8(u4w(cur.cd[j], s), cur.sd[j]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ha[s]), b, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.la[s]), b, acc[j], 0, 0, 0);
+      for (int j = 0; j < kTiles; ++j) {
+        cd[j] = make_uint4(0, 0, 0, 0);
+        sd[j] = 127;
+        if (bok) {
+          const size_t c = col[j] + (size_t)blk * H;
+          cd[j] = ld16(dc + c * 16);
+          sd[j] = ds[c];
         }
+      }
+      const bool ok1 = mok && kb + (q >> 1) < kb_hi, ok2 = mok && kb + 2 + (q >> 1) < kb_hi;
+      const i32x8 a0 = load_act(t0row, kb, q, ok1, ok2);
+      const i32x8 a1 = load_act(t1row, kb, q, ok1, ok2);
+      const i32x8 a2 = load_act(t2row, kb, q, ok1, ok2);
+      const int sh = (bok && mok) ? hs[r * KB + blk] : 127;
+#pragma unroll
+      for (int j = 0; j < kTiles; ++j) {
+        const i32x8 b = fp4_operand(cd[j]);
+        acc[j] = mma_f8f4(a0, b, acc[j], sh, sd[j]);
+        acc[j] = mma_f8f4(a1, b, acc[j], sh - 4, sd[j]);
+        acc[j] = mma_f8f4(a2, b, acc[j], sh - 8, sd[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) red[wave][j][lane] = acc[j];
     __syncthreads();
-    {
-      const int j = wave;
+    if (wave < kTiles) {
+      const int j = wave;  // wave w finishes column tile w
       f32x4 sum = red[0][j][lane];
 #pragma unroll
       for (int w = 1; w < kSplit; ++w) sum += red[w][j][lane];
       const int n = n0 + 16 * j + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * q + i;
-        if (n < H && tok < nt) {
-          const int r = row0 + c0 + tok;
-          const int slot = r < tk ? perm[r] : r;
-          const float wt = r < tk ? wts[slot] : 1.0f;
+        const int tk_i = 4 * q + i;  // lane (n, q) holds tokens 4q .. 4q+3 of row n
+        if (n < H && tk_i < nt) {
+          const int rr = row0 + c0 + tk_i;
+          const int slot = rr < tk ? perm[rr] : rr;
+          const float wt = rr < tk ? wts[slot] : 1.0f;
           staging[(size_t)slot * H + n] = sum[i] * wt;
         }
       }
@@ -256,12 +266,13 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int max_act, hipStream_t s) {
+  (void)x;
   dim3 grid((d.I + 16 * kTiles - 1) / (16 * kTiles), max_act);
-  uint16_t* hhi = static_cast<uint16_t*>(b.h);
-  uint16_t* hlo = hhi + (size_t)T * (d.K + d.S) * d.I;
+  const int R = T * (d.K + d.S);
   const int tk = timing_begin("gemv_gateup", s);
-  gemv_gateup_kernel<<<grid, 64 * kSplit, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
-                                                  b.act, b.info, b.grp_row0, b.grp_rows, hhi, hlo, T, d.K, d.H, d.I);
+  gemv_gateup_kernel<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
+                                                  b.act, b.info, b.grp_row0, b.grp_rows,
+                                                  static_cast<uint8_t*>(b.h), T, d.K, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }
@@ -269,11 +280,11 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
                             hipStream_t s) {
   dim3 grid((d.H + 16 * kTiles - 1) / (16 * kTiles), max_act);
-  const uint16_t* hhi = static_cast<const uint16_t*>(b.h);
-  const uint16_t* hlo = hhi + (size_t)T * (d.K + d.S) * d.I;
+  const int R = T * (d.K + d.S);
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(hhi, hlo, w.down_codes, w.down_scales, b.perm, b.w, b.act, b.info,
-                                                b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H, d.I);
+  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,
+                                                b.w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H,
+                                                d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }

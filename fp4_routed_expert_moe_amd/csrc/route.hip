@@ -19,16 +19,56 @@ namespace moe {
 // ------------------------------------------------------------------------------------
 constexpr int kRouterTT = 8;
 
+// When xq is not NULL the workgroups of a token tile also write the tile's activations as
+// two exact FP8 terms with a scale per 32-value block (the decode kernels' A operand):
+// xq = [2][T][H] e4m3 bytes, then [T][H/32] e8m0 scales.
+__device__ void quantize_x_block(const uint16_t* __restrict__ src, uint8_t* __restrict__ hi,
+                                 uint8_t* __restrict__ lo, uint8_t* __restrict__ sc) {
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  const int s = fp8_block_scale(amax);
+  const float inv = fp8_inv_scale(s);
+  uint32_t th[8], tl[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[4] = {bf16_lo(w[2 * i]) * inv, bf16_hi(w[2 * i]) * inv, bf16_lo(w[2 * i + 1]) * inv,
+                  bf16_hi(w[2 * i + 1]) * inv};
+    th[i] = pack_fp8x4(v[0], v[1], v[2], v[3]);
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (v[j] - f32_of_fp8((th[i] >> (8 * j)) & 0xFFu)) * 16.f;
+    tl[i] = pack_fp8x4(r[0], r[1], r[2], r[3]);
+  }
+  reinterpret_cast<uint4*>(hi)[0] = make_uint4(th[0], th[1], th[2], th[3]);
+  reinterpret_cast<uint4*>(hi)[1] = make_uint4(th[4], th[5], th[6], th[7]);
+  reinterpret_cast<uint4*>(lo)[0] = make_uint4(tl[0], tl[1], tl[2], tl[3]);
+  reinterpret_cast<uint4*>(lo)[1] = make_uint4(tl[4], tl[5], tl[6], tl[7]);
+  *sc = (uint8_t)s;
+}
+
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T, int E,
-                                                            int H) {
+                                                            int H, uint8_t* __restrict__ xq) {
   __shared__ float part[4][kRouterTT];
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kRouterTT;
   const int nt = min(kRouterTT, T - t0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (xq) {
+    const int KB = H >> 5;
+    for (int j = e * 256 + tid; j < nt * KB; j += E * 256) {
+      const int t = t0 + j / KB, b = j % KB;
+      quantize_x_block(x + (size_t)t * H + b * 32, xq + (size_t)t * H + b * 32,
+                       xq + (size_t)(T + t) * H + b * 32, xq + (size_t)2 * T * H + (size_t)t * KB + b);
+    }
+  }
   float acc[kRouterTT];
 #pragma unroll
   for (int i = 0; i < kRouterTT; ++i) acc[i] = 0.f;
@@ -333,10 +373,10 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                float* logits, int T, hipStream_t s) {
+                                float* logits, int T, uint8_t* xq, hipStream_t s) {
   dim3 grid(d.E, (T + kRouterTT - 1) / kRouterTT);
   const int tk = timing_begin("router_logits", s);
-  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, bias, logits, T, d.E, d.H);
+  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, bias, logits, T, d.E, d.H, xq);
   timing_end(tk, s);
   return hipGetLastError();
 }

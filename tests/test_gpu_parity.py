@@ -122,10 +122,10 @@ def test_every_token_on_one_expert():
 
 
 def test_zero_and_extreme_scales():
-    # s=0 blocks contribute exactly zero; scales far from 1 stay exact inside the converts.
-    # The GEMV path keeps fp32 activations end to end, so it is held to rel-L2 1e-5 over a
-    # wide scale range; the GEMM path rounds h to bf16 (heavier-tailed outputs here), so it
-    # gets a narrower range under the standard gate.
+    # s=0 blocks contribute exactly zero; the e8m0 scales are applied exactly by the hardware.
+    # The GEMV path carries x exactly and h with 12 significant bits (three FP8 terms), so it
+    # is held to rel-L2 1e-4 over a wide scale range; the GEMM path rounds h to bf16 (8 bits;
+    # heavier-tailed outputs here), so it gets a narrower range under the standard gate.
     for path, lo, hi in (("gemv", 110, 136), ("gemm", 120, 130)):
         groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=lo, scale_hi=hi)
         for g in groups[::2]:
@@ -135,7 +135,7 @@ def test_zero_and_extreme_scales():
         if path == "gemv":
             ref = oracle.moe_forward(x, wr, b, groups, 2, 1)["y"]
             d = outs["gemv"]["y"].astype(np.float64) - ref
-            assert np.linalg.norm(d) <= 1e-5 * np.linalg.norm(ref)
+            assert np.linalg.norm(d) <= 1e-4 * np.linalg.norm(ref)
 
 
 def test_single_token_and_batch_equals_single():
