@@ -37,26 +37,28 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link the shared library; returns its path."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB_PATH, build_dir: str = BUILD_DIR) -> str:
+    """Compile every source (always) and link the shared library; returns its path.
+
+    ``extra_flags`` (e.g. ``-DMOE_GEMV_TILES=2``) and ``out`` build a variant elsewhere."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     jobs = []
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         for src in SOURCES:
-            obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+            obj = os.path.join(build_dir, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd))
         for j in jobs:
-            out = j.result()
-            if verbose and out.strip():
-                print(out, file=sys.stderr)
-    tmp = LIB_PATH + ".tmp"
+            log = j.result()
+            if verbose and log.strip():
+                print(log, file=sys.stderr)
+    tmp = out + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -50,6 +50,8 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   const size_t gnz = std::min<size_t>(d.E, tk) + d.S;
   const size_t mt_bound = (rows + gnz * (moe::kGemmBM - 1)) / moe::kGemmBM + 1;
   moe::CallBufs t{};
+  // control words first: their offset must not depend on T (zero between calls)
+  t.ctrl = reinterpret_cast<int32_t*>(take(256));
   t.logits = reinterpret_cast<float*>(take((size_t)T * d.E * 4));
   t.idx = reinterpret_cast<int32_t*>(take(tk * 4));
   t.w = reinterpret_cast<float*>(take(tk * 4));
@@ -263,9 +265,8 @@ static int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void
 static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
                              bool quantize_x) {
   const moe::Dims& d = L->dims;
-  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b.logits, T,
-                                           quantize_x ? b.xq : nullptr, s);
-  if (e == hipSuccess) e = T <= moe::kChunk ? moe::launch_route_small(d, b, T, s) : moe::launch_route_chunked(d, b, T, s);
+  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, quantize_x, s);
+  if (e == hipSuccess && !moe::route_fused(d, T)) e = moe::launch_route_chunked(d, b, T, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }

@@ -13,6 +13,65 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
+// ---- cross-lane reductions on DPP (no LDS round trips) ------------------------------
+// quad_perm [1,0,3,2] and [2,3,0,1], then row_ror 4 and 8: every lane of a 16-lane row holds
+// the row's result; the four row results are read from lanes 15, 31, 47, 63 and combined in a
+// fixed order, so the outcome is the same on every lane and on every call.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x124>(v));
+  v = max(v, dpp_u32<0x128>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 15), b = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 47), d = __builtin_amdgcn_readlane(v, 63);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 15));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 31));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 47));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+  return ((a + b) + c) + d;
+}
+// ---- cross-workgroup hand-off inside one kernel ---------------------------------------
+// Values another workgroup reads in the same launch are written and read with agent-scope
+// relaxed atomics (stores write through the XCD-local L2, loads miss it), the writer waits
+// for its stores to complete before it bumps a counter, and the workgroup that brings the
+// counter to its final value does the dependent work.  No device-scope fence is used: on
+// gfx950 that writes back the whole L2 and costs far more than the data it publishes.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores (and loads) have completed.
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+}
+// Called by all threads after their agent-scope stores; true in every thread of the
+// workgroup that arrives last among `total`.  That workgroup resets the counter when done.
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int total, int* lds_flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *lds_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+  __syncthreads();
+  return *lds_flag != 0;
+}
+__device__ __forceinline__ void reset_counter(int32_t* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Read-only views in the constant address space: uniform loads through them become scalar
 // loads (SGPRs), which is how a value shared by every lane of a wave is best fetched.
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
@@ -79,6 +138,7 @@ __device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgc
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
+
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
@@ -108,6 +168,7 @@ struct CallBufs {
   int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles
   int32_t* mt_group;  // [mt_bound]
   int32_t* mt_row0;   // [mt_bound]
+  int32_t* ctrl;      // control words (zero between calls): [0] routing arrival counter
   void* h;            // GEMV path: h as FP8 terms + scales (see gemv.hip); GEMM path: bf16 [T(k+S)][I]
   uint8_t* xq;        // GEMV path: x as 2 FP8 terms [2][T][H] then e8m0 scales [T][H/32]
   float* staging;     // [T(k+S)][H] weighted expert outputs, slot-indexed
@@ -118,9 +179,13 @@ int timing_begin(const char* name, hipStream_t s);
 void timing_end(int token, hipStream_t s);
 
 // ---- launchers (return hipGetLastError of the launch) ---------------------------------
+// Batches routed by the router kernel's last workgroup: one bit per token in a 64-bit mask,
+// and every score of the batch held in that workgroup's LDS.
+constexpr int kFusedMaxT = 64;
+constexpr int kTailScores = 8192;
+inline bool route_fused(const Dims& d, int T) { return T <= kFusedMaxT && T * d.E <= kTailScores; }
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                float* logits, int T, uint8_t* xq, hipStream_t s);
-hipError_t launch_route_small(const Dims& d, const CallBufs& b, int T, hipStream_t s);
+                                const CallBufs& b, int T, bool quantize_x, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,

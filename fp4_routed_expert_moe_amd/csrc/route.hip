@@ -7,21 +7,21 @@
 // scoring rule open, so scores are a plain fp32 dot product (+ optional bias), selection is
 // the k largest (ties to the lower index), and the weights are a softmax over the k selected
 // scores.
+//
+// Small batches (route_fused: T <= 64 and T*E <= kTailScores) are routed in one launch: the
+// router workgroups publish their scores, and the last one to finish (device-scope counter
+// in the workspace, left at zero again) runs top-k, the grouping tables and the scatter.
+// Larger batches use a per-chunk top-k kernel, a one-workgroup scan and a per-chunk scatter.
 #include "common.h"
 
 namespace moe {
 
-// ------------------------------------------------------------------------------------
-// Router scores l[t][e] = x[t] . W_r[e] + b[e]  (fp32 accumulate, bf16 activations).
-// One workgroup per (expert, tile of kRouterTT tokens): the 256 threads split the hidden
-// axis (8 values each per step), partial sums are reduced across each wave and then the
-// 4 waves in a fixed order, so a score does not depend on the other tokens of the batch.
-// ------------------------------------------------------------------------------------
-constexpr int kRouterTT = 8;
+constexpr int kRouterTT = 8;  // tokens per router workgroup
 
-// When xq is not NULL the workgroups of a token tile also write the tile's activations as
-// two exact FP8 terms with a scale per 32-value block (the decode kernels' A operand):
-// xq = [2][T][H] e4m3 bytes, then [T][H/32] e8m0 scales.
+// ------------------------------------------------------------------------------------
+// Activations as two exact FP8 terms with a scale per 32-value block (the decode kernels'
+// A operand): xq = [2][T][H] e4m3 bytes, then [T][H/32] e8m0 scales.
+// ------------------------------------------------------------------------------------
 __device__ void quantize_x_block(const uint16_t* __restrict__ src, uint8_t* __restrict__ hi,
                                  uint8_t* __restrict__ lo, uint8_t* __restrict__ sc) {
   uint4 raw[4];
@@ -51,62 +51,6 @@ __device__ void quantize_x_block(const uint16_t* __restrict__ src, uint8_t* __re
   *sc = (uint8_t)s;
 }
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ logits, int T, int E,
-                                                            int H, uint8_t* __restrict__ xq) {
-  __shared__ float part[4][kRouterTT];
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * kRouterTT;
-  const int nt = min(kRouterTT, T - t0);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (xq) {
-    const int KB = H >> 5;
-    for (int j = e * 256 + tid; j < nt * KB; j += E * 256) {
-      const int t = t0 + j / KB, b = j % KB;
-      quantize_x_block(x + (size_t)t * H + b * 32, xq + (size_t)t * H + b * 32,
-                       xq + (size_t)(T + t) * H + b * 32, xq + (size_t)2 * T * H + (size_t)t * KB + b);
-    }
-  }
-  float acc[kRouterTT];
-#pragma unroll
-  for (int i = 0; i < kRouterTT; ++i) acc[i] = 0.f;
-  const float* wrow = wr + (size_t)e * H;
-  for (int h = tid * 8; h < H; h += 256 * 8) {  // H % 32 == 0, so h + 8 <= H
-    const float4 w0 = *reinterpret_cast<const float4*>(wrow + h);
-    const float4 w1 = *reinterpret_cast<const float4*>(wrow + h + 4);
-#pragma unroll
-    for (int i = 0; i < kRouterTT; ++i) {
-      if (i < nt) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H + h);
-        float a = acc[i];
-        a = fmaf(bf16_lo(v.x), w0.x, a);
-        a = fmaf(bf16_hi(v.x), w0.y, a);
-        a = fmaf(bf16_lo(v.y), w0.z, a);
-        a = fmaf(bf16_hi(v.y), w0.w, a);
-        a = fmaf(bf16_lo(v.z), w1.x, a);
-        a = fmaf(bf16_hi(v.z), w1.y, a);
-        a = fmaf(bf16_lo(v.w), w1.z, a);
-        a = fmaf(bf16_hi(v.w), w1.w, a);
-        acc[i] = a;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kRouterTT; ++i) {
-    float v = acc[i];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    if (lane == 0) part[wave][i] = v;
-  }
-  __syncthreads();
-  if (tid < nt) {
-    const float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
-    logits[(size_t)(t0 + tid) * E + e] = v + (bias ? bias[e] : 0.f);
-  }
-}
-
 // ------------------------------------------------------------------------------------
 // Top-k of one token by one wave.
 // Each score becomes a 64-bit rank key: high word = order-preserving image of the float
@@ -115,36 +59,37 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t rank_key(float v, int e) {
   uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  uint32_t ord;
-  if (v != v)
-    ord = 0u;
-  else
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = u == 0x80000000u ? 0u : u;
+  const uint32_t ord = v != v ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
   return ((uint64_t)ord + 1ull) << 32 | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t o = __shfl_xor(v, m, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+// The score whose key has high word `hi` (-0 comes back as +0).
+__device__ __forceinline__ float hi_value(uint32_t hi) {
+  const uint32_t ord = hi - 1u;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
-// Writes idx[0..k), w[0..k) of the token and sets bit `tbit` of mask[e] for each pick;
-// also copies the picks to sel (LDS) when sel is not NULL.  Q = scores per lane (E <= 64*Q).
+// Lane l owns experts l, l + 64, ...  (Q = scores per lane, E <= 64*Q).  Each round finds
+// the largest remaining key: the wave-wide maximum of the high words on DPP, then the low
+// word of the one lane that holds it (a second reduction only when several lanes tie).
+// Every pick is wave-uniform, so the per-round bookkeeping is scalar.  At the end the wave
+// writes idx[0..k) and w[0..k) of the token (softmax over the k picked scores, summed in a
+// fixed order), sets bit `tbit` of mask[e] for each pick and copies the picks to sel when
+// sel is not NULL.
 template <int Q>
-__device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lane,
-                           int32_t* __restrict__ idx_out, float* __restrict__ w_out, uint64_t* mask,
-                           int tbit, int32_t* sel) {
-  uint64_t key[Q];
+__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* __restrict__ idx_out,
+                                          float* __restrict__ w_out, uint64_t* mask, int tbit, uint16_t* sel) {
+  const int lane = threadIdx.x & 63;
   float val[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int e = lane + 64 * q;
-    val[q] = e < E ? lrow[e] : 0.f;
+    val[q] = row[e < E ? e : 0];
+  }
+  uint64_t key[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + 64 * q;
     key[q] = e < E ? rank_key(val[q], e) : 0ull;
   }
   int selE[Q];
@@ -156,36 +101,34 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lan
   }
   float vtop = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0ull;
+    uint64_t m = key[0];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) best = key[q] > best ? key[q] : best;
-    best = wave_max_u64(best);
-    const int e = __builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu - (uint32_t)best));
-    float mine = 0.f;
+    for (int q = 1; q < Q; ++q) m = key[q] > m ? key[q] : m;
+    const uint32_t mhi = (uint32_t)(m >> 32), mlo = (uint32_t)m;
+    const uint32_t bhi = wave_max_u32(mhi);
+    const uint64_t tied = __ballot(mhi == bhi);
+    uint32_t blo;
+    if (__popcll(tied) == 1)
+      blo = __builtin_amdgcn_readlane(mlo, __ffsll((unsigned long long)tied) - 1);
+    else
+      blo = wave_max_u32(mhi == bhi ? mlo : 0u);
+    const int e = (int)(0xFFFFFFFFu - blo);
+    const float v = hi_value(bhi);
+    if (j == 0) vtop = v;
+    const bool owner = (e & 63) == lane;
+    const int qe = e >> 6;
 #pragma unroll
     for (int q = 0; q < Q; ++q)
-      if (q == (e >> 6)) mine = val[q];
-    const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine), e & 63));
-    if (j == 0) vtop = v;
-    if ((e & 63) == lane) {
+      if (q == qe) key[q] = owner ? 0ull : key[q];
+    const bool rec = (j & 63) == lane;
+    const int qj = j >> 6;
 #pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (q == (e >> 6)) key[q] = 0ull;
-    }
-    if ((j & 63) == lane) {
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (q == (j >> 6)) {
-          selE[q] = e;
-          selV[q] = v;
-        }
-    }
-    if (lane == 0) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&mask[e]), 1ull << tbit);
-      if (sel) sel[j] = e;
-    }
+    for (int q = 0; q < Q; ++q)
+      if (q == qj) {
+        selE[q] = rec ? e : selE[q];
+        selV[q] = rec ? v : selV[q];
+      }
   }
-  // softmax over the k picked scores; xor-butterfly sums are identical on every lane
   float p[Q];
   float s = 0.f;
 #pragma unroll
@@ -197,167 +140,284 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int lan
       s += p[q];
     }
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  s = wave_sum_f32(s);
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int j = lane + 64 * q;
     if (j < k) {
       idx_out[j] = selE[q];
       w_out[j] = p[q] / s;
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[selE[q]]), 1ull << tbit);
+      if (sel) sel[j] = (uint16_t)selE[q];
     }
   }
 }
 
-// Calls topk_token with the smallest Q >= ceil(E/64) among 1, 2, 4, 8, 16.
-__device__ __forceinline__ void topk_any(int E, const float* lrow, int k, int lane, int32_t* idx_out,
-                                         float* w_out, uint64_t* mask, int tbit, int32_t* sel) {
+// Tokens [0, T) of scores [T][E] (T <= 64), one token per wave at a time over the NT
+// threads of the block.  Token t sets bit t of the expert masks; its picks go to
+// sel[t*k ..] when sel != NULL.
+template <int NT, int Q>
+__device__ __forceinline__ void topk_block(const float* scores, int T, int E, int k, int32_t* idx, float* w,
+                                           uint64_t* mask, uint16_t* sel) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int t = wave; t < T; t += NT / 64)
+    topk_wave<Q>(scores + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k, mask, t,
+                 sel ? sel + t * k : nullptr);
+}
+template <int NT>
+__device__ __forceinline__ void topk_block_any(const float* scores, int T, int E, int k, int32_t* idx, float* w,
+                                               uint64_t* mask, uint16_t* sel) {
   if (E <= 64)
-    topk_token<1>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+    topk_block<NT, 1>(scores, T, E, k, idx, w, mask, sel);
   else if (E <= 128)
-    topk_token<2>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+    topk_block<NT, 2>(scores, T, E, k, idx, w, mask, sel);
   else if (E <= 256)
-    topk_token<4>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+    topk_block<NT, 4>(scores, T, E, k, idx, w, mask, sel);
   else if (E <= 512)
-    topk_token<8>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+    topk_block<NT, 8>(scores, T, E, k, idx, w, mask, sel);
   else
-    topk_token<16>(lrow, E, k, lane, idx_out, w_out, mask, tbit, sel);
+    topk_block<NT, 16>(scores, T, E, k, idx, w, mask, sel);
 }
 
 // ------------------------------------------------------------------------------------
-// Block-wide exclusive scan over 1024 threads (16 waves).
+// Grouping tables, built by one wave (no block barriers) from per-expert row counts
+// cnt[0..E) in LDS.  Lane l owns experts [l*J, l*J+J), J = ceil(E/64).  Writes counts,
+// offsets, group rows/first rows, the active-group list (shared expert last), the M-tile
+// list, and each expert's first grouped row to offs[] (LDS; may be the same array as cnt).
 // ------------------------------------------------------------------------------------
-__device__ int scan1024(int v, int* lds16, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
   int x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  if (lane == 63) lds16[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    int s = lane < 16 ? lds16[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const int y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
-    }
-    if (lane < 16) lds16[lane] = s;
-  }
-  __syncthreads();
-  const int base = wave > 0 ? lds16[wave - 1] : 0;
-  *total = lds16[15];
-  __syncthreads();
-  return base + x - v;
+  *total = __shfl(x, 63, 64);
+  return x - v;
 }
 
-// Expert tables from per-expert row counts (thread e holds count of expert e; 0 past E).
-// Returns the expert's first grouped row.  Requires blockDim.x == 1024 and E <= 1024.
-__device__ int build_tables(int cnt, int T, int E, int k, int S, const CallBufs& b, int* lds16) {
-  const int tid = threadIdx.x;
-  int total;
-  const int off = scan1024(cnt, lds16, &total);
-  if (tid < E) {
-    b.counts[tid] = cnt;
-    b.offsets[tid] = off;
-    b.grp_row0[tid] = off;
-    b.grp_rows[tid] = cnt;
+__device__ void build_tables_wave(const int* cnt, int T, int E, int k, int S, const CallBufs& b, int* offs) {
+  const int lane = threadIdx.x & 63;
+  const int J = (E + 63) >> 6;
+  const int e0 = lane * J;
+  int rows = 0, acts = 0, mts = 0;
+  for (int i = 0; i < J; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt[e];
+      rows += c;
+      acts += c > 0;
+      mts += (c + kGemmBM - 1) / kGemmBM;
+    }
   }
-  if (tid == 0) {
+  int total, nact, nmt;
+  int off = wave_excl_scan(rows, &total);
+  int apos = wave_excl_scan(acts, &nact);
+  int mpos = wave_excl_scan(mts, &nmt);
+  for (int i = 0; i < J; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = cnt[e];
+    b.counts[e] = c;
+    b.offsets[e] = off;
+    b.grp_row0[e] = off;
+    b.grp_rows[e] = c;
+    offs[e] = off;
+    off += c;
+    if (c > 0) b.act[apos++] = e;
+    for (int m = 0; m < (c + kGemmBM - 1) / kGemmBM; ++m) {
+      b.mt_group[mpos] = e;
+      b.mt_row0[mpos++] = m * kGemmBM;
+    }
+  }
+  const int mt_shared = S ? (T + kGemmBM - 1) / kGemmBM : 0;
+  for (int i = lane; i < mt_shared; i += 64) {
+    b.mt_group[nmt + i] = E;
+    b.mt_row0[nmt + i] = i * kGemmBM;
+  }
+  if (lane == 0) {
     b.offsets[E] = total;
     if (S) {
       b.grp_row0[E] = T * k;
       b.grp_rows[E] = T;
+      b.act[nact] = E;
     }
-  }
-  int nact;
-  const int apos = scan1024(cnt > 0 ? 1 : 0, lds16, &nact);
-  if (cnt > 0) b.act[apos] = tid;
-  if (tid == 0 && S) b.act[nact] = E;
-  const int mt = (cnt + kGemmBM - 1) / kGemmBM;
-  int nmt;
-  const int mpos = scan1024(mt, lds16, &nmt);
-  for (int i = 0; i < mt; ++i) {
-    b.mt_group[mpos + i] = tid;
-    b.mt_row0[mpos + i] = i * kGemmBM;
-  }
-  const int mts = S ? (T + kGemmBM - 1) / kGemmBM : 0;
-  for (int i = tid; i < mts; i += 1024) {
-    b.mt_group[nmt + i] = E;
-    b.mt_row0[nmt + i] = i * kGemmBM;
-  }
-  if (tid == 0) {
     b.info[0] = nact + S;
-    b.info[1] = nmt + mts;
+    b.info[1] = nmt + mt_shared;
   }
-  return off;
 }
 
 // ------------------------------------------------------------------------------------
-// Small batches (T <= 64): top-k, tables and scatter in one 1024-thread workgroup.
+// The routing tail of a small batch (route_fused), run by the router kernel's last
+// workgroup once every score is published: top-k, grouping tables, stable scatter.
 // ------------------------------------------------------------------------------------
-constexpr int kSmallSel = 4096;  // picks kept in LDS by the one-workgroup route (T*k)
+constexpr int kTailThreads = 1024;
 
-__global__ __launch_bounds__(1024) void route_small_kernel(CallBufs b, int T, int E, int k, int S) {
-  __shared__ uint64_t mask[1024];
+__device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int K, int S) {
+  __shared__ float sc[kTailScores];
+  __shared__ uint16_t sel[kTailScores];  // picks of token t at [t*K, t*K+K); T*K <= T*E
+  __shared__ uint64_t mask[1024];        // bit t: token t picked expert e
   __shared__ int offs[1024];
-  __shared__ int32_t sel[kSmallSel];
-  __shared__ int lds16[16];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool in_lds = T * k <= kSmallSel;
-  if (tid < E) mask[tid] = 0ull;
-  __syncthreads();
-  for (int t = wave; t < T; t += 16)
-    topk_any(E, b.logits + (size_t)t * E, k, lane, b.idx + (size_t)t * k, b.w + (size_t)t * k, mask, t,
-             in_lds ? sel + t * k : nullptr);
-  __syncthreads();
-  const int cnt = tid < E ? __popcll(mask[tid]) : 0;
-  const int off = build_tables(cnt, T, E, k, S, b, lds16);
-  if (tid < E) offs[tid] = off;
-  __syncthreads();
-  if (tid < T) {
-    const uint64_t below = (1ull << tid) - 1ull;
-    for (int j = 0; j < k; ++j) {
-      const int e = in_lds ? sel[tid * k + j] : b.idx[tid * k + j];
-      b.perm[offs[e] + __popcll(mask[e] & below)] = tid * k + j;
+  const int tid = threadIdx.x;
+  const int n = T * E;
+  // every score in one round of loads, then into LDS
+  for (int i0 = 0; i0 < n; i0 += kTailThreads * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kTailThreads + tid;
+      v[u] = i < n ? ld_agent(b.logits + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kTailThreads + tid;
+      if (i < n) sc[i] = v[u];
     }
   }
+  for (int i = tid; i < E; i += kTailThreads) mask[i] = 0ull;
+  __syncthreads();
+  topk_block_any<kTailThreads>(sc, T, E, K, b.idx, b.w, mask, sel);
+  __syncthreads();
+  for (int i = tid; i < E; i += kTailThreads) offs[i] = __popcll(mask[i]);
+  __syncthreads();
+  if (tid < 64) build_tables_wave(offs, T, E, K, S, b, offs);
+  __syncthreads();
+  // pick i = t*K + j lands after the rows of lower tokens routed to the same expert
+  for (int i = tid; i < T * K; i += kTailThreads) {
+    const int t = i / K, e = sel[i];
+    b.perm[offs[e] + __popcll(mask[e] & ((1ull << t) - 1ull))] = i;
+  }
 }
 
 // ------------------------------------------------------------------------------------
-// Any T: per-chunk top-k + masks, one-workgroup scan, per-chunk stable scatter.
+// Router scores l[t][e] = x[t] . W_r[e] + b[e]  (fp32 accumulate, bf16 activations).
+// One workgroup of NT threads per (expert, tile of kRouterTT tokens): the threads split the
+// hidden axis (8 values each per step, U steps in flight); partial sums are added in
+// ascending hidden order per thread, across each wave, then over the waves in a fixed
+// order, so a score does not depend on the other tokens of the batch.
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_chunk_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int32_t* __restrict__ idx,
-                                                         float* __restrict__ w,
-                                                         uint64_t* __restrict__ gmask) {
+template <bool FUSED>
+__global__ __launch_bounds__(FUSED ? kTailThreads : 256) void router_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, CallBufs b,
+    int T, int E, int H, int K, int S, int quantize) {
+  constexpr int NT = FUSED ? kTailThreads : 256;
+  constexpr int NW = NT / 64;
+  constexpr int U = FUSED ? 1 : 4;
+  __shared__ float part[NW][kRouterTT];
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * kRouterTT;
+  const int nt = min(kRouterTT, T - t0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (quantize) {
+    const int KB = H >> 5;
+    uint8_t* xq = b.xq;
+    for (int j = e * NT + tid; j < nt * KB; j += E * NT) {
+      const int t = t0 + j / KB, bb = j % KB;
+      quantize_x_block(x + (size_t)t * H + bb * 32, xq + (size_t)t * H + bb * 32,
+                       xq + (size_t)(T + t) * H + bb * 32, xq + (size_t)2 * T * H + (size_t)t * KB + bb);
+    }
+  }
+  float acc[kRouterTT];
+#pragma unroll
+  for (int i = 0; i < kRouterTT; ++i) acc[i] = 0.f;
+  const float* wrow = wr + (size_t)e * H;
+  const uint16_t* xt = x + (size_t)t0 * H;
+  for (int h0 = tid * 8; h0 < H; h0 += NT * 8 * U) {  // H % 32 == 0, so h + 8 <= H
+    float4 w[U][2];
+    uint4 xv[U][kRouterTT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int h = h0 + u * NT * 8;
+      if (h < H) {
+        w[u][0] = *reinterpret_cast<const float4*>(wrow + h);
+        w[u][1] = *reinterpret_cast<const float4*>(wrow + h + 4);
+#pragma unroll
+        for (int i = 0; i < kRouterTT; ++i)
+          if (i < nt) xv[u][i] = *reinterpret_cast<const uint4*>(xt + (size_t)i * H + h);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (h0 + u * NT * 8 < H) {
+        const float4 w0 = w[u][0], w1 = w[u][1];
+#pragma unroll
+        for (int i = 0; i < kRouterTT; ++i) {
+          if (i < nt) {
+            const uint4 v = xv[u][i];
+            float a = acc[i];
+            a = fmaf(bf16_lo(v.x), w0.x, a);
+            a = fmaf(bf16_hi(v.x), w0.y, a);
+            a = fmaf(bf16_lo(v.y), w0.z, a);
+            a = fmaf(bf16_hi(v.y), w0.w, a);
+            a = fmaf(bf16_lo(v.z), w1.x, a);
+            a = fmaf(bf16_hi(v.z), w1.y, a);
+            a = fmaf(bf16_lo(v.w), w1.z, a);
+            a = fmaf(bf16_hi(v.w), w1.w, a);
+            acc[i] = a;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRouterTT; ++i) {
+    const float v = wave_sum_f32(acc[i]);
+    if (lane == 0) part[wave][i] = v;
+  }
+  __syncthreads();
+  if (tid < nt) {
+    float v = part[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += part[w][tid];
+    const float l = v + (bias ? bias[e] : 0.f);
+    if constexpr (FUSED)
+      st_agent(b.logits + (size_t)(t0 + tid) * E + e, l);
+    else
+      b.logits[(size_t)(t0 + tid) * E + e] = l;
+  }
+  if constexpr (FUSED) {
+    // the last workgroup to finish routes the whole batch, then re-arms the counter
+    __shared__ int is_last;
+    if (!arrive_last(&b.ctrl[0], (int)(gridDim.x * gridDim.y), &is_last)) return;
+    route_tail(b, T, E, K, S);
+    if (tid == 0) reset_counter(&b.ctrl[0]);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Any T: per-chunk top-k + masks, one-workgroup table build, per-chunk stable scatter.
+// ------------------------------------------------------------------------------------
+constexpr int kChunkThreads = 1024;
+
+__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(const float* __restrict__ logits, int T, int E,
+                                                                   int k, int32_t* __restrict__ idx,
+                                                                   float* __restrict__ w,
+                                                                   uint64_t* __restrict__ gmask) {
   __shared__ uint64_t mask[1024];
   const int c = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+  for (int e = threadIdx.x; e < E; e += kChunkThreads) mask[e] = 0ull;
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = wave; i < kChunk; i += 4) {
-    const int t = c * kChunk + i;
-    if (t >= T) break;
-    topk_any(E, logits + (size_t)t * E, k, lane, idx + (size_t)t * k, w + (size_t)t * k, mask, i, nullptr);
-  }
+  const size_t t0 = (size_t)c * kChunk;
+  topk_block_any<kChunkThreads>(logits + t0 * E, min(kChunk, T - (int)t0), E, k, idx + t0 * k, w + t0 * k, mask,
+                                nullptr);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) gmask[(size_t)c * E + e] = mask[e];
+  for (int e = threadIdx.x; e < E; e += kChunkThreads) gmask[(size_t)c * E + e] = mask[e];
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(CallBufs b, int T, int E, int k, int S, int C) {
-  __shared__ int lds16[16];
+  __shared__ int cnt[1024];
   const int e = threadIdx.x;
-  int cnt = 0;
   if (e < E) {
-    for (int c = 0; c < C; ++c) {
-      b.cbase[(size_t)c * E + e] = cnt;
-      cnt += __popcll(b.gmask[(size_t)c * E + e]);
+    int c = 0;
+    for (int ch = 0; ch < C; ++ch) {
+      b.cbase[(size_t)ch * E + e] = c;
+      c += __popcll(b.gmask[(size_t)ch * E + e]);
     }
+    cnt[e] = c;
   }
-  build_tables(cnt, T, E, k, S, b, lds16);
+  __syncthreads();
+  if (threadIdx.x < 64) build_tables_wave(cnt, T, E, k, S, b, cnt);
 }
 
 __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, int E, int k) {
@@ -373,17 +433,14 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                float* logits, int T, uint8_t* xq, hipStream_t s) {
+                                const CallBufs& b, int T, bool quantize_x, hipStream_t s) {
   dim3 grid(d.E, (T + kRouterTT - 1) / kRouterTT);
-  const int tk = timing_begin("router_logits", s);
-  router_logits_kernel<<<grid, 256, 0, s>>>(x, wr, bias, logits, T, d.E, d.H, xq);
-  timing_end(tk, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_route_small(const Dims& d, const CallBufs& b, int T, hipStream_t s) {
-  const int tk = timing_begin("route_small", s);
-  route_small_kernel<<<1, 1024, 0, s>>>(b, T, d.E, d.K, d.S);
+  const bool fused = route_fused(d, T);
+  const int tk = timing_begin(fused ? "router_route" : "router_logits", s);
+  if (fused)
+    router_kernel<true><<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
+  else
+    router_kernel<false><<<grid, 256, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
   timing_end(tk, s);
   return hipGetLastError();
 }
@@ -391,7 +448,7 @@ hipError_t launch_route_small(const Dims& d, const CallBufs& b, int T, hipStream
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s) {
   const int C = (T + kChunk - 1) / kChunk;
   int tk = timing_begin("topk_chunk", s);
-  topk_chunk_kernel<<<C, 256, 0, s>>>(b.logits, T, d.E, d.K, b.idx, b.w, b.gmask);
+  topk_chunk_kernel<<<C, kChunkThreads, 0, s>>>(b.logits, T, d.E, d.K, b.idx, b.w, b.gmask);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

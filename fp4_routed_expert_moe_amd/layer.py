@@ -108,7 +108,8 @@ class MoeLayer:
         return int(self.lib.moe_workspace_bytes(self._h, max_tokens))
 
     def workspace(self, max_tokens: int) -> torch.Tensor:
-        return torch.empty(self.workspace_bytes(max_tokens), dtype=torch.uint8, device=self.device)
+        """A zero-filled workspace (the library's control words must start at zero)."""
+        return torch.zeros(self.workspace_bytes(max_tokens), dtype=torch.uint8, device=self.device)
 
     def route_buffers(self, tokens: int) -> dict:
         d, k, e = self.device, self.top_k, self.n_experts

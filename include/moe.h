@@ -120,7 +120,10 @@ int32_t moe_layer_create(const moe_layer_desc* desc, moe_layer** out);
 void moe_layer_destroy(moe_layer* layer);
 
 /* Bytes of device workspace one call with up to max_tokens tokens needs (0 on bad
- * arguments).  The caller allocates and owns it; it must be 256-byte aligned. */
+ * arguments).  The caller allocates and owns it; it must be 256-byte aligned and filled with
+ * zeros before its first use.  Its first bytes are control words (device-scope counters the
+ * kernels use to let the last workgroup finish a stage); every call leaves them at zero, so a
+ * workspace is zeroed once, not per call.  A workspace serves one stream at a time. */
 uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens);
 
 /* Steps 1-3 for x (bf16 bit patterns, device, [T][H]) into `route` (all five pointers

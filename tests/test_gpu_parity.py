@@ -180,6 +180,27 @@ def test_deterministic_repeat():
     np.testing.assert_array_equal(a["y"], c["y"])
 
 
+def test_workspace_reuse_across_sizes_and_paths():
+    # The control words in the workspace must be back at zero after every call, whatever
+    # mix of fused (T <= 64) and chunked routing, GEMV and GEMM paths used it before.
+    groups, wr, b, x = _random_case(15, 256, 32, 4, 1, 128, 150)
+    weights = stack_groups(groups)
+    gemv = make_layer(wr, weights, 4, 1, b, "gemv")
+    gemm = make_layer(wr, weights, 4, 1, b, "gemm")
+    ws = gemv.workspace(150)
+    fresh = {}
+    for t in (8, 150, 64, 65):
+        fresh[("gemv", t)] = run_layer(gemv, x[:t])
+        fresh[("gemm", t)] = run_layer(gemm, x[:t])
+    for rep in range(2):
+        for t in (8, 150, 1, 64, 65, 8):
+            for name, layer in (("gemv", gemv), ("gemm", gemm)):
+                got = run_layer(layer, x[:t], workspace=ws)
+                ref = fresh.get((name, t)) or run_layer(layer, x[:t])
+                np.testing.assert_array_equal(got["y"], ref["y"])
+                np.testing.assert_array_equal(got["perm"], ref["perm"])
+
+
 def test_workspace_errors():
     from fp4_routed_expert_moe_amd import MoeError
     groups, wr, b, x = _random_case(14, 128, 8, 2, 1, 64, 10)
