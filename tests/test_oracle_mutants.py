@@ -1,0 +1,153 @@
+"""Planted mistakes in the oracle must each make at least one pin fail.
+
+Each mutant below swaps one piece of the float64 oracle for a plausibly wrong
+version (a dropped term, a wrong sign, a swapped index or operand, an off-by-one
+in the format) and runs every pin of ``test_oracle_pins.py`` against it.  A mutant
+that no pin notices would mean the pins do not constrain that part of the oracle.
+Everything here runs on the CPU and touches nothing but the oracle.
+"""
+import contextlib
+import inspect
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.fp4 as ofp4
+import oracle.moe as omoe
+import test_oracle_pins as pins
+
+ORIG = {
+    "dequant": ofp4.dequant,
+    "e8m0_value": ofp4.e8m0_value,
+    "select_experts": omoe.select_experts,
+    "group_rows": omoe.group_rows,
+    "router_logits": omoe.router_logits,
+    "expert_ffn": omoe.expert_ffn,
+    "moe_forward": omoe.moe_forward,
+    "silu": omoe.silu,
+    "bf16_bits_to_f64": omoe.bf16_bits_to_f64,
+}
+
+
+@contextlib.contextmanager
+def patched(name, value, modules=(ofp4, omoe, oracle)):
+    """Replace `name` in every oracle namespace that holds it (package re-exports included)."""
+    saved = [(m, getattr(m, name)) for m in modules if hasattr(m, name)]
+    try:
+        for m, _ in saved:
+            setattr(m, name, value)
+        yield
+    finally:
+        for m, v in saved:
+            setattr(m, name, v)
+
+
+def _dequant_nibbles_swapped(codes, scales):
+    codes = np.asarray(codes, dtype=np.uint8)
+    swapped = ((codes & 0x0F) << 4) | (codes >> 4)
+    return ORIG["dequant"](swapped.astype(np.uint8), scales)
+
+
+def _dequant_scale_block_16(codes, scales):
+    v = ORIG["dequant"](codes, np.zeros_like(np.asarray(scales)) + 127)  # values, unscaled
+    s = ofp4.E8M0_VALUES[np.asarray(scales, dtype=np.uint8)]
+    k = v.shape[1]
+    block = (np.arange(k) // 16) % s.shape[1]   # scale j read as covering 16 values, wrapping
+    with np.errstate(invalid="ignore"):
+        return v * s[:, block]
+
+
+def _select_full_softmax(logits, k):
+    idx, _, l32 = ORIG["select_experts"](logits, k)
+    l = l32.astype(np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return idx, np.take_along_axis(p, idx.astype(np.int64), axis=1), l32
+
+
+def _select_ties_high(logits, k):
+    l32 = np.asarray(logits, dtype=np.float64).astype(np.float32)
+    t, e = l32.shape
+    ids = np.broadcast_to(np.arange(e)[::-1], (t, e))
+    order = np.lexsort((ids, -l32.astype(np.float64)), axis=-1)
+    idx = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(l32, idx, axis=1).astype(np.float64)
+    p = np.exp(sel - sel[:, :1])
+    return idx, p / p.sum(axis=1, keepdims=True), l32
+
+
+def _select_unit_weights(logits, k):
+    idx, w, l32 = ORIG["select_experts"](logits, k)
+    return idx, np.ones_like(w), l32
+
+
+def _group_unstable(idx, n_experts):
+    counts, offsets, perm = ORIG["group_rows"](idx, n_experts)
+    perm = perm.copy()
+    for e in range(n_experts):
+        perm[offsets[e]:offsets[e + 1]] = perm[offsets[e]:offsets[e + 1]][::-1]
+    return counts, offsets, perm
+
+
+def _router_no_bias(x_bits, w_router, bias=None):
+    return ORIG["router_logits"](x_bits, w_router, None)
+
+
+def _ffn_gate_up_swapped(xrows, weights):
+    return ORIG["expert_ffn"](xrows, dict(gate=weights["up"], up=weights["gate"], down=weights["down"]))
+
+
+def _forward_no_shared(x_bits, w_router, bias, experts, top_k, n_shared):
+    return ORIG["moe_forward"](x_bits, w_router, bias, experts, top_k, 0)
+
+
+def _bf16_shift15(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15
+    return b.view(np.float32).astype(np.float64)
+
+
+MUTANTS = {
+    "nibble order swapped": [("dequant", _dequant_nibbles_swapped)],
+    "scale blocks of 16": [("dequant", _dequant_scale_block_16)],
+    "e8m0 off by one": [("E8M0_VALUES", ofp4.E8M0_VALUES * 2.0),
+                        ("e8m0_value", lambda s: 2.0 * ORIG["e8m0_value"](s))],
+    "e2m1 mantissa weight": [("E2M1_VALUES", np.where(np.arange(16) & 1,
+                                                      ofp4.E2M1_VALUES * 1.125, ofp4.E2M1_VALUES))],
+    "silu sign": [("silu", lambda z: np.asarray(z, np.float64) / (1.0 + np.exp(np.asarray(z, np.float64))))],
+    "softmax over all experts": [("select_experts", _select_full_softmax)],
+    "ties to higher index": [("select_experts", _select_ties_high)],
+    "routing weights dropped": [("select_experts", _select_unit_weights)],
+    "grouping not stable": [("group_rows", _group_unstable)],
+    "router bias ignored": [("router_logits", _router_no_bias)],
+    "gate and up swapped": [("expert_ffn", _ffn_gate_up_swapped)],
+    "shared expert dropped": [("moe_forward", _forward_no_shared)],
+    "bf16 decode shifted": [("bf16_bits_to_f64", _bf16_shift15)],
+}
+
+
+def _pin_functions():
+    out = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if name.startswith("test_") and not inspect.signature(fn).parameters:
+            out.append((name, fn))
+    return out
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant):
+    caught = []
+    with contextlib.ExitStack() as stack:
+        for name, value in MUTANTS[mutant]:
+            stack.enter_context(patched(name, value))
+        for name, fn in _pin_functions():
+            try:
+                fn()
+            except Exception:  # an assertion, or the mutant breaking a shape
+                caught.append(name)
+    assert caught, f"no pin notices the mutant '{mutant}'"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for name, fn in _pin_functions():
+        fn()
