@@ -311,7 +311,7 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   if (route) use_route_out(b, route);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
-  st = enqueue_route(L, x, T, b, s, gemv);
+  st = enqueue_route(L, x, T, b, s, true);
   if (st != MOE_OK) return st;
   hipError_t e;
   if (gemv) {

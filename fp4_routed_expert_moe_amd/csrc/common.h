@@ -144,6 +144,27 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float
 
 // Token of grouped row r: routed rows carry t*k+j in perm; the shared expert's rows
 // (r >= T*k) are the tokens in order.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Operands of v_mfma_scale_f32_16x16x128_f8f6f4 (probed lane layout, 16x16 output tile):
+// * FP4 operand, lane (n, q) = (lane % 16, lane / 16): the 32 values of K block q of row/column
+//   n, i.e. 16 bytes, plus that block's e8m0 scale.
+// * FP8 operand, lane (m, q): bytes 16q..16q+15 and 64+16q..64+16q+15 of the 128-value K step
+//   of row m; its scale is that of K block q of row m.
+// * Result: lane l, element i -> row 4*(l/16) + i, column l % 16.
+__device__ __forceinline__ i32x8 fp4_operand(const uint4& c) {
+  return i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};  // FP4 reads the low 4 dwords
+}
+__device__ __forceinline__ i32x8 fp8_operand(const uint4& lo, const uint4& hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+// acc += A(fp8, scale sa) x B(fp4, scale sb)
+__device__ __forceinline__ f32x4 mma_f8f4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ int row_token(const int32_t* perm, int r, int tk, int k) {
   return r < tk ? perm[r] / k : r - tk;
 }

@@ -1,172 +1,270 @@
-// Prefill path: expert-grouped GEMM over the sorted token rows on bf16 MFMA.
+// Prefill path: expert-grouped GEMM over the sorted token rows on the block-scaled matrix
+// cores (v_mfma_scale_f32_16x16x128_f8f6f4).
 //
 // "feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine" (PR #1055, "What it is",
-// prefill MoE) runs expert-grouped GEMM rows after routing on the device.  Here each
-// workgroup takes one M-tile (64 grouped rows of one group, listed on the device by the
-// routing scan) and 64 output columns; its four waves each own 16 columns and all 64 rows.
+// prefill MoE) runs expert-grouped GEMM rows after routing on the device.  Here:
 //
-// * Activation rows (gathered by token for gate/up, contiguous h rows for down) are staged
-//   through LDS and shared by the four waves.
-// * Weights never touch LDS: the 16x16x32 bf16 MFMA's B operand for one lane is 8
-//   consecutive K values of one weight row, i.e. 4 bytes of e2m1 codes plus that row's e8m0
-//   scale, so each lane loads one dword and converts it with the gfx950 scaled FP4->bf16
-//   converts.  In the block-interleaved kernel layout (pack.hip) a wave's 64 dwords are 256
-//   contiguous bytes.  Every dequantised product is exact (e2m1 * 2^(s-127) has 2
-//   significant bits).
-// * Epilogues: SwiGLU into bf16 h (gate/up); weight * y into the slot-indexed staging rows
-//   (down).
+// * Weights (B) enter the matrix cores as stored: e2m1 codes with their e8m0 block scales, no
+//   convert instruction touches them.  Each wave loads its own weight operands from the
+//   block-interleaved kernel layout straight into registers, one K step ahead.
+// * Activations (A) are exact FP8 (e4m3) term splits with an e8m0 scale per 32 values: x as
+//   two terms (all 8 bf16 significand bits, written by the router kernel), h as two terms
+//   (about 8 significant bits, the precision of bf16) written by the gate/up epilogue.  One
+//   MFMA per term, all accumulating in fp32.
+// * A workgroup takes one M-tile (64 grouped rows of one group, from the device-built M-tile
+//   list) and 256 output columns.  Its four waves each own 64 columns of all 64 rows: 4 x 4
+//   16x16 tiles, for gate and up at once in the gate/up kernel, so SwiGLU stays in registers.
+//   The activation tile of each 256-value K step is staged in LDS (double-buffered) and read
+//   by all four waves; 16-row subtiles past the group's last row are skipped.
+// * Workgroup b takes N-tile b % NT of M-tile b / NT.  Workgroups reach the 8 XCDs
+//   round-robin, so when NT is a multiple of 8 every XCD streams a fixed slice of columns of
+//   every expert and no expert's weight tile is fetched by two XCDs.
 #include "common.h"
 
 namespace moe {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64, LDA = BK + 8;  // LDS row pitch in bf16
+constexpr int kPM = kGemmBM;      // rows per M-tile (64)
+constexpr int kPNW = 64;          // output columns per wave
+constexpr int kPN = 4 * kPNW;     // output columns per workgroup
+constexpr int kPU = 2;            // MFMA K chunks (128 values each) per step
+constexpr int kPK = 128 * kPU;    // K values per step
+constexpr int kPKB = kPK / 32;    // K blocks per step
+constexpr int kALd = kPK + 16;    // LDS row pitch of the activation tile (bytes)
 
-__device__ __forceinline__ float silu_g(float g) { return g / (1.0f + expf(-g)); }
+struct ATile {                    // one K step of the activation tile
+  uint8_t v[2][kPM][kALd];        // FP8 terms
+  uint8_t s[kPM][kPKB];           // e8m0 scales of the step's K blocks
+};
 
-// 8 consecutive K values (k % 8 == 0) of one weight row as scaled bf16.  codes_col/scales_col
-// point at block 0 of the row in the kernel layout; block kb is N chunks further.
-__device__ __forceinline__ bf16x8 load_b_frag(const uint8_t* __restrict__ codes_col,
-                                              const uint8_t* __restrict__ scales_col, size_t N, int k) {
-  const size_t kb = (size_t)(k >> 5);
-  const uint32_t c = *reinterpret_cast<const uint32_t*>(codes_col + kb * N * 16 + ((k & 31) >> 1));
-  const float s = e8m0_to_f32(scales_col[kb * N]);
-  return fp4x8_to_bf16x8(c, s);
+// Activation rows: term planes hi/lo [rows][K] bytes and scales [rows][K/32].
+struct ARows {
+  const uint8_t* hi;
+  const uint8_t* lo;
+  const uint8_t* sc;
+  int K;
+};
+
+// Thread t of 256 moves K blocks u*4 + p (u < kPU, p = t%4) of K step `step` of tile row t/4,
+// both terms and scales, into LDS.  `src_row` < 0 marks a row past the group: zeros with
+// scale 127 (as are blocks past K).
+struct AStage {
+  uint4 c[kPU][4];
+  uint32_t s[kPU];
+};
+__device__ __forceinline__ AStage a_fetch(const ARows& a, int src_row, int step, int p) {
+  AStage st;
+  const int KB = a.K >> 5;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < kPU; ++u) {
+    const int blk = step * kPKB + 4 * u + p;
+    const bool ok = src_row >= 0 && blk < KB;
+    const size_t o = (size_t)src_row * a.K + 32 * blk;
+    st.c[u][0] = ok ? ld16(a.hi + o) : z;
+    st.c[u][1] = ok ? ld16(a.hi + o + 16) : z;
+    st.c[u][2] = ok ? ld16(a.lo + o) : z;
+    st.c[u][3] = ok ? ld16(a.lo + o + 16) : z;
+    st.s[u] = ok ? a.sc[(size_t)src_row * KB + blk] : 127u;
+  }
+  return st;
+}
+__device__ __forceinline__ void a_store(ATile& t, const AStage& st, int r, int p) {
+#pragma unroll
+  for (int u = 0; u < kPU; ++u) {
+    const int b = 128 * u + 32 * p;
+    *reinterpret_cast<uint4*>(&t.v[0][r][b]) = st.c[u][0];
+    *reinterpret_cast<uint4*>(&t.v[0][r][b + 16]) = st.c[u][1];
+    *reinterpret_cast<uint4*>(&t.v[1][r][b]) = st.c[u][2];
+    *reinterpret_cast<uint4*>(&t.v[1][r][b + 16]) = st.c[u][3];
+    t.s[r][4 * u + p] = (uint8_t)st.s[u];
+  }
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
+// Weight operands of one wave for one K step: kPU chunks x NM matrices x 4 column tiles.
+template <int NM>
+struct BFrag {
+  uint4 c[kPU][NM][4];
+  int s[kPU][NM][4];
+};
+template <int NM>
+__device__ __forceinline__ void b_fetch(BFrag<NM>& f, const uint8_t* const* codes, const uint8_t* const* scales,
+                                        const size_t* col, int N, int KB, int step, int q) {
+#pragma unroll
+  for (int u = 0; u < kPU; ++u) {
+    const int kb = step * kPKB + 4 * u + q;
+    const bool ok = kb < KB;
+#pragma unroll
+    for (int mtx = 0; mtx < NM; ++mtx)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const size_t o = (size_t)kb * N + col[c];
+        f.c[u][mtx][c] = ok ? ld16(codes[mtx] + o * 16) : make_uint4(0, 0, 0, 0);
+        f.s[u][mtx][c] = ok ? scales[mtx][o] : 127;
+      }
+  }
+}
+
+// One K step: acc[mtx][rs][c] += A(rs) x B(mtx, c) for both FP8 terms, rs < nsub.
+template <int NM>
+__device__ __forceinline__ void k_step(const ATile& t, const BFrag<NM>& f, f32x4 (&acc)[NM][4][4], int nsub, int m,
+                                       int q) {
+#pragma unroll
+  for (int u = 0; u < kPU; ++u)
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      if (rs >= nsub) break;
+      const int r = 16 * rs + m;
+      const int b = 128 * u + 16 * q;
+      const i32x8 a0 = fp8_operand(*reinterpret_cast<const uint4*>(&t.v[0][r][b]),
+                                   *reinterpret_cast<const uint4*>(&t.v[0][r][b + 64]));
+      const i32x8 a1 = fp8_operand(*reinterpret_cast<const uint4*>(&t.v[1][r][b]),
+                                   *reinterpret_cast<const uint4*>(&t.v[1][r][b + 64]));
+      const int sa = t.s[r][4 * u + q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int mtx = 0; mtx < NM; ++mtx) {
+          const i32x8 bb = fp4_operand(f.c[u][mtx][c]);
+          acc[mtx][rs][c] = mma_f8f4(a0, bb, acc[mtx][rs][c], sa, f.s[u][mtx][c]);
+          acc[mtx][rs][c] = mma_f8f4(a1, bb, acc[mtx][rs][c], sa - 4, f.s[u][mtx][c]);
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------
-// gate/up: h[row][n] = bf16( silu(x_t . Wg[n]) * (x_t . Wu[n]) )
+// GATEUP: h[r][n] = silu(x_t(r) . Wg[n]) * (x_t(r) . Wu[n]) as 2 FP8 terms + e8m0 per 32
+//         (h8 = [2][R][I] bytes then [R][I/32] scales).
+// DOWN:   staging[slot(r)][n] = weight(r) * (h_r . Wd[n]).
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemm_gateup_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
-    const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void gemm_f8f4_kernel(
+    ARows a, const uint8_t* __restrict__ c0p, const uint8_t* __restrict__ s0p, const uint8_t* __restrict__ c1p,
+    const uint8_t* __restrict__ s1p, const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
-    const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint16_t* __restrict__ hout,
-    int T, int k, int H, int I) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  const int mt = blockIdx.x;
+    const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8,
+    float* __restrict__ staging, int T, int k, int N, int R, int NT) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  __shared__ ATile tile[2];
+  const int mt = blockIdx.x / NT, nt = blockIdx.x - mt * NT;
   if (mt >= info[1]) return;
-  const int g = mt_group[mt], m0 = mt_row0[mt];
-  const int rows = grp_rows[g], row0 = grp_row0[g];
-  const int tk = T * k;
+  const int g = mt_group[mt];
+  const int r0 = grp_row0[g] + mt_row0[mt];          // first grouped row of the tile
+  const int nrows = min(kPM, grp_rows[g] - mt_row0[mt]);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ncol = blockIdx.y * BN + wave * 16 + (lane & 15);
-  const bool col_ok = ncol < I;
-  const size_t col = (size_t)g * (H >> 5) * I + (col_ok ? ncol : I - 1);
-  const uint8_t* gcr = gc + col * 16;
-  const uint8_t* gsr = gs + col;
-  const uint8_t* ucr = uc + col * 16;
-  const uint8_t* usr = us + col;
-  // activation loader: 64 rows x 4 segments of 16 bf16
-  const int arow = tid >> 2, aseg = tid & 3;
-  const bool a_ok = m0 + arow < rows;
-  const int atok = a_ok ? row_token(perm, row0 + m0 + arow, tk, k) : 0;
-  const uint16_t* asrc = x + (size_t)atok * H + aseg * 16;
-  const int kq = (lane >> 4) * 8;
-  f32x4 accg[4], accu[4];
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) accg[ms] = accu[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += BK) {
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (a_ok && k0 + aseg * 16 < H) {
-      v0 = *reinterpret_cast<const uint4*>(asrc + k0);
-      v1 = *reinterpret_cast<const uint4*>(asrc + k0 + 8);
-    }
-    __syncthreads();
-    *reinterpret_cast<uint4*>(&As[arow * LDA + aseg * 16]) = v0;
-    *reinterpret_cast<uint4*>(&As[arow * LDA + aseg * 16 + 8]) = v1;
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      if (k0 + kk < H) {
-        const bf16x8 bg = load_b_frag(gcr, gsr, I, k0 + kk + kq);
-        const bf16x8 bu = load_b_frag(ucr, usr, I, k0 + kk + kq);
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[(ms * 16 + (lane & 15)) * LDA + kk + kq]);
-          accg[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bg, accg[ms], 0, 0, 0);
-          accu[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bu, accu[ms], 0, 0, 0);
-        }
-      }
-    }
-  }
-  if (!col_ok) return;
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m0 + ms * 16 + (lane >> 4) * 4 + i;
-      if (r < rows) {
-        const float hv = silu_g(accg[ms][i]) * accu[ms][i];
-        hout[(size_t)(row0 + r) * I + ncol] = f32_to_bf16_bits(hv);
-      }
-    }
-  }
-}
+  const int m = lane & 15, q = lane >> 4;
+  const int tk = T * k;
+  const int KB = a.K >> 5;
+  const int nsteps = (a.K + kPK - 1) / kPK;
 
-// ------------------------------------------------------------------------------------
-// down: staging[slot(r)][n] = weight(r) * (h_r . Wd[n])
-// ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemm_down_kernel(
-    const uint16_t* __restrict__ hin, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
-    const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ info,
-    const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, float* __restrict__ staging, int T, int k, int H, int I) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  const int mt = blockIdx.x;
-  if (mt >= info[1]) return;
-  const int g = mt_group[mt], m0 = mt_row0[mt];
-  const int rows = grp_rows[g], row0 = grp_row0[g];
-  const int tk = T * k;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ncol = blockIdx.y * BN + wave * 16 + (lane & 15);
-  const bool col_ok = ncol < H;
-  const size_t col = (size_t)g * (I >> 5) * H + (col_ok ? ncol : H - 1);
-  const uint8_t* dcr = dc + col * 16;
-  const uint8_t* dsr = ds + col;
-  const int arow = tid >> 2, aseg = tid & 3;
-  const bool a_ok = m0 + arow < rows;
-  const uint16_t* asrc = hin + (size_t)(row0 + (a_ok ? m0 + arow : 0)) * I + aseg * 16;
-  const int kq = (lane >> 4) * 8;
-  f32x4 acc[4];
+  // the activation row this thread stages
+  const int lr = tid >> 2, lp = tid & 3;
+  int src = -1;
+  if (lr < nrows) src = GATEUP ? row_token(perm, r0 + lr, tk, k) : r0 + lr;
+
+  // this wave's weight columns (clamped; stores are masked)
+  const int n0 = nt * kPN + wave * kPNW;
+  const size_t gbase = (size_t)g * KB * N;
+  size_t col[4];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) acc[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < I; k0 += BK) {
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (a_ok && k0 + aseg * 16 < I) {
-      v0 = *reinterpret_cast<const uint4*>(asrc + k0);
-      v1 = *reinterpret_cast<const uint4*>(asrc + k0 + 8);
+  for (int c = 0; c < 4; ++c) col[c] = gbase + min(n0 + 16 * c + m, N - 1);
+  const uint8_t* codes[2] = {c0p, c1p};
+  const uint8_t* scales[2] = {s0p, s1p};
+  const int nsub = (nrows + 15) >> 4;
+
+  f32x4 acc[NM][4][4];
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx)
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[mtx][rs][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  BFrag<NM> fb[2];
+  a_store(tile[0], a_fetch(a, src, 0, lp), lr, lp);
+  b_fetch<NM>(fb[0], codes, scales, col, N, KB, 0, q);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    // even step: compute from tile[0] / fb[0], prefetch step s+1 into tile[1] / fb[1]
+    {
+      const bool more = s + 1 < nsteps;
+      AStage st;
+      if (more) {
+        st = a_fetch(a, src, s + 1, lp);
+        b_fetch<NM>(fb[1], codes, scales, col, N, KB, s + 1, q);
+      }
+      k_step<NM>(tile[0], fb[0], acc, nsub, m, q);
+      if (more) a_store(tile[1], st, lr, lp);
+      __syncthreads();
+      if (!more) break;
     }
-    __syncthreads();
-    *reinterpret_cast<uint4*>(&As[arow * LDA + aseg * 16]) = v0;
-    *reinterpret_cast<uint4*>(&As[arow * LDA + aseg * 16 + 8]) = v1;
-    __syncthreads();
+    // odd step
+    {
+      const bool more = s + 2 < nsteps;
+      AStage st;
+      if (more) {
+        st = a_fetch(a, src, s + 2, lp);
+        b_fetch<NM>(fb[0], codes, scales, col, N, KB, s + 2, q);
+      }
+      k_step<NM>(tile[1], fb[1], acc, nsub, m, q);
+      if (more) a_store(tile[0], st, lr, lp);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  if constexpr (GATEUP) {
+    uint8_t* h_lo = h8 + (size_t)R * N;
+    uint8_t* hs = h8 + (size_t)2 * R * N;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      if (k0 + kk < I) {
-        const bf16x8 bd = load_b_frag(dcr, dsr, H, k0 + kk + kq);
+    for (int rs = 0; rs < 4; ++rs) {
+      if (rs >= nsub) break;
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[(ms * 16 + (lane & 15)) * LDA + kk + kq]);
-          acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bd, acc[ms], 0, 0, 0);
+      for (int p = 0; p < 2; ++p) {  // 32-column block = column tiles 2p, 2p+1
+        const int nb = n0 + 32 * p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lrow = 16 * rs + 4 * q + i;
+          float hv[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) hv[c] = silu(acc[0][rs][2 * p + c][i]) * acc[1][rs][2 * p + c][i];
+          // lanes with the same q hold the same row: |h| max over the block's 32 columns
+          float amax = fmaxf(fabsf(hv[0]), fabsf(hv[1]));
+#pragma unroll
+          for (int msk = 1; msk < 16; msk <<= 1) amax = fmaxf(amax, __shfl_xor(amax, msk, 64));
+          const int sc = fp8_block_scale(amax);
+          const float inv = fp8_inv_scale(sc);
+          if (lrow < nrows && nb < N) {
+            const size_t r = (size_t)(r0 + lrow);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const float v = hv[c] * inv;
+              const uint32_t t0 = fp8_of(v);
+              const uint32_t t1 = fp8_of((v - f32_of_fp8(t0)) * 16.f);
+              const size_t o = r * N + nb + 16 * c + m;
+              h8[o] = (uint8_t)t0;
+              h_lo[o] = (uint8_t)t1;
+            }
+            if (m == 0) hs[r * (N >> 5) + (nb >> 5)] = (uint8_t)sc;
+          }
         }
       }
     }
-  }
-  if (!col_ok) return;
+  } else {
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
+    for (int rs = 0; rs < 4; ++rs) {
+      if (rs >= nsub) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m0 + ms * 16 + (lane >> 4) * 4 + i;
-      if (r < rows) {
-        const int gr = row0 + r;
-        const int slot = gr < tk ? perm[gr] : gr;
-        const float wt = gr < tk ? wts[slot] : 1.0f;
-        staging[(size_t)slot * H + ncol] = acc[ms][i] * wt;
+      for (int i = 0; i < 4; ++i) {
+        const int lrow = 16 * rs + 4 * q + i;
+        if (lrow >= nrows) continue;
+        const int rr = r0 + lrow;
+        const int slot = rr < tk ? perm[rr] : rr;
+        const float wt = rr < tk ? wts[slot] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = n0 + 16 * c + m;
+          if (n < N) staging[(size_t)slot * N + n] = acc[0][rs][c][i] * wt;
+        }
       }
     }
   }
@@ -175,22 +273,29 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int mt_bound, hipStream_t s) {
-  dim3 grid(mt_bound, (d.I + BN - 1) / BN);
+  (void)x;
+  const int NT = (d.I + kPN - 1) / kPN;
+  const int R = T * (d.K + d.S);
+  const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H};
   const int tk = timing_begin("gemm_gateup", s);
-  gemm_gateup_kernel<<<grid, 256, 0, s>>>(x, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
-                                          b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows,
-                                          static_cast<uint16_t*>(b.h), T, d.K, d.H, d.I);
+  gemm_f8f4_kernel<true><<<mt_bound * NT, 256, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
+                                                       b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
+                                                       b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, T, d.K, d.I,
+                                                       R, NT);
   timing_end(tk, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s) {
-  dim3 grid(mt_bound, (d.H + BN - 1) / BN);
+  const int NT = (d.H + kPN - 1) / kPN;
+  const int R = T * (d.K + d.S);
+  const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
+  const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
   const int tk = timing_begin("gemm_down", s);
-  gemm_down_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(b.h), w.down_codes, w.down_scales, b.perm,
-                                        b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, b.staging, T,
-                                        d.K, d.H, d.I);
+  gemm_f8f4_kernel<false><<<mt_bound * NT, 256, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
+                                                        b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
+                                                        b.grp_rows, nullptr, b.staging, T, d.K, d.H, R, NT);
   timing_end(tk, s);
   return hipGetLastError();
 }

@@ -35,22 +35,6 @@ constexpr int kSkM = 16;    // tokens per pass (MFMA M)
 constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (even)
 constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ __forceinline__ i32x8 fp4_operand(const uint4& c) {
-  return i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};  // FP4 reads the low 4 dwords
-}
-__device__ __forceinline__ i32x8 fp8_operand(const uint4& lo, const uint4& hi) {
-  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// acc += A(fp8, scale sa) x B(fp4, scale sb)
-__device__ __forceinline__ f32x4 mma_f8f4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
-}
-
 // Loads the FP8 activation operand of term `t` for lane (m, q) at step kb: K values
 // kb*32 + 16q .. +16 (block kb + q/2) and kb*32 + 64 + 16q .. +16 (block kb + 2 + q/2).
 __device__ __forceinline__ i32x8 load_act(const uint8_t* __restrict__ row, int kb, int q, bool ok1, bool ok2) {
@@ -143,7 +127,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
           usum += red[w][j][1][lane];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[c][i] = silu_f(gsum[i]) * usum[i];
+        for (int i = 0; i < 4; ++i) hv[c][i] = silu(gsum[i]) * usum[i];
       }
       const int nb = n0 + 32 * p;  // first column of the block
 #pragma unroll

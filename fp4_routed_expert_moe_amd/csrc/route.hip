@@ -291,19 +291,19 @@ __device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int 
 }
 
 // ------------------------------------------------------------------------------------
-// Router scores l[t][e] = x[t] . W_r[e] + b[e]  (fp32 accumulate, bf16 activations).
-// One workgroup of NT threads per (expert, tile of kRouterTT tokens): the threads split the
-// hidden axis (8 values each per step, U steps in flight); partial sums are added in
-// ascending hidden order per thread, across each wave, then over the waves in a fixed
-// order, so a score does not depend on the other tokens of the batch.
+// Small batches: router scores l[t][e] = x[t] . W_r[e] + b[e] (fp32 accumulate, bf16
+// activations) and the routing tail in one launch.  One workgroup of NT threads per (expert,
+// tile of kRouterTT tokens): the threads split the hidden axis (8 values each per step);
+// partial sums are added in ascending hidden order per thread, across each wave, then over
+// the waves in a fixed order, so a score does not depend on the other tokens of the batch.
 // ------------------------------------------------------------------------------------
-template <bool FUSED>
-__global__ __launch_bounds__(FUSED ? kTailThreads : 256) void router_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, CallBufs b,
-    int T, int E, int H, int K, int S, int quantize) {
-  constexpr int NT = FUSED ? kTailThreads : 256;
+__global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ wr,
+                                                             const float* __restrict__ bias, CallBufs b, int T,
+                                                             int E, int H, int K, int S, int quantize) {
+  constexpr int NT = kTailThreads;
   constexpr int NW = NT / 64;
-  constexpr int U = FUSED ? 1 : 4;
+  constexpr int U = 1;
   __shared__ float part[NW][kRouterTT];
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kRouterTT;
@@ -370,19 +370,130 @@ __global__ __launch_bounds__(FUSED ? kTailThreads : 256) void router_kernel(
     float v = part[0][tid];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += part[w][tid];
-    const float l = v + (bias ? bias[e] : 0.f);
-    if constexpr (FUSED)
-      st_agent(b.logits + (size_t)(t0 + tid) * E + e, l);
-    else
-      b.logits[(size_t)(t0 + tid) * E + e] = l;
+    st_agent(b.logits + (size_t)(t0 + tid) * E + e, v + (bias ? bias[e] : 0.f));
   }
-  if constexpr (FUSED) {
-    // the last workgroup to finish routes the whole batch, then re-arms the counter
-    __shared__ int is_last;
-    if (!arrive_last(&b.ctrl[0], (int)(gridDim.x * gridDim.y), &is_last)) return;
-    route_tail(b, T, E, K, S);
-    if (tid == 0) reset_counter(&b.ctrl[0]);
+  // the last workgroup to finish routes the whole batch, then re-arms the counter
+  __shared__ int is_last;
+  if (!arrive_last(&b.ctrl[0], (int)(gridDim.x * gridDim.y), &is_last)) return;
+  route_tail(b, T, E, K, S);
+  if (tid == 0) reset_counter(&b.ctrl[0]);
+}
+
+// ------------------------------------------------------------------------------------
+// Larger batches: router scores on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+// W_r (fp32) is split on the fly into three bf16 terms whose sum is exactly W_r: the top,
+// middle and low 8 bits of the 24-bit significand, each remainder exact (it is the float
+// minus its own truncation).  x (bf16) times each term is exact in fp32, so a score is the
+// fp32 dot product up to summation order, which is fixed per (token, expert).  64 tokens x
+// 64 experts per workgroup, 32 x 32 per wave (2 x 2 MFMA tiles, three terms each).
+// Operand layout: lane l holds row (token or expert) l % 16, K values 8*(l/16) .. +8 of each
+// 32-value step; result lane l, element i -> token 4*(l/16) + i, expert l % 16.
+// ------------------------------------------------------------------------------------
+constexpr int kRouterGemmTile = 64;
+
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {  // (bf16 of a) | (bf16 of b) << 16
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+// 8 consecutive fp32 weights -> three bf16x8 terms with t0 + t1 + t2 == w exactly.
+__device__ __forceinline__ void split3(const float4& p, const float4& r, bf16x8 (&t)[3]) {
+  uint32_t w[8] = {__float_as_uint(p.x), __float_as_uint(p.y), __float_as_uint(p.z), __float_as_uint(p.w),
+                   __float_as_uint(r.x), __float_as_uint(r.y), __float_as_uint(r.z), __float_as_uint(r.w)};
+  uint32_t u[3][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = w[i] & 0xFFFF0000u;
+    const float r1 = __uint_as_float(w[i]) - __uint_as_float(a);
+    const uint32_t b = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(b);  // at most 8 significant bits: exact in bf16
+    u[0][i] = a;
+    u[1][i] = b;
+    u[2][i] = __float_as_uint(r2);
   }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const uint4 v = make_uint4(hi_halves(u[j][0], u[j][1]), hi_halves(u[j][2], u[j][3]),
+                               hi_halves(u[j][4], u[j][5]), hi_halves(u[j][6], u[j][7]));
+    t[j] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int T, int E, int H) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+  const int t0 = blockIdx.x * kRouterGemmTile + (wave & 1) * 32;
+  const int e0 = blockIdx.y * kRouterGemmTile + (wave >> 1) * 32;
+  const uint16_t* xa[2];
+  const float* wb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xa[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 8 * kq;
+    wb[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * H + 8 * kq;
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;  // 32-value K steps loaded together
+  for (int k0 = 0; k0 < H; k0 += 32 * U) {
+    uint4 xr[U][2];
+    float4 wv[U][2][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + 32 * u;
+      if (k < H) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          xr[u][i] = *reinterpret_cast<const uint4*>(xa[i] + k);
+          wv[u][i][0] = *reinterpret_cast<const float4*>(wb[i] + k);
+          wv[u][i][1] = *reinterpret_cast<const float4*>(wb[i] + k + 4);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + 32 * u >= H) break;
+      bf16x8 bt[2][3];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[u][i]), bt[j][t],
+                                                                acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + 16 * j + r;
+      if (e >= E) continue;
+      const float be = bias ? bias[e] : 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 16 * i + 4 * kq + v;
+        if (t < T) logits[(size_t)t * E + e] = acc[i][j][v] + be;
+      }
+    }
+}
+
+// FP8 term split of x for the expert kernels (larger batches; small ones do it in the
+// router kernel): one thread per 32-value block.
+__global__ __launch_bounds__(256) void quantize_x_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
+                                                         int T, int H) {
+  const int KB = H >> 5;
+  const size_t j = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= (size_t)T * KB) return;
+  const size_t t = j / KB, bb = j % KB;
+  quantize_x_block(x + t * H + bb * 32, xq + t * H + bb * 32, xq + ((size_t)T + t) * H + bb * 32,
+                   xq + (size_t)2 * T * H + t * KB + bb);
 }
 
 // ------------------------------------------------------------------------------------
@@ -434,13 +545,22 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 const CallBufs& b, int T, bool quantize_x, hipStream_t s) {
-  dim3 grid(d.E, (T + kRouterTT - 1) / kRouterTT);
-  const bool fused = route_fused(d, T);
-  const int tk = timing_begin(fused ? "router_route" : "router_logits", s);
-  if (fused)
-    router_kernel<true><<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
-  else
-    router_kernel<false><<<grid, 256, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
+  if (route_fused(d, T)) {
+    dim3 grid(d.E, (T + kRouterTT - 1) / kRouterTT);
+    const int tk = timing_begin("router_route", s);
+    router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
+    timing_end(tk, s);
+    return hipGetLastError();
+  }
+  dim3 grid((T + kRouterGemmTile - 1) / kRouterGemmTile, (d.E + kRouterGemmTile - 1) / kRouterGemmTile);
+  int tk = timing_begin("router_gemm", s);
+  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, T, d.E, d.H);
+  timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !quantize_x) return e;
+  const size_t blocks = (size_t)T * (d.H / 32);
+  tk = timing_begin("quantize_x", s);
+  quantize_x_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(x, b.xq, T, d.H);
   timing_end(tk, s);
   return hipGetLastError();
 }

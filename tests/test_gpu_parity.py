@@ -38,7 +38,7 @@ def _check_case(groups, wr, b, x, top_k, shared, paths=("gemv", "gemm"), what=""
     for path in paths:
         layer = make_layer(wr, weights, top_k, shared, b, path)
         got = run_layer(layer, x)
-        check_routing(got, ref)
+        check_routing(got, ref, x, wr, b)
         check_outputs(got["y"], ref["y"], f"{what} path={path}")
         outs[path] = got
     return outs
@@ -74,7 +74,7 @@ def test_tiny_workload_both_paths():
     ref = oracle.moe_forward(x, wr, None, synth.LazyExperts(wl, 0, cache=wl.groups), wl.top_k, wl.shared)
     for path in ("auto", "gemv", "gemm"):
         got = run_layer(make_layer(wr, weights, wl.top_k, wl.shared, None, path), x)
-        check_routing(got, ref)
+        check_routing(got, ref, x, wr)
         check_outputs(got["y"], ref["y"], f"tiny path={path}")
 
 
@@ -229,7 +229,7 @@ def _full_size(name, sample_tokens, layer_index=0, bias=True):
     say(f"[{name}] GPU forward T={x.shape[0]}")
     got = run_layer(layer, x)
     ref_route = oracle_routing(x, wr, b, wl.top_k)
-    check_routing(got, ref_route)
+    check_routing(got, ref_route, x, wr, b)
     sample = np.linspace(0, x.shape[0] - 1, min(sample_tokens, x.shape[0])).astype(int)
     say(f"[{name}] oracle on {len(sample)} sampled tokens")
     ref = oracle.moe_forward(x[sample], wr, b, synth.LazyExperts(wl, layer_index, cache=4), wl.top_k, wl.shared)
@@ -282,7 +282,7 @@ def test_stacked_decode_16_layers():
     for (s, l), r in routes.items():
         ref = oracle_routing(xs[(s, l)], routers[l], None, wl.top_k)
         got = {k: v.cpu().numpy() for k, v in r.items()}
-        check_routing(got, ref)
+        check_routing(got, ref, xs[(s, l)], routers[l])
     for (s, l) in [(0, 0), (17, 5), (128, 9), (255, 15)]:
         ref = oracle.moe_forward(xs[(s, l)], routers[l], None, synth.LazyExperts(wl, l, cache=2), wl.top_k,
                                  wl.shared)
