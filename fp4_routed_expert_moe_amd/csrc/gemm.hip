@@ -6,16 +6,18 @@
 //
 // * Weights (B) enter the matrix cores as stored: e2m1 codes with their e8m0 block scales, no
 //   convert instruction touches them.  Each wave loads its own weight operands from the
-//   block-interleaved kernel layout straight into registers, one K step ahead.
+//   block-interleaved kernel layout straight into registers.
 // * Activations (A) are exact FP8 (e4m3) term splits with an e8m0 scale per 32 values: x as
 //   two terms (all 8 bf16 significand bits, written by the router kernel), h as two terms
 //   (about 8 significant bits, the precision of bf16) written by the gate/up epilogue.  One
 //   MFMA per term, all accumulating in fp32.
 // * A workgroup takes one M-tile (64 grouped rows of one group, from the device-built M-tile
-//   list) and 256 output columns.  Its four waves each own 64 columns of all 64 rows: 4 x 4
-//   16x16 tiles, for gate and up at once in the gate/up kernel, so SwiGLU stays in registers.
-//   The activation tile of each 256-value K step is staged in LDS (double-buffered) and read
-//   by all four waves; 16-row subtiles past the group's last row are skipped.
+//   list) and a slice of output columns.  Each wave owns a column slice of all 64 rows: 64 columns
+//   (4 x 4 16x16 tiles) in the down kernel, 32 columns for gate and up at once in the gate/up
+//   kernel (eight waves), so SwiGLU stays in registers.
+//   The activation tile of each 128-value K step is staged in LDS (double-buffered) and read
+//   by all waves; 16-row subtiles past the group's last row are skipped.  Loads run two
+//   steps ahead of the matrix work, and two workgroups share a CU.
 // * Workgroup b takes N-tile b % NT of M-tile b / NT.  Workgroups reach the 8 XCDs
 //   round-robin, so when NT is a multiple of 8 every XCD streams a fixed slice of columns of
 //   every expert and no expert's weight tile is fetched by two XCDs.
@@ -24,16 +26,38 @@
 namespace moe {
 
 constexpr int kPM = kGemmBM;      // rows per M-tile (64)
-constexpr int kPNW = 64;          // output columns per wave
-constexpr int kPN = 4 * kPNW;     // output columns per workgroup
-constexpr int kPU = 2;            // MFMA K chunks (128 values each) per step
-constexpr int kPK = 128 * kPU;    // K values per step
-constexpr int kPKB = kPK / 32;    // K blocks per step
-constexpr int kALd = kPK + 16;    // LDS row pitch of the activation tile (bytes)
 
+// Per-kernel shape: NW waves of CT 16-column tiles each (PN = NW * CT * 16 columns per
+// workgroup); PU = 128-value MFMA K chunks per step; OCC = workgroups per CU the register
+// budget targets.
+template <int NW_, int CT_, int PU_, int OCC_>
+struct GemmShape {
+  static constexpr int NW = NW_;
+  static constexpr int CT = CT_;
+  static constexpr int NTH = 64 * NW;      // threads
+  static constexpr int TPR = NTH / kPM;    // threads staging one activation row
+  static constexpr int PU = PU_;
+  static constexpr int OCC = OCC_;
+  static constexpr int PK = 128 * PU;      // K values per step
+  static constexpr int PKB = PK / 32;      // K blocks per step
+  static constexpr int ALD = PK + 16;      // LDS row pitch of the activation tile (bytes)
+  static constexpr int CH = 128 / TPR / 16;  // 16-byte chunks per thread, term and K chunk
+  static constexpr int PN = NW * CT * 16;    // output columns per workgroup
+  static_assert(TPR == 4 || TPR == 8, "workgroup shape");
+};
+#ifndef MOE_GU_SHAPE
+#define MOE_GU_SHAPE 4, 2, 1, 2
+#endif
+#ifndef MOE_DN_SHAPE
+#define MOE_DN_SHAPE 4, 4, 1, 2
+#endif
+using GateUpShape = GemmShape<MOE_GU_SHAPE>;
+using DownShape = GemmShape<MOE_DN_SHAPE>;
+
+template <class SH>
 struct ATile {                    // one K step of the activation tile
-  uint8_t v[2][kPM][kALd];        // FP8 terms
-  uint8_t s[kPM][kPKB];           // e8m0 scales of the step's K blocks
+  uint8_t v[2][kPM][SH::ALD];     // FP8 terms
+  uint8_t s[kPM][SH::PKB];        // e8m0 scales of the step's K blocks
 };
 
 // Activation rows: term planes hi/lo [rows][K] bytes and scales [rows][K/32].
@@ -44,59 +68,66 @@ struct ARows {
   int K;
 };
 
-// Thread t of 256 moves K blocks u*4 + p (u < kPU, p = t%4) of K step `step` of tile row t/4,
-// both terms and scales, into LDS.  `src_row` < 0 marks a row past the group: zeros with
-// scale 127 (as are blocks past K).
+// Thread t moves bytes [p*B, p*B + B) (B = 128/TPR, p = t % TPR) of each 128-value chunk u of
+// K step `step` of tile row t/TPR, both terms, into LDS, and threads p < 4 the scale of K
+// block 4u + p.  `src_row` < 0 marks a row past the group: zeros with scale 127 (as are
+// blocks past K).
+template <class SH>
 struct AStage {
-  uint4 c[kPU][4];
-  uint32_t s[kPU];
+  uint4 c[SH::PU][2][SH::CH];
+  uint32_t s[SH::PU];
 };
-__device__ __forceinline__ AStage a_fetch(const ARows& a, int src_row, int step, int p) {
-  AStage st;
+template <class SH>
+__device__ __forceinline__ AStage<SH> a_fetch(const ARows& a, int src_row, int step, int p) {
+  AStage<SH> st;
   const int KB = a.K >> 5;
   const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int u = 0; u < kPU; ++u) {
-    const int blk = step * kPKB + 4 * u + p;
-    const bool ok = src_row >= 0 && blk < KB;
-    const size_t o = (size_t)src_row * a.K + 32 * blk;
-    st.c[u][0] = ok ? ld16(a.hi + o) : z;
-    st.c[u][1] = ok ? ld16(a.hi + o + 16) : z;
-    st.c[u][2] = ok ? ld16(a.lo + o) : z;
-    st.c[u][3] = ok ? ld16(a.lo + o + 16) : z;
-    st.s[u] = ok ? a.sc[(size_t)src_row * KB + blk] : 127u;
+  for (int u = 0; u < SH::PU; ++u) {
+    const int kbyte = step * SH::PK + 128 * u + 16 * SH::CH * p;
+    const bool ok = src_row >= 0 && kbyte < a.K;
+    const size_t o = (size_t)src_row * a.K + kbyte;
+#pragma unroll
+    for (int j = 0; j < SH::CH; ++j) {
+      st.c[u][0][j] = ok ? ld16(a.hi + o + 16 * j) : z;
+      st.c[u][1][j] = ok ? ld16(a.lo + o + 16 * j) : z;
+    }
+    const int blk = step * SH::PKB + 4 * u + p;
+    st.s[u] = (p < 4 && src_row >= 0 && blk < KB) ? a.sc[(size_t)src_row * KB + blk] : 127u;
   }
   return st;
 }
-__device__ __forceinline__ void a_store(ATile& t, const AStage& st, int r, int p) {
+template <class SH>
+__device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int r, int p) {
 #pragma unroll
-  for (int u = 0; u < kPU; ++u) {
-    const int b = 128 * u + 32 * p;
-    *reinterpret_cast<uint4*>(&t.v[0][r][b]) = st.c[u][0];
-    *reinterpret_cast<uint4*>(&t.v[0][r][b + 16]) = st.c[u][1];
-    *reinterpret_cast<uint4*>(&t.v[1][r][b]) = st.c[u][2];
-    *reinterpret_cast<uint4*>(&t.v[1][r][b + 16]) = st.c[u][3];
-    t.s[r][4 * u + p] = (uint8_t)st.s[u];
+  for (int u = 0; u < SH::PU; ++u) {
+    const int b = 128 * u + 16 * SH::CH * p;
+#pragma unroll
+    for (int j = 0; j < SH::CH; ++j) {
+      *reinterpret_cast<uint4*>(&t.v[0][r][b + 16 * j]) = st.c[u][0][j];
+      *reinterpret_cast<uint4*>(&t.v[1][r][b + 16 * j]) = st.c[u][1][j];
+    }
+    if (p < 4) t.s[r][4 * u + p] = (uint8_t)st.s[u];
   }
 }
 
-// Weight operands of one wave for one K step: kPU chunks x NM matrices x 4 column tiles.
-template <int NM>
+// Weight operands of one wave for one K step: PU chunks x NM matrices x CT column tiles.
+template <class SH, int NM>
 struct BFrag {
-  uint4 c[kPU][NM][4];
-  int s[kPU][NM][4];
+  uint4 c[SH::PU][NM][SH::CT];
+  int s[SH::PU][NM][SH::CT];
 };
-template <int NM>
-__device__ __forceinline__ void b_fetch(BFrag<NM>& f, const uint8_t* const* codes, const uint8_t* const* scales,
+template <class SH, int NM>
+__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const uint8_t* const* codes, const uint8_t* const* scales,
                                         const size_t* col, int N, int KB, int step, int q) {
 #pragma unroll
-  for (int u = 0; u < kPU; ++u) {
-    const int kb = step * kPKB + 4 * u + q;
+  for (int u = 0; u < SH::PU; ++u) {
+    const int kb = step * SH::PKB + 4 * u + q;
     const bool ok = kb < KB;
 #pragma unroll
     for (int mtx = 0; mtx < NM; ++mtx)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < SH::CT; ++c) {
         const size_t o = (size_t)kb * N + col[c];
         f.c[u][mtx][c] = ok ? ld16(codes[mtx] + o * 16) : make_uint4(0, 0, 0, 0);
         f.s[u][mtx][c] = ok ? scales[mtx][o] : 127;
@@ -105,11 +136,11 @@ __device__ __forceinline__ void b_fetch(BFrag<NM>& f, const uint8_t* const* code
 }
 
 // One K step: acc[mtx][rs][c] += A(rs) x B(mtx, c) for both FP8 terms, rs < nsub.
-template <int NM>
-__device__ __forceinline__ void k_step(const ATile& t, const BFrag<NM>& f, f32x4 (&acc)[NM][4][4], int nsub, int m,
-                                       int q) {
+template <class SH, int NM>
+__device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& f, f32x4 (&acc)[NM][4][SH::CT],
+                                       int nsub, int m, int q) {
 #pragma unroll
-  for (int u = 0; u < kPU; ++u)
+  for (int u = 0; u < SH::PU; ++u)
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
@@ -121,7 +152,7 @@ __device__ __forceinline__ void k_step(const ATile& t, const BFrag<NM>& f, f32x4
                                    *reinterpret_cast<const uint4*>(&t.v[1][r][b + 64]));
       const int sa = t.s[r][4 * u + q];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < SH::CT; ++c)
 #pragma unroll
         for (int mtx = 0; mtx < NM; ++mtx) {
           const i32x8 bb = fp4_operand(f.c[u][mtx][c]);
@@ -136,15 +167,15 @@ __device__ __forceinline__ void k_step(const ATile& t, const BFrag<NM>& f, f32x4
 //         (h8 = [2][R][I] bytes then [R][I/32] scales).
 // DOWN:   staging[slot(r)][n] = weight(r) * (h_r . Wd[n]).
 // ------------------------------------------------------------------------------------
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void gemm_f8f4_kernel(
+template <bool GATEUP, class SH>
+__global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     ARows a, const uint8_t* __restrict__ c0p, const uint8_t* __restrict__ s0p, const uint8_t* __restrict__ c1p,
     const uint8_t* __restrict__ s1p, const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
     const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8,
     float* __restrict__ staging, int T, int k, int N, int R, int NT) {
   constexpr int NM = GATEUP ? 2 : 1;
-  __shared__ ATile tile[2];
+  __shared__ ATile<SH> tile[2];
   const int mt = blockIdx.x / NT, nt = blockIdx.x - mt * NT;
   if (mt >= info[1]) return;
   const int g = mt_group[mt];
@@ -154,61 +185,62 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(
   const int m = lane & 15, q = lane >> 4;
   const int tk = T * k;
   const int KB = a.K >> 5;
-  const int nsteps = (a.K + kPK - 1) / kPK;
+  const int nsteps = (a.K + SH::PK - 1) / SH::PK;
 
   // the activation row this thread stages
-  const int lr = tid >> 2, lp = tid & 3;
+  const int lr = tid / SH::TPR, lp = tid % SH::TPR;
   int src = -1;
   if (lr < nrows) src = GATEUP ? row_token(perm, r0 + lr, tk, k) : r0 + lr;
 
   // this wave's weight columns (clamped; stores are masked)
-  const int n0 = nt * kPN + wave * kPNW;
+  const int n0 = nt * SH::PN + wave * 16 * SH::CT;
   const size_t gbase = (size_t)g * KB * N;
-  size_t col[4];
+  size_t col[SH::CT];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) col[c] = gbase + min(n0 + 16 * c + m, N - 1);
+  for (int c = 0; c < SH::CT; ++c) col[c] = gbase + min(n0 + 16 * c + m, N - 1);
   const uint8_t* codes[2] = {c0p, c1p};
   const uint8_t* scales[2] = {s0p, s1p};
   const int nsub = (nrows + 15) >> 4;
 
-  f32x4 acc[NM][4][4];
+  f32x4 acc[NM][4][SH::CT];
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx)
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[mtx][rs][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < SH::CT; ++c) acc[mtx][rs][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BFrag<NM> fb[2];
-  a_store(tile[0], a_fetch(a, src, 0, lp), lr, lp);
-  b_fetch<NM>(fb[0], codes, scales, col, N, KB, 0, q);
+  // Three-deep pipeline: while step s runs on the matrix cores, the activation rows of step
+  // s+2 and the weight operands of step s+2 are in flight, and step s+1's rows (loaded one
+  // step earlier) go from registers into the other LDS buffer.
+  AStage<SH> ast[2];
+  BFrag<SH, NM> fb[3];
+  a_store<SH>(tile[0], a_fetch<SH>(a, src, 0, lp), lr, lp);
+  b_fetch<SH, NM>(fb[0], codes, scales, col, N, KB, 0, q);
+  if (nsteps > 1) {
+    ast[1] = a_fetch<SH>(a, src, 1, lp);
+    b_fetch<SH, NM>(fb[1], codes, scales, col, N, KB, 1, q);
+  }
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    // even step: compute from tile[0] / fb[0], prefetch step s+1 into tile[1] / fb[1]
-    {
-      const bool more = s + 1 < nsteps;
-      AStage st;
-      if (more) {
-        st = a_fetch(a, src, s + 1, lp);
-        b_fetch<NM>(fb[1], codes, scales, col, N, KB, s + 1, q);
-      }
-      k_step<NM>(tile[0], fb[0], acc, nsub, m, q);
-      if (more) a_store(tile[1], st, lr, lp);
-      __syncthreads();
-      if (!more) break;
+  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BFrag<SH, NM>& fc,
+                  BFrag<SH, NM>& f_far) -> bool {
+    if (s + 2 < nsteps) {
+      a_far = a_fetch<SH>(a, src, s + 2, lp);
+      b_fetch<SH, NM>(f_far, codes, scales, col, N, KB, s + 2, q);
     }
-    // odd step
-    {
-      const bool more = s + 2 < nsteps;
-      AStage st;
-      if (more) {
-        st = a_fetch(a, src, s + 2, lp);
-        b_fetch<NM>(fb[0], codes, scales, col, N, KB, s + 2, q);
-      }
-      k_step<NM>(tile[1], fb[1], acc, nsub, m, q);
-      if (more) a_store(tile[0], st, lr, lp);
-      __syncthreads();
-    }
+    k_step<SH, NM>(tc, fc, acc, nsub, m, q);
+    const bool more = s + 1 < nsteps;
+    if (more) a_store<SH>(tn, a_next, lr, lp);
+    __syncthreads();
+    return more;
+  };
+  for (int s = 0; s < nsteps; s += 6) {
+    if (!step(s + 0, tile[0], tile[1], ast[1], ast[0], fb[0], fb[2])) break;
+    if (!step(s + 1, tile[1], tile[0], ast[0], ast[1], fb[1], fb[0])) break;
+    if (!step(s + 2, tile[0], tile[1], ast[1], ast[0], fb[2], fb[1])) break;
+    if (!step(s + 3, tile[1], tile[0], ast[0], ast[1], fb[0], fb[2])) break;
+    if (!step(s + 4, tile[0], tile[1], ast[1], ast[0], fb[1], fb[0])) break;
+    if (!step(s + 5, tile[1], tile[0], ast[0], ast[1], fb[2], fb[1])) break;
   }
 
   // ---- epilogue ----
@@ -219,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {  // 32-column block = column tiles 2p, 2p+1
+      for (int p = 0; p < SH::CT / 2; ++p) {  // 32-column block = column tiles 2p, 2p+1
         const int nb = n0 + 32 * p;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -261,7 +293,7 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(
         const int slot = rr < tk ? perm[rr] : rr;
         const float wt = rr < tk ? wts[slot] : 1.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < SH::CT; ++c) {
           const int n = n0 + 16 * c + m;
           if (n < N) staging[(size_t)slot * N + n] = acc[0][rs][c][i] * wt;
         }
@@ -274,11 +306,11 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int mt_bound, hipStream_t s) {
   (void)x;
-  const int NT = (d.I + kPN - 1) / kPN;
+  const int NT = (d.I + GateUpShape::PN - 1) / GateUpShape::PN;
   const int R = T * (d.K + d.S);
   const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H};
   const int tk = timing_begin("gemm_gateup", s);
-  gemm_f8f4_kernel<true><<<mt_bound * NT, 256, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
+  gemm_f8f4_kernel<true, GateUpShape><<<mt_bound * NT, GateUpShape::NTH, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
                                                        b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
                                                        b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, T, d.K, d.I,
                                                        R, NT);
@@ -288,12 +320,12 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
 
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s) {
-  const int NT = (d.H + kPN - 1) / kPN;
+  const int NT = (d.H + DownShape::PN - 1) / DownShape::PN;
   const int R = T * (d.K + d.S);
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
   const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
   const int tk = timing_begin("gemm_down", s);
-  gemm_f8f4_kernel<false><<<mt_bound * NT, 256, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
+  gemm_f8f4_kernel<false, DownShape><<<mt_bound * NT, DownShape::NTH, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
                                                         b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
                                                         b.grp_rows, nullptr, b.staging, T, d.K, d.H, R, NT);
   timing_end(tk, s);
