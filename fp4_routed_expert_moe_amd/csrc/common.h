@@ -136,6 +136,7 @@ __device__ __forceinline__ uint32_t fp8_of(float v) {
 }
 __device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 

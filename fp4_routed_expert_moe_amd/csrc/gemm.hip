@@ -68,32 +68,45 @@ struct ARows {
   int K;
 };
 
-// Thread t moves bytes [p*B, p*B + B) (B = 128/TPR, p = t % TPR) of each 128-value chunk u of
-// K step `step` of tile row t/TPR, both terms, into LDS, and threads p < 4 the scale of K
-// block 4u + p.  `src_row` < 0 marks a row past the group: zeros with scale 127 (as are
-// blocks past K).
+// Activation K blocks past the end of K (only in the last step when K % PK != 0) read a valid
+// part of the row instead, with scale byte 4; the weights there read as zero codes with scale
+// byte 0, so every such product is 0, and term 1's scale (byte - 4) stays >= 0.
+constexpr uint32_t kTailScaleA = 4;
+
+// Thread t stages bytes [p*B, p*B + B) (B = 128/TPR, p = t % TPR) of each 128-value chunk u of
+// a K step of tile row t/TPR, both terms, and threads p < 4 the scale of K block 4u + p.
+// Rows past the group's end stage a copy of the tile's first row (their results are dropped).
 template <class SH>
 struct AStage {
-  uint4 c[SH::PU][2][SH::CH];
+  i32x4 c[SH::PU][2][SH::CH];
   uint32_t s[SH::PU];
 };
+struct APtr {
+  const uint8_t* hi;   // this thread's bytes of its row at K step 0
+  const uint8_t* lo;
+  const uint8_t* sc;   // scale of block p at step 0
+};
 template <class SH>
-__device__ __forceinline__ AStage<SH> a_fetch(const ARows& a, int src_row, int step, int p) {
+__device__ __forceinline__ AStage<SH> a_fetch(const APtr& ap, int K, int step, int p) {
   AStage<SH> st;
-  const int KB = a.K >> 5;
-  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int KB = K >> 5;
+  const bool tail = (step + 1) * SH::PK > K;  // uniform
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
-    const int kbyte = step * SH::PK + 128 * u + 16 * SH::CH * p;
-    const bool ok = src_row >= 0 && kbyte < a.K;
-    const size_t o = (size_t)src_row * a.K + kbyte;
+    int off = step * SH::PK + 128 * u;  // chunk start (uniform); this thread adds 16*CH*p
+    int blk = step * SH::PKB + 4 * u;   // first block of the chunk (uniform); this thread's is blk + p
+    bool sok = true;
+    if (tail) {
+      if (off + 16 * SH::CH * p >= K) off = K - 16 * SH::CH * (p + 1);  // a valid part of the row
+      sok = blk + p < KB;
+      if (!sok) blk = KB - 1 - p;
+    }
 #pragma unroll
     for (int j = 0; j < SH::CH; ++j) {
-      st.c[u][0][j] = ok ? ld16(a.hi + o + 16 * j) : z;
-      st.c[u][1][j] = ok ? ld16(a.lo + o + 16 * j) : z;
+      st.c[u][0][j] = *reinterpret_cast<const i32x4*>(ap.hi + off + 16 * j);
+      st.c[u][1][j] = *reinterpret_cast<const i32x4*>(ap.lo + off + 16 * j);
     }
-    const int blk = step * SH::PKB + 4 * u + p;
-    st.s[u] = (p < 4 && src_row >= 0 && blk < KB) ? a.sc[(size_t)src_row * KB + blk] : 127u;
+    st.s[u] = p < 4 ? (sok ? (uint32_t)ap.sc[blk] : kTailScaleA) : 127u;
   }
   return st;
 }
@@ -104,33 +117,41 @@ __device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int 
     const int b = 128 * u + 16 * SH::CH * p;
 #pragma unroll
     for (int j = 0; j < SH::CH; ++j) {
-      *reinterpret_cast<uint4*>(&t.v[0][r][b + 16 * j]) = st.c[u][0][j];
-      *reinterpret_cast<uint4*>(&t.v[1][r][b + 16 * j]) = st.c[u][1][j];
+      *reinterpret_cast<i32x4*>(&t.v[0][r][b + 16 * j]) = st.c[u][0][j];
+      *reinterpret_cast<i32x4*>(&t.v[1][r][b + 16 * j]) = st.c[u][1][j];
     }
     if (p < 4) t.s[r][4 * u + p] = (uint8_t)st.s[u];
   }
 }
 
 // Weight operands of one wave for one K step: PU chunks x NM matrices x CT column tiles.
+// Lane (n, q) reads K block 4u + q of its column: one 16-byte chunk and its scale byte.  The
+// loads go through buffer descriptors spanning one group's matrix, so the per-lane offset is
+// fixed, the K position is a scalar offset, and reads past the matrix (the K tail) return 0:
+// zero codes with scale byte 0.
 template <class SH, int NM>
 struct BFrag {
-  uint4 c[SH::PU][NM][SH::CT];
+  i32x4 c[SH::PU][NM][SH::CT];
   int s[SH::PU][NM][SH::CT];
 };
+template <int NM>
+struct BSrc {
+  __amdgpu_buffer_rsrc_t c[NM], s[NM];
+  int voff_c, voff_s;  // column tile 0, K block q, step 0
+};
+constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
 template <class SH, int NM>
-__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const uint8_t* const* codes, const uint8_t* const* scales,
-                                        const size_t* col, int N, int KB, int step, int q) {
+__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<NM>& bs, int N, int step) {
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
-    const int kb = step * SH::PKB + 4 * u + q;
-    const bool ok = kb < KB;
+    const int kb = step * SH::PKB + 4 * u;  // uniform; kept in scalar registers
+    const int so_s = __builtin_amdgcn_readfirstlane(kb * N), so_c = so_s * 16;
 #pragma unroll
     for (int mtx = 0; mtx < NM; ++mtx)
 #pragma unroll
       for (int c = 0; c < SH::CT; ++c) {
-        const size_t o = (size_t)kb * N + col[c];
-        f.c[u][mtx][c] = ok ? ld16(codes[mtx] + o * 16) : make_uint4(0, 0, 0, 0);
-        f.s[u][mtx][c] = ok ? scales[mtx][o] : 127;
+        f.c[u][mtx][c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + 256 * c, so_c, 0));
+        f.s[u][mtx][c] = __builtin_amdgcn_raw_buffer_load_b8(bs.s[mtx], bs.voff_s + 16 * c, so_s, 0);
       }
   }
 }
@@ -146,16 +167,19 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& 
       if (rs >= nsub) break;
       const int r = 16 * rs + m;
       const int b = 128 * u + 16 * q;
-      const i32x8 a0 = fp8_operand(*reinterpret_cast<const uint4*>(&t.v[0][r][b]),
-                                   *reinterpret_cast<const uint4*>(&t.v[0][r][b + 64]));
-      const i32x8 a1 = fp8_operand(*reinterpret_cast<const uint4*>(&t.v[1][r][b]),
-                                   *reinterpret_cast<const uint4*>(&t.v[1][r][b + 64]));
+      const i32x8 a0 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[0][r][b]),
+                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b + 64]), 0, 1, 2, 3, 4,
+                                               5, 6, 7);
+      const i32x8 a1 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[1][r][b]),
+                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b + 64]), 0, 1, 2, 3, 4,
+                                               5, 6, 7);
       const int sa = t.s[r][4 * u + q];
 #pragma unroll
       for (int c = 0; c < SH::CT; ++c)
 #pragma unroll
         for (int mtx = 0; mtx < NM; ++mtx) {
-          const i32x8 bb = fp4_operand(f.c[u][mtx][c]);
+          // FP4 reads the low four registers of the operand; the rest are left undefined
+          const i32x8 bb = __builtin_shufflevector(f.c[u][mtx][c], f.c[u][mtx][c], 0, 1, 2, 3, -1, -1, -1, -1);
           acc[mtx][rs][c] = mma_f8f4(a0, bb, acc[mtx][rs][c], sa, f.s[u][mtx][c]);
           acc[mtx][rs][c] = mma_f8f4(a1, bb, acc[mtx][rs][c], sa - 4, f.s[u][mtx][c]);
         }
@@ -178,28 +202,40 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   __shared__ ATile<SH> tile[2];
   const int mt = blockIdx.x / NT, nt = blockIdx.x - mt * NT;
   if (mt >= info[1]) return;
-  const int g = mt_group[mt];
-  const int r0 = grp_row0[g] + mt_row0[mt];          // first grouped row of the tile
-  const int nrows = min(kPM, grp_rows[g] - mt_row0[mt]);
+  // tile metadata is the same for every lane: keep it in scalar registers
+  const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
+  const int mr0 = __builtin_amdgcn_readfirstlane(mt_row0[mt]);
+  const int r0 = __builtin_amdgcn_readfirstlane(grp_row0[g]) + mr0;  // first grouped row of the tile
+  const int nrows = min(kPM, __builtin_amdgcn_readfirstlane(grp_rows[g]) - mr0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, q = lane >> 4;
   const int tk = T * k;
   const int KB = a.K >> 5;
   const int nsteps = (a.K + SH::PK - 1) / SH::PK;
 
-  // the activation row this thread stages
+  // the activation row this thread stages (rows past the group repeat the tile's first row)
   const int lr = tid / SH::TPR, lp = tid % SH::TPR;
-  int src = -1;
-  if (lr < nrows) src = GATEUP ? row_token(perm, r0 + lr, tk, k) : r0 + lr;
+  const int srow = GATEUP ? row_token(perm, r0 + min(lr, nrows - 1) * (lr < nrows), tk, k) : r0 + lr * (lr < nrows);
+  APtr ap;
+  ap.hi = a.hi + (size_t)srow * a.K + 16 * SH::CH * lp;
+  ap.lo = a.lo + (size_t)srow * a.K + 16 * SH::CH * lp;
+  ap.sc = a.sc + (size_t)srow * KB + lp;
 
-  // this wave's weight columns (clamped; stores are masked)
+  // this wave's weight columns (columns past N read other bytes of the group or zeros; their
+  // results are not stored)
   const int n0 = nt * SH::PN + wave * 16 * SH::CT;
-  const size_t gbase = (size_t)g * KB * N;
-  size_t col[SH::CT];
-#pragma unroll
-  for (int c = 0; c < SH::CT; ++c) col[c] = gbase + min(n0 + 16 * c + m, N - 1);
   const uint8_t* codes[2] = {c0p, c1p};
   const uint8_t* scales[2] = {s0p, s1p};
+  BSrc<NM> bs;
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx) {
+    bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
+                                                  KB * N * 16, kBufferFlags);
+    bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * KB * N), (short)0, KB * N,
+                                                  kBufferFlags);
+  }
+  bs.voff_s = q * N + n0 + m;
+  bs.voff_c = bs.voff_s * 16;
   const int nsub = (nrows + 15) >> 4;
 
   f32x4 acc[NM][4][SH::CT];
@@ -215,18 +251,18 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   // step earlier) go from registers into the other LDS buffer.
   AStage<SH> ast[2];
   BFrag<SH, NM> fb[3];
-  a_store<SH>(tile[0], a_fetch<SH>(a, src, 0, lp), lr, lp);
-  b_fetch<SH, NM>(fb[0], codes, scales, col, N, KB, 0, q);
+  a_store<SH>(tile[0], a_fetch<SH>(ap, a.K, 0, lp), lr, lp);
+  b_fetch<SH, NM>(fb[0], bs, N, 0);
   if (nsteps > 1) {
-    ast[1] = a_fetch<SH>(a, src, 1, lp);
-    b_fetch<SH, NM>(fb[1], codes, scales, col, N, KB, 1, q);
+    ast[1] = a_fetch<SH>(ap, a.K, 1, lp);
+    b_fetch<SH, NM>(fb[1], bs, N, 1);
   }
   __syncthreads();
   auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BFrag<SH, NM>& fc,
                   BFrag<SH, NM>& f_far) -> bool {
     if (s + 2 < nsteps) {
-      a_far = a_fetch<SH>(a, src, s + 2, lp);
-      b_fetch<SH, NM>(f_far, codes, scales, col, N, KB, s + 2, q);
+      a_far = a_fetch<SH>(ap, a.K, s + 2, lp);
+      b_fetch<SH, NM>(f_far, bs, N, s + 2);
     }
     k_step<SH, NM>(tc, fc, acc, nsub, m, q);
     const bool more = s + 1 < nsteps;
