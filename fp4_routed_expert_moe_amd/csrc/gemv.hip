@@ -10,13 +10,15 @@
 //
 // * B (weights, FP4): lane (n, q) holds block kb+q of row n -- one 16-byte chunk of the
 //   block-interleaved kernel layout (a wave reads 4 x 256 contiguous bytes per column tile)
-//   -- and that block's scale byte.
+//   -- and that block's scale byte, through buffer loads.
 // * A (activations, FP8 e4m3): lane (m, q) holds 16 values at K offset 16q and 16 at 64+16q
 //   of the 128-value step for token m, plus the scale of block kb+q.  Activations arrive as
 //   exact FP8 term splits (x: 2 terms = all 8 bf16 bits; h: 3 terms = 12 bits), one MFMA
 //   per term, all accumulating in fp32.
 // * A wave owns 64 rows (4 column tiles of 16 sharing the activation operand) and one
-//   quarter of the reduction axis; the 4 quarters are added through LDS in a fixed order.
+//   quarter of the reduction axis (whole 128-value iterations, the next one's loads in
+//   flight while the current one runs); the 4 quarters are added through LDS in a fixed
+//   order.
 //   Gate and up row n meet in the same lane, so SwiGLU stays in registers.  The tokens of
 //   a group are the MFMA's M side, up to 16 per pass: one pass per group in decode.
 // * A token's result depends only on its own activations (fixed K and reduction order), so
@@ -35,36 +37,120 @@ constexpr int kSkM = 16;    // tokens per pass (MFMA M)
 constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (even)
 constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
 
-// Loads the FP8 activation operand of term `t` for lane (m, q) at step kb: K values
-// kb*32 + 16q .. +16 (block kb + q/2) and kb*32 + 64 + 16q .. +16 (block kb + 2 + q/2).
-__device__ __forceinline__ i32x8 load_act(const uint8_t* __restrict__ row, int kb, int q, bool ok1, bool ok2) {
-  const uint8_t* p = row + (size_t)kb * 32 + 16 * q;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  return fp8_operand(ok1 ? ld16(p) : z, ok2 ? ld16(p + 64) : z);
+// One K iteration (4 blocks = 128 values) of a wave's operands.  Weights come through buffer
+// descriptors spanning one group's matrix: a fixed per-lane offset, the K position as a
+// scalar offset, and reads past the matrix return zero codes with scale 0, so the last
+// iteration of K needs no masking on that side.  Activations come from the token rows of
+// the pass; past the end of K they read a valid part of the row (multiplied by zero weights).
+constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
+
+template <int NM, int NA>
+struct GFrag {
+  i32x4 c[NM][kTiles];
+  int s[NM][kTiles];
+  i32x4 a[NA][2];
+  int sa;
+};
+template <int NM>
+struct GSrc {
+  __amdgpu_buffer_rsrc_t c[NM], s[NM];
+  int voff_c[kTiles], voff_s[kTiles];  // column tile j, K block q, K iteration 0
+};
+template <int NM>
+__device__ __forceinline__ void gsrc_init(GSrc<NM>& src, const uint8_t* const* codes, const uint8_t* const* scales,
+                                          int g, int KB, int N, int n0, int m, int q) {
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx) {
+    src.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
+                                                   KB * N * 16, kBufferFlags);
+    src.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * KB * N), (short)0, KB * N,
+                                                   kBufferFlags);
+  }
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    src.voff_s[j] = q * N + min(n0 + 16 * j + m, N - 1);
+    src.voff_c[j] = src.voff_s[j] * 16;
+  }
+}
+template <int NM, int NA>
+__device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, int N, const uint8_t* const* arow,
+                                        const uint8_t* asc, int K, int it, int q) {
+  const int kb = 4 * it;
+  const int so_s = __builtin_amdgcn_readfirstlane(kb * N), so_c = so_s * 16;
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx)
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      f.c[mtx][j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], src.voff_c[j], so_c, 0));
+      f.s[mtx][j] = __builtin_amdgcn_raw_buffer_load_b8(src.s[mtx], src.voff_s[j], so_s, 0);
+    }
+  int o1 = kb * 32 + 16 * q, o2 = o1 + 64;
+  if ((kb + 4) * 32 > K) {  // last iteration of a K that is not a multiple of 128 (uniform)
+    o1 = min(o1, K - 16);
+    o2 = min(o2, K - 16);
+  }
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    f.a[t][0] = *reinterpret_cast<const i32x4*>(arow[t] + o1);
+    f.a[t][1] = *reinterpret_cast<const i32x4*>(arow[t] + o2);
+  }
+  f.sa = asc[min(kb + q, (K >> 5) - 1)];
+}
+// acc[mtx][j] += sum over the NA terms of A(term) x B(mtx, tile j); term t has scale sa - 4t.
+template <int NM, int NA>
+__device__ __forceinline__ void gv_mma(const GFrag<NM, NA>& f, f32x4 (&acc)[NM][kTiles]) {
+  i32x8 a[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j)
+#pragma unroll
+    for (int mtx = 0; mtx < NM; ++mtx) {
+      const i32x8 b = __builtin_shufflevector(f.c[mtx][j], f.c[mtx][j], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+      for (int t = 0; t < NA; ++t) acc[mtx][j] = mma_f8f4(a[t], b, acc[mtx][j], f.sa - 4 * t, f.s[mtx][j]);
+    }
+}
+// This wave's K iterations [it_lo, it_hi), the loads of iteration i+1 in flight while
+// iteration i runs on the matrix cores.
+template <int NM, int NA>
+__device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>& src, int N,
+                                        const uint8_t* const* arow, const uint8_t* asc, int K, int it_lo, int it_hi,
+                                        int q) {
+  GFrag<NM, NA> f[2];
+  if (it_lo < it_hi) gv_load<NM, NA>(f[0], src, N, arow, asc, K, it_lo, q);
+  for (int it = it_lo; it < it_hi; it += 2) {
+    if (it + 1 < it_hi) gv_load<NM, NA>(f[1], src, N, arow, asc, K, it + 1, q);
+    gv_mma<NM, NA>(f[0], acc);
+    if (it + 1 >= it_hi) break;
+    if (it + 2 < it_hi) gv_load<NM, NA>(f[0], src, N, arow, asc, K, it + 2, q);
+    gv_mma<NM, NA>(f[1], acc);
+  }
 }
 
 // ------------------------------------------------------------------------------------
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
 // (h8 = [3][rows][I] bytes, hs = [rows][I/32] e8m0).
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(
+__global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
     const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, int T, int k, int H, int I, int R) {
   __shared__ f32x4 red[kSplit][kTiles][2][64];
   if ((int)blockIdx.y >= info[0]) return;
-  const int g = act[blockIdx.y];
-  const int rows = grp_rows[g], row0 = grp_row0[g];
+  const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
+  const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * kTiles);
   const int KB = H >> 5;
-  const int kb_lo = wave * KB / kSplit, kb_hi = (wave + 1) * KB / kSplit;
-  const size_t gbase = (size_t)g * KB * I;
-  size_t col[kTiles];
-#pragma unroll
-  for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, I - 1);
+  const int NI = (KB + 3) >> 2;  // K iterations of 4 blocks
+  const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
+  const uint8_t* codes[2] = {gc, uc};
+  const uint8_t* scales[2] = {gs, us};
+  GSrc<2> src;
+  gsrc_init<2>(src, codes, scales, g, KB, I, n0, m, q);
   const uint8_t* x_hi = xq;
   const uint8_t* x_lo = xq + (size_t)T * H;
   const uint8_t* x_sc = xq + (size_t)2 * T * H;
@@ -72,41 +158,15 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
-    const bool mok = m < nt;
-    const int tok = mok ? row_token(perm, row0 + c0 + m, tk, k) : 0;
-    f32x4 ag[kTiles], au[kTiles];
+    // lanes past the pass's tokens repeat its first token (their results are dropped)
+    const int tok = row_token(perm, row0 + c0 + (m < nt ? m : 0), tk, k);
+    const uint8_t* arow[2] = {x_hi + (size_t)tok * H, x_lo + (size_t)tok * H};
+    f32x4 acc[2][kTiles];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = kb_lo; kb < kb_hi; kb += 4) {
-      const int blk = kb + q;
-      const bool bok = blk < kb_hi;
-      uint4 cg[kTiles], cu[kTiles];
-      int sg[kTiles], su[kTiles];
-#pragma unroll
-      for (int j = 0; j < kTiles; ++j) {
-        cg[j] = cu[j] = make_uint4(0, 0, 0, 0);
-        sg[j] = su[j] = 127;
-        if (bok) {
-          const size_t c = col[j] + (size_t)blk * I;
-          cg[j] = ld16(gc + c * 16);
-          cu[j] = ld16(uc + c * 16);
-          sg[j] = gs[c];
-          su[j] = us[c];
-        }
-      }
-      const bool ok1 = mok && kb + (q >> 1) < kb_hi, ok2 = mok && kb + 2 + (q >> 1) < kb_hi;
-      const i32x8 a0 = load_act(x_hi + (size_t)tok * H, kb, q, ok1, ok2);
-      const i32x8 a1 = load_act(x_lo + (size_t)tok * H, kb, q, ok1, ok2);
-      const int sx = (bok && mok) ? x_sc[(size_t)tok * KB + blk] : 127;
-#pragma unroll
-      for (int j = 0; j < kTiles; ++j) {
-        const i32x8 bg = fp4_operand(cg[j]), bu = fp4_operand(cu[j]);
-        ag[j] = mma_f8f4(a0, bg, ag[j], sx, sg[j]);
-        au[j] = mma_f8f4(a0, bu, au[j], sx, su[j]);
-        ag[j] = mma_f8f4(a1, bg, ag[j], sx - 4, sg[j]);
-        au[j] = mma_f8f4(a1, bu, au[j], sx - 4, su[j]);
-      }
-    }
+    for (int j = 0; j < kTiles; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gv_pass<2, 2>(acc, src, I, arow, x_sc + (size_t)tok * KB, H, it_lo, it_hi, q);
+    f32x4 (&ag)[kTiles] = acc[0];
+    f32x4 (&au)[kTiles] = acc[1];
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) {
       red[wave][j][0][lane] = ag[j];
@@ -165,64 +225,36 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 // ------------------------------------------------------------------------------------
 // down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gemv_down_kernel(
+__global__ __launch_bounds__(256, 2) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
     float* __restrict__ staging, int T, int k, int H, int I, int R) {
   __shared__ f32x4 red[kSplit][kTiles][64];
   if ((int)blockIdx.y >= info[0]) return;
-  const int g = act[blockIdx.y];
-  const int rows = grp_rows[g], row0 = grp_row0[g];
+  const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
+  const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * kTiles);
   const int KB = I >> 5;
-  const int kb_lo = wave * KB / kSplit, kb_hi = (wave + 1) * KB / kSplit;
-  const size_t gbase = (size_t)g * KB * H;
-  size_t col[kTiles];
-#pragma unroll
-  for (int j = 0; j < kTiles; ++j) col[j] = gbase + min(n0 + 16 * j + m, H - 1);
+  const int NI = (KB + 3) >> 2;
+  const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
+  const uint8_t* codes[1] = {dc};
+  const uint8_t* scales[1] = {ds};
+  GSrc<1> src;
+  gsrc_init<1>(src, codes, scales, g, KB, H, n0, m, q);
   const uint8_t* hs = h8 + (size_t)3 * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
-    const bool mok = m < nt;
-    const size_t r = (size_t)(row0 + c0 + (mok ? m : 0));
-    const uint8_t* t0row = h8 + r * I;
-    const uint8_t* t1row = t0row + (size_t)R * I;
-    const uint8_t* t2row = t1row + (size_t)R * I;
-    f32x4 acc[kTiles];
+    const size_t r = (size_t)(row0 + c0 + (m < nt ? m : 0));
+    const uint8_t* arow[3] = {h8 + r * I, h8 + (size_t)R * I + r * I, h8 + (size_t)2 * R * I + r * I};
+    f32x4 acc2[1][kTiles];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = kb_lo; kb < kb_hi; kb += 4) {
-      const int blk = kb + q;
-      const bool bok = blk < kb_hi;
-      uint4 cd[kTiles];
-      int sd[kTiles];
-#pragma unroll
-      for (int j = 0; j < kTiles; ++j) {
-        cd[j] = make_uint4(0, 0, 0, 0);
-        sd[j] = 127;
-        if (bok) {
-          const size_t c = col[j] + (size_t)blk * H;
-          cd[j] = ld16(dc + c * 16);
-          sd[j] = ds[c];
-        }
-      }
-      const bool ok1 = mok && kb + (q >> 1) < kb_hi, ok2 = mok && kb + 2 + (q >> 1) < kb_hi;
-      const i32x8 a0 = load_act(t0row, kb, q, ok1, ok2);
-      const i32x8 a1 = load_act(t1row, kb, q, ok1, ok2);
-      const i32x8 a2 = load_act(t2row, kb, q, ok1, ok2);
-      const int sh = (bok && mok) ? hs[r * KB + blk] : 127;
-#pragma unroll
-      for (int j = 0; j < kTiles; ++j) {
-        const i32x8 b = fp4_operand(cd[j]);
-        acc[j] = mma_f8f4(a0, b, acc[j], sh, sd[j]);
-        acc[j] = mma_f8f4(a1, b, acc[j], sh - 4, sd[j]);
-        acc[j] = mma_f8f4(a2, b, acc[j], sh - 8, sd[j]);
-      }
-    }
+    for (int j = 0; j < kTiles; ++j) acc2[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gv_pass<1, 3>(acc2, src, H, arow, hs + r * KB, I, it_lo, it_hi, q);
+    f32x4 (&acc)[kTiles] = acc2[0];
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) red[wave][j][lane] = acc[j];
     __syncthreads();
