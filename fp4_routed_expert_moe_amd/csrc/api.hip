@@ -337,13 +337,16 @@ int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t*
                 groups, rows, cols);
   if (!aligned16(codes_in) || !aligned16(codes_out))
     return fail(MOE_ERR_INVALID, "moe_pack_fp4: code arrays must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(scales_out) & 3u)
+    return fail(MOE_ERR_INVALID, "moe_pack_fp4: scales_out must be 4-byte aligned");
   const size_t cb = (size_t)groups * rows * (cols / 2), sb = (size_t)groups * rows * (cols / 32);
+  const size_t sb_out = (size_t)groups * moe::scale_slab_bytes(rows, cols);
   auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
     const char* pa = static_cast<const char*>(a);
     const char* pb = static_cast<const char*>(b);
     return pa < pb + nb && pb < pa + na;
   };
-  if (overlap(codes_in, cb, codes_out, cb) || overlap(scales_in, sb, scales_out, sb))
+  if (overlap(codes_in, cb, codes_out, cb) || overlap(scales_in, sb, scales_out, sb_out))
     return fail(MOE_ERR_INVALID, "moe_pack_fp4: output overlaps input");
   const hipError_t e = moe::launch_pack(codes_in, scales_in, codes_out, scales_out, groups, rows, cols,
                                         static_cast<hipStream_t>(stream));

@@ -165,9 +165,22 @@ __device__ __forceinline__ i32x8 fp8_operand(const uint4& lo, const uint4& hi) {
 __device__ __forceinline__ f32x4 mma_f8f4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
 }
+// The same with B's scale taken from byte SELB of the register sb.
+template <int SELB>
+__device__ __forceinline__ f32x4 mma_f8f4_sb(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, SELB, sb);
+}
 
 __device__ __forceinline__ int row_token(const int32_t* perm, int r, int tk, int k) {
   return r < tk ? perm[r] / k : r - tk;
+}
+
+// Bytes of one matrix's scales in the kernel layout: [ceil(K/128)][ceil(N/64)][16][4][4].
+// Byte (i, t, m, q, j) is the scale of row 64t + 16j + m, K block 4i + q (0 past the matrix),
+// so lane (m, q) of a wave finds the scales of its four 16-row column tiles of one 128-value
+// K step in one dword, and the 64 lanes' dwords are 256 contiguous bytes.
+__host__ __device__ inline size_t scale_slab_bytes(int N, int K) {
+  return (size_t)((K / 32 + 3) / 4) * (size_t)((N + 63) / 64) * 256;
 }
 
 struct Dims {

@@ -125,33 +125,47 @@ __device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int 
 }
 
 // Weight operands of one wave for one K step: PU chunks x NM matrices x CT column tiles.
-// Lane (n, q) reads K block 4u + q of its column: one 16-byte chunk and its scale byte.  The
-// loads go through buffer descriptors spanning one group's matrix, so the per-lane offset is
-// fixed, the K position is a scalar offset, and reads past the matrix (the K tail) return 0:
-// zero codes with scale byte 0.
+// Lane (n, q) reads K block 4u + q of its column: one 16-byte chunk and its scale byte (from
+// the kernel scale layout, where a lane's four 16-row tiles share a dword).  The loads go
+// through buffer descriptors spanning one group's matrix, so the per-lane offset is fixed and
+// the K position is a scalar offset.
 template <class SH, int NM>
 struct BFrag {
   i32x4 c[SH::PU][NM][SH::CT];
   int s[SH::PU][NM][SH::CT];
 };
-template <int NM>
+template <class SH, int NM>
 struct BSrc {
   __amdgpu_buffer_rsrc_t c[NM], s[NM];
-  int voff_c, voff_s;  // column tile 0, K block q, step 0
+  int voff_c;          // column tile 0, K block q, step 0
+  int voff_s[SH::CT];  // scale byte of column tile c, K block q, step 0
+  int nt64;            // 64-row tiles of the matrix
 };
 constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
+// Steps past the last one (the prefetch runs ahead unconditionally) and lanes whose block is
+// past K move their per-lane offsets past the descriptor's range: they read zeros and touch
+// no memory.  (The scalar offset is not relied on for the range check.)
+constexpr int kOutOfRange = 1 << 30;
 template <class SH, int NM>
-__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<NM>& bs, int N, int step) {
+__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<SH, NM>& bs, int N, int KB, int step, int q) {
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
-    const int kb = step * SH::PKB + 4 * u;  // uniform; kept in scalar registers
-    const int so_s = __builtin_amdgcn_readfirstlane(kb * N), so_c = so_s * 16;
+    const int chunk = step * SH::PU + u;  // 128-value K chunk (uniform; kept in scalar registers)
+    const int kb = 4 * chunk;
+    const int so_c = __builtin_amdgcn_readfirstlane(kb * N * 16);
+    const int so_s = __builtin_amdgcn_readfirstlane(chunk * bs.nt64 * 256);
+    int bias_c = 0, bias_s = 0;
+    if (kb + 4 > KB) {  // uniform
+      bias_c = kb + q >= KB ? kOutOfRange : 0;
+      bias_s = kb >= KB ? kOutOfRange : 0;
+    }
 #pragma unroll
     for (int mtx = 0; mtx < NM; ++mtx)
 #pragma unroll
       for (int c = 0; c < SH::CT; ++c) {
-        f.c[u][mtx][c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + 256 * c, so_c, 0));
-        f.s[u][mtx][c] = __builtin_amdgcn_raw_buffer_load_b8(bs.s[mtx], bs.voff_s + 16 * c, so_s, 0);
+        f.c[u][mtx][c] =
+            __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + bias_c + 256 * c, so_c, 0));
+        f.s[u][mtx][c] = __builtin_amdgcn_raw_buffer_load_b8(bs.s[mtx], bs.voff_s[c] + bias_s, so_s, 0);
       }
   }
 }
@@ -226,16 +240,22 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   const int n0 = nt * SH::PN + wave * 16 * SH::CT;
   const uint8_t* codes[2] = {c0p, c1p};
   const uint8_t* scales[2] = {s0p, s1p};
-  BSrc<NM> bs;
+  BSrc<SH, NM> bs;
+  const int slab = (int)scale_slab_bytes(N, a.K);
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
     bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
                                                   KB * N * 16, kBufferFlags);
-    bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * KB * N), (short)0, KB * N,
+    bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
                                                   kBufferFlags);
   }
-  bs.voff_s = q * N + n0 + m;
-  bs.voff_c = bs.voff_s * 16;
+  bs.voff_c = (q * N + n0 + m) * 16;
+  bs.nt64 = (N + 63) >> 6;
+#pragma unroll
+  for (int c = 0; c < SH::CT; ++c) {
+    const int col0 = n0 + 16 * c;  // this column tile's 64-row tile and 16-row slot in it
+    bs.voff_s[c] = (((col0 >> 6) * 16 + m) * 4 + q) * 4 + ((col0 >> 4) & 3);
+  }
   const int nsub = (nrows + 15) >> 4;
 
   f32x4 acc[NM][4][SH::CT];
@@ -251,19 +271,19 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   // step earlier) go from registers into the other LDS buffer.
   AStage<SH> ast[2];
   BFrag<SH, NM> fb[3];
+  // The loads run ahead unconditionally: past the last step the activation rows repeat the
+  // last step (cache hits) and the weights read zeros without memory traffic, so no wait
+  // in the loop has to assume a missing load.
+  const int last = nsteps - 1;
   a_store<SH>(tile[0], a_fetch<SH>(ap, a.K, 0, lp), lr, lp);
-  b_fetch<SH, NM>(fb[0], bs, N, 0);
-  if (nsteps > 1) {
-    ast[1] = a_fetch<SH>(ap, a.K, 1, lp);
-    b_fetch<SH, NM>(fb[1], bs, N, 1);
-  }
+  b_fetch<SH, NM>(fb[0], bs, N, KB, 0, q);
+  ast[1] = a_fetch<SH>(ap, a.K, min(1, last), lp);
+  b_fetch<SH, NM>(fb[1], bs, N, KB, 1, q);
   __syncthreads();
   auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BFrag<SH, NM>& fc,
                   BFrag<SH, NM>& f_far) -> bool {
-    if (s + 2 < nsteps) {
-      a_far = a_fetch<SH>(ap, a.K, s + 2, lp);
-      b_fetch<SH, NM>(f_far, bs, N, s + 2);
-    }
+    a_far = a_fetch<SH>(ap, a.K, min(s + 2, last), lp);
+    b_fetch<SH, NM>(f_far, bs, N, KB, s + 2, q);
     k_step<SH, NM>(tc, fc, acc, nsub, m, q);
     const bool more = s + 1 < nsteps;
     if (more) a_store<SH>(tn, a_next, lr, lp);

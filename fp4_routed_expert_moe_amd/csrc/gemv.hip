@@ -10,7 +10,8 @@
 //
 // * B (weights, FP4): lane (n, q) holds block kb+q of row n -- one 16-byte chunk of the
 //   block-interleaved kernel layout (a wave reads 4 x 256 contiguous bytes per column tile)
-//   -- and that block's scale byte, through buffer loads.
+//   -- through buffer loads; one dword per lane holds the scales of its four column tiles
+//   (a wave's scales for a K step are 256 contiguous bytes), picked by the MFMA's byte select.
 // * A (activations, FP8 e4m3): lane (m, q) holds 16 values at K offset 16q and 16 at 64+16q
 //   of the 128-value step for token m, plus the scale of block kb+q.  Activations arrive as
 //   exact FP8 term splits (x: 2 terms = all 8 bf16 bits; h: 3 terms = 12 bits), one MFMA
@@ -38,52 +39,58 @@ constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (ev
 constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
 
 // One K iteration (4 blocks = 128 values) of a wave's operands.  Weights come through buffer
-// descriptors spanning one group's matrix: a fixed per-lane offset, the K position as a
-// scalar offset, and reads past the matrix return zero codes with scale 0, so the last
-// iteration of K needs no masking on that side.  Activations come from the token rows of
+// descriptors spanning one group's matrix: a fixed per-lane offset and the K position as a
+// scalar offset; in the last iteration of a K that is not a multiple of 128 the lanes past K
+// read zero codes (their packed scales are 0 too).  Activations come from the token rows of
 // the pass; past the end of K they read a valid part of the row (multiplied by zero weights).
 constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
+constexpr int kOutOfRange = 1 << 30;      // added to a lane's buffer offset: reads zeros
 
 template <int NM, int NA>
 struct GFrag {
   i32x4 c[NM][kTiles];
-  int s[NM][kTiles];
+  int s[NM];  // byte j: scale of column tile j
   i32x4 a[NA][2];
   int sa;
 };
 template <int NM>
 struct GSrc {
   __amdgpu_buffer_rsrc_t c[NM], s[NM];
-  int voff_c[kTiles], voff_s[kTiles];  // column tile j, K block q, K iteration 0
+  int voff_c, voff_s;  // column tile 0, K block q, K iteration 0 (tile j is 16 columns on)
 };
 template <int NM>
 __device__ __forceinline__ void gsrc_init(GSrc<NM>& src, const uint8_t* const* codes, const uint8_t* const* scales,
                                           int g, int KB, int N, int n0, int m, int q) {
+  const int slab = (int)scale_slab_bytes(N, 32 * KB);
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
     src.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
                                                    KB * N * 16, kBufferFlags);
-    src.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * KB * N), (short)0, KB * N,
+    src.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
                                                    kBufferFlags);
   }
-#pragma unroll
-  for (int j = 0; j < kTiles; ++j) {
-    src.voff_s[j] = q * N + min(n0 + 16 * j + m, N - 1);
-    src.voff_c[j] = src.voff_s[j] * 16;
-  }
+  // columns past N read other bytes of the group (or zeros past its end); they are not stored
+  src.voff_c = (q * N + n0 + m) * 16;
+  src.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;  // n0 is a multiple of 64
 }
 template <int NM, int NA>
 __device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, int N, const uint8_t* const* arow,
                                         const uint8_t* asc, int K, int it, int q) {
   const int kb = 4 * it;
-  const int so_s = __builtin_amdgcn_readfirstlane(kb * N), so_c = so_s * 16;
+  const int so_c = __builtin_amdgcn_readfirstlane(kb * N * 16);
+  const int so_s = __builtin_amdgcn_readfirstlane(it * ((N + 63) >> 6) * 256);
+  // Lanes whose block is past K (last iteration only) move their per-lane offset past the
+  // descriptor's range: they read zeros and touch no memory.  (The scalar offset is not
+  // relied on for the range check.)
+  int voff_c = src.voff_c;
+  if (kb + 4 > (K >> 5)) voff_c += (kb + q >= (K >> 5)) ? kOutOfRange : 0;
 #pragma unroll
-  for (int mtx = 0; mtx < NM; ++mtx)
+  for (int mtx = 0; mtx < NM; ++mtx) {
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) {
-      f.c[mtx][j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], src.voff_c[j], so_c, 0));
-      f.s[mtx][j] = __builtin_amdgcn_raw_buffer_load_b8(src.s[mtx], src.voff_s[j], so_s, 0);
-    }
+    for (int j = 0; j < kTiles; ++j)
+      f.c[mtx][j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], voff_c + 256 * j, so_c, 0));
+    f.s[mtx] = __builtin_amdgcn_raw_buffer_load_b32(src.s[mtx], src.voff_s, so_s, 0);
+  }
   int o1 = kb * 32 + 16 * q, o2 = o1 + 64;
   if ((kb + 4) * 32 > K) {  // last iteration of a K that is not a multiple of 128 (uniform)
     o1 = min(o1, K - 16);
@@ -102,14 +109,22 @@ __device__ __forceinline__ void gv_mma(const GFrag<NM, NA>& f, f32x4 (&acc)[NM][
   i32x8 a[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
+  static_assert(kTiles == 4, "one scale dword covers four 16-row column tiles");
 #pragma unroll
-  for (int j = 0; j < kTiles; ++j)
+  for (int mtx = 0; mtx < NM; ++mtx) {
+    i32x8 b[kTiles];
 #pragma unroll
-    for (int mtx = 0; mtx < NM; ++mtx) {
-      const i32x8 b = __builtin_shufflevector(f.c[mtx][j], f.c[mtx][j], 0, 1, 2, 3, -1, -1, -1, -1);
+    for (int j = 0; j < kTiles; ++j)
+      b[j] = __builtin_shufflevector(f.c[mtx][j], f.c[mtx][j], 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
-      for (int t = 0; t < NA; ++t) acc[mtx][j] = mma_f8f4(a[t], b, acc[mtx][j], f.sa - 4 * t, f.s[mtx][j]);
+    for (int t = 0; t < NA; ++t) {
+      const int sa = f.sa - 4 * t;
+      acc[mtx][0] = mma_f8f4_sb<0>(a[t], b[0], acc[mtx][0], sa, f.s[mtx]);
+      acc[mtx][1] = mma_f8f4_sb<1>(a[t], b[1], acc[mtx][1], sa, f.s[mtx]);
+      acc[mtx][2] = mma_f8f4_sb<2>(a[t], b[2], acc[mtx][2], sa, f.s[mtx]);
+      acc[mtx][3] = mma_f8f4_sb<3>(a[t], b[3], acc[mtx][3], sa, f.s[mtx]);
     }
+  }
 }
 // This wave's K iterations [it_lo, it_hi), the loads of iteration i+1 in flight while
 // iteration i runs on the matrix cores.
@@ -117,13 +132,24 @@ template <int NM, int NA>
 __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>& src, int N,
                                         const uint8_t* const* arow, const uint8_t* asc, int K, int it_lo, int it_hi,
                                         int q) {
+  // Every path through the loop issues the next loads before the current MFMAs (the tail
+  // iterations leave by their own exits), so the wait before the MFMAs only covers the
+  // older loads.
+  if (it_lo >= it_hi) return;
   GFrag<NM, NA> f[2];
-  if (it_lo < it_hi) gv_load<NM, NA>(f[0], src, N, arow, asc, K, it_lo, q);
-  for (int it = it_lo; it < it_hi; it += 2) {
-    if (it + 1 < it_hi) gv_load<NM, NA>(f[1], src, N, arow, asc, K, it + 1, q);
+  gv_load<NM, NA>(f[0], src, N, arow, asc, K, it_lo, q);
+  for (int it = it_lo;; it += 2) {
+    if (it + 1 >= it_hi) {
+      gv_mma<NM, NA>(f[0], acc);
+      break;
+    }
+    gv_load<NM, NA>(f[1], src, N, arow, asc, K, it + 1, q);
     gv_mma<NM, NA>(f[0], acc);
-    if (it + 1 >= it_hi) break;
-    if (it + 2 < it_hi) gv_load<NM, NA>(f[0], src, N, arow, asc, K, it + 2, q);
+    if (it + 2 >= it_hi) {
+      gv_mma<NM, NA>(f[1], acc);
+      break;
+    }
+    gv_load<NM, NA>(f[0], src, N, arow, asc, K, it + 2, q);
     gv_mma<NM, NA>(f[1], acc);
   }
 }
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
   if ((int)blockIdx.y >= info[0]) return;
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * kTiles);
   const int KB = H >> 5;
@@ -234,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
   if ((int)blockIdx.y >= info[0]) return;
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * kTiles);
   const int KB = I >> 5;

@@ -2,7 +2,8 @@
 // kernels stream.
 //
 // Checkpoint layout (row-major, per group g):   codes [N][K/2],       scales [N][K/32]
-// Kernel layout (block-interleaved, per group):  codes [K/32][N][16],  scales [K/32][N]
+// Kernel layout (block-interleaved, per group):  codes [K/32][N][16],
+//                                                scales [K/128][N/64][16][4][4] (see below)
 //
 // In the kernel layout the 16 code bytes of block kb of rows n, n+1, ... are adjacent, so a
 // wave whose lanes own consecutive rows reads 1 KiB contiguous per instruction, and the
@@ -38,24 +39,28 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint4* __restrict
   }
 }
 
-__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
-                                                          int N, int KB, int ntiles) {
-  __shared__ uint8_t tile[kPackTile][kPackTile + 4];
-  const int g = blockIdx.x / ntiles;
-  const int n0 = (blockIdx.x - g * ntiles) * kPackTile;
-  const int kb0 = blockIdx.y * kPackTile;
-  const size_t gin = (size_t)g * N * KB;
-  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
-    const int r = i / kPackTile, c = i % kPackTile;
-    const int n = n0 + r, kb = kb0 + c;
-    if (n < N && kb < KB) tile[r][c] = in[gin + (size_t)n * KB + kb];
+// Scales into the kernel layout [KI][NT][16 m][4 q][4 j] (KI = ceil(K/128), NT = ceil(N/64)):
+// byte (i, t, m, q, j) is the scale of row 64t + 16j + m, block 4i + q, or 0 past the matrix.
+// One thread per output dword (the four j of one (i, t, m, q)).
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ in, uint32_t* __restrict__ out,
+                                                          int N, int KB, int groups) {
+  const int KI = (KB + 3) / 4, NT = (N + 63) / 64;
+  const size_t per_group = (size_t)KI * NT * 64;  // dwords
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= per_group * groups) return;
+  const int g = (int)(id / per_group);
+  size_t r = id - (size_t)g * per_group;
+  const int q = (int)(r & 3), m = (int)((r >> 2) & 15);
+  r >>= 6;
+  const int t = (int)(r % NT), i = (int)(r / NT);
+  const int kb = 4 * i + q;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 64 * t + 16 * j + m;
+    if (n < N && kb < KB) v |= (uint32_t)in[((size_t)g * N + n) * KB + kb] << (8 * j);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
-    const int c = i / kPackTile, r = i % kPackTile;
-    const int n = n0 + r, kb = kb0 + c;
-    if (n < N && kb < KB) out[gin + (size_t)kb * N + n] = tile[r][c];
-  }
+  out[id] = v;
 }
 
 hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
@@ -70,7 +75,9 @@ hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   tk = timing_begin("pack_scales", s);
-  pack_scales_kernel<<<grid, 256, 0, s>>>(scales_in, scales_out, N, KB, ntiles);
+  const size_t dwords = scale_slab_bytes(N, K) / 4 * groups;
+  pack_scales_kernel<<<(unsigned)((dwords + 255) / 256), 256, 0, s>>>(scales_in, reinterpret_cast<uint32_t*>(scales_out),
+                                                                      N, KB, groups);
   timing_end(tk, s);
   return hipGetLastError();
 }

@@ -33,9 +33,14 @@ def device_supported(device: int = 0):
     return bool(ok), buf.value.decode()
 
 
+def kernel_scale_shape(groups: int, n: int, k: int):
+    """Shape of the kernel-layout scales: [G][ceil(K/128)][ceil(N/64)][16][4][4]."""
+    return (groups, (k // 32 + 3) // 4, (n + 63) // 64, 16, 4, 4)
+
+
 def pack_fp4(codes: torch.Tensor, scales: torch.Tensor, stream=None):
     """Checkpoint layout (codes [G][N][K/2], scales [G][N][K/32]) -> kernel layout
-    (codes [G][K/32][N][16], scales [G][K/32][N]), by the library's pack kernel."""
+    (codes [G][K/32][N][16], scales as ``kernel_scale_shape``), by the library's pack kernel."""
     lib = _lib.load()
     g, n, half_k = codes.shape
     k = 2 * half_k
@@ -44,7 +49,7 @@ def pack_fp4(codes: torch.Tensor, scales: torch.Tensor, stream=None):
     if not (codes.is_cuda and scales.is_cuda and codes.is_contiguous() and scales.is_contiguous()):
         raise ValueError("pack_fp4 wants contiguous CUDA tensors")
     out_c = torch.empty((g, k // 32, n, 16), dtype=torch.uint8, device=codes.device)
-    out_s = torch.empty((g, k // 32, n), dtype=torch.uint8, device=codes.device)
+    out_s = torch.empty(kernel_scale_shape(g, n, k), dtype=torch.uint8, device=codes.device)
     _lib.check(lib.moe_pack_fp4(_ptr(codes), _ptr(scales), _ptr(out_c), _ptr(out_s), g, n, k,
                                 _stream_handle(stream)), lib)
     return out_c, out_s
@@ -54,7 +59,7 @@ class MoeLayer:
     """One routed FP4-expert MoE layer over borrowed device weights.
 
     ``gate``/``up``/``down`` are (codes, scales) uint8 CUDA tensors in the kernel
-    layout: codes [E+S][K/32][N][16], scales [E+S][K/32][N] (see ``pack_fp4``);
+    layout: codes [E+S][K/32][N][16], scales ``kernel_scale_shape`` (see ``pack_fp4``);
     the library keeps only their pointers, so this object holds references to
     keep them alive.
     """
@@ -67,7 +72,7 @@ class MoeLayer:
         if g != e + n_shared or hb * 32 != h or sixteen != 16:
             raise ValueError(f"gate codes {tuple(gate[0].shape)} do not match E={e}, S={n_shared}, H={h}")
         for name, (c, s), n, k in (("gate", gate, inter, h), ("up", up, inter, h), ("down", down, h, inter)):
-            if tuple(c.shape) != (g, k // 32, n, 16) or tuple(s.shape) != (g, k // 32, n):
+            if tuple(c.shape) != (g, k // 32, n, 16) or tuple(s.shape) != kernel_scale_shape(g, n, k):
                 raise ValueError(f"{name} weights: codes {tuple(c.shape)} / scales {tuple(s.shape)}, "
                                  f"expected {(g, k // 32, n, 16)} / {(g, k // 32, n)} (kernel layout)")
             if c.dtype != torch.uint8 or s.dtype != torch.uint8 or not c.is_cuda or not s.is_cuda:

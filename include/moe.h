@@ -30,9 +30,13 @@
  * (s = 0 is +0, s = 255 is +inf), as "DeepSeek V4: the CUDA kernels, as a tier rather than an
  * engine" (PR #772) describes for the MXFP4 decode.
  *   checkpoint layout (row-major):   codes uint8 [E+S][N][K/2],       scales uint8 [E+S][N][K/32]
- *   kernel layout (block-interleaved): codes uint8 [E+S][K/32][N][16], scales uint8 [E+S][K/32][N]
+ *   kernel layout (block-interleaved): codes uint8 [E+S][K/32][N][16],
+ *                                      scales uint8 [E+S][ceil(K/128)][ceil(N/64)][16][4][4]
  * In the kernel layout the 16 code bytes of block kb of consecutive rows are adjacent, which
  * is what the decode kernels stream (one lane per row, one contiguous KiB per wave load).
+ * Scale byte (i, t, m, q, j) of a group is the scale of row 64t + 16j + m, block 4i + q
+ * (0 where that row or block is past the matrix): the four scales one lane needs for a
+ * 128-value K step of a 64-row tile share a dword.
  * moe_pack_fp4 converts the first into the second once, at load time; the layer reads the
  * kernel layout only.
  *
@@ -142,7 +146,8 @@ int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, f
                     void* stream);
 
 /* Repack `groups` FP4 matrices of `rows` x `cols` (cols = reduction axis, multiple of 32)
- * from the checkpoint layout into the kernel layout (device pointers; codes 16-byte aligned;
+ * from the checkpoint layout into the kernel layout (device pointers; codes 16-byte aligned,
+ * scales_out 4-byte aligned and groups * ceil(cols/128) * ceil(rows/64) * 256 bytes long;
  * outputs must not overlap inputs).  Asynchronous on `stream` (a hipStream_t, NULL = default
  * stream) of the current device.  "Add DeepSeek V4 Flash CPU inference with NVMe expert
  * streaming" (PR #165) likewise repacks each expert once into its kernels' interleaved layout. */

@@ -67,6 +67,18 @@ def run_layer(layer, x_bits, workspace=None):
     return out
 
 
+def kernel_layout_scales(scales):
+    """The kernel scale layout written out: [G][K/128][N/64][16 m][4 q][4 j] holds the scale of
+    row 64t + 16j + m, block 4i + q, zero-padded past the matrix."""
+    g, n, kb = scales.shape
+    ki, nt = -(-kb // 4), -(-n // 64)
+    padded = np.zeros((g, nt * 64, ki * 4), dtype=np.uint8)
+    padded[:, :n, :kb] = scales
+    # row 64t + 16j + m -> (t, j, m); block 4i + q -> (i, q)
+    six = padded.reshape(g, nt, 4, 16, ki, 4)           # [g][t][j][m][i][q]
+    return six.transpose(0, 4, 1, 3, 5, 2)              # [g][i][t][m][q][j]
+
+
 def weight_tolerance(x_bits, w_router, bias, idx):
     """Per-token bound on |w_gpu - w_ref| from the arithmetic (not fitted to results).
 

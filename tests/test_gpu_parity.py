@@ -10,8 +10,8 @@ import torch
 import moe_synth as synth
 import oracle
 from helpers import random_experts, screened_tokens, identity_experts
-from gpu_util import (check_device_weights, check_outputs, check_routing, make_layer, oracle_routing,
-                      pack_weights, require_gpu, run_layer, say, stack_groups, x_to_device)
+from gpu_util import (check_device_weights, check_outputs, check_routing, kernel_layout_scales, make_layer,
+                      oracle_routing, pack_weights, require_gpu, run_layer, say, stack_groups, x_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,8 @@ def test_pack_is_the_block_transpose(shape):
     pc, ps = pack_fp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
     torch.cuda.synchronize()
     want_c = codes.reshape(g, n, k // 32, 16).transpose(0, 2, 1, 3)
-    want_s = scales.transpose(0, 2, 1)
     np.testing.assert_array_equal(pc.cpu().numpy(), want_c)
-    np.testing.assert_array_equal(ps.cpu().numpy(), want_s)
+    np.testing.assert_array_equal(ps.cpu().numpy(), kernel_layout_scales(scales))
 
 
 # ------------------------------------------------------------------------------- tiny

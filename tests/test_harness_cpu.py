@@ -4,7 +4,7 @@ import numpy as np
 import moe_synth as synth
 import oracle
 from oracle.moe import bf16_bits_to_f64
-from gpu_util import U32, weight_tolerance
+from gpu_util import U32, kernel_layout_scales, weight_tolerance
 
 
 def test_weight_tolerance_follows_the_summation_bound():
@@ -22,3 +22,11 @@ def test_weight_tolerance_follows_the_summation_bound():
     n = 2 * (3 * wl.hidden // 32) + 64 + 1
     want = 2 * n * U32 * np.take_along_axis(s, idx.astype(np.int64), axis=1).max(axis=1) + 1e-6
     np.testing.assert_allclose(tol, want, rtol=1e-12)
+
+
+def test_kernel_scale_layout_by_hand():
+    """One entry spelled out: row 64*1 + 16*2 + 5 = 101, block 4*1 + 3 = 7."""
+    s = np.zeros((1, 130, 12), dtype=np.uint8)
+    s[0, 101, 7] = 9
+    lay = kernel_layout_scales(s)
+    assert lay.shape == (1, 3, 3, 16, 4, 4) and lay.sum() == 9 and lay[0, 1, 1, 5, 3, 2] == 9
