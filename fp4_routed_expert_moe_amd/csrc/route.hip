@@ -185,15 +185,22 @@ __device__ __forceinline__ void topk_block_any(const float* scores, int T, int E
 // offsets, group rows/first rows, the active-group list (shared expert last), the M-tile
 // list, and each expert's first grouped row to offs[] (LDS; may be the same array as cnt).
 // ------------------------------------------------------------------------------------
+// Exclusive prefix sum over the wave on DPP: row_shr 1, 2, 4, 8 scans each 16-lane row, then
+// row_bcast 15 and 31 carry the row totals into the rows above (checked lane by lane on the
+// device against a serial sum).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, false);
+}
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  const int lane = threadIdx.x & 63;
   int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  *total = __shfl(x, 63, 64);
+  x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  *total = __builtin_amdgcn_readlane(x, 63);
   return x - v;
 }
 
@@ -310,9 +317,11 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
   const int nt = min(kRouterTT, T - t0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (quantize) {
+    // the token tile's nt*KB blocks, an equal slice per expert workgroup (a few per workgroup)
     const int KB = H >> 5;
+    const int nb = nt * KB, per = (nb + E - 1) / E;
     uint8_t* xq = b.xq;
-    for (int j = e * NT + tid; j < nt * KB; j += E * NT) {
+    for (int j = e * per + tid; j < min(nb, (e + 1) * per); j += NT) {
       const int t = t0 + j / KB, bb = j % KB;
       quantize_x_block(x + (size_t)t * H + bb * 32, xq + (size_t)t * H + bb * 32,
                        xq + (size_t)(T + t) * H + bb * 32, xq + (size_t)2 * T * H + (size_t)t * KB + bb);
