@@ -8,22 +8,45 @@ top-6, 1 shared expert, I=2048, 8 tokens).  Steps rotate over 16 independent lay
 weights (55 GB resident) and 64 token batches, so no layer's weights are still in the
 256 MB last-level cache when it runs again.
 
-Prints one JSON line (rank 0).  Also reports the dominant kernel against its roofline
-(HIP-event timing of every launch inside the library, on the launching stream) and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line.  Besides tokens/s it reports:
+* ``roofline``: the dominant kernel against its roof.  ``achieved`` = algorithmic bytes
+  (or flops) per launch / the kernel's mean duration, timed with HIP events recorded on
+  the stream the library launches it on.  ``traffic`` = HBM bytes per launch from the
+  committed hardware-counter summary of the same kernel and workload (profiles/), or
+  null when the kernel's sources changed since those counters were taken.
+* ``cpu_baseline``: the float64 CPU oracle on a bounded sample of the same workload.
+
+``--pmc-summary FETCH_DIR WRITE_DIR`` instead digests two rocprofv3 ``--pmc`` runs of
+this script (FETCH_SIZE, then WRITE_SIZE, both with ``--copy-probe-mib``) into the
+markdown summary that ``traffic`` is read from.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "fp4_routed_expert_moe_amd", "csrc")
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+# Sources each timed kernel is compiled from: a change to any of them voids its counters.
+KERNEL_SOURCES = {
+    "gemv_gateup": ("gemv.hip", "common.h"),
+    "gemv_down": ("gemv.hip", "common.h"),
+    "gemm_gateup": ("gemm.hip", "common.h"),
+    "gemm_down": ("gemm.hip", "common.h"),
+    "decode_layer": ("decode.hip", "gemv.hip", "route.hip", "common.h"),
+}
 
 
 def parse():
@@ -35,10 +58,15 @@ def parse():
     p.add_argument("--layers", type=int, default=16, help="independent weight sets rotated per step")
     p.add_argument("--batches", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = one batch (capped at 8 tokens)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="the CPU oracle runs batches of the workload until this much time is spent")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB before the steps (a known-size "
                         "reference for hardware byte counters)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs of this script instead of benchmarking")
+    p.add_argument("--pmc-log", help="the stdout of the FETCH_SIZE run (its JSON line)")
+    p.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     return p.parse_args()
 
 
@@ -48,8 +76,35 @@ def expert_bytes(wl):
     return 3 * per_matrix, 2 * per_matrix, per_matrix  # whole expert, gate+up, down
 
 
+def sources_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, ()):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel, workload):
+    """HBM bytes per launch of `kernel` at `workload` from the committed counter summary, or
+    None if there is none or the kernel's sources changed since it was taken."""
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*hbm_traffic*.md"))):
+        with open(path) as f:
+            m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") != workload:
+            continue
+        k = rec.get("kernels", {}).get(kernel)
+        if k and k.get("sources") == sources_digest(kernel):
+            return k["traffic_bytes_per_launch"]
+    return None
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        return pmc_summary(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path)", file=sys.stderr)
@@ -123,23 +178,28 @@ def main():
 
     e_all, e_gu, e_dn = expert_bytes(wl)
     groups_per_step = [active[(s % nl, s % nb)] + wl.shared for s in range(args.steps)]
-    fp4_bytes_step = float(np.mean(groups_per_step)) * e_all
+    groups = float(np.mean(groups_per_step))
+    fp4_bytes_step = groups * e_all
     flops_step = 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
-    gemv = "gemv_gateup" in kt
-    dom = "gemv_gateup" if gemv else "gemm_gateup"
-    launches, total_ms = kt.get(dom, (0, 0.0))
-    avg_ms = total_ms / launches if launches else float("nan")
-    if gemv:
-        roof = dict(bound="hbm", achieved=float(np.mean(groups_per_step)) * e_gu / (avg_ms * 1e-3) / 1e9,
-                    peak=HBM_PEAK_GBPS, unit="GB/s")
+    # the dominant kernel and its algorithmic work per launch
+    if "decode_layer" in kt:
+        dom, work, bound = "decode_layer", groups * e_all, "hbm"
+    elif "gemv_gateup" in kt:
+        dom, work, bound = "gemv_gateup", groups * e_gu, "hbm"
     else:
-        fl = 2.0 * T * (wl.top_k + wl.shared) * 2 * wl.hidden * wl.inter
-        roof = dict(bound="mfma", achieved=fl / (avg_ms * 1e-3) / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+        dom, work, bound = "gemm_gateup", 2.0 * T * (wl.top_k + wl.shared) * 2 * wl.hidden * wl.inter, "mfma"
+    launches, total_ms = kt.get(dom, (0, 0.0))
+    avg_s = total_ms * 1e-3 / launches if launches else float("nan")
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=work / avg_s / 1e9, peak=HBM_PEAK_GBPS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=work / avg_s / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = traffic_record(dom, wl.name)
     roof["kernel"] = dom
-    roof["avg_launch_us"] = avg_ms * 1e3
-    roof["algorithmic_bytes_per_launch"] = float(np.mean(groups_per_step)) * e_gu if gemv else None
+    roof["avg_launch_us"] = avg_s * 1e6
+    roof["algorithmic_per_launch"] = work
+    roof["algorithmic_unit"] = "bytes" if bound == "hbm" else "flops"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -165,41 +225,129 @@ def main():
         "fp4_weight_GBps": fp4_bytes_step / (ms_per_step * 1e-3) / 1e9,
         "fp4_weight_frac_hbm": fp4_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "tflops": flops_step / (ms_per_step * 1e-3) / 1e12,
-        "active_groups_per_step": float(np.mean(groups_per_step)),
+        "tflops_frac_bf16": flops_step / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "active_groups_per_step": groups,
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    if args.copy_probe_mib:
+        out["copy_probe_mib"] = args.copy_probe_mib
     print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(wl, args, synth):
-    """The float64 CPU oracle on one batch of the same workload (time excludes weight generation)."""
+    """The float64 CPU oracle on whole batches of the same workload, one after another, until
+    ``--cpu-seconds`` of oracle time is spent (at least one batch, at most 16).  Weight
+    generation is outside the timed region."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
-    t = args.cpu_sample_tokens or min(wl.tokens, 8)
-    x = synth.tokens(wl, layer=0, step=0)[:t]
+    t_batch = min(wl.tokens, 8)
     wr = synth.router_weights(wl, 0)
     b = synth.router_bias(wl)
-    idx, _, _ = oracle.select_experts(oracle.router_logits(x, wr, b), wl.top_k)
-    needed = sorted(set(idx.reshape(-1).tolist()) | ({wl.experts} if wl.shared else set()))
-    lazy = synth.LazyExperts(wl, 0, cache=len(needed) + 1)
-    experts = {g: lazy[g] for g in needed}
+    total_t, total_s, batches = 0, 0.0, 0
+    while batches < 16 and (batches == 0 or total_s < args.cpu_seconds):
+        x = synth.tokens(wl, layer=0, step=batches)[:t_batch]
+        idx, _, _ = oracle.select_experts(oracle.router_logits(x, wr, b), wl.top_k)
+        needed = sorted(set(idx.reshape(-1).tolist()) | ({wl.experts} if wl.shared else set()))
+        lazy = synth.LazyExperts(wl, 0, cache=len(needed) + 1)
+        experts = {g: lazy[g] for g in needed}
 
-    class Pre:
-        def __getitem__(self, g):
-            return experts[g]
+        class Pre:
+            def __getitem__(self, g):
+                return experts[g]
 
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):          # the oracle as it stands: numpy, one thread
-        t0 = time.perf_counter()
-        oracle.moe_forward(x, wr, b, Pre(), wl.top_k, wl.shared)
-        dt = time.perf_counter() - t0
-    cores = 1
-    return {"value": t / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{t} tokens of {wl.name} layer 0 ({len(needed)} expert groups), {dt:.2f} s"}
+        with threadpool_limits(limits=1):          # the oracle as it stands: numpy, one thread
+            t0 = time.perf_counter()
+            oracle.moe_forward(x, wr, b, Pre(), wl.top_k, wl.shared)
+            total_s += time.perf_counter() - t0
+        total_t += t_batch
+        batches += 1
+    return {"value": total_t / total_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{batches} batch(es) of {t_batch} tokens of {wl.name} layer 0, "
+                      f"{total_s:.1f} s of oracle time (float64 numpy, one thread)"}
+
+
+# ---------------------------------------------------------------------------------------
+# Hardware-counter summary (FETCH_SIZE / WRITE_SIZE per dispatch, calibrated on a copy)
+# ---------------------------------------------------------------------------------------
+
+def _short_name(full):
+    m = re.match(r"(?:void )?moe::(\w+?)(?:_kernel)?\b", full)
+    return m.group(1) if m else None
+
+
+def _read_pmc(directory):
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def pmc_summary(args):
+    fetch = _read_pmc(args.pmc_summary[0])
+    write = _read_pmc(args.pmc_summary[1])
+    run = {}
+    if args.pmc_log:
+        with open(args.pmc_log) as f:
+            for line in f:
+                if line.startswith("{"):
+                    run = json.loads(line)
+    probe = (run.get("copy_probe_mib") or 512) << 20
+
+    def calib(rows):
+        # the copy probe is the largest plain device copy of the run
+        cp = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        return probe / (max(cp) * 1024.0)
+
+    ff, fw = calib(fetch), calib(write)
+
+    def per_kernel(rows):
+        acc = {}
+        for r in rows:
+            n = _short_name(r["Kernel_Name"])
+            if n:
+                acc.setdefault(n, []).append(float(r["Counter_Value"]))
+        return acc
+
+    kf, kw = per_kernel(fetch), per_kernel(write)
+    wl = run.get("config", {}).get("workload", "decode_t8")
+    roof = run.get("roofline", {})
+    kernels = {}
+    lines = []
+    for n in sorted(kf):
+        f_kib = sum(kf[n]) / len(kf[n])
+        w_kib = sum(kw.get(n, [0.0])) / max(len(kw.get(n, [])), 1)
+        tb = (f_kib * ff + w_kib * fw) * 1024.0
+        rec = {"dispatches": len(kf[n]), "fetch_kib": f_kib, "write_kib": w_kib, "traffic_bytes_per_launch": tb}
+        if n in KERNEL_SOURCES:
+            rec["sources"] = sources_digest(n)
+        if n == roof.get("kernel"):
+            rec["algorithmic_bytes_per_launch"] = roof.get("algorithmic_per_launch")
+        kernels[n] = rec
+        alg = rec.get("algorithmic_bytes_per_launch")
+        ratio = f"{tb / alg:.3f}" if alg else "-"
+        lines.append(f"| {n} | {len(kf[n])} | {f_kib:,.0f} | {w_kib:,.0f} | {tb / 1e6:,.1f} | {ratio} |")
+    rec = {"workload": wl, "fetch_factor": ff, "write_factor": fw, "kernels": kernels}
+    print(f"# HBM traffic per dispatch: {wl}\n")
+    print("Commands (repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n")
+    print("```\n" + (args.pmc_command or "(not recorded)") + "\n```\n")
+    print(f"Calibration: a {probe >> 20} MiB device copy (`__amd_rocclr_copyBuffer`) reads "
+          f"FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {fw:.3f} of its true byte counts; those factors scale "
+          "every kernel's counters below.\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB / launch | traffic / algorithmic |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(lines))
+    print("\n`sources` is a digest of the files the kernel is built from; `bench.py` reports `traffic` only "
+          "while it matches.\n")
+    print("```json\n" + json.dumps(rec, indent=None) + "\n```")
 
 
 if __name__ == "__main__":
