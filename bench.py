@@ -45,7 +45,6 @@ KERNEL_SOURCES = {
     "gemv_down": ("gemv.hip", "common.h"),
     "gemm_gateup": ("gemm.hip", "common.h"),
     "gemm_down": ("gemm.hip", "common.h"),
-    "decode_layer": ("decode.hip", "gemv.hip", "route.hip", "common.h"),
 }
 
 
@@ -182,9 +181,7 @@ def main():
     fp4_bytes_step = groups * e_all
     flops_step = 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
     # the dominant kernel and its algorithmic work per launch
-    if "decode_layer" in kt:
-        dom, work, bound = "decode_layer", groups * e_all, "hbm"
-    elif "gemv_gateup" in kt:
+    if "gemv_gateup" in kt:
         dom, work, bound = "gemv_gateup", groups * e_gu, "hbm"
     else:
         dom, work, bound = "gemm_gateup", 2.0 * T * (wl.top_k + wl.shared) * 2 * wl.hidden * wl.inter, "mfma"

@@ -51,13 +51,14 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   const size_t mt_bound = (rows + gnz * (moe::kGemmBM - 1)) / moe::kGemmBM + 1;
   moe::CallBufs t{};
   // control words first: their offset must not depend on T (zero between calls)
-  t.ctrl = reinterpret_cast<int32_t*>(take(256));
+  t.ctrl = reinterpret_cast<int32_t*>(take((size_t)moe::ctrl_layout(d.H, d.E, d.S, d.I).words * 4));
   t.logits = reinterpret_cast<float*>(take((size_t)T * d.E * 4));
   t.idx = reinterpret_cast<int32_t*>(take(tk * 4));
   t.w = reinterpret_cast<float*>(take(tk * 4));
   t.counts = reinterpret_cast<int32_t*>(take((size_t)d.E * 4));
   t.offsets = reinterpret_cast<int32_t*>(take((size_t)(d.E + 1) * 4));
   t.perm = reinterpret_cast<int32_t*>(take(tk * 4));
+  t.row_w = reinterpret_cast<float*>(take(tk * 4));
   t.gmask = reinterpret_cast<uint64_t*>(take(C * d.E * 8));
   t.cbase = reinterpret_cast<int32_t*>(take(C * d.E * 4));
   t.grp_row0 = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
@@ -80,6 +81,7 @@ int mt_bound_of(const moe::Dims& d, int T) {
   return (int)((rows + gnz * (moe::kGemmBM - 1)) / moe::kGemmBM + 1);
 }
 
+// upper bound of the active groups (routed experts hit plus shared experts) of a T-token call
 int max_active_of(const moe::Dims& d, int T) {
   return (int)(std::min<size_t>(d.E, (size_t)T * d.K) + d.S);
 }
@@ -311,19 +313,20 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   if (route) use_route_out(b, route);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
+  hipError_t e;
   st = enqueue_route(L, x, T, b, s, true);
   if (st != MOE_OK) return st;
-  hipError_t e;
   if (gemv) {
+    // the down kernel also adds each token's rows into y
     const int na = max_active_of(d, T);
     e = moe::launch_gemv_gateup(d, L->desc, x, b, T, na, s);
-    if (e == hipSuccess) e = moe::launch_gemv_down(d, L->desc, b, T, na, s);
+    if (e == hipSuccess) e = moe::launch_gemv_down(d, L->desc, b, y, T, na, s);
   } else {
     const int mb = mt_bound_of(d, T);
     e = moe::launch_gemm_gateup(d, L->desc, x, b, T, mb, s);
     if (e == hipSuccess) e = moe::launch_gemm_down(d, L->desc, b, T, mb, s);
+    if (e == hipSuccess) e = moe::launch_combine(d, b, y, T, s);
   }
-  if (e == hipSuccess) e = moe::launch_combine(d, b, y, T, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_forward: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }

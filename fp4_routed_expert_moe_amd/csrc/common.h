@@ -47,12 +47,21 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // for its stores to complete before it bumps a counter, and the workgroup that brings the
 // counter to its final value does the dependent work.  No device-scope fence is used: on
 // gfx950 that writes back the whole L2 and costs far more than the data it publishes.
-__device__ __forceinline__ void st_agent(float* p, float v) {
+template <class V>
+__device__ __forceinline__ void st_agent(V* p, V v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_agent(const float* p) {
+template <class V>
+__device__ __forceinline__ V ld_agent(const V* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int add_agent(int32_t* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Cache-policy bits of buffer loads and stores: sc1 makes them coherent across the XCDs'
+// L2 caches (the encoding agent-scope atomics use), for data another workgroup of the
+// same launch produces or consumes.
+constexpr int kSC1 = 16;
 // Wait until this wave's stores (and loads) have completed.
 __device__ __forceinline__ void wait_stores() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -76,6 +85,24 @@ __device__ __forceinline__ void reset_counter(int32_t* counter) {
 // loads (SGPRs), which is how a value shared by every lane of a wave is best fetched.
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
 typedef const __attribute__((address_space(4))) float c_f32;
+
+// Control area at the start of the workspace (int32 words).  Its size depends only on the
+// layer's dims, so its place does not move with the batch size.  A fresh workspace is all
+// zero; afterwards a word is either a counter that every call leaves at zero, the call
+// sequence number ("epoch", advanced once per call by the routing), or a flag that holds
+// zero or the epoch of an earlier call.
+struct CtrlLayout {
+  static constexpr int kRoute = 0;     // router_kernel: arrival counter of its workgroups
+  static constexpr int kEpoch = 1;     // sequence number of the current call
+  static constexpr int kDown = 64;     // decode down: [E+S][ceil(H/16)] column tiles finished
+  int words;
+};
+inline CtrlLayout ctrl_layout(int H, int E, int S, int I) {
+  (void)I;
+  CtrlLayout c;
+  c.words = CtrlLayout::kDown + (E + S) * ((H + 15) / 16);
+  return c;
+}
 
 constexpr int kWave = 64;
 constexpr int kChunk = 64;        // tokens per routing chunk (one bit per token in a 64-bit mask)
@@ -195,6 +222,7 @@ struct CallBufs {
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]
   int32_t* perm;      // [T*k]
+  float* row_w;       // [T*k] routing weight of grouped row r (= w[perm[r]])
   uint64_t* gmask;    // [C][E] per-chunk token masks
   int32_t* cbase;     // [C][E] rows of expert e in chunks before c
   int32_t* grp_row0;  // [G] first grouped row of group g
@@ -219,13 +247,17 @@ void timing_end(int token, hipStream_t s);
 constexpr int kFusedMaxT = 64;
 constexpr int kTailScores = 8192;
 inline bool route_fused(const Dims& d, int T) { return T <= kFusedMaxT && T * d.E <= kTailScores; }
+// Layers whose decode launch also routes (the routing tail inside it ranks up to 256 experts).
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 const CallBufs& b, int T, bool quantize_x, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
-hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
-                              int T, int max_act, hipStream_t s);
-hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
+// The whole layer for a small batch in one launch (decode.hip).  With `route_inside` the
+// launch also scores, quantizes x and routes (route_fused batches); otherwise the routing
+// tables and the FP8 activation terms come from earlier launches on the stream.
+hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b, int T,
+                              int max_act, hipStream_t s);
+hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T, int max_act,
                             hipStream_t s);
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int mt_bound, hipStream_t s);

@@ -388,4 +388,32 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------
+// y[t] = staging[shared slot of t] + sum_j staging[t*k + j]
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ st, float* __restrict__ y, int T,
+                                                      int H, int k, int S) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (S) acc = *reinterpret_cast<const float4*>(st + ((size_t)T * k + t) * H + c);
+  for (int j = 0; j < k; ++j) {
+    const float4 v = *reinterpret_cast<const float4*>(st + ((size_t)t * k + j) * H + c);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(y + (size_t)t * H + c) = acc;
+}
+
+hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s) {
+  dim3 grid((d.H / 4 + 255) / 256, T);
+  const int tk = timing_begin("combine", s);
+  combine_kernel<<<grid, 256, 0, s>>>(b.staging, y, T, d.H, d.K, d.S);
+  timing_end(tk, s);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -44,6 +44,7 @@ constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis 
 // read zero codes (their packed scales are 0 too).  Activations come from the token rows of
 // the pass; past the end of K they read a valid part of the row (multiplied by zero weights).
 constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
+constexpr int kWeightAux = 2;             // nontemporal: the weights are streamed once
 constexpr int kOutOfRange = 1 << 30;      // added to a lane's buffer offset: reads zeros
 
 template <int NM, int NA>
@@ -88,8 +89,9 @@ __device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, i
   for (int mtx = 0; mtx < NM; ++mtx) {
 #pragma unroll
     for (int j = 0; j < kTiles; ++j)
-      f.c[mtx][j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], voff_c + 256 * j, so_c, 0));
-    f.s[mtx] = __builtin_amdgcn_raw_buffer_load_b32(src.s[mtx], src.voff_s, so_s, 0);
+      f.c[mtx][j] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], voff_c + 256 * j, so_c, kWeightAux));
+    f.s[mtx] = __builtin_amdgcn_raw_buffer_load_b32(src.s[mtx], src.voff_s, so_s, kWeightAux);
   }
   int o1 = kb * 32 + 16 * q, o2 = o1 + 64;
   if ((kb + 4) * 32 > K) {  // last iteration of a K that is not a multiple of 128 (uniform)
@@ -249,15 +251,26 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-// down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms
+// down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms, and
+// y[t][n] = staging[shared slot of t][n] + sum_j staging[t*k + j][n].
+// Workgroup (c, a) handles column tile c of active group a.  Workgroups start in order of
+// their linear index (column tile fastest), so when the one of the last active group starts,
+// every other group's workgroup of its tile has started: it waits for their completion flags
+// (agent-scope flags holding this call's epoch, the number the routing kernel advanced), then
+// adds the tile's rows in the combine order of the prefill path.
 // ------------------------------------------------------------------------------------
+constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
+
 __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
-    const int32_t* __restrict__ perm, const float* __restrict__ wts, const int32_t* __restrict__ act,
+    const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
-    float* __restrict__ staging, int T, int k, int H, int I, int R) {
+    float* __restrict__ staging, float* __restrict__ y, int32_t* __restrict__ ctrl, int dn_flags, int T, int k, int S,
+    int H, int I, int R) {
   __shared__ f32x4 red[kSplit][kTiles][64];
-  if ((int)blockIdx.y >= info[0]) return;
+  const int nact = info[0];
+  if ((int)blockIdx.y >= nact) return;
+  const int epoch = ld_agent(ctrl + CtrlLayout::kEpoch);
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -275,6 +288,15 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
     const size_t r = (size_t)(row0 + c0 + (m < nt ? m : 0));
+    // staging slot and weight of the rows this lane finishes, loaded now (they arrive during the K loop)
+    int slot_i[4];
+    float wt_i[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = row0 + c0 + min(4 * q + i, nt - 1);
+      slot_i[i] = rr < tk ? perm[rr] : rr;
+      wt_i[i] = rr < tk ? row_w[rr] : 1.0f;
+    }
     const uint8_t* arow[3] = {h8 + r * I, h8 + (size_t)R * I + r * I, h8 + (size_t)2 * R * I + r * I};
     f32x4 acc2[1][kTiles];
 #pragma unroll
@@ -291,17 +313,33 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
       for (int w = 1; w < kSplit; ++w) sum += red[w][j][lane];
       const int n = n0 + 16 * j + m;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk_i = 4 * q + i;  // lane (n, q) holds tokens 4q .. 4q+3 of row n
-        if (n < H && tk_i < nt) {
-          const int rr = row0 + c0 + tk_i;
-          const int slot = rr < tk ? perm[rr] : rr;
-          const float wt = rr < tk ? wts[slot] : 1.0f;
-          staging[(size_t)slot * H + n] = sum[i] * wt;
-        }
-      }
+      for (int i = 0; i < 4; ++i)  // lane (n, q) holds rows 4q .. 4q+3 of the pass
+        if (n < H && 4 * q + i < nt) st_agent(staging + (size_t)slot_i[i] * H + n, sum[i] * wt_i[i]);
     }
     __syncthreads();
+  }
+  // this group's rows of the tile are out
+  wait_stores();
+  __syncthreads();
+  int32_t* flags = ctrl + dn_flags;  // [active group slot][column tile]
+  const int ntile = gridDim.x;
+  if ((int)blockIdx.y != nact - 1) {
+    if (threadIdx.x == 0) st_agent(flags + blockIdx.y * ntile + blockIdx.x, (int32_t)epoch);
+    return;
+  }
+  for (int round = 0; round < kFlagPolls; ++round) {
+    bool mine = true;
+    for (int a = threadIdx.x; a < nact - 1; a += 256) mine &= ld_agent(flags + a * ntile + blockIdx.x) == epoch;
+    if (__syncthreads_and(mine)) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __asm__ __volatile__("" ::: "memory");
+  for (int i = threadIdx.x; i < T * 64; i += 256) {
+    const int t = i >> 6, n = n0 + (i & 63);
+    if (n >= H) continue;
+    float sacc = S ? ld_agent(staging + ((size_t)tk + t) * H + n) : 0.f;
+    for (int j = 0; j < k; ++j) sacc += ld_agent(staging + ((size_t)t * k + j) * H + n);
+    y[(size_t)t * H + n] = sacc;
   }
 }
 
@@ -319,42 +357,14 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int max_act,
-                            hipStream_t s) {
+hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T,
+                            int max_act, hipStream_t s) {
   dim3 grid((d.H + 16 * kTiles - 1) / (16 * kTiles), max_act);
   const int R = T * (d.K + d.S);
   const int tk = timing_begin("gemv_down", s);
   gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,
-                                                b.w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, T, d.K, d.H,
-                                                d.I, R);
-  timing_end(tk, s);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------
-// y[t] = staging[shared slot of t] + sum_j staging[t*k + j]
-// ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ st, float* __restrict__ y, int T,
-                                                      int H, int k, int S) {
-  const int t = blockIdx.y;
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (c >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (S) acc = *reinterpret_cast<const float4*>(st + ((size_t)T * k + t) * H + c);
-  for (int j = 0; j < k; ++j) {
-    const float4 v = *reinterpret_cast<const float4*>(st + ((size_t)t * k + j) * H + c);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  *reinterpret_cast<float4*>(y + (size_t)t * H + c) = acc;
-}
-
-hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s) {
-  dim3 grid((d.H / 4 + 255) / 256, T);
-  const int tk = timing_begin("combine", s);
-  combine_kernel<<<grid, 256, 0, s>>>(b.staging, y, T, d.H, d.K, d.S);
+                                                b.row_w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, b.ctrl,
+                                                CtrlLayout::kDown, T, d.K, d.S, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }

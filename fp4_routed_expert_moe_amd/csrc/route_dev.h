@@ -1,0 +1,438 @@
+// Device-side routing steps shared by the routing kernels (route.hip) and the fused decode
+// kernel (decode.hip): router scores, the FP8 term split of the activations, top-k with
+// renormalised softmax weights, and the stable token->expert grouping tables.
+//
+// "feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine" (PR #1055, "What it is",
+// prefill MoE) routes on the device and feeds expert-grouped GEMM rows; the pages leave the
+// scoring rule open, so scores are a plain fp32 dot product (+ optional bias), selection is
+// the k largest (ties to the lower index), and the weights are a softmax over the k selected
+// scores.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------
+// Router score of one expert for up to kScoreTT tokens, computed by a group of four waves:
+// wave w of the group adds x[h]*w[h] over its quarter of the hidden axis, lane l taking
+// h = w*H/4 + 8l + 512j + i (j ascending, i = 0..7) with fused multiply-adds in that order;
+// the lanes are summed in the fixed DPP order of wave_sum_f32 and the four quarters in wave
+// order.  Every kernel that scores uses this, so a token's scores depend neither on the batch
+// nor on the kernel.  All of a lane's loads are issued before the first product.
+// ------------------------------------------------------------------------------------
+constexpr int kScoreTT = 8;
+constexpr int kScoreWaves = 4;
+
+// Quarter sums of one wave (wq = wave index in the group), same value on every lane.
+__device__ __forceinline__ void score_quarter(const uint16_t* __restrict__ x, int nt, const float* __restrict__ w,
+                                              int H, int wq, float (&out)[kScoreTT]) {
+  const int lane = threadIdx.x & 63;
+  const int hq = H / kScoreWaves;  // H % 32 == 0: a multiple of 8
+  const int h_end = (wq + 1) * hq;
+  float acc[kScoreTT];
+#pragma unroll
+  for (int i = 0; i < kScoreTT; ++i) acc[i] = 0.f;
+  for (int h0 = wq * hq + lane * 8; h0 < h_end; h0 += 1024) {
+    // two 512-value steps at once (their loads in flight together)
+    float4 wv[2][2];
+    uint4 xv[2][kScoreTT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int h = h0 + 512 * u;
+      if (h < h_end) {
+        wv[u][0] = *reinterpret_cast<const float4*>(w + h);
+        wv[u][1] = *reinterpret_cast<const float4*>(w + h + 4);
+#pragma unroll
+        for (int i = 0; i < kScoreTT; ++i)
+          if (i < nt) xv[u][i] = *reinterpret_cast<const uint4*>(x + (size_t)i * H + h);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (h0 + 512 * u >= h_end) break;
+      const float4 w0 = wv[u][0], w1 = wv[u][1];
+#pragma unroll
+      for (int i = 0; i < kScoreTT; ++i) {
+        if (i < nt) {
+          const uint4 v = xv[u][i];
+          float a = acc[i];
+          a = fmaf(bf16_lo(v.x), w0.x, a);
+          a = fmaf(bf16_hi(v.x), w0.y, a);
+          a = fmaf(bf16_lo(v.y), w0.z, a);
+          a = fmaf(bf16_hi(v.y), w0.w, a);
+          a = fmaf(bf16_lo(v.z), w1.x, a);
+          a = fmaf(bf16_hi(v.z), w1.y, a);
+          a = fmaf(bf16_lo(v.w), w1.z, a);
+          a = fmaf(bf16_hi(v.w), w1.w, a);
+          acc[i] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kScoreTT; ++i) out[i] = wave_sum_f32(acc[i]);
+}
+
+// Scores of expert e for tokens [t0, t0+nt) (nt <= kScoreTT), published to logits[t][e] with
+// agent-scope stores (the routing tail may run in another workgroup of the same launch).
+// Called by every thread of the block; the group of waves [4g, 4g+4) handles expert e (valid
+// false: the group only takes part in the barrier).  part: kScoreWaves * kScoreTT floats of
+// LDS per group.
+__device__ __forceinline__ void score_expert(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                            const float* __restrict__ bias, float* logits, int t0, int nt, int e,
+                                            bool valid, int E, int H, float* part) {
+  const int wq = (threadIdx.x >> 6) % kScoreWaves, lane = threadIdx.x & 63;
+  if (valid) {
+    float s[kScoreTT];
+    score_quarter(x + (size_t)t0 * H, nt, wr + (size_t)e * H, H, wq, s);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kScoreTT; ++i) part[wq * kScoreTT + i] = s[i];
+    }
+  }
+  __syncthreads();
+  if (valid && wq == 0 && lane < nt) {
+    const float v = ((part[lane] + part[kScoreTT + lane]) + part[2 * kScoreTT + lane]) + part[3 * kScoreTT + lane];
+    st_agent(logits + (size_t)(t0 + lane) * E + e, v + (bias ? bias[e] : 0.f));
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------
+// Activations as two exact FP8 terms with a scale per 32-value block (the expert kernels'
+// A operand): xq = [2][T][H] e4m3 bytes, then [T][H/32] e8m0 scales.
+// ------------------------------------------------------------------------------------
+struct XBlock {
+  uint4 hi[2], lo[2];  // 32 e4m3 bytes of each term
+  uint32_t s;          // e8m0 scale of term 0 (term 1: s - 4)
+};
+__device__ __forceinline__ XBlock quantize_x_block(const uint16_t* __restrict__ src) {
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(raw);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  const int s = fp8_block_scale(amax);
+  const float inv = fp8_inv_scale(s);
+  uint32_t th[8], tl[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[4] = {bf16_lo(w[2 * i]) * inv, bf16_hi(w[2 * i]) * inv, bf16_lo(w[2 * i + 1]) * inv,
+                  bf16_hi(w[2 * i + 1]) * inv};
+    th[i] = pack_fp8x4(v[0], v[1], v[2], v[3]);
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (v[j] - f32_of_fp8((th[i] >> (8 * j)) & 0xFFu)) * 16.f;
+    tl[i] = pack_fp8x4(r[0], r[1], r[2], r[3]);
+  }
+  XBlock b;
+  b.hi[0] = make_uint4(th[0], th[1], th[2], th[3]);
+  b.hi[1] = make_uint4(th[4], th[5], th[6], th[7]);
+  b.lo[0] = make_uint4(tl[0], tl[1], tl[2], tl[3]);
+  b.lo[1] = make_uint4(tl[4], tl[5], tl[6], tl[7]);
+  b.s = (uint32_t)s;
+  return b;
+}
+
+// ------------------------------------------------------------------------------------
+// Top-k of one token by one wave.
+// Each score becomes a 64-bit rank key: high word = order-preserving image of the float
+// (+1, so that NaN -> 1 still beats an excluded entry, which is 0), low word = ~index so
+// that equal scores prefer the lower expert.  -0 is ranked as +0.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  const uint32_t ord = v != v ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return ((uint64_t)ord + 1ull) << 32 | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+// The score whose key has high word `hi` (-0 comes back as +0).
+__device__ __forceinline__ float hi_value(uint32_t hi) {
+  const uint32_t ord = hi - 1u;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// Lane l owns experts l, l + 64, ...  (Q = scores per lane, E <= 64*Q) and first sorts its Q
+// keys in descending order.  Each round then takes the largest of the lanes' first keys: the
+// wave-wide maximum of their high words on DPP, then the low word of the one lane that holds
+// it (a second reduction only when several lanes tie), and that lane drops its first key.
+// Every pick is wave-uniform.  The picks and their weights (softmax over the k picked scores,
+// summed in a fixed order) go to sel_e[0..k) / sel_w[0..k) in LDS, and bit `tbit` of mask[e]
+// is set for each pick; the caller writes the results out.
+template <int Q>
+__device__ __forceinline__ void topk_wave(const float* row, int E, int k, uint16_t* sel_e, float* sel_w,
+                                          uint64_t* mask, int tbit) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + 64 * q;
+    key[q] = e < E ? rank_key(row[e], e) : 0ull;
+  }
+  // descending order within the lane (odd-even transposition: Q rounds)
+#pragma unroll
+  for (int r = 0; r < Q; ++r)
+#pragma unroll
+    for (int q = r & 1; q + 1 < Q; q += 2) {
+      const uint64_t a = key[q], b = key[q + 1];
+      key[q] = a > b ? a : b;
+      key[q + 1] = a > b ? b : a;
+    }
+  int selE[Q];
+  float selV[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    selE[q] = 0;
+    selV[q] = 0.f;
+  }
+  float vtop = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t mhi = (uint32_t)(key[0] >> 32), mlo = (uint32_t)key[0];
+    const uint32_t bhi = wave_max_u32(mhi);
+    const uint64_t tied = __ballot(mhi == bhi);
+    uint32_t blo;
+    if (__popcll(tied) == 1)
+      blo = __builtin_amdgcn_readlane(mlo, __ffsll((unsigned long long)tied) - 1);
+    else
+      blo = wave_max_u32(mhi == bhi ? mlo : 0u);
+    const int e = (int)(0xFFFFFFFFu - blo);
+    const float v = hi_value(bhi);
+    if (j == 0) vtop = v;
+    if ((e & 63) == lane) {  // the owner drops its first key
+#pragma unroll
+      for (int q = 0; q + 1 < Q; ++q) key[q] = key[q + 1];
+      key[Q - 1] = 0ull;
+    }
+    const bool rec = (j & 63) == lane;
+    const int qj = j >> 6;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (q == qj) {
+        selE[q] = rec ? e : selE[q];
+        selV[q] = rec ? v : selV[q];
+      }
+  }
+  float p[Q];
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = lane + 64 * q;
+    p[q] = 0.f;
+    if (j < k) {
+      p[q] = expf(selV[q] - vtop);
+      s += p[q];
+    }
+  }
+  s = wave_sum_f32(s);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = lane + 64 * q;
+    if (j < k) {
+      sel_e[j] = (uint16_t)selE[q];
+      sel_w[j] = p[q] / s;
+      atomicOr(reinterpret_cast<unsigned long long*>(&mask[selE[q]]), 1ull << tbit);
+    }
+  }
+}
+
+// Tokens [0, T) of scores [T][E] (T <= 64), one token per wave at a time over the NT
+// threads of the block.  Token t sets bit t of the expert masks; its picks go to
+// sel_e/sel_w[t*k ..].
+template <int NT, int Q>
+__device__ __forceinline__ void topk_block(const float* scores, int T, int E, int k, uint16_t* sel_e, float* sel_w,
+                                           uint64_t* mask) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int t = wave; t < T; t += NT / 64)
+    topk_wave<Q>(scores + (size_t)t * E, E, k, sel_e + t * k, sel_w + t * k, mask, t);
+}
+// Experts up to 64 * QMAX (QMAX = 16 covers the layer's limit of 1024).
+template <int NT, int QMAX = 16>
+__device__ __forceinline__ void topk_block_any(const float* scores, int T, int E, int k, uint16_t* sel_e,
+                                               float* sel_w, uint64_t* mask) {
+  if (E <= 64)
+    topk_block<NT, 1>(scores, T, E, k, sel_e, sel_w, mask);
+  else if (E <= 128 || QMAX < 4)
+    topk_block<NT, 2>(scores, T, E, k, sel_e, sel_w, mask);
+  else if (E <= 256 || QMAX < 8)
+    topk_block<NT, (QMAX < 4 ? 2 : 4)>(scores, T, E, k, sel_e, sel_w, mask);
+  else if (E <= 512 || QMAX < 16)
+    topk_block<NT, (QMAX < 8 ? 4 : 8)>(scores, T, E, k, sel_e, sel_w, mask);
+  else
+    topk_block<NT, (QMAX < 16 ? 8 : 16)>(scores, T, E, k, sel_e, sel_w, mask);
+}
+
+// ------------------------------------------------------------------------------------
+// Grouping tables.  One wave scans the per-expert row counts cnt[0..E) (LDS) into exclusive
+// offsets offs[] (LDS; may be the same array as cnt) and the ascending list of experts with
+// rows act[] (LDS), with the totals in GroupScan (LDS); it also writes the grouped GEMM's
+// M-tile list when asked.  Every thread of the block then writes the tables out with one
+// store per entry (write_tables), so no store waits on another.
+// ------------------------------------------------------------------------------------
+// Exclusive prefix sum over the wave on DPP: row_shr 1, 2, 4, 8 scans each 16-lane row, then
+// row_bcast 15 and 31 carry the row totals into the rows above (checked lane by lane on the
+// device against a serial sum).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  int x = v;
+  x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+struct GroupScan {
+  int nact, total, nmt;
+};
+
+template <bool MTILES>
+__device__ __forceinline__ void group_scan_wave(int* cnt_offs, int* act, GroupScan* gs, int T, int E, int S,
+                                                const CallBufs& b) {
+  const int lane = threadIdx.x & 63;
+  const int J = (E + 63) >> 6;
+  const int e0 = lane * J;
+  int rows = 0, acts = 0, mts = 0;
+  for (int i = 0; i < J; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt_offs[e];
+      rows += c;
+      acts += c > 0;
+      mts += (c + kGemmBM - 1) / kGemmBM;
+    }
+  }
+  int total, nact, nmt;
+  int off = wave_excl_scan(rows, &total);
+  int apos = wave_excl_scan(acts, &nact);
+  int mpos = wave_excl_scan(mts, &nmt);
+  for (int i = 0; i < J; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = cnt_offs[e];
+    cnt_offs[e] = off;
+    off += c;
+    if (c > 0) act[apos++] = e;
+    if (MTILES)
+      for (int m = 0; m < (c + kGemmBM - 1) / kGemmBM; ++m) {
+        st_agent(b.mt_group + mpos, e);
+        st_agent(b.mt_row0 + mpos++, m * kGemmBM);
+      }
+  }
+  const int mt_shared = S ? (T + kGemmBM - 1) / kGemmBM : 0;
+  if (MTILES)
+    for (int i = lane; i < mt_shared; i += 64) {
+      st_agent(b.mt_group + nmt + i, E);
+      st_agent(b.mt_row0 + nmt + i, i * kGemmBM);
+    }
+  if (lane == 0) {
+    gs->nact = nact;
+    gs->total = total;
+    gs->nmt = nmt + mt_shared;
+  }
+}
+
+// counts, offsets, group rows and first rows, the active list (shared expert last) and the
+// info words, from the scan's LDS results (cnt[e] = rows of expert e, offs[e] = its first row).
+template <int NT, class CNT>
+__device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, const int* act, const GroupScan& gs,
+                                             int T, int E, int K, int S, const CallBufs& b) {
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int c = cnt(e), o = offs[e];
+    st_agent(b.counts + e, c);
+    st_agent(b.offsets + e, o);
+    st_agent(b.grp_row0 + e, o);
+    st_agent(b.grp_rows + e, c);
+  }
+  for (int a = threadIdx.x; a < gs.nact; a += NT) {
+    const int e = act[a];
+    st_agent(b.act + a, e);
+  }
+  if (threadIdx.x == 0) {
+    st_agent(b.offsets + E, gs.total);
+    if (S) {
+      st_agent(b.grp_row0 + E, T * K);
+      st_agent(b.grp_rows + E, T);
+      st_agent(b.act + gs.nact, E);
+    }
+    // one call, one epoch: the decode down kernel's completion flags carry it
+    st_agent(b.ctrl + CtrlLayout::kEpoch, ld_agent(b.ctrl + CtrlLayout::kEpoch) + 1);
+    st_agent(b.info + 0, gs.nact + S);
+    st_agent(b.info + 1, gs.nmt);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The routing tail of a small batch (route_fused), run by one workgroup of NT threads once
+// every score is published: top-k, grouping tables, stable scatter.  Everything is built in
+// LDS and written out at the end.  TailLayout<MAXE, MAXTK> sizes the caller's LDS for up to
+// MAXE experts and MAXTK = T*k picks (T*E <= kTailScores always).
+// ------------------------------------------------------------------------------------
+template <int MAXE, int MAXTK>
+struct TailLayout {
+  static constexpr int kSc = 0;                           // f32 [kTailScores]
+  static constexpr int kSelE = kSc + kTailScores * 4;     // u16 [MAXTK] picks of token t at [t*K, t*K+K)
+  static constexpr int kSelW = kSelE + MAXTK * 2;         // f32 [MAXTK] their weights
+  static constexpr int kMask = (kSelW + MAXTK * 4 + 7) / 8 * 8;  // u64 [MAXE] bit t: token t picked e
+  static constexpr int kOffs = kMask + MAXE * 8;          // i32 [MAXE]
+  static constexpr int kAct = kOffs + MAXE * 4;           // i32 [MAXE]
+  static constexpr int kScan = kAct + MAXE * 4;           // GroupScan
+  static constexpr int kBytes = kScan + 16;
+};
+
+template <int NT, int QMAX, int MAXE, int MAXTK, bool MTILES>
+__device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int K, int S, char* lds) {
+  using L = TailLayout<MAXE, MAXTK>;
+  float* sc = reinterpret_cast<float*>(lds + L::kSc);
+  uint16_t* sel_e = reinterpret_cast<uint16_t*>(lds + L::kSelE);
+  float* sel_w = reinterpret_cast<float*>(lds + L::kSelW);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(lds + L::kMask);
+  int* offs = reinterpret_cast<int*>(lds + L::kOffs);
+  int* act = reinterpret_cast<int*>(lds + L::kAct);
+  GroupScan* gs = reinterpret_cast<GroupScan*>(lds + L::kScan);
+  const int tid = threadIdx.x;
+  const int n = T * E;
+  // every score in one round of loads, then into LDS
+  for (int i0 = 0; i0 < n; i0 += NT * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT + tid;
+      v[u] = i < n ? ld_agent(b.logits + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT + tid;
+      if (i < n) sc[i] = v[u];
+    }
+  }
+  for (int i = tid; i < E; i += NT) mask[i] = 0ull;
+  __syncthreads();
+  topk_block_any<NT, QMAX>(sc, T, E, K, sel_e, sel_w, mask);
+  __syncthreads();
+  for (int i = tid; i < E; i += NT) offs[i] = __popcll(mask[i]);
+  __syncthreads();
+  if (tid < 64) group_scan_wave<MTILES>(offs, act, gs, T, E, S, b);
+  __syncthreads();
+  write_tables<NT>([&](int e) { return __popcll(mask[e]); }, offs, act, *gs, T, E, K, S, b);
+  // pick i = t*K + j lands after the rows of lower tokens routed to the same expert
+  for (int i = tid; i < T * K; i += NT) {
+    const int t = i / K, e = sel_e[i];
+    const float w = sel_w[i];
+    const int r = offs[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
+    st_agent(b.idx + i, e);
+    st_agent(b.w + i, w);
+    st_agent(b.perm + r, (int32_t)i);
+    st_agent(b.row_w + r, w);
+  }
+}
+
+}  // namespace moe
