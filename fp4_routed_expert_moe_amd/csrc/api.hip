@@ -68,7 +68,7 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   t.mt_group = reinterpret_cast<int32_t*>(take(mt_bound * 4));
   t.mt_row0 = reinterpret_cast<int32_t*>(take(mt_bound * 4));
   t.h = take(rows * d.I * 4);
-  t.xq = reinterpret_cast<uint8_t*>(take((size_t)T * d.H * 2 + (size_t)T * (d.H / 32)));
+  t.xq = reinterpret_cast<uint8_t*>(take((size_t)T * d.H * 2 + (size_t)T * moe::kb_pad(d.H)));
   t.staging = reinterpret_cast<float*>(take(rows * d.H * 4));
   if (b) *b = t;
   return off;

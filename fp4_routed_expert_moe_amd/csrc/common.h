@@ -206,6 +206,9 @@ __device__ __forceinline__ int row_token(const int32_t* perm, int r, int tk, int
 // Byte (i, t, m, q, j) is the scale of row 64t + 16j + m, K block 4i + q (0 past the matrix),
 // so lane (m, q) of a wave finds the scales of its four 16-row column tiles of one 128-value
 // K step in one dword, and the 64 lanes' dwords are 256 contiguous bytes.
+// Activation scale rows ([rows][kb_pad(K)] e8m0) are padded to whole 128-value K steps; the
+// pad bytes hold 127 (a finite scale that only ever meets zero weights).
+__host__ __device__ inline int kb_pad(int K) { return (K / 32 + 3) / 4 * 4; }
 __host__ __device__ inline size_t scale_slab_bytes(int N, int K) {
   return (size_t)((K / 32 + 3) / 4) * (size_t)((N + 63) / 64) * 256;
 }
@@ -232,8 +235,8 @@ struct CallBufs {
   int32_t* mt_group;  // [mt_bound]
   int32_t* mt_row0;   // [mt_bound]
   int32_t* ctrl;      // control words (zero between calls): [0] routing arrival counter
-  void* h;            // GEMV path: h as FP8 terms + scales (see gemv.hip); GEMM path: bf16 [T(k+S)][I]
-  uint8_t* xq;        // GEMV path: x as 2 FP8 terms [2][T][H] then e8m0 scales [T][H/32]
+  void* h;            // h as FP8 terms [3 decode / 2 prefill][R][I] then e8m0 scales [R][kb_pad(I)]
+  uint8_t* xq;        // x as 2 FP8 terms [2][T][H] then e8m0 scales [T][kb_pad(H)]
   float* staging;     // [T(k+S)][H] weighted expert outputs, slot-indexed
 };
 

@@ -60,7 +60,7 @@ struct ATile {                    // one K step of the activation tile
   uint8_t s[kPM][SH::PKB];        // e8m0 scales of the step's K blocks
 };
 
-// Activation rows: term planes hi/lo [rows][K] bytes and scales [rows][K/32].
+// Activation rows: term planes hi/lo [rows][K] bytes and scales [rows][kb_pad(K)].
 struct ARows {
   const uint8_t* hi;
   const uint8_t* lo;
@@ -132,14 +132,14 @@ __device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int 
 template <class SH, int NM>
 struct BFrag {
   i32x4 c[SH::PU][NM][SH::CT];
-  int s[SH::PU][NM][SH::CT];
+  int s[SH::PU][NM];  // scale dword of the lane's four 16-row tiles
 };
 template <class SH, int NM>
 struct BSrc {
   __amdgpu_buffer_rsrc_t c[NM], s[NM];
-  int voff_c;          // column tile 0, K block q, step 0
-  int voff_s[SH::CT];  // scale byte of column tile c, K block q, step 0
-  int nt64;            // 64-row tiles of the matrix
+  int voff_c;  // column tile 0, K block q, step 0
+  int voff_s;  // scale dword of this wave's 64-row tile, K block q, step 0
+  int nt64;    // 64-row tiles of the matrix
 };
 constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit data format
 // Steps past the last one (the prefetch runs ahead unconditionally) and lanes whose block is
@@ -160,22 +160,26 @@ __device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<SH, NM>& bs
       bias_s = kb >= KB ? kOutOfRange : 0;
     }
 #pragma unroll
-    for (int mtx = 0; mtx < NM; ++mtx)
+    for (int mtx = 0; mtx < NM; ++mtx) {
 #pragma unroll
-      for (int c = 0; c < SH::CT; ++c) {
+      for (int c = 0; c < SH::CT; ++c)
         f.c[u][mtx][c] =
             __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + bias_c + 256 * c, so_c, 0));
-        f.s[u][mtx][c] = __builtin_amdgcn_raw_buffer_load_b8(bs.s[mtx], bs.voff_s[c] + bias_s, so_s, 0);
-      }
+      f.s[u][mtx] = __builtin_amdgcn_raw_buffer_load_b32(bs.s[mtx], bs.voff_s + bias_s, so_s, 0);
+    }
   }
 }
 
-// One K step: acc[mtx][rs][c] += A(rs) x B(mtx, c) for both FP8 terms, rs < nsub.
+// One K step: acc[mtx][rs][c] += A(rs) x B(mtx, c) for both FP8 terms, rs < nsub.  sh: the
+// bit offset of this wave's first tile in its scale dword (0 or 16 when CT == 2).
 template <class SH, int NM>
 __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& f, f32x4 (&acc)[NM][4][SH::CT],
-                                       int nsub, int m, int q) {
+                                       int nsub, int m, int q, int sh) {
 #pragma unroll
-  for (int u = 0; u < SH::PU; ++u)
+  for (int u = 0; u < SH::PU; ++u) {
+    int sb[NM];
+#pragma unroll
+    for (int mtx = 0; mtx < NM; ++mtx) sb[mtx] = SH::CT == 4 ? f.s[u][mtx] : (int)((uint32_t)f.s[u][mtx] >> sh);
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
@@ -194,16 +198,23 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& 
         for (int mtx = 0; mtx < NM; ++mtx) {
           // FP4 reads the low four registers of the operand; the rest are left undefined
           const i32x8 bb = __builtin_shufflevector(f.c[u][mtx][c], f.c[u][mtx][c], 0, 1, 2, 3, -1, -1, -1, -1);
-          acc[mtx][rs][c] = mma_f8f4(a0, bb, acc[mtx][rs][c], sa, f.s[u][mtx][c]);
-          acc[mtx][rs][c] = mma_f8f4(a1, bb, acc[mtx][rs][c], sa - 4, f.s[u][mtx][c]);
+          f32x4 x = acc[mtx][rs][c];
+          switch (c) {  // B's scale: byte c of sb
+            case 0: x = mma_f8f4_sb<0>(a0, bb, x, sa, sb[mtx]); x = mma_f8f4_sb<0>(a1, bb, x, sa - 4, sb[mtx]); break;
+            case 1: x = mma_f8f4_sb<1>(a0, bb, x, sa, sb[mtx]); x = mma_f8f4_sb<1>(a1, bb, x, sa - 4, sb[mtx]); break;
+            case 2: x = mma_f8f4_sb<2>(a0, bb, x, sa, sb[mtx]); x = mma_f8f4_sb<2>(a1, bb, x, sa - 4, sb[mtx]); break;
+            default: x = mma_f8f4_sb<3>(a0, bb, x, sa, sb[mtx]); x = mma_f8f4_sb<3>(a1, bb, x, sa - 4, sb[mtx]); break;
+          }
+          acc[mtx][rs][c] = x;
         }
     }
+  }
 }
 
 // ------------------------------------------------------------------------------------
 // GATEUP: h[r][n] = silu(x_t(r) . Wg[n]) * (x_t(r) . Wu[n]) as 2 FP8 terms + e8m0 per 32
-//         (h8 = [2][R][I] bytes then [R][I/32] scales).
-// DOWN:   staging[slot(r)][n] = weight(r) * (h_r . Wd[n]).
+//         (h8 = [2][R][I] bytes then [R][kb_pad(I)] scales).
+// DOWN:   staging[slot(r)][n] = weight(r) * (h_r . Wd[n])  (wts: weight of grouped row r).
 // ------------------------------------------------------------------------------------
 template <bool GATEUP, class SH>
 __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   APtr ap;
   ap.hi = a.hi + (size_t)srow * a.K + 16 * SH::CH * lp;
   ap.lo = a.lo + (size_t)srow * a.K + 16 * SH::CH * lp;
-  ap.sc = a.sc + (size_t)srow * KB + lp;
+  ap.sc = a.sc + (size_t)srow * kb_pad(a.K) + lp;
 
   // this wave's weight columns (columns past N read other bytes of the group or zeros; their
   // results are not stored)
@@ -251,11 +262,9 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   }
   bs.voff_c = (q * N + n0 + m) * 16;
   bs.nt64 = (N + 63) >> 6;
-#pragma unroll
-  for (int c = 0; c < SH::CT; ++c) {
-    const int col0 = n0 + 16 * c;  // this column tile's 64-row tile and 16-row slot in it
-    bs.voff_s[c] = (((col0 >> 6) * 16 + m) * 4 + q) * 4 + ((col0 >> 4) & 3);
-  }
+  bs.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;
+  const int sh = 8 * ((n0 >> 4) & 3);  // CT == 2: this wave's tiles are bytes sh/8 and sh/8 + 1
+  static_assert(SH::CT == 2 || SH::CT == 4, "a wave's tiles share one scale dword");
   const int nsub = (nrows + 15) >> 4;
 
   f32x4 acc[NM][4][SH::CT];
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
                   BFrag<SH, NM>& f_far) -> bool {
     a_far = a_fetch<SH>(ap, a.K, min(s + 2, last), lp);
     b_fetch<SH, NM>(f_far, bs, N, KB, s + 2, q);
-    k_step<SH, NM>(tc, fc, acc, nsub, m, q);
+    k_step<SH, NM>(tc, fc, acc, nsub, m, q, sh);
     const bool more = s + 1 < nsteps;
     if (more) a_store<SH>(tn, a_next, lr, lp);
     __syncthreads();
@@ -332,26 +341,37 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
               h8[o] = (uint8_t)t0;
               h_lo[o] = (uint8_t)t1;
             }
-            if (m == 0) hs[r * (N >> 5) + (nb >> 5)] = (uint8_t)sc;
+            if (m == 0) {
+              hs[r * kb_pad(N) + (nb >> 5)] = (uint8_t)sc;
+              if ((nb >> 5) == (N >> 5) - 1)  // pad bytes of the row
+                for (int j = N >> 5; j < kb_pad(N); ++j) hs[r * kb_pad(N) + j] = (uint8_t)127;
+            }
           }
         }
       }
     }
   } else {
+    // staging slot and routing weight of the 16 rows this lane finishes (all loads first)
+    int slot[4][4];
+    float wt[4][4];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = r0 + min(16 * rs + 4 * q + i, nrows - 1);
+        slot[rs][i] = rr < tk ? perm[rr] : rr;
+        wt[rs][i] = rr < tk ? wts[rr] : 1.0f;
+      }
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int lrow = 16 * rs + 4 * q + i;
-        if (lrow >= nrows) continue;
-        const int rr = r0 + lrow;
-        const int slot = rr < tk ? perm[rr] : rr;
-        const float wt = rr < tk ? wts[slot] : 1.0f;
+        if (16 * rs + 4 * q + i >= nrows) continue;
 #pragma unroll
         for (int c = 0; c < SH::CT; ++c) {
           const int n = n0 + 16 * c + m;
-          if (n < N) staging[(size_t)slot * N + n] = acc[0][rs][c][i] * wt;
+          if (n < N) staging[(size_t)slot[rs][i] * N + n] = acc[0][rs][c][i] * wt[rs][i];
         }
       }
     }
@@ -382,7 +402,7 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
   const int tk = timing_begin("gemm_down", s);
   gemm_f8f4_kernel<false, DownShape><<<mt_bound * NT, DownShape::NTH, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
-                                                        b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
+                                                        b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
                                                         b.grp_rows, nullptr, b.staging, T, d.K, d.H, R, NT);
   timing_end(tk, s);
   return hipGetLastError();

@@ -59,16 +59,19 @@ struct GSrc {
   __amdgpu_buffer_rsrc_t c[NM], s[NM];
   int voff_c, voff_s;  // column tile 0, K block q, K iteration 0 (tile j is 16 columns on)
 };
+// Matrix mtx's columns start at n0 + mtx * col_step (col_step a multiple of 64): gate and up
+// use the same columns of two matrices, down two adjacent 64-column blocks of one.
 template <int NM>
 __device__ __forceinline__ void gsrc_init(GSrc<NM>& src, const uint8_t* const* codes, const uint8_t* const* scales,
-                                          int g, int KB, int N, int n0, int m, int q) {
+                                          int g, int KB, int N, int n0, int m, int q, int col_step) {
   const int slab = (int)scale_slab_bytes(N, 32 * KB);
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
-    src.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
-                                                   KB * N * 16, kBufferFlags);
-    src.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
-                                                   kBufferFlags);
+    const int dc = mtx * col_step * 16, dsb = mtx * (col_step >> 6) * 256;
+    src.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16 + dc), (short)0,
+                                                   KB * N * 16 - dc, kBufferFlags);
+    src.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab + dsb), (short)0,
+                                                   slab - dsb, kBufferFlags);
   }
   // columns past N read other bytes of the group (or zeros past its end); they are not stored
   src.voff_c = (q * N + n0 + m) * 16;
@@ -111,7 +114,7 @@ __device__ __forceinline__ void gv_mma(const GFrag<NM, NA>& f, f32x4 (&acc)[NM][
   i32x8 a[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
-  static_assert(kTiles == 4, "one scale dword covers four 16-row column tiles");
+  static_assert(kTiles == 4 && kSplit == 4, "one scale dword covers four 16-row column tiles");
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
     i32x8 b[kTiles];
@@ -158,7 +161,7 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>
 
 // ------------------------------------------------------------------------------------
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
-// (h8 = [3][rows][I] bytes, hs = [rows][I/32] e8m0).
+// (h8 = [3][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
   const uint8_t* codes[2] = {gc, uc};
   const uint8_t* scales[2] = {gs, us};
   GSrc<2> src;
-  gsrc_init<2>(src, codes, scales, g, KB, I, n0, m, q);
+  gsrc_init<2>(src, codes, scales, g, KB, I, n0, m, q, 0);
   const uint8_t* x_hi = xq;
   const uint8_t* x_lo = xq + (size_t)T * H;
   const uint8_t* x_sc = xq + (size_t)2 * T * H;
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
     f32x4 acc[2][kTiles];
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gv_pass<2, 2>(acc, src, I, arow, x_sc + (size_t)tok * KB, H, it_lo, it_hi, q);
+    gv_pass<2, 2>(acc, src, I, arow, x_sc + (size_t)tok * kb_pad(H), H, it_lo, it_hi, q);
     f32x4 (&ag)[kTiles] = acc[0];
     f32x4 (&au)[kTiles] = acc[1];
 #pragma unroll
@@ -242,7 +245,11 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
             h8[(size_t)R * I + o] = (uint8_t)t1;
             h8[(size_t)2 * R * I + o] = (uint8_t)t2;
           }
-          if (m == 0) hs[r * (I >> 5) + (nb >> 5)] = (uint8_t)sc;
+          if (m == 0) {
+            hs[r * kb_pad(I) + (nb >> 5)] = (uint8_t)sc;
+            if ((nb >> 5) == (I >> 5) - 1)  // pad bytes of the row
+              for (int j = I >> 5; j < kb_pad(I); ++j) hs[r * kb_pad(I) + j] = (uint8_t)127;
+          }
         }
       }
     }
@@ -261,13 +268,16 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
 // ------------------------------------------------------------------------------------
 constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
 
+constexpr int kDnBlocks = 1;                     // 64-column blocks per down workgroup
+constexpr int kDnCols = kDnBlocks * 16 * kTiles;  // output columns per down workgroup
+
 __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
     float* __restrict__ staging, float* __restrict__ y, int32_t* __restrict__ ctrl, int dn_flags, int T, int k, int S,
     int H, int I, int R) {
-  __shared__ f32x4 red[kSplit][kTiles][64];
+  __shared__ f32x4 red[kSplit][kDnBlocks][kTiles][64];
   const int nact = info[0];
   if ((int)blockIdx.y >= nact) return;
   const int epoch = ld_agent(ctrl + CtrlLayout::kEpoch);
@@ -275,14 +285,14 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * (16 * kTiles);
+  const int n0 = blockIdx.x * kDnCols;
   const int KB = I >> 5;
   const int NI = (KB + 3) >> 2;
   const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
-  const uint8_t* codes[1] = {dc};
-  const uint8_t* scales[1] = {ds};
-  GSrc<1> src;
-  gsrc_init<1>(src, codes, scales, g, KB, H, n0, m, q);
+  const uint8_t* codes[kDnBlocks] = {dc};
+  const uint8_t* scales[kDnBlocks] = {ds};
+  GSrc<kDnBlocks> src;
+  gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * kTiles);
   const uint8_t* hs = h8 + (size_t)3 * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
@@ -298,20 +308,25 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
       wt_i[i] = rr < tk ? row_w[rr] : 1.0f;
     }
     const uint8_t* arow[3] = {h8 + r * I, h8 + (size_t)R * I + r * I, h8 + (size_t)2 * R * I + r * I};
-    f32x4 acc2[1][kTiles];
+    f32x4 acc[kDnBlocks][kTiles];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) acc2[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gv_pass<1, 3>(acc2, src, H, arow, hs + r * KB, I, it_lo, it_hi, q);
-    f32x4 (&acc)[kTiles] = acc2[0];
+    for (int c = 0; c < kDnBlocks; ++c)
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) red[wave][j][lane] = acc[j];
+      for (int j = 0; j < kTiles; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gv_pass<kDnBlocks, 3>(acc, src, H, arow, hs + r * kb_pad(I), I, it_lo, it_hi, q);
+#pragma unroll
+    for (int c = 0; c < kDnBlocks; ++c)
+#pragma unroll
+      for (int j = 0; j < kTiles; ++j) red[wave][c][j][lane] = acc[c][j];
     __syncthreads();
-    if (wave < kTiles) {
-      const int j = wave;  // wave w finishes column tile w
-      f32x4 sum = red[0][j][lane];
+    // wave w finishes column tiles kDnBlocks*w .. kDnBlocks*w + kDnBlocks - 1
 #pragma unroll
-      for (int w = 1; w < kSplit; ++w) sum += red[w][j][lane];
-      const int n = n0 + 16 * j + m;
+    for (int u = 0; u < kDnBlocks; ++u) {
+      const int jj = kDnBlocks * wave + u, c = jj / kTiles, j = jj % kTiles;
+      f32x4 sum = red[0][c][j][lane];
+#pragma unroll
+      for (int w = 1; w < kSplit; ++w) sum += red[w][c][j][lane];
+      const int n = n0 + 16 * jj + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // lane (n, q) holds rows 4q .. 4q+3 of the pass
         if (n < H && 4 * q + i < nt) st_agent(staging + (size_t)slot_i[i] * H + n, sum[i] * wt_i[i]);
@@ -334,8 +349,8 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
     __builtin_amdgcn_s_sleep(2);
   }
   __asm__ __volatile__("" ::: "memory");
-  for (int i = threadIdx.x; i < T * 64; i += 256) {
-    const int t = i >> 6, n = n0 + (i & 63);
+  for (int i = threadIdx.x; i < T * kDnCols; i += 256) {
+    const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;
     float sacc = S ? ld_agent(staging + ((size_t)tk + t) * H + n) : 0.f;
     for (int j = 0; j < k; ++j) sacc += ld_agent(staging + ((size_t)t * k + j) * H + n);
@@ -359,7 +374,7 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
 
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T,
                             int max_act, hipStream_t s) {
-  dim3 grid((d.H + 16 * kTiles - 1) / (16 * kTiles), max_act);
+  dim3 grid((d.H + kDnCols - 1) / kDnCols, max_act);
   const int R = T * (d.K + d.S);
   const int tk = timing_begin("gemv_down", s);
   gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,

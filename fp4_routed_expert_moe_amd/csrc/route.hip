@@ -45,7 +45,10 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
       hi[1] = q.hi[1];
       lo[0] = q.lo[0];
       lo[1] = q.lo[1];
-      xq[(size_t)2 * T * H + (size_t)t * KB + bb] = (uint8_t)q.s;
+      uint8_t* xs = xq + (size_t)2 * T * H + (size_t)t * kb_pad(H);
+      xs[bb] = (uint8_t)q.s;
+      if (bb == KB - 1)  // pad bytes of the row (finite; they only meet zero weights)
+        for (int j = KB; j < kb_pad(H); ++j) xs[j] = (uint8_t)127;
     }
   }
   __shared__ float part[kRouterEPB][kScoreWaves * kScoreTT];
@@ -180,7 +183,10 @@ __global__ __launch_bounds__(256) void quantize_x_kernel(const uint16_t* __restr
   hi[1] = q.hi[1];
   lo[0] = q.lo[0];
   lo[1] = q.lo[1];
-  xq[(size_t)2 * T * H + t * KB + bb] = (uint8_t)q.s;
+  uint8_t* xs = xq + (size_t)2 * T * H + t * kb_pad(H);
+  xs[bb] = (uint8_t)q.s;
+  if ((int)bb == KB - 1)  // pad bytes of the row (finite; they only meet zero weights)
+    for (int j = KB; j < kb_pad(H); ++j) xs[j] = (uint8_t)127;
 }
 
 // ------------------------------------------------------------------------------------

@@ -101,7 +101,7 @@ __device__ __forceinline__ void score_expert(const uint16_t* __restrict__ x, con
 
 // ------------------------------------------------------------------------------------
 // Activations as two exact FP8 terms with a scale per 32-value block (the expert kernels'
-// A operand): xq = [2][T][H] e4m3 bytes, then [T][H/32] e8m0 scales.
+// A operand): xq = [2][T][H] e4m3 bytes, then [T][kb_pad(H)] e8m0 scales.
 // ------------------------------------------------------------------------------------
 struct XBlock {
   uint4 hi[2], lo[2];  // 32 e4m3 bytes of each term
