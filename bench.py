@@ -273,8 +273,14 @@ def cpu_baseline(wl, args, synth):
 # ---------------------------------------------------------------------------------------
 
 def _short_name(full):
-    m = re.match(r"(?:void )?moe::(\w+?)(?:_kernel)?\b", full)
-    return m.group(1) if m else None
+    """Kernel symbol -> the name its launches are timed under (the grouped GEMM template is
+    one symbol for gate/up and down)."""
+    m = re.match(r"(?:void )?moe::(\w+?)(?:_kernel)?\b(<\w+)?", full)
+    if not m:
+        return None
+    if m.group(1) == "gemm_f8f4":
+        return "gemm_gateup" if m.group(2) == "<true" else "gemm_down"
+    return m.group(1)
 
 
 def _read_pmc(directory):

@@ -35,6 +35,11 @@ constexpr int kSkM = 16;    // tokens per pass (MFMA M)
 #ifndef MOE_GEMV_SPLIT
 #define MOE_GEMV_SPLIT 4
 #endif
+#ifndef MOE_DEC_HTERMS
+#define MOE_DEC_HTERMS 3
+#endif
+constexpr int kHTerms = MOE_DEC_HTERMS;  // FP8 terms of h between gate/up and down (2 or 3)
+static_assert(kHTerms == 2 || kHTerms == 3, "h term count");
 constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (even)
 constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
 
@@ -114,7 +119,7 @@ __device__ __forceinline__ void gv_mma(const GFrag<NM, NA>& f, f32x4 (&acc)[NM][
   i32x8 a[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
-  static_assert(kTiles == 4 && kSplit == 4, "one scale dword covers four 16-row column tiles");
+  static_assert(kTiles == 4 && kSplit >= 2, "one scale dword covers four 16-row column tiles");
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
     i32x8 b[kTiles];
@@ -161,9 +166,9 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>
 
 // ------------------------------------------------------------------------------------
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
-// (h8 = [3][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
+// (h8 = [kHTerms][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
+__global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
   const uint8_t* x_hi = xq;
   const uint8_t* x_lo = xq + (size_t)T * H;
   const uint8_t* x_sc = xq + (size_t)2 * T * H;
-  uint8_t* hs = h8 + (size_t)3 * R * I;
+  uint8_t* hs = h8 + (size_t)kHTerms * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void gemv_gateup_kernel(
             const size_t o = r * I + nb + 16 * c + m;
             h8[o] = (uint8_t)t0;
             h8[(size_t)R * I + o] = (uint8_t)t1;
-            h8[(size_t)2 * R * I + o] = (uint8_t)t2;
+            if (kHTerms == 3) h8[(size_t)2 * R * I + o] = (uint8_t)t2;
           }
           if (m == 0) {
             hs[r * kb_pad(I) + (nb >> 5)] = (uint8_t)sc;
@@ -270,14 +275,22 @@ constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
 
 constexpr int kDnBlocks = 1;                     // 64-column blocks per down workgroup
 constexpr int kDnCols = kDnBlocks * 16 * kTiles;  // output columns per down workgroup
+#ifndef MOE_DN_SPLIT
+#define MOE_DN_SPLIT 4
+#endif
+constexpr int kDnSplit = MOE_DN_SPLIT;            // waves per down workgroup = reduction-axis slices
+constexpr int kDnThreads = 64 * kDnSplit;
+// column tiles each wave finishes (waves past the last tile only reduce)
+constexpr int kDnPerWave = kDnBlocks * kTiles > kDnSplit ? kDnBlocks * kTiles / kDnSplit : 1;
+static_assert(kDnPerWave * kDnSplit >= kDnBlocks * kTiles, "down workgroup shape");
 
-__global__ __launch_bounds__(256, 2) void gemv_down_kernel(
+__global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
     float* __restrict__ staging, float* __restrict__ y, int32_t* __restrict__ ctrl, int dn_flags, int T, int k, int S,
     int H, int I, int R) {
-  __shared__ f32x4 red[kSplit][kDnBlocks][kTiles][64];
+  __shared__ f32x4 red[kDnSplit][kDnBlocks][kTiles][64];
   const int nact = info[0];
   if ((int)blockIdx.y >= nact) return;
   const int epoch = ld_agent(ctrl + CtrlLayout::kEpoch);
@@ -288,12 +301,12 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
   const int n0 = blockIdx.x * kDnCols;
   const int KB = I >> 5;
   const int NI = (KB + 3) >> 2;
-  const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
+  const int it_lo = wave * NI / kDnSplit, it_hi = (wave + 1) * NI / kDnSplit;
   const uint8_t* codes[kDnBlocks] = {dc};
   const uint8_t* scales[kDnBlocks] = {ds};
   GSrc<kDnBlocks> src;
   gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * kTiles);
-  const uint8_t* hs = h8 + (size_t)3 * R * I;
+  const uint8_t* hs = h8 + (size_t)kHTerms * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
     const int nt = min(kSkM, rows - c0);
@@ -307,25 +320,30 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
       slot_i[i] = rr < tk ? perm[rr] : rr;
       wt_i[i] = rr < tk ? row_w[rr] : 1.0f;
     }
-    const uint8_t* arow[3] = {h8 + r * I, h8 + (size_t)R * I + r * I, h8 + (size_t)2 * R * I + r * I};
+    const uint8_t* arow[kHTerms] = {h8 + r * I, h8 + (size_t)R * I + r * I
+#if MOE_DEC_HTERMS == 3
+                                    , h8 + (size_t)2 * R * I + r * I
+#endif
+    };
     f32x4 acc[kDnBlocks][kTiles];
 #pragma unroll
     for (int c = 0; c < kDnBlocks; ++c)
 #pragma unroll
       for (int j = 0; j < kTiles; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gv_pass<kDnBlocks, 3>(acc, src, H, arow, hs + r * kb_pad(I), I, it_lo, it_hi, q);
+    gv_pass<kDnBlocks, kHTerms>(acc, src, H, arow, hs + r * kb_pad(I), I, it_lo, it_hi, q);
 #pragma unroll
     for (int c = 0; c < kDnBlocks; ++c)
 #pragma unroll
       for (int j = 0; j < kTiles; ++j) red[wave][c][j][lane] = acc[c][j];
     __syncthreads();
-    // wave w finishes column tiles kDnBlocks*w .. kDnBlocks*w + kDnBlocks - 1
+    // wave w finishes column tiles kDnPerWave*w .. kDnPerWave*w + kDnPerWave - 1
 #pragma unroll
-    for (int u = 0; u < kDnBlocks; ++u) {
-      const int jj = kDnBlocks * wave + u, c = jj / kTiles, j = jj % kTiles;
+    for (int u = 0; u < kDnPerWave; ++u) {
+      const int jj = kDnPerWave * wave + u, c = jj / kTiles, j = jj % kTiles;
+      if (jj >= kDnBlocks * kTiles) break;
       f32x4 sum = red[0][c][j][lane];
 #pragma unroll
-      for (int w = 1; w < kSplit; ++w) sum += red[w][c][j][lane];
+      for (int w = 1; w < kDnSplit; ++w) sum += red[w][c][j][lane];
       const int n = n0 + 16 * jj + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // lane (n, q) holds rows 4q .. 4q+3 of the pass
@@ -344,12 +362,12 @@ __global__ __launch_bounds__(256, 2) void gemv_down_kernel(
   }
   for (int round = 0; round < kFlagPolls; ++round) {
     bool mine = true;
-    for (int a = threadIdx.x; a < nact - 1; a += 256) mine &= ld_agent(flags + a * ntile + blockIdx.x) == epoch;
+    for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) mine &= ld_agent(flags + a * ntile + blockIdx.x) == epoch;
     if (__syncthreads_and(mine)) break;
     __builtin_amdgcn_s_sleep(2);
   }
   __asm__ __volatile__("" ::: "memory");
-  for (int i = threadIdx.x; i < T * kDnCols; i += 256) {
+  for (int i = threadIdx.x; i < T * kDnCols; i += kDnThreads) {
     const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;
     float sacc = S ? ld_agent(staging + ((size_t)tk + t) * H + n) : 0.f;
@@ -377,7 +395,7 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   dim3 grid((d.H + kDnCols - 1) / kDnCols, max_act);
   const int R = T * (d.K + d.S);
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<<<grid, 64 * kSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,
+  gemv_down_kernel<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,
                                                 b.row_w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, b.ctrl,
                                                 CtrlLayout::kDown, T, d.K, d.S, d.H, d.I, R);
   timing_end(tk, s);
