@@ -88,12 +88,10 @@ typedef const __attribute__((address_space(4))) float c_f32;
 
 // Control area at the start of the workspace (int32 words).  Its size depends only on the
 // layer's dims, so its place does not move with the batch size.  A fresh workspace is all
-// zero; afterwards a word is either a counter that every call leaves at zero, the call
-// sequence number ("epoch", advanced once per call by the routing), or a flag that holds
-// zero or the epoch of an earlier call.
+// zero, and every call leaves every word at zero again: a counter is reset by the workgroup
+// that brings it to its final value, a flag by the workgroup that consumes it.
 struct CtrlLayout {
   static constexpr int kRoute = 0;     // router_kernel: arrival counter of its workgroups
-  static constexpr int kEpoch = 1;     // sequence number of the current call
   static constexpr int kDown = 64;     // decode down: [E+S][ceil(H/16)] column tiles finished
   int words;
 };

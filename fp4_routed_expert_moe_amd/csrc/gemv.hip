@@ -268,8 +268,8 @@ __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gem
 // Workgroup (c, a) handles column tile c of active group a.  Workgroups start in order of
 // their linear index (column tile fastest), so when the one of the last active group starts,
 // every other group's workgroup of its tile has started: it waits for their completion flags
-// (agent-scope flags holding this call's epoch, the number the routing kernel advanced), then
-// adds the tile's rows in the combine order of the prefill path.
+// (agent-scope words set to 1), adds the tile's rows in the combine order of the prefill
+// path, and clears the flags again, so they are all 0 between calls.
 // ------------------------------------------------------------------------------------
 constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
 
@@ -293,7 +293,6 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   __shared__ f32x4 red[kDnSplit][kDnBlocks][kTiles][64];
   const int nact = info[0];
   if ((int)blockIdx.y >= nact) return;
-  const int epoch = ld_agent(ctrl + CtrlLayout::kEpoch);
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -357,16 +356,17 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   int32_t* flags = ctrl + dn_flags;  // [active group slot][column tile]
   const int ntile = gridDim.x;
   if ((int)blockIdx.y != nact - 1) {
-    if (threadIdx.x == 0) st_agent(flags + blockIdx.y * ntile + blockIdx.x, (int32_t)epoch);
+    if (threadIdx.x == 0) st_agent(flags + blockIdx.y * ntile + blockIdx.x, (int32_t)1);
     return;
   }
   for (int round = 0; round < kFlagPolls; ++round) {
     bool mine = true;
-    for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) mine &= ld_agent(flags + a * ntile + blockIdx.x) == epoch;
+    for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) mine &= ld_agent(flags + a * ntile + blockIdx.x) != 0;
     if (__syncthreads_and(mine)) break;
     __builtin_amdgcn_s_sleep(2);
   }
   __asm__ __volatile__("" ::: "memory");
+  for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) st_agent(flags + a * ntile + blockIdx.x, (int32_t)0);
   for (int i = threadIdx.x; i < T * kDnCols; i += kDnThreads) {
     const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;

@@ -1,6 +1,6 @@
-// Device-side routing steps shared by the routing kernels (route.hip) and the fused decode
-// kernel (decode.hip): router scores, the FP8 term split of the activations, top-k with
-// renormalised softmax weights, and the stable token->expert grouping tables.
+// Device-side routing steps shared by the routing kernels (route.hip): router scores, the FP8
+// term split of the activations, top-k with renormalised softmax weights, and the stable
+// token->expert grouping tables.
 //
 // "feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine" (PR #1055, "What it is",
 // prefill MoE) routes on the device and feeds expert-grouped GEMM rows; the pages leave the
@@ -363,8 +363,6 @@ __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, co
       st_agent(b.grp_rows + E, T);
       st_agent(b.act + gs.nact, E);
     }
-    // one call, one epoch: the decode down kernel's completion flags carry it
-    st_agent(b.ctrl + CtrlLayout::kEpoch, ld_agent(b.ctrl + CtrlLayout::kEpoch) + 1);
     st_agent(b.info + 0, gs.nact + S);
     st_agent(b.info + 1, gs.nmt);
   }

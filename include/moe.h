@@ -68,9 +68,9 @@ enum moe_status {
 };
 
 /* Execution path for the expert products.  AUTO picks by token count: the FP4 GEMV
- * kernels (decode: HBM-bound, few rows per expert) or the FP4 grouped GEMM on bf16
- * MFMA (prefill).  The two others force one path (A/B testing, the kill-switch pattern
- * of PR #165's AVX2 series). */
+ * kernels (decode: HBM-bound, few rows per expert) or the FP4 grouped GEMM (prefill); both
+ * run on the block-scaled FP8 x FP4 matrix cores.  The two others force one path (A/B
+ * testing, the kill-switch pattern of PR #165's AVX2 series). */
 enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
 
 /* Layer description.  All pointers are device pointers on `device`.  The library BORROWS
@@ -87,11 +87,11 @@ typedef struct moe_layer_desc {
   const float* w_router;       /* fp32 [E][H] */
   const float* router_bias;    /* fp32 [E], or NULL for no bias */
   const uint8_t* gate_codes;   /* kernel layout (see above): [E+S][H/32][I][16] */
-  const uint8_t* gate_scales;  /* [E+S][H/32][I] */
+  const uint8_t* gate_scales;  /* [E+S][ceil(H/128)][ceil(I/64)][16][4][4] */
   const uint8_t* up_codes;     /* [E+S][H/32][I][16] */
-  const uint8_t* up_scales;    /* [E+S][H/32][I] */
+  const uint8_t* up_scales;    /* [E+S][ceil(H/128)][ceil(I/64)][16][4][4] */
   const uint8_t* down_codes;   /* [E+S][I/32][H][16] */
-  const uint8_t* down_scales;  /* [E+S][I/32][H] */
+  const uint8_t* down_scales;  /* [E+S][ceil(I/128)][ceil(H/64)][16][4][4] */
 } moe_layer_desc;
 
 /* Routing results (device pointers), written by moe_route / moe_forward. */
@@ -125,9 +125,11 @@ void moe_layer_destroy(moe_layer* layer);
 
 /* Bytes of device workspace one call with up to max_tokens tokens needs (0 on bad
  * arguments).  The caller allocates and owns it; it must be 256-byte aligned and filled with
- * zeros before its first use.  Its first bytes are control words (device-scope counters the
- * kernels use to let the last workgroup finish a stage); every call leaves them at zero, so a
- * workspace is zeroed once, not per call.  A workspace serves one stream at a time. */
+ * zeros before its first use.  Its first bytes are control words (device-scope counters and
+ * completion flags the kernels use to let one workgroup finish a stage for the others; their
+ * number depends only on the layer's dims); every call that completes leaves them at zero, so
+ * a workspace is zeroed once, not per call, and may serve any layer it is large enough for.
+ * A workspace serves one stream at a time: calls that overlap on one workspace race. */
 uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens);
 
 /* Steps 1-3 for x (bf16 bit patterns, device, [T][H]) into `route` (all five pointers
