@@ -18,9 +18,9 @@
 //   The activation tile of each 128-value K step is staged in LDS (double-buffered) and read
 //   by all waves; 16-row subtiles past the group's last row are skipped.  Loads run two
 //   steps ahead of the matrix work, and two workgroups share a CU.
-// * Workgroup b takes N-tile b % NT of M-tile b / NT.  Workgroups reach the 8 XCDs
-//   round-robin, so when NT is a multiple of 8 every XCD streams a fixed slice of columns of
-//   every expert and no expert's weight tile is fetched by two XCDs.
+// * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes the M-tiles 8i + x, every
+//   column slice of each in turn: an M-tile's activation rows are fetched into one XCD's L2
+//   only, and with small batches (one M-tile per expert) the XCDs stream different experts.
 #include "common.h"
 
 namespace moe {
@@ -225,7 +225,9 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     float* __restrict__ staging, int T, int k, int N, int R, int NT) {
   constexpr int NM = GATEUP ? 2 : 1;
   __shared__ ATile<SH> tile[2];
-  const int mt = blockIdx.x / NT, nt = blockIdx.x - mt * NT;
+  // XCD x (= b % 8) takes the M-tiles mt = 8i + x, all NT column slices of each
+  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
+  const int mt = (jj / NT) * 8 + xcd, nt = jj % NT;
   if (mt >= info[1]) return;
   // tile metadata is the same for every lane: keep it in scalar registers
   const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
@@ -386,7 +388,7 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int R = T * (d.K + d.S);
   const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H};
   const int tk = timing_begin("gemm_gateup", s);
-  gemm_f8f4_kernel<true, GateUpShape><<<mt_bound * NT, GateUpShape::NTH, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
+  gemm_f8f4_kernel<true, GateUpShape><<<(mt_bound + 7) / 8 * 8 * NT, GateUpShape::NTH, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
                                                        b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
                                                        b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, T, d.K, d.I,
                                                        R, NT);
@@ -401,7 +403,7 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
   const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
   const int tk = timing_begin("gemm_down", s);
-  gemm_f8f4_kernel<false, DownShape><<<mt_bound * NT, DownShape::NTH, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
+  gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
                                                         b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
                                                         b.grp_rows, nullptr, b.staging, T, d.K, d.H, R, NT);
   timing_end(tk, s);
