@@ -52,7 +52,15 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   moe::CallBufs t{};
   // control words first: their offset must not depend on T (zero between calls)
   t.ctrl = reinterpret_cast<int32_t*>(take((size_t)moe::ctrl_layout(d.H, d.E, d.S, d.I).words * 4));
-  t.logits = reinterpret_cast<float*>(take((size_t)T * d.E * 4));
+  // partial scores: the largest slices x tokens over the batch sizes up to T (slices only change
+  // at multiples of 64 tokens, and within such a range the product grows with the tokens)
+  size_t score_rows = (size_t)T;
+  if (!moe::route_fused(d, T))
+    for (int t = 64; t <= T + 63; t += 64) {
+      const int tt = t < T ? t : T;
+      score_rows = std::max(score_rows, (size_t)tt * moe::router_slices(d, tt));
+    }
+  t.logits = reinterpret_cast<float*>(take(score_rows * d.E * 4));
   t.idx = reinterpret_cast<int32_t*>(take(tk * 4));
   t.w = reinterpret_cast<float*>(take(tk * 4));
   t.counts = reinterpret_cast<int32_t*>(take((size_t)d.E * 4));

@@ -217,7 +217,7 @@ struct Dims {
 
 // Device buffers of one call, carved from the workspace (and the caller's route buffers).
 struct CallBufs {
-  float* logits;      // [T][E]
+  float* logits;      // [T][E] scores (fused routing), or [slices][T][E] partial scores
   int32_t* idx;       // [T][k]
   float* w;           // [T][k]
   int32_t* counts;    // [E]
@@ -248,6 +248,16 @@ void timing_end(int token, hipStream_t s);
 constexpr int kFusedMaxT = 64;
 constexpr int kTailScores = 8192;
 inline bool route_fused(const Dims& d, int T) { return T <= kFusedMaxT && T * d.E <= kTailScores; }
+// Router GEMM of larger batches: the hidden axis is cut into router_slices(T, E) slices, one
+// workgroup per (64-token tile, 64-expert tile, slice), so even a few token tiles fill the
+// GPU; the slices' partial scores ([slices][T][E]) are added in slice order by the top-k.
+constexpr int kRouterMaxSlices = 16;
+inline int router_slices(const Dims& d, int T) {
+  const int tiles = ((T + 63) / 64) * ((d.E + 63) / 64);
+  int ks = (512 + tiles - 1) / tiles;
+  ks = ks < 1 ? 1 : (ks > kRouterMaxSlices ? kRouterMaxSlices : ks);
+  return ks < d.H / 32 ? ks : d.H / 32;
+}
 // Layers whose decode launch also routes (the routing tail inside it ranks up to 256 experts).
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 const CallBufs& b, int T, bool quantize_x, hipStream_t s);

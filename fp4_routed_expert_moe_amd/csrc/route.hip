@@ -104,7 +104,39 @@ __device__ __forceinline__ void split3(const float4& p, const float4& r, bf16x8 
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           const float* __restrict__ bias,
-                                                          float* __restrict__ logits, int T, int E, int H) {
+                                                          float* __restrict__ logits, uint8_t* __restrict__ xq,
+                                                          uint64_t* __restrict__ gmask, int T, int E, int H) {
+  // hidden-axis slice blockIdx.z of gridDim.z (whole 32-value steps); its partial scores go to
+  // logits[slice][T][E], the bias into slice 0's
+  const int nk = H >> 5, ks = blockIdx.z, KS = gridDim.z;
+  const int k_lo = 32 * (ks * nk / KS), k_hi = 32 * ((ks + 1) * nk / KS);
+  logits += (size_t)ks * T * E;
+  {
+    // clear the per-chunk expert masks the top-k ORs its bits into
+    const size_t nmask = (size_t)((T + kChunk - 1) / kChunk) * E;
+    const size_t wg = ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const size_t nwg = (size_t)gridDim.x * gridDim.y * gridDim.z;
+    for (size_t i = wg * 256 + threadIdx.x; i < nmask; i += nwg * 256) gmask[i] = 0ull;
+  }
+  if (xq) {
+    // the FP8 term split of this token tile's x over this slice, shared by the expert tiles
+    const int tt0 = blockIdx.x * kRouterGemmTile, ntt = min(kRouterGemmTile, T - tt0);
+    const int b_lo = k_lo >> 5, nb = (k_hi - k_lo) >> 5, KB = H >> 5;
+    for (int j = blockIdx.y * 256 + threadIdx.x; j < ntt * nb; j += 256 * gridDim.y) {
+      const int t = tt0 + j / nb, bb = b_lo + j % nb;
+      const XBlock q = quantize_x_block(x + (size_t)t * H + bb * 32);
+      uint4* hi = reinterpret_cast<uint4*>(xq + (size_t)t * H + bb * 32);
+      uint4* lo = reinterpret_cast<uint4*>(xq + (size_t)(T + t) * H + bb * 32);
+      hi[0] = q.hi[0];
+      hi[1] = q.hi[1];
+      lo[0] = q.lo[0];
+      lo[1] = q.lo[1];
+      uint8_t* xs = xq + (size_t)2 * T * H + (size_t)t * kb_pad(H);
+      xs[bb] = (uint8_t)q.s;
+      if (bb == KB - 1)  // pad bytes of the row (finite; they only meet zero weights)
+        for (int jj = KB; jj < kb_pad(H); ++jj) xs[jj] = (uint8_t)127;
+    }
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * kRouterGemmTile + (wave & 1) * 32;
@@ -122,13 +154,13 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int U = 4;  // 32-value K steps loaded together
-  for (int k0 = 0; k0 < H; k0 += 32 * U) {
+  for (int k0 = k_lo; k0 < k_hi; k0 += 32 * U) {
     uint4 xr[U][2];
     float4 wv[U][2][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 32 * u;
-      if (k < H) {
+      if (k < k_hi) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           xr[u][i] = *reinterpret_cast<const uint4*>(xa[i] + k);
@@ -139,7 +171,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (k0 + 32 * u >= H) break;
+      if (k0 + 32 * u >= k_hi) break;
       bf16x8 bt[2][3];
 #pragma unroll
       for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
@@ -159,7 +191,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     for (int j = 0; j < 2; ++j) {
       const int e = e0 + 16 * j + r;
       if (e >= E) continue;
-      const float be = bias ? bias[e] : 0.f;
+      const float be = bias && ks == 0 ? bias[e] : 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + 16 * i + 4 * kq + v;
@@ -168,70 +200,52 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     }
 }
 
-// FP8 term split of x for the expert kernels (larger batches; small ones do it in the
-// router kernel): one thread per 32-value block.
-__global__ __launch_bounds__(256) void quantize_x_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
-                                                         int T, int H) {
-  const int KB = H >> 5;
-  const size_t j = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= (size_t)T * KB) return;
-  const size_t t = j / KB, bb = j % KB;
-  const XBlock q = quantize_x_block(x + t * H + bb * 32);
-  uint4* hi = reinterpret_cast<uint4*>(xq + t * H + bb * 32);
-  uint4* lo = reinterpret_cast<uint4*>(xq + ((size_t)T + t) * H + bb * 32);
-  hi[0] = q.hi[0];
-  hi[1] = q.hi[1];
-  lo[0] = q.lo[0];
-  lo[1] = q.lo[1];
-  uint8_t* xs = xq + (size_t)2 * T * H + t * kb_pad(H);
-  xs[bb] = (uint8_t)q.s;
-  if ((int)bb == KB - 1)  // pad bytes of the row (finite; they only meet zero weights)
-    for (int j = KB; j < kb_pad(H); ++j) xs[j] = (uint8_t)127;
-}
-
 // ------------------------------------------------------------------------------------
 // Any T: per-chunk top-k + masks, one-workgroup table build, per-chunk stable scatter.
 // ------------------------------------------------------------------------------------
 constexpr int kChunkThreads = 1024;
 
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(const float* __restrict__ logits, int T, int E,
-                                                                   int k, int32_t* __restrict__ idx,
+// One workgroup per kTopkTokens tokens, one wave per token; the tokens' bits of the per-chunk
+// expert masks are ORed into gmask (cleared by the router GEMM earlier in the call).
+constexpr int kTopkTokens = kChunkThreads / 64;
+
+__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(const float* __restrict__ logits, int KS, int T,
+                                                                   int E, int k, int32_t* __restrict__ idx,
                                                                    float* __restrict__ w,
                                                                    uint64_t* __restrict__ gmask) {
   __shared__ uint64_t mask[1024];
-  __shared__ uint16_t sel_e[kChunk * 32];
-  __shared__ float sel_w[kChunk * 32];
-  const int c = blockIdx.x;
+  __shared__ uint16_t sel_e[kTopkTokens * 1024];
+  __shared__ float sel_w[kTopkTokens * 1024];
   for (int e = threadIdx.x; e < E; e += kChunkThreads) mask[e] = 0ull;
   __syncthreads();
-  const size_t t0 = (size_t)c * kChunk;
-  const int nt = min(kChunk, T - (int)t0);
-  // picks of up to 32 tokens at a time in LDS, then written out
-  const int tpass = max(1, min(nt, (kChunk * 32) / k));
-  for (int p0 = 0; p0 < nt; p0 += tpass) {
-    const int np = min(tpass, nt - p0);
-    const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < np; t += kChunkThreads / 64) {
-      const float* row = logits + (t0 + p0 + t) * E;
-      if (E <= 64)
-        topk_wave<1>(row, E, k, sel_e + t * k, sel_w + t * k, mask, p0 + t);
-      else if (E <= 128)
-        topk_wave<2>(row, E, k, sel_e + t * k, sel_w + t * k, mask, p0 + t);
-      else if (E <= 256)
-        topk_wave<4>(row, E, k, sel_e + t * k, sel_w + t * k, mask, p0 + t);
-      else if (E <= 512)
-        topk_wave<8>(row, E, k, sel_e + t * k, sel_w + t * k, mask, p0 + t);
-      else
-        topk_wave<16>(row, E, k, sel_e + t * k, sel_w + t * k, mask, p0 + t);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < np * k; i += kChunkThreads) {
-      idx[(t0 + p0) * k + i] = sel_e[i];
-      w[(t0 + p0) * k + i] = sel_w[i];
-    }
-    __syncthreads();
+  const size_t t0 = (size_t)blockIdx.x * kTopkTokens;
+  const int nt = min(kTopkTokens, T - (int)t0);
+  const int wave = threadIdx.x >> 6;
+  const int tbit = (int)(t0 % kChunk) + wave;  // bit of this token in its chunk's masks
+  if (wave < nt) {
+    const float* row = logits + (t0 + wave) * E;
+    const size_t st = (size_t)T * E;
+    uint16_t* se = sel_e + wave * k;
+    float* sw = sel_w + wave * k;
+    if (E <= 64)
+      topk_wave<1>(row, E, k, se, sw, mask, tbit, KS, st);
+    else if (E <= 128)
+      topk_wave<2>(row, E, k, se, sw, mask, tbit, KS, st);
+    else if (E <= 256)
+      topk_wave<4>(row, E, k, se, sw, mask, tbit, KS, st);
+    else if (E <= 512)
+      topk_wave<8>(row, E, k, se, sw, mask, tbit, KS, st);
+    else
+      topk_wave<16>(row, E, k, se, sw, mask, tbit, KS, st);
   }
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) gmask[(size_t)c * E + e] = mask[e];
+  __syncthreads();
+  for (int i = threadIdx.x; i < nt * k; i += kChunkThreads) {
+    idx[t0 * k + i] = sel_e[i];
+    w[t0 * k + i] = sel_w[i];
+  }
+  uint64_t* gm = gmask + (t0 / kChunk) * E;
+  for (int e = threadIdx.x; e < E; e += kChunkThreads)
+    if (mask[e]) atomicOr(reinterpret_cast<unsigned long long*>(gm + e), (unsigned long long)mask[e]);
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(CallBufs b, int T, int E, int k, int S, int C) {
@@ -276,15 +290,11 @@ hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* w
     timing_end(tk, s);
     return hipGetLastError();
   }
-  dim3 grid((T + kRouterGemmTile - 1) / kRouterGemmTile, (d.E + kRouterGemmTile - 1) / kRouterGemmTile);
-  int tk = timing_begin("router_gemm", s);
-  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, T, d.E, d.H);
-  timing_end(tk, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !quantize_x) return e;
-  const size_t blocks = (size_t)T * (d.H / 32);
-  tk = timing_begin("quantize_x", s);
-  quantize_x_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(x, b.xq, T, d.H);
+  dim3 grid((T + kRouterGemmTile - 1) / kRouterGemmTile, (d.E + kRouterGemmTile - 1) / kRouterGemmTile,
+            router_slices(d, T));
+  const int tk = timing_begin("router_gemm", s);
+  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, quantize_x ? b.xq : nullptr, b.gmask, T, d.E,
+                                          d.H);
   timing_end(tk, s);
   return hipGetLastError();
 }
@@ -292,7 +302,8 @@ hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* w
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s) {
   const int C = (T + kChunk - 1) / kChunk;
   int tk = timing_begin("topk_chunk", s);
-  topk_chunk_kernel<<<C, kChunkThreads, 0, s>>>(b.logits, T, d.E, d.K, b.idx, b.w, b.gmask);
+  topk_chunk_kernel<<<(T + kTopkTokens - 1) / kTopkTokens, kChunkThreads, 0, s>>>(b.logits, router_slices(d, T), T,
+                                                                                 d.E, d.K, b.idx, b.w, b.gmask);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -162,15 +162,38 @@ __device__ __forceinline__ float hi_value(uint32_t hi) {
 // Every pick is wave-uniform.  The picks and their weights (softmax over the k picked scores,
 // summed in a fixed order) go to sel_e[0..k) / sel_w[0..k) in LDS, and bit `tbit` of mask[e]
 // is set for each pick; the caller writes the results out.
+// The score of expert e is row[e] (nparts = 1) or the sum of nparts partial scores
+// row[p*stride + e], added in p order.
 template <int Q>
 __device__ __forceinline__ void topk_wave(const float* row, int E, int k, uint16_t* sel_e, float* sel_w,
-                                          uint64_t* mask, int tbit) {
+                                          uint64_t* mask, int tbit, int nparts = 1, size_t stride = 0) {
   const int lane = threadIdx.x & 63;
+  float v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < E ? row[e] : 0.f;
+  }
+  for (int p0 = 1; p0 < nparts; p0 += 4) {  // four partials' loads in flight at a time
+    float pv[4][Q];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        pv[u][q] = p0 + u < nparts && e < E ? row[(p0 + u) * stride + e] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (p0 + u < nparts) v[q] += pv[u][q];
+  }
   uint64_t key[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int e = lane + 64 * q;
-    key[q] = e < E ? rank_key(row[e], e) : 0ull;
+    key[q] = e < E ? rank_key(v[q], e) : 0ull;
   }
   // descending order within the lane (odd-even transposition: Q rounds)
 #pragma unroll
