@@ -248,23 +248,33 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(const float* 
     if (mask[e]) atomicOr(reinterpret_cast<unsigned long long*>(gm + e), (unsigned long long)mask[e]);
 }
 
+// Per expert: the prefix over the chunks of its pick counts (16 chunks' masks loaded at a
+// time), then the grouping tables.
 __global__ __launch_bounds__(1024) void route_scan_kernel(CallBufs b, int T, int E, int k, int S, int C) {
-  __shared__ int cnt[1024], offs[1024], act[1024];
+  __shared__ int cnt[1024], offs[1024], act[1024], mt_off[1024];
   __shared__ GroupScan gs;
   const int e = threadIdx.x;
   if (e < E) {
+    const uint64_t* __restrict__ gm = b.gmask;
+    int32_t* __restrict__ cb = b.cbase;
     int c = 0;
-    for (int ch = 0; ch < C; ++ch) {
-      b.cbase[(size_t)ch * E + e] = c;
-      c += __popcll(b.gmask[(size_t)ch * E + e]);
+    for (int ch0 = 0; ch0 < C; ch0 += 16) {
+      uint64_t mv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mv[u] = ch0 + u < C ? gm[(size_t)(ch0 + u) * E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (ch0 + u < C) cb[(size_t)(ch0 + u) * E + e] = c;
+        c += __popcll(mv[u]);
+      }
     }
     cnt[e] = c;
     offs[e] = c;
   }
   __syncthreads();
-  if (threadIdx.x < 64) group_scan_wave<true>(offs, act, &gs, T, E, S, b);
+  if (threadIdx.x < 64) group_scan_wave<true>(offs, act, mt_off, &gs, T, E, S);
   __syncthreads();
-  write_tables<1024>([&](int i) { return cnt[i]; }, offs, act, gs, T, E, k, S, b);
+  write_tables<1024, true>([&](int i) { return cnt[i]; }, offs, act, mt_off, gs, T, E, k, S, b);
 }
 
 __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, int E, int k) {

@@ -314,12 +314,14 @@ __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
 }
 
 struct GroupScan {
-  int nact, total, nmt;
+  int nact, total, nmt, nmt_routed;
 };
 
+// One wave: rows and M-tiles of each expert -> first grouped row (cnt_offs[e], in place), the
+// active-expert list, each expert's first M-tile (mt_off[e], when MTILES) and the totals.
 template <bool MTILES>
-__device__ __forceinline__ void group_scan_wave(int* cnt_offs, int* act, GroupScan* gs, int T, int E, int S,
-                                                const CallBufs& b) {
+__device__ __forceinline__ void group_scan_wave(int* cnt_offs, int* act, int* mt_off, GroupScan* gs, int T, int E,
+                                                int S) {
   const int lane = threadIdx.x & 63;
   const int J = (E + 63) >> 6;
   const int e0 = lane * J;
@@ -344,50 +346,57 @@ __device__ __forceinline__ void group_scan_wave(int* cnt_offs, int* act, GroupSc
     cnt_offs[e] = off;
     off += c;
     if (c > 0) act[apos++] = e;
-    if (MTILES)
-      for (int m = 0; m < (c + kGemmBM - 1) / kGemmBM; ++m) {
-        st_agent(b.mt_group + mpos, e);
-        st_agent(b.mt_row0 + mpos++, m * kGemmBM);
-      }
-  }
-  const int mt_shared = S ? (T + kGemmBM - 1) / kGemmBM : 0;
-  if (MTILES)
-    for (int i = lane; i < mt_shared; i += 64) {
-      st_agent(b.mt_group + nmt + i, E);
-      st_agent(b.mt_row0 + nmt + i, i * kGemmBM);
+    if (MTILES) {
+      mt_off[e] = mpos;
+      mpos += (c + kGemmBM - 1) / kGemmBM;
     }
+  }
   if (lane == 0) {
     gs->nact = nact;
     gs->total = total;
-    gs->nmt = nmt + mt_shared;
+    gs->nmt = nmt + (MTILES && S ? (T + kGemmBM - 1) / kGemmBM : 0);
+    gs->nmt_routed = nmt;
   }
 }
 
-// counts, offsets, group rows and first rows, the active list (shared expert last) and the
-// info words, from the scan's LDS results (cnt[e] = rows of expert e, offs[e] = its first row).
-template <int NT, class CNT>
-__device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, const int* act, const GroupScan& gs,
-                                             int T, int E, int K, int S, const CallBufs& b) {
+// The tables the expert kernels read, from the scan's LDS results (cnt(e) = rows of expert e,
+// offs[e] = its first row, mt_off[e] = its first M-tile): counts, offsets, group rows and first
+// rows, the active list (shared expert last), the M-tile list (a wave per expert, its lanes
+// over the expert's tiles) and the info words.  Only later kernels read them: plain stores.
+template <int NT, bool MTILES, class CNT>
+__device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, const int* act, const int* mt_off,
+                                             const GroupScan& gs, int T, int E, int K, int S, const CallBufs& b) {
   for (int e = threadIdx.x; e < E; e += NT) {
     const int c = cnt(e), o = offs[e];
-    st_agent(b.counts + e, c);
-    st_agent(b.offsets + e, o);
-    st_agent(b.grp_row0 + e, o);
-    st_agent(b.grp_rows + e, c);
+    b.counts[e] = c;
+    b.offsets[e] = o;
+    b.grp_row0[e] = o;
+    b.grp_rows[e] = c;
   }
-  for (int a = threadIdx.x; a < gs.nact; a += NT) {
-    const int e = act[a];
-    st_agent(b.act + a, e);
+  for (int a = threadIdx.x; a < gs.nact; a += NT) b.act[a] = act[a];
+  if (MTILES) {
+    const int lane = threadIdx.x & 63;
+    for (int e = threadIdx.x >> 6; e < E; e += NT / 64) {
+      const int nm = (cnt(e) + kGemmBM - 1) / kGemmBM, m0 = mt_off[e];
+      for (int m = lane; m < nm; m += 64) {
+        b.mt_group[m0 + m] = e;
+        b.mt_row0[m0 + m] = m * kGemmBM;
+      }
+    }
+    for (int i = threadIdx.x; i < gs.nmt - gs.nmt_routed; i += NT) {
+      b.mt_group[gs.nmt_routed + i] = E;
+      b.mt_row0[gs.nmt_routed + i] = i * kGemmBM;
+    }
   }
   if (threadIdx.x == 0) {
-    st_agent(b.offsets + E, gs.total);
+    b.offsets[E] = gs.total;
     if (S) {
-      st_agent(b.grp_row0 + E, T * K);
-      st_agent(b.grp_rows + E, T);
-      st_agent(b.act + gs.nact, E);
+      b.grp_row0[E] = T * K;
+      b.grp_rows[E] = T;
+      b.act[gs.nact] = E;
     }
-    st_agent(b.info + 0, gs.nact + S);
-    st_agent(b.info + 1, gs.nmt);
+    b.info[0] = gs.nact + S;
+    b.info[1] = gs.nmt;
   }
 }
 
@@ -405,7 +414,8 @@ struct TailLayout {
   static constexpr int kMask = (kSelW + MAXTK * 4 + 7) / 8 * 8;  // u64 [MAXE] bit t: token t picked e
   static constexpr int kOffs = kMask + MAXE * 8;          // i32 [MAXE]
   static constexpr int kAct = kOffs + MAXE * 4;           // i32 [MAXE]
-  static constexpr int kScan = kAct + MAXE * 4;           // GroupScan
+  static constexpr int kMtOff = kAct + MAXE * 4;          // i32 [MAXE]
+  static constexpr int kScan = kMtOff + MAXE * 4;         // GroupScan
   static constexpr int kBytes = kScan + 16;
 };
 
@@ -418,6 +428,7 @@ __device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int 
   uint64_t* mask = reinterpret_cast<uint64_t*>(lds + L::kMask);
   int* offs = reinterpret_cast<int*>(lds + L::kOffs);
   int* act = reinterpret_cast<int*>(lds + L::kAct);
+  int* mt_off = reinterpret_cast<int*>(lds + L::kMtOff);
   GroupScan* gs = reinterpret_cast<GroupScan*>(lds + L::kScan);
   const int tid = threadIdx.x;
   const int n = T * E;
@@ -441,18 +452,18 @@ __device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int 
   __syncthreads();
   for (int i = tid; i < E; i += NT) offs[i] = __popcll(mask[i]);
   __syncthreads();
-  if (tid < 64) group_scan_wave<MTILES>(offs, act, gs, T, E, S, b);
+  if (tid < 64) group_scan_wave<MTILES>(offs, act, mt_off, gs, T, E, S);
   __syncthreads();
-  write_tables<NT>([&](int e) { return __popcll(mask[e]); }, offs, act, *gs, T, E, K, S, b);
+  write_tables<NT, MTILES>([&](int e) { return __popcll(mask[e]); }, offs, act, mt_off, *gs, T, E, K, S, b);
   // pick i = t*K + j lands after the rows of lower tokens routed to the same expert
   for (int i = tid; i < T * K; i += NT) {
     const int t = i / K, e = sel_e[i];
     const float w = sel_w[i];
     const int r = offs[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
-    st_agent(b.idx + i, e);
-    st_agent(b.w + i, w);
-    st_agent(b.perm + r, (int32_t)i);
-    st_agent(b.row_w + r, w);
+    b.idx[i] = e;
+    b.w[i] = w;
+    b.perm[r] = (int32_t)i;
+    b.row_w[r] = w;
   }
 }
 
