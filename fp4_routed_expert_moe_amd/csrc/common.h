@@ -67,16 +67,6 @@ __device__ __forceinline__ void wait_stores() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
 }
-// Called by all threads after their agent-scope stores; true in every thread of the
-// workgroup that arrives last among `total`.  That workgroup resets the counter when done.
-__device__ __forceinline__ bool arrive_last(int32_t* counter, int total, int* lds_flag) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *lds_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
-  __syncthreads();
-  return *lds_flag != 0;
-}
 __device__ __forceinline__ void reset_counter(int32_t* counter) {
   __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -260,7 +250,7 @@ inline int router_slices(const Dims& d, int T) {
 }
 // Layers whose decode launch also routes (the routing tail inside it ranks up to 256 experts).
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, hipStream_t s);
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
 // The whole layer for a small batch in one launch (decode.hip).  With `route_inside` the

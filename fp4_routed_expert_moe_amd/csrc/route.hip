@@ -23,21 +23,30 @@ constexpr int kRouterEPB = kTailThreads / 64 / kScoreWaves;  // experts per rout
 
 using RouterTail = TailLayout<1024, kTailScores>;
 
+// flags: kRouteQuantize = also split x into FP8 terms (the workgroups that are not last, after
+// publishing their scores, so the split never delays the routing); kRouteMTiles = also build
+// the grouped GEMM's M-tile list.
+constexpr int kRouteQuantize = 1, kRouteMTiles = 2;
+
 __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ wr,
                                                              const float* __restrict__ bias, CallBufs b, int T,
-                                                             int E, int H, int K, int S, int quantize) {
+                                                             int E, int H, int K, int S, int flags) {
   __shared__ __align__(16) char lds[RouterTail::kBytes];
   const int t0 = blockIdx.y * kScoreTT;
   const int nt = min(kScoreTT, T - t0);
   const int wave = threadIdx.x >> 6;
-  if (quantize) {
-    // the token tile's nt*KB blocks, an equal slice per expert workgroup (a few per workgroup)
+  __shared__ float part[kRouterEPB][kScoreWaves * kScoreTT];
+  const int grp = wave / kScoreWaves;
+  const int e = blockIdx.x * kRouterEPB + grp;
+  score_expert(x, wr, bias, b.logits, t0, nt, e, e < E, E, H, part[grp]);
+  // the x split: slice `part` of `parts` of all T*KB blocks
+  auto quantize = [&](int slice, int parts) {
     const int KB = H >> 5;
-    const int nb = nt * KB, per = (nb + gridDim.x - 1) / gridDim.x;
+    const int nb = T * KB, per = (nb + parts - 1) / parts;
     uint8_t* xq = b.xq;
-    for (int j = blockIdx.x * per + threadIdx.x; j < min(nb, ((int)blockIdx.x + 1) * per); j += kTailThreads) {
-      const int t = t0 + j / KB, bb = j % KB;
+    for (int j = slice * per + threadIdx.x; j < min(nb, (slice + 1) * per); j += kTailThreads) {
+      const int t = j / KB, bb = j % KB;
       const XBlock q = quantize_x_block(x + (size_t)t * H + bb * 32);
       uint4* hi = reinterpret_cast<uint4*>(xq + (size_t)t * H + bb * 32);
       uint4* lo = reinterpret_cast<uint4*>(xq + (size_t)(T + t) * H + bb * 32);
@@ -48,19 +57,28 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
       uint8_t* xs = xq + (size_t)2 * T * H + (size_t)t * kb_pad(H);
       xs[bb] = (uint8_t)q.s;
       if (bb == KB - 1)  // pad bytes of the row (finite; they only meet zero weights)
-        for (int j = KB; j < kb_pad(H); ++j) xs[j] = (uint8_t)127;
+        for (int jj = KB; jj < kb_pad(H); ++jj) xs[jj] = (uint8_t)127;
     }
-  }
-  __shared__ float part[kRouterEPB][kScoreWaves * kScoreTT];
-  const int grp = wave / kScoreWaves;
-  const int e = blockIdx.x * kRouterEPB + grp;
-  score_expert(x, wr, bias, b.logits, t0, nt, e, e < E, E, H, part[grp]);
-  // the last workgroup to finish routes the whole batch, then re-arms the counter
-  __shared__ int is_last;
+  };
+  // The last workgroup to finish routes the whole batch, then re-arms the counter; the others
+  // split x, one slice per arrival ticket.
+  __shared__ int ticket;
   int32_t* counter = b.ctrl + CtrlLayout::kRoute;
-  if (!arrive_last(counter, (int)(gridDim.x * gridDim.y), &is_last)) return;
-  route_tail<kTailThreads, 16, 1024, kTailScores, true>(b, T, E, K, S, lds);
+  const int total = (int)(gridDim.x * gridDim.y);
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) ticket = add_agent(counter, 1);
+  __syncthreads();
+  if (ticket < total - 1) {
+    if (flags & kRouteQuantize) quantize(ticket, total - 1);
+    return;
+  }
+  if (flags & kRouteMTiles)
+    route_tail<kTailThreads, 16, 1024, kTailScores, true>(b, T, E, K, S, lds);
+  else
+    route_tail<kTailThreads, 16, 1024, kTailScores, false>(b, T, E, K, S, lds);
   if (threadIdx.x == 0) reset_counter(counter);
+  if ((flags & kRouteQuantize) && total == 1) quantize(0, 1);
 }
 
 // ------------------------------------------------------------------------------------
@@ -292,11 +310,12 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, hipStream_t s) {
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, hipStream_t s) {
   if (route_fused(d, T)) {
     dim3 grid((d.E + kRouterEPB - 1) / kRouterEPB, (T + kScoreTT - 1) / kScoreTT);
     const int tk = timing_begin("router_route", s);
-    router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, quantize_x ? 1 : 0);
+    const int flags = (quantize_x ? kRouteQuantize : 0) | (mtiles ? kRouteMTiles : 0);
+    router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, flags);
     timing_end(tk, s);
     return hipGetLastError();
   }
