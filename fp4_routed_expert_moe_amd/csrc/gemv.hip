@@ -29,9 +29,6 @@
 namespace moe {
 
 constexpr int kSkM = 16;    // tokens per pass (MFMA M)
-#ifndef MOE_GEMV_TILES
-#define MOE_GEMV_TILES 4
-#endif
 #ifndef MOE_GEMV_SPLIT
 #define MOE_GEMV_SPLIT 4
 #endif
@@ -40,8 +37,9 @@ constexpr int kSkM = 16;    // tokens per pass (MFMA M)
 #endif
 constexpr int kHTerms = MOE_DEC_HTERMS;  // FP8 terms of h between gate/up and down (2 or 3)
 static_assert(kHTerms == 2 || kHTerms == 3, "h term count");
-constexpr int kTiles = MOE_GEMV_TILES;  // 16-row MFMA column tiles per wave (even)
-constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per workgroup = reduction-axis slices (>= kTiles)
+constexpr int kSplit = MOE_GEMV_SPLIT;  // waves per gate/up workgroup = reduction-axis slices
+// TL = 16-row MFMA column tiles per wave (4, or 2 / 1 when few groups are active: more
+// workgroups over the same bytes); all TL tiles share one scale dword.
 
 // One K iteration (4 blocks = 128 values) of a wave's operands.  Weights come through buffer
 // descriptors spanning one group's matrix: a fixed per-lane offset and the K position as a
@@ -52,10 +50,10 @@ constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit d
 constexpr int kWeightAux = 2;             // nontemporal: the weights are streamed once
 constexpr int kOutOfRange = 1 << 30;      // added to a lane's buffer offset: reads zeros
 
-template <int NM, int NA>
+template <int NM, int NA, int TL>
 struct GFrag {
-  i32x4 c[NM][kTiles];
-  int s[NM];  // byte j: scale of column tile j
+  i32x4 c[NM][TL];
+  int s[NM];  // byte sel + j: scale of column tile j
   i32x4 a[NA][2];
   int sa;
 };
@@ -63,6 +61,7 @@ template <int NM>
 struct GSrc {
   __amdgpu_buffer_rsrc_t c[NM], s[NM];
   int voff_c, voff_s;  // column tile 0, K block q, K iteration 0 (tile j is 16 columns on)
+  int sel;             // byte of tile 0 in the lane's scale dword
 };
 // Matrix mtx's columns start at n0 + mtx * col_step (col_step a multiple of 64): gate and up
 // use the same columns of two matrices, down two adjacent 64-column blocks of one.
@@ -80,10 +79,11 @@ __device__ __forceinline__ void gsrc_init(GSrc<NM>& src, const uint8_t* const* c
   }
   // columns past N read other bytes of the group (or zeros past its end); they are not stored
   src.voff_c = (q * N + n0 + m) * 16;
-  src.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;  // n0 is a multiple of 64
+  src.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;  // n0 is a multiple of 16
+  src.sel = (n0 >> 4) & 3;
 }
-template <int NM, int NA>
-__device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, int N, const uint8_t* const* arow,
+template <int NM, int NA, int TL>
+__device__ __forceinline__ void gv_load(GFrag<NM, NA, TL>& f, const GSrc<NM>& src, int N, const uint8_t* const* arow,
                                         const uint8_t* asc, int K, int it, int q) {
   const int kb = 4 * it;
   const int so_c = __builtin_amdgcn_readfirstlane(kb * N * 16);
@@ -96,7 +96,7 @@ __device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, i
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j)
+    for (int j = 0; j < TL; ++j)
       f.c[mtx][j] = __builtin_bit_cast(
           i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], voff_c + 256 * j, so_c, kWeightAux));
     f.s[mtx] = __builtin_amdgcn_raw_buffer_load_b32(src.s[mtx], src.voff_s, so_s, kWeightAux);
@@ -114,53 +114,56 @@ __device__ __forceinline__ void gv_load(GFrag<NM, NA>& f, const GSrc<NM>& src, i
   f.sa = asc[min(kb + q, (K >> 5) - 1)];
 }
 // acc[mtx][j] += sum over the NA terms of A(term) x B(mtx, tile j); term t has scale sa - 4t.
-template <int NM, int NA>
-__device__ __forceinline__ void gv_mma(const GFrag<NM, NA>& f, f32x4 (&acc)[NM][kTiles]) {
+template <int NM, int NA, int TL>
+__device__ __forceinline__ void gv_mma(const GFrag<NM, NA, TL>& f, f32x4 (&acc)[NM][TL], int sel) {
   i32x8 a[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
-  static_assert(kTiles == 4 && kSplit >= 2, "one scale dword covers four 16-row column tiles");
+  static_assert(TL == 1 || TL == 2 || TL == 4, "a wave's tiles share one scale dword");
 #pragma unroll
   for (int mtx = 0; mtx < NM; ++mtx) {
-    i32x8 b[kTiles];
+    const int sb = TL == 4 ? f.s[mtx] : (int)((uint32_t)f.s[mtx] >> (8 * sel));  // tile j at byte j
+    i32x8 b[TL];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j)
+    for (int j = 0; j < TL; ++j)
       b[j] = __builtin_shufflevector(f.c[mtx][j], f.c[mtx][j], 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       const int sa = f.sa - 4 * t;
-      acc[mtx][0] = mma_f8f4_sb<0>(a[t], b[0], acc[mtx][0], sa, f.s[mtx]);
-      acc[mtx][1] = mma_f8f4_sb<1>(a[t], b[1], acc[mtx][1], sa, f.s[mtx]);
-      acc[mtx][2] = mma_f8f4_sb<2>(a[t], b[2], acc[mtx][2], sa, f.s[mtx]);
-      acc[mtx][3] = mma_f8f4_sb<3>(a[t], b[3], acc[mtx][3], sa, f.s[mtx]);
+      acc[mtx][0] = mma_f8f4_sb<0>(a[t], b[0], acc[mtx][0], sa, sb);
+      if constexpr (TL > 1) acc[mtx][1] = mma_f8f4_sb<1>(a[t], b[1], acc[mtx][1], sa, sb);
+      if constexpr (TL > 2) {
+        acc[mtx][2] = mma_f8f4_sb<2>(a[t], b[2], acc[mtx][2], sa, sb);
+        acc[mtx][3] = mma_f8f4_sb<3>(a[t], b[3], acc[mtx][3], sa, sb);
+      }
     }
   }
 }
 // This wave's K iterations [it_lo, it_hi), the loads of iteration i+1 in flight while
 // iteration i runs on the matrix cores.
-template <int NM, int NA>
-__device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>& src, int N,
+template <int NM, int NA, int TL>
+__device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& src, int N,
                                         const uint8_t* const* arow, const uint8_t* asc, int K, int it_lo, int it_hi,
                                         int q) {
   // Every path through the loop issues the next loads before the current MFMAs (the tail
   // iterations leave by their own exits), so the wait before the MFMAs only covers the
   // older loads.
   if (it_lo >= it_hi) return;
-  GFrag<NM, NA> f[2];
-  gv_load<NM, NA>(f[0], src, N, arow, asc, K, it_lo, q);
+  GFrag<NM, NA, TL> f[2];
+  gv_load<NM, NA, TL>(f[0], src, N, arow, asc, K, it_lo, q);
   for (int it = it_lo;; it += 2) {
     if (it + 1 >= it_hi) {
-      gv_mma<NM, NA>(f[0], acc);
+      gv_mma<NM, NA, TL>(f[0], acc, src.sel);
       break;
     }
-    gv_load<NM, NA>(f[1], src, N, arow, asc, K, it + 1, q);
-    gv_mma<NM, NA>(f[0], acc);
+    gv_load<NM, NA, TL>(f[1], src, N, arow, asc, K, it + 1, q);
+    gv_mma<NM, NA, TL>(f[0], acc, src.sel);
     if (it + 2 >= it_hi) {
-      gv_mma<NM, NA>(f[1], acc);
+      gv_mma<NM, NA, TL>(f[1], acc, src.sel);
       break;
     }
-    gv_load<NM, NA>(f[0], src, N, arow, asc, K, it + 2, q);
-    gv_mma<NM, NA>(f[1], acc);
+    gv_load<NM, NA, TL>(f[0], src, N, arow, asc, K, it + 2, q);
+    gv_mma<NM, NA, TL>(f[1], acc, src.sel);
   }
 }
 
@@ -168,18 +171,20 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][kTiles], const GSrc<NM>
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
 // (h8 = [kHTerms][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
+template <int TL>
 __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
     const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, int T, int k, int H, int I, int R) {
-  __shared__ f32x4 red[kSplit][kTiles][2][64];
+  static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
+  __shared__ f32x4 red[kSplit][TL][2][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * (16 * kTiles);
+  const int n0 = blockIdx.x * (16 * TL);
   const int KB = H >> 5;
   const int NI = (KB + 3) >> 2;  // K iterations of 4 blocks
   const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
@@ -197,19 +202,19 @@ __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gem
     // lanes past the pass's tokens repeat its first token (their results are dropped)
     const int tok = row_token(perm, row0 + c0 + (m < nt ? m : 0), tk, k);
     const uint8_t* arow[2] = {x_hi + (size_t)tok * H, x_lo + (size_t)tok * H};
-    f32x4 acc[2][kTiles];
+    f32x4 acc[2][TL];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gv_pass<2, 2>(acc, src, I, arow, x_sc + (size_t)tok * kb_pad(H), H, it_lo, it_hi, q);
-    f32x4 (&ag)[kTiles] = acc[0];
-    f32x4 (&au)[kTiles] = acc[1];
+    for (int j = 0; j < TL; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gv_pass<2, 2, TL>(acc, src, I, arow, x_sc + (size_t)tok * kb_pad(H), H, it_lo, it_hi, q);
+    f32x4 (&ag)[TL] = acc[0];
+    f32x4 (&au)[TL] = acc[1];
 #pragma unroll
-    for (int j = 0; j < kTiles; ++j) {
+    for (int j = 0; j < TL; ++j) {
       red[wave][j][0][lane] = ag[j];
       red[wave][j][1][lane] = au[j];
     }
     __syncthreads();
-    if (wave < kTiles / 2) {
+    if (wave < TL / 2) {
       // wave p finishes column tiles 2p and 2p+1 = one 32-column block of h
       const int p = wave;
       float hv[2][4];
@@ -273,24 +278,25 @@ __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gem
 // ------------------------------------------------------------------------------------
 constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
 
-constexpr int kDnBlocks = 1;                     // 64-column blocks per down workgroup
-constexpr int kDnCols = kDnBlocks * 16 * kTiles;  // output columns per down workgroup
+constexpr int kDnBlocks = 1;  // column blocks (of TL tiles) per down workgroup
 #ifndef MOE_DN_SPLIT
 #define MOE_DN_SPLIT 4
 #endif
 constexpr int kDnSplit = MOE_DN_SPLIT;            // waves per down workgroup = reduction-axis slices
 constexpr int kDnThreads = 64 * kDnSplit;
-// column tiles each wave finishes (waves past the last tile only reduce)
-constexpr int kDnPerWave = kDnBlocks * kTiles > kDnSplit ? kDnBlocks * kTiles / kDnSplit : 1;
-static_assert(kDnPerWave * kDnSplit >= kDnBlocks * kTiles, "down workgroup shape");
 
+template <int TL>
 __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
     float* __restrict__ staging, float* __restrict__ y, int32_t* __restrict__ ctrl, int dn_flags, int T, int k, int S,
     int H, int I, int R) {
-  __shared__ f32x4 red[kDnSplit][kDnBlocks][kTiles][64];
+  constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
+  // column tiles each wave finishes (waves past the last tile only reduce)
+  constexpr int kDnPerWave = kDnBlocks * TL > kDnSplit ? kDnBlocks * TL / kDnSplit : 1;
+  static_assert(kDnPerWave * kDnSplit >= kDnBlocks * TL, "down workgroup shape");
+  __shared__ f32x4 red[kDnSplit][kDnBlocks][TL][64];
   const int nact = info[0];
   if ((int)blockIdx.y >= nact) return;
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   const uint8_t* codes[kDnBlocks] = {dc};
   const uint8_t* scales[kDnBlocks] = {ds};
   GSrc<kDnBlocks> src;
-  gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * kTiles);
+  gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * TL);
   const uint8_t* hs = h8 + (size_t)kHTerms * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
@@ -324,22 +330,22 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
                                     , h8 + (size_t)2 * R * I + r * I
 #endif
     };
-    f32x4 acc[kDnBlocks][kTiles];
+    f32x4 acc[kDnBlocks][TL];
 #pragma unroll
     for (int c = 0; c < kDnBlocks; ++c)
 #pragma unroll
-      for (int j = 0; j < kTiles; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    gv_pass<kDnBlocks, kHTerms>(acc, src, H, arow, hs + r * kb_pad(I), I, it_lo, it_hi, q);
+      for (int j = 0; j < TL; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gv_pass<kDnBlocks, kHTerms, TL>(acc, src, H, arow, hs + r * kb_pad(I), I, it_lo, it_hi, q);
 #pragma unroll
     for (int c = 0; c < kDnBlocks; ++c)
 #pragma unroll
-      for (int j = 0; j < kTiles; ++j) red[wave][c][j][lane] = acc[c][j];
+      for (int j = 0; j < TL; ++j) red[wave][c][j][lane] = acc[c][j];
     __syncthreads();
     // wave w finishes column tiles kDnPerWave*w .. kDnPerWave*w + kDnPerWave - 1
 #pragma unroll
     for (int u = 0; u < kDnPerWave; ++u) {
-      const int jj = kDnPerWave * wave + u, c = jj / kTiles, j = jj % kTiles;
-      if (jj >= kDnBlocks * kTiles) break;
+      const int jj = kDnPerWave * wave + u, c = jj / TL, j = jj % TL;
+      if (jj >= kDnBlocks * TL) break;
       f32x4 sum = red[0][c][j][lane];
 #pragma unroll
       for (int w = 1; w < kDnSplit; ++w) sum += red[w][c][j][lane];
@@ -377,27 +383,36 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// Few active groups (small batches) get narrower column tiles per workgroup, so the grid
+// still covers the GPU several times over.
+constexpr int kMinGemvGroups = 512;
+
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
                               int T, int max_act, hipStream_t s) {
   (void)x;
-  dim3 grid((d.I + 16 * kTiles - 1) / (16 * kTiles), max_act);
   const int R = T * (d.K + d.S);
+  const bool narrow = (size_t)max_act * ((d.I + 63) / 64) < kMinGemvGroups;
+  const int cols = narrow ? 32 : 64;
+  dim3 grid((d.I + cols - 1) / cols, max_act);
   const int tk = timing_begin("gemv_gateup", s);
-  gemv_gateup_kernel<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm,
-                                                  b.act, b.info, b.grp_row0, b.grp_rows,
-                                                  static_cast<uint8_t*>(b.h), T, d.K, d.H, d.I, R);
+  auto kern = narrow ? gemv_gateup_kernel<2> : gemv_gateup_kernel<4>;
+  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.act, b.info,
+                                    b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), T, d.K, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T,
                             int max_act, hipStream_t s) {
-  dim3 grid((d.H + kDnCols - 1) / kDnCols, max_act);
   const int R = T * (d.K + d.S);
+  // (narrower down tiles measured slower: a down workgroup's bytes are already few)
+  constexpr int kCols = kDnBlocks * 16 * 4;
+  dim3 grid((d.H + kCols - 1) / kCols, max_act);
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm,
-                                                b.row_w, b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, b.ctrl,
-                                                CtrlLayout::kDown, T, d.K, d.S, d.H, d.I, R);
+  auto kern = gemv_down_kernel<4>;
+  kern<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm, b.row_w,
+                                   b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, b.ctrl, CtrlLayout::kDown, T,
+                                   d.K, d.S, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }
