@@ -223,7 +223,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8xfp4->fp32",
-        "data": "synthetic (seeded; random-init weights at DeepSeek V4 Flash expert shapes)",
+        "data": "synthetic (seeded; random-init weights at the workload's DeepSeek V4 expert shapes)",
         "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
                    "shared": wl.shared, "inter": wl.inter, "tokens": T, "layers_rotated": nl,
                    "batches_rotated": nb, "parallelism": "single GPU"},

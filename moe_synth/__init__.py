@@ -68,6 +68,9 @@ WORKLOADS = {
     "prefill_t512": Workload("prefill_t512", 4096, 256, 6, 1, 2048, 512),
     "prefill_t4096_zipf": Workload("prefill_t4096_zipf", 4096, 256, 6, 1, 2048, 4096, zipf=1.1),
     "stacked_decode_16l": Workload("stacked_decode_16l", 4096, 256, 6, 1, 2048, 1, layers=16, steps=256),
+    # DeepSeek V4 Pro scale (hidden 7168, 384 experts, same expert format); intermediate 2048
+    # and top-6 are readings (the pages give neither for Pro)
+    "decode_pro_t8": Workload("decode_pro_t8", 7168, 384, 6, 1, 2048, 8),
 }
 _WORKLOAD_IDS = {n: i + 1 for i, n in enumerate(WORKLOADS)}
 

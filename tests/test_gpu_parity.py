@@ -249,6 +249,12 @@ def test_prefill_4096_zipf_full_size():
     assert got["counts"].max() > 0.10 * got["idx"].size
 
 
+def test_decode_pro_scale_full_size():
+    # DeepSeek V4 Pro scale: hidden 7168 (56 K steps of 128), 384 experts (top-k over 6 keys
+    # per lane), 9 GB of FP4 experts
+    _full_size("decode_pro_t8", 4)
+
+
 def test_stacked_decode_16_layers():
     wl = synth.WORKLOADS["stacked_decode_16l"]
     layers, routers = [], []
