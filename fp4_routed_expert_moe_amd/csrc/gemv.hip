@@ -171,14 +171,14 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& sr
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
 // (h8 = [kHTerms][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
-template <int TL>
-__global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gemv_gateup_kernel(
+template <int TL, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
     const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, int T, int k, int H, int I, int R) {
   static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
-  __shared__ f32x4 red[kSplit][TL][2][64];
+  __shared__ f32x4 red[SPLIT][TL][2][64];
   if ((int)blockIdx.y >= info[0]) return;
   const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
   const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gem
   const int n0 = blockIdx.x * (16 * TL);
   const int KB = H >> 5;
   const int NI = (KB + 3) >> 2;  // K iterations of 4 blocks
-  const int it_lo = wave * NI / kSplit, it_hi = (wave + 1) * NI / kSplit;
+  const int it_lo = wave * NI / SPLIT, it_hi = (wave + 1) * NI / SPLIT;
   const uint8_t* codes[2] = {gc, uc};
   const uint8_t* scales[2] = {gs, us};
   GSrc<2> src;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64 * kSplit, kSplit <= 4 ? 8 / kSplit : 1) void gem
         const int j = 2 * p + c;
         f32x4 gsum = red[0][j][0][lane], usum = red[0][j][1][lane];
 #pragma unroll
-        for (int w = 1; w < kSplit; ++w) {
+        for (int w = 1; w < SPLIT; ++w) {
           gsum += red[w][j][0][lane];
           usum += red[w][j][1][lane];
         }
@@ -395,7 +395,7 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int cols = narrow ? 32 : 64;
   dim3 grid((d.I + cols - 1) / cols, max_act);
   const int tk = timing_begin("gemv_gateup", s);
-  auto kern = narrow ? gemv_gateup_kernel<2> : gemv_gateup_kernel<4>;
+  auto kern = narrow ? gemv_gateup_kernel<2, kSplit> : gemv_gateup_kernel<4, kSplit>;
   kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.act, b.info,
                                     b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), T, d.K, d.H, d.I, R);
   timing_end(tk, s);
