@@ -176,7 +176,15 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, int T, int k, int H, int I, int R) {
+    const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, uint32_t* __restrict__ stage_clear,
+    int T, int k, int H, int I, int R) {
+  {
+    // clear the staging rows the down kernel fills next (R x H words)
+    const size_t n = (size_t)R * H;
+    const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x, nwg = (size_t)gridDim.x * gridDim.y;
+    for (size_t i = (wg * (64 * SPLIT) + threadIdx.x) * 4; i < n; i += nwg * (64 * SPLIT) * 4)
+      *reinterpret_cast<uint4*>(stage_clear + i) = make_uint4(0u, 0u, 0u, 0u);
+  }
   static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
   __shared__ f32x4 red[SPLIT][TL][2][64];
   if ((int)blockIdx.y >= info[0]) return;
@@ -270,13 +278,16 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
 // ------------------------------------------------------------------------------------
 // down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms, and
 // y[t][n] = staging[shared slot of t][n] + sum_j staging[t*k + j][n].
-// Workgroup (c, a) handles column tile c of active group a.  Workgroups start in order of
-// their linear index (column tile fastest), so when the one of the last active group starts,
-// every other group's workgroup of its tile has started: it waits for their completion flags
-// (agent-scope words set to 1), adds the tile's rows in the combine order of the prefill
-// path, and clears the flags again, so they are all 0 between calls.
+// Workgroup (c, a) handles column tile c of active group a.  The workgroup of the last active
+// group of each tile also adds the tile's rows, in the combine order of the prefill path,
+// once they are all in staging: a staging word is 0 until its row is written (the gate/up
+// kernel of the call clears them), so no writer waits for its stores to complete.
 // ------------------------------------------------------------------------------------
-constexpr int kFlagPolls = 1 << 20;  // bound of the wait (~1 s): never hangs
+constexpr int kFlagPolls = 1 << 20;  // bound of each word's wait: never hangs
+// Staging words hold a row value's bits XOR kStageKey, so a word is 0 only until written: the
+// key is a signalling-NaN pattern, which no arithmetic result has (results are quiet).  The
+// gate/up kernel clears the staging rows of the call.
+constexpr uint32_t kStageKey = 0x7F800001u;
 
 constexpr int kDnBlocks = 1;  // column blocks (of TL tiles) per down workgroup
 #ifndef MOE_DN_SPLIT
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
     const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
-    float* __restrict__ staging, float* __restrict__ y, int32_t* __restrict__ ctrl, int dn_flags, int T, int k, int S,
+    float* __restrict__ staging, float* __restrict__ y, int T, int k, int S,
     int H, int I, int R) {
   constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
   // column tiles each wave finishes (waves past the last tile only reduce)
@@ -352,32 +363,30 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
       const int n = n0 + 16 * jj + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // lane (n, q) holds rows 4q .. 4q+3 of the pass
-        if (n < H && 4 * q + i < nt) st_agent(staging + (size_t)slot_i[i] * H + n, sum[i] * wt_i[i]);
+        if (n < H && 4 * q + i < nt)
+          st_agent(reinterpret_cast<uint32_t*>(staging) + (size_t)slot_i[i] * H + n,
+                   __float_as_uint(sum[i] * wt_i[i]) ^ kStageKey);
     }
     __syncthreads();
   }
-  // this group's rows of the tile are out
-  wait_stores();
-  __syncthreads();
-  int32_t* flags = ctrl + dn_flags;  // [active group slot][column tile]
-  const int ntile = gridDim.x;
-  if ((int)blockIdx.y != nact - 1) {
-    if (threadIdx.x == 0) st_agent(flags + blockIdx.y * ntile + blockIdx.x, (int32_t)1);
-    return;
-  }
-  for (int round = 0; round < kFlagPolls; ++round) {
-    bool mine = true;
-    for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) mine &= ld_agent(flags + a * ntile + blockIdx.x) != 0;
-    if (__syncthreads_and(mine)) break;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  __asm__ __volatile__("" ::: "memory");
-  for (int a = threadIdx.x; a < nact - 1; a += kDnThreads) st_agent(flags + a * ntile + blockIdx.x, (int32_t)0);
+  // The last active group's workgroup of the tile adds the tile's rows once they are all
+  // there (a word is 0 until its row is written; the others need not wait for their stores).
+  if ((int)blockIdx.y != nact - 1) return;
+  const uint32_t* st = reinterpret_cast<const uint32_t*>(staging);
   for (int i = threadIdx.x; i < T * kDnCols; i += kDnThreads) {
     const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;
-    float sacc = S ? ld_agent(staging + ((size_t)tk + t) * H + n) : 0.f;
-    for (int j = 0; j < k; ++j) sacc += ld_agent(staging + ((size_t)t * k + j) * H + n);
+    float sacc = 0.f;
+    for (int j = 0; j < k + S; ++j) {
+      const size_t slot = j < S ? (size_t)tk + t : (size_t)t * k + (j - S);
+      uint32_t w = ld_agent(st + slot * H + n);
+      for (int round = 0; w == 0u && round < kFlagPolls; ++round) {
+        __builtin_amdgcn_s_sleep(1);
+        w = ld_agent(st + slot * H + n);
+      }
+      const float v = __uint_as_float(w ^ kStageKey);
+      sacc = j == 0 ? v : sacc + v;
+    }
     y[(size_t)t * H + n] = sacc;
   }
 }
@@ -397,7 +406,8 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int tk = timing_begin("gemv_gateup", s);
   auto kern = narrow ? gemv_gateup_kernel<2, kSplit> : gemv_gateup_kernel<4, kSplit>;
   kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.act, b.info,
-                                    b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), T, d.K, d.H, d.I, R);
+                                    b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h),
+                                    reinterpret_cast<uint32_t*>(b.staging), T, d.K, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }
@@ -411,8 +421,8 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const int tk = timing_begin("gemv_down", s);
   auto kern = gemv_down_kernel<4>;
   kern<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm, b.row_w,
-                                   b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, b.ctrl, CtrlLayout::kDown, T,
-                                   d.K, d.S, d.H, d.I, R);
+                                   b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, T, d.K, d.S, d.H, d.I,
+                                   R);
   timing_end(tk, s);
   return hipGetLastError();
 }

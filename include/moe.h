@@ -125,10 +125,10 @@ void moe_layer_destroy(moe_layer* layer);
 
 /* Bytes of device workspace one call with up to max_tokens tokens needs (0 on bad
  * arguments).  The caller allocates and owns it; it must be 256-byte aligned and filled with
- * zeros before its first use.  Its first bytes are control words (device-scope counters and
- * completion flags the kernels use to let one workgroup finish a stage for the others; their
- * number depends only on the layer's dims); every call that completes leaves them at zero, so
- * a workspace is zeroed once, not per call, and may serve any layer it is large enough for.
+ * zeros before its first use.  Its first bytes are control words (device-scope counters the
+ * kernels use to let one workgroup finish a stage for the others; their number is fixed);
+ * every call that completes leaves them at zero, so a workspace is zeroed once, not per
+ * call, and may serve any layer it is large enough for.
  * A workspace serves one stream at a time: calls that overlap on one workspace race. */
 uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens);
 
