@@ -71,7 +71,7 @@ size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
   t.cbase = reinterpret_cast<int32_t*>(take(C * d.E * 4));
   t.grp_row0 = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
   t.grp_rows = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
-  t.act = reinterpret_cast<int32_t*>(take((size_t)d.G * 4));
+  t.grec = reinterpret_cast<moe::GroupRec*>(take((size_t)d.G * sizeof(moe::GroupRec)));
   t.info = reinterpret_cast<int32_t*>(take(16));
   t.mt_group = reinterpret_cast<int32_t*>(take(mt_bound * 4));
   t.mt_row0 = reinterpret_cast<int32_t*>(take(mt_bound * 4));

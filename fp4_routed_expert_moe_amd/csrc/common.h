@@ -205,6 +205,12 @@ struct Dims {
 };
 
 // Device buffers of one call, carved from the workspace (and the caller's route buffers).
+// Active-group slot of the decode kernels: one 16-byte load gives a workgroup its group, the
+// group's rows and the number of active slots (slots past that count hold only the count).
+struct alignas(16) GroupRec {
+  int32_t group, row0, rows, nact;
+};
+
 struct CallBufs {
   float* logits;      // [T][E] scores (fused routing), or [slices][T][E] partial scores
   int32_t* idx;       // [T][k]
@@ -217,7 +223,7 @@ struct CallBufs {
   int32_t* cbase;     // [C][E] rows of expert e in chunks before c
   int32_t* grp_row0;  // [G] first grouped row of group g
   int32_t* grp_rows;  // [G] rows of group g
-  int32_t* act;       // [G] groups with rows, ascending, shared last
+  GroupRec* grec;     // [G] groups with rows, ascending, shared last; then count-only slots
   int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles
   int32_t* mt_group;  // [mt_bound]
   int32_t* mt_row0;   // [mt_bound]

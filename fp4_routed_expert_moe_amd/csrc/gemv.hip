@@ -175,8 +175,7 @@ template <int TL, int SPLIT>
 __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ act, const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0,
-    const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8, uint32_t* __restrict__ stage_clear,
+    const GroupRec* __restrict__ grec, uint8_t* __restrict__ h8, uint32_t* __restrict__ stage_clear,
     int T, int k, int H, int I, int R) {
   {
     // clear the staging rows the down kernel fills next (R x H words)
@@ -187,9 +186,10 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
   }
   static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
   __shared__ f32x4 red[SPLIT][TL][2][64];
-  if ((int)blockIdx.y >= info[0]) return;
-  const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
-  const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
+  const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
+  if ((int)blockIdx.y >= rec.w) return;
+  const int g = __builtin_amdgcn_readfirstlane(rec.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(rec.y), rows = __builtin_amdgcn_readfirstlane(rec.z);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * TL);
@@ -299,8 +299,7 @@ constexpr int kDnThreads = 64 * kDnSplit;
 template <int TL>
 __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
-    const int32_t* __restrict__ perm, const float* __restrict__ row_w, const int32_t* __restrict__ act,
-    const int32_t* __restrict__ info, const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows,
+    const int32_t* __restrict__ perm, const float* __restrict__ row_w, const GroupRec* __restrict__ grec,
     float* __restrict__ staging, float* __restrict__ y, int T, int k, int S,
     int H, int I, int R) {
   constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
@@ -308,10 +307,11 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   constexpr int kDnPerWave = kDnBlocks * TL > kDnSplit ? kDnBlocks * TL / kDnSplit : 1;
   static_assert(kDnPerWave * kDnSplit >= kDnBlocks * TL, "down workgroup shape");
   __shared__ f32x4 red[kDnSplit][kDnBlocks][TL][64];
-  const int nact = info[0];
+  const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
+  const int nact = rec.w;
   if ((int)blockIdx.y >= nact) return;
-  const int g = __builtin_amdgcn_readfirstlane(act[blockIdx.y]);
-  const int rows = __builtin_amdgcn_readfirstlane(grp_rows[g]), row0 = __builtin_amdgcn_readfirstlane(grp_row0[g]);
+  const int g = __builtin_amdgcn_readfirstlane(rec.x);
+  const int row0 = __builtin_amdgcn_readfirstlane(rec.y), rows = __builtin_amdgcn_readfirstlane(rec.z);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * kDnCols;
@@ -405,8 +405,8 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   dim3 grid((d.I + cols - 1) / cols, max_act);
   const int tk = timing_begin("gemv_gateup", s);
   auto kern = narrow ? gemv_gateup_kernel<2, kSplit> : gemv_gateup_kernel<4, kSplit>;
-  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.act, b.info,
-                                    b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h),
+  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.grec,
+                                    static_cast<uint8_t*>(b.h),
                                     reinterpret_cast<uint32_t*>(b.staging), T, d.K, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
@@ -421,8 +421,7 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const int tk = timing_begin("gemv_down", s);
   auto kern = gemv_down_kernel<4>;
   kern<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm, b.row_w,
-                                   b.act, b.info, b.grp_row0, b.grp_rows, b.staging, y, T, d.K, d.S, d.H, d.I,
-                                   R);
+                                   b.grec, b.staging, y, T, d.K, d.S, d.H, d.I, R);
   timing_end(tk, s);
   return hipGetLastError();
 }

@@ -361,7 +361,7 @@ __device__ __forceinline__ void group_scan_wave(int* cnt_offs, int* act, int* mt
 
 // The tables the expert kernels read, from the scan's LDS results (cnt(e) = rows of expert e,
 // offs[e] = its first row, mt_off[e] = its first M-tile): counts, offsets, group rows and first
-// rows, the active list (shared expert last), the M-tile list (a wave per expert, its lanes
+// rows, the active-group slots (shared expert last), the M-tile list (a wave per expert, its lanes
 // over the expert's tiles) and the info words.  Only later kernels read them: plain stores.
 template <int NT, bool MTILES, class CNT>
 __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, const int* act, const int* mt_off,
@@ -373,7 +373,22 @@ __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, co
     b.grp_row0[e] = o;
     b.grp_rows[e] = c;
   }
-  for (int a = threadIdx.x; a < gs.nact; a += NT) b.act[a] = act[a];
+  // every slot of the active list, so a workgroup's one load also tells it whether it has work
+  const int G = E + S, nslots = gs.nact + S;
+  for (int a = threadIdx.x; a < G; a += NT) {
+    GroupRec r{0, 0, 0, nslots};
+    if (a < gs.nact) {
+      const int e = act[a];
+      r.group = e;
+      r.row0 = offs[e];
+      r.rows = cnt(e);
+    } else if (a < nslots) {  // the shared expert
+      r.group = E;
+      r.row0 = T * K;
+      r.rows = T;
+    }
+    *reinterpret_cast<int4*>(b.grec + a) = make_int4(r.group, r.row0, r.rows, r.nact);
+  }
   if (MTILES) {
     const int lane = threadIdx.x & 63;
     for (int e = threadIdx.x >> 6; e < E; e += NT / 64) {
@@ -393,7 +408,6 @@ __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, co
     if (S) {
       b.grp_row0[E] = T * K;
       b.grp_rows[E] = T;
-      b.act[gs.nact] = E;
     }
     b.info[0] = gs.nact + S;
     b.info[1] = gs.nmt;
