@@ -95,6 +95,9 @@ def test_identity_experts_closed_form_on_gpu():
     (3, 96, 5, 2, 1, 32, 7),        # H, I not multiples of 64; E < 64
     (4, 1024, 64, 8, 0, 512, 33),   # no shared expert
     (5, 288, 70, 3, 1, 160, 65),    # E not a multiple of 64
+    (7, 128, 1024, 8, 1, 64, 8),    # the layer's expert limit, routed in one launch
+    (8, 160, 1000, 4, 1, 96, 40),   # near the limit, chunked routing (T*E past one workgroup's LDS)
+    (10, 64, 2, 1, 1, 32, 64),      # two experts, top-1, the one-launch routing's token limit
 ])
 def test_random_shapes_both_paths(case):
     seed, hidden, experts, k, shared, inter, tokens = case
