@@ -372,20 +372,37 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   // The last active group's workgroup of the tile adds the tile's rows once they are all
   // there (a word is 0 until its row is written; the others need not wait for their stores).
   if ((int)blockIdx.y != nact - 1) return;
+  // The slots of an output are read 8 at a time with their loads issued together; a word
+  // still 0 is polled again on its own.
   const uint32_t* st = reinterpret_cast<const uint32_t*>(staging);
+  const int ns = k + S;
   for (int i = threadIdx.x; i < T * kDnCols; i += kDnThreads) {
     const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;
     float sacc = 0.f;
-    for (int j = 0; j < k + S; ++j) {
-      const size_t slot = j < S ? (size_t)tk + t : (size_t)t * k + (j - S);
-      uint32_t w = ld_agent(st + slot * H + n);
-      for (int round = 0; w == 0u && round < kFlagPolls; ++round) {
-        __builtin_amdgcn_s_sleep(1);
-        w = ld_agent(st + slot * H + n);
+    for (int j0 = 0; j0 < ns; j0 += 8) {
+      uint32_t wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const size_t slot = j < S ? (size_t)tk + t : (size_t)t * k + (j - S);
+        wv[u] = j < ns ? ld_agent(st + slot * H + n) : 0u;
       }
-      const float v = __uint_as_float(w ^ kStageKey);
-      sacc = j == 0 ? v : sacc + v;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j >= ns) break;
+        uint32_t w = wv[u];
+        if (w == 0u) {
+          const size_t slot = j < S ? (size_t)tk + t : (size_t)t * k + (j - S);
+          for (int round = 0; w == 0u && round < kFlagPolls; ++round) {
+            __builtin_amdgcn_s_sleep(1);
+            w = ld_agent(st + slot * H + n);
+          }
+        }
+        const float v = __uint_as_float(w ^ kStageKey);
+        sacc = j == 0 ? v : sacc + v;
+      }
     }
     y[(size_t)t * H + n] = sacc;
   }
