@@ -271,12 +271,14 @@ static int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void
 }
 
 // Routing; with `forward` set the routing kernels also write the FP8 activation terms the
-// expert kernels read, and (for the grouped GEMM) its M-tile list.
+// expert kernels read, and (for the grouped GEMM) its M-tile list.  route_out: the caller
+// reads the routing (idx, weights, counts, offsets, perm), so every table is written.
 static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
-                             bool forward, bool gemm) {
+                             bool forward, bool gemm, bool route_out) {
   const moe::Dims& d = L->dims;
-  hipError_t e =
-      moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, forward, forward && gemm, s);
+  const bool lean = forward && !gemm && !route_out;
+  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, forward,
+                                           forward && gemm, lean, s);
   if (e == hipSuccess && !moe::route_fused(d, T)) e = moe::launch_route_chunked(d, b, T, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -304,7 +306,7 @@ int32_t moe_route(const moe_layer* L, const uint16_t* x, int32_t T, const moe_ro
   moe::CallBufs b;
   carve(L->dims, T, static_cast<char*>(ws), &b);
   use_route_out(b, route);
-  return enqueue_route(L, x, T, b, static_cast<hipStream_t>(stream), false, false);
+  return enqueue_route(L, x, T, b, static_cast<hipStream_t>(stream), false, false, true);
 }
 
 int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
@@ -323,7 +325,7 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
   hipError_t e;
-  st = enqueue_route(L, x, T, b, s, true, !gemv);
+  st = enqueue_route(L, x, T, b, s, true, !gemv, route != nullptr);
   if (st != MOE_OK) return st;
   if (gemv) {
     // the down kernel also adds each token's rows into y

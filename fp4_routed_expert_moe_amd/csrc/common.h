@@ -253,9 +253,13 @@ inline int router_slices(const Dims& d, int T) {
   ks = ks < 1 ? 1 : (ks > kRouterMaxSlices ? kRouterMaxSlices : ks);
   return ks < d.H / 32 ? ks : d.H / 32;
 }
-// Layers whose decode launch also routes (the routing tail inside it ranks up to 256 experts).
+// Router scores (and, for batches route_fused takes, the whole routing in the same launch).
+// quantize_x: also write the FP8 activation terms; mtiles: also the grouped GEMM's M-tile
+// list; lean: the caller only runs the decode kernels and reads no routing output, so with
+// at most kLeanMaxPicks picks only their tables are built.
+constexpr int kLeanMaxPicks = 64;
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, bool mtiles, hipStream_t s);
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
 // The whole layer for a small batch in one launch (decode.hip).  With `route_inside` the

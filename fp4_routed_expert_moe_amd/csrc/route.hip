@@ -25,8 +25,9 @@ using RouterTail = TailLayout<1024, kTailScores>;
 
 // flags: kRouteQuantize = also split x into FP8 terms (the workgroups that are not last, after
 // publishing their scores, so the split never delays the routing); kRouteMTiles = also build
-// the grouped GEMM's M-tile list.
-constexpr int kRouteQuantize = 1, kRouteMTiles = 2;
+// the grouped GEMM's M-tile list; kRouteLean = only the tables the decode kernels read (at
+// most 64 picks).
+constexpr int kRouteQuantize = 1, kRouteMTiles = 2, kRouteLean = 4;
 
 __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ wr,
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
     if (flags & kRouteQuantize) quantize(ticket, total - 1);
     return;
   }
-  if (flags & kRouteMTiles)
+  if (flags & kRouteLean)
+    route_tail<kTailThreads, 16, 1024, kTailScores, false, true>(b, T, E, K, S, lds);
+  else if (flags & kRouteMTiles)
     route_tail<kTailThreads, 16, 1024, kTailScores, true>(b, T, E, K, S, lds);
   else
     route_tail<kTailThreads, 16, 1024, kTailScores, false>(b, T, E, K, S, lds);
@@ -310,11 +313,12 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, bool mtiles, hipStream_t s) {
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s) {
   if (route_fused(d, T)) {
     dim3 grid((d.E + kRouterEPB - 1) / kRouterEPB, (T + kScoreTT - 1) / kScoreTT);
     const int tk = timing_begin("router_route", s);
-    const int flags = (quantize_x ? kRouteQuantize : 0) | (mtiles ? kRouteMTiles : 0);
+    const int flags = (quantize_x ? kRouteQuantize : 0) | (mtiles ? kRouteMTiles : 0) |
+                      (lean && !mtiles && T * d.K <= kLeanMaxPicks ? kRouteLean : 0);
     router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, flags);
     timing_end(tk, s);
     return hipGetLastError();

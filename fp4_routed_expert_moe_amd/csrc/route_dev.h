@@ -415,6 +415,43 @@ __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, co
 }
 
 // ------------------------------------------------------------------------------------
+// Grouping of at most 64 picks when only the decode kernels read it (perm, row weights and
+// the active-group slots; no counts, offsets or per-token lists).  One wave: lane i holds
+// pick i = t*K + j with key (expert, token); its rank among the keys is its grouped row
+// (experts ascending, tokens ascending within an expert, as the full tables order them).
+// The rows that start a new expert, as a ballot, give each group's slot and row count.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void lean_tables(const uint16_t* sel_e, const float* sel_w, int T, int E, int K, int S,
+                                            const CallBufs& b) {
+  const int lane = threadIdx.x & 63;
+  const int np = T * K;  // <= 64
+  const bool live = lane < np;
+  const int key = live ? (int)sel_e[lane] * 64 + lane / K : 0x7FFFFFFF;
+  int rank = 0;
+  for (int j = 0; j < np; ++j) rank += __builtin_amdgcn_readlane(key, j) < key;
+  if (!live) rank = lane;  // the rest keep their places: the ranks stay a permutation
+  if (live) {
+    b.perm[rank] = lane;
+    b.row_w[rank] = sel_w[lane];
+  }
+  // lane r receives the key of rank r, then compares its expert with lane r-1's
+  const int skey = __builtin_amdgcn_ds_permute(rank * 4, key);
+  const int er = skey >> 6;
+  const int eprev = __builtin_amdgcn_ds_bpermute(((lane + 63) & 63) * 4, skey) >> 6;
+  const bool first = lane < np && (lane == 0 || er != eprev);
+  const uint64_t starts = __ballot(first);
+  const int nact = __popcll(starts), nslots = nact + S;
+  if (first) {
+    const int slot = __popcll(starts & ((1ull << lane) - 1ull));
+    const uint64_t after = lane < 63 ? starts >> (lane + 1) : 0ull;
+    const int next = after ? lane + 1 + __builtin_ctzll(after) : np;
+    *reinterpret_cast<int4*>(b.grec + slot) = make_int4(er, lane, next - lane, nslots);
+  }
+  for (int a = nact + lane; a < E + S; a += 64)  // the shared expert, then count-only slots
+    *reinterpret_cast<int4*>(b.grec + a) = a < nslots ? make_int4(E, np, T, nslots) : make_int4(0, 0, 0, nslots);
+}
+
+// ------------------------------------------------------------------------------------
 // The routing tail of a small batch (route_fused), run by one workgroup of NT threads once
 // every score is published: top-k, grouping tables, stable scatter.  Everything is built in
 // LDS and written out at the end.  TailLayout<MAXE, MAXTK> sizes the caller's LDS for up to
@@ -433,7 +470,7 @@ struct TailLayout {
   static constexpr int kBytes = kScan + 16;
 };
 
-template <int NT, int QMAX, int MAXE, int MAXTK, bool MTILES>
+template <int NT, int QMAX, int MAXE, int MAXTK, bool MTILES, bool LEAN = false>
 __device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int K, int S, char* lds) {
   using L = TailLayout<MAXE, MAXTK>;
   float* sc = reinterpret_cast<float*>(lds + L::kSc);
@@ -464,6 +501,10 @@ __device__ __forceinline__ void route_tail(const CallBufs& b, int T, int E, int 
   __syncthreads();
   topk_block_any<NT, QMAX>(sc, T, E, K, sel_e, sel_w, mask);
   __syncthreads();
+  if constexpr (LEAN) {
+    if (tid < 64) lean_tables(sel_e, sel_w, T, E, K, S, b);
+    return;
+  }
   for (int i = tid; i < E; i += NT) offs[i] = __popcll(mask[i]);
   __syncthreads();
   if (tid < 64) group_scan_wave<MTILES>(offs, act, mt_off, gs, T, E, S);
