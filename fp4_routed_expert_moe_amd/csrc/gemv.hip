@@ -157,12 +157,14 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& sr
       break;
     }
     gv_load<NM, NA, TL>(f[1], src, N, arow, asc, K, it + 1, q);
+    __builtin_amdgcn_sched_barrier(0);  // the next loads issue before this step's wait
     gv_mma<NM, NA, TL>(f[0], acc, src.sel);
     if (it + 2 >= it_hi) {
       gv_mma<NM, NA, TL>(f[1], acc, src.sel);
       break;
     }
     gv_load<NM, NA, TL>(f[0], src, N, arow, asc, K, it + 2, q);
+    __builtin_amdgcn_sched_barrier(0);
     gv_mma<NM, NA, TL>(f[1], acc, src.sel);
   }
 }
