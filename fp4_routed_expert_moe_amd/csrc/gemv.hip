@@ -140,32 +140,32 @@ __device__ __forceinline__ void gv_mma(const GFrag<NM, NA, TL>& f, f32x4 (&acc)[
   }
 }
 // This wave's K iterations [it_lo, it_hi), the loads of iteration i+1 in flight while
-// iteration i runs on the matrix cores.
+// iteration i runs on the matrix cores.  The steady-state loop body is one block whose loads
+// are issued before the matrix work (a scheduling barrier keeps them there), so the wait
+// before each step's MFMAs covers only that step's own loads.
 template <int NM, int NA, int TL>
 __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& src, int N,
                                         const uint8_t* const* arow, const uint8_t* asc, int K, int it_lo, int it_hi,
                                         int q) {
-  // Every path through the loop issues the next loads before the current MFMAs (the tail
-  // iterations leave by their own exits), so the wait before the MFMAs only covers the
-  // older loads.
   if (it_lo >= it_hi) return;
-  GFrag<NM, NA, TL> f[2];
-  gv_load<NM, NA, TL>(f[0], src, N, arow, asc, K, it_lo, q);
-  for (int it = it_lo;; it += 2) {
-    if (it + 1 >= it_hi) {
-      gv_mma<NM, NA, TL>(f[0], acc, src.sel);
-      break;
-    }
-    gv_load<NM, NA, TL>(f[1], src, N, arow, asc, K, it + 1, q);
-    __builtin_amdgcn_sched_barrier(0);  // the next loads issue before this step's wait
-    gv_mma<NM, NA, TL>(f[0], acc, src.sel);
-    if (it + 2 >= it_hi) {
-      gv_mma<NM, NA, TL>(f[1], acc, src.sel);
-      break;
-    }
-    gv_load<NM, NA, TL>(f[0], src, N, arow, asc, K, it + 2, q);
+  GFrag<NM, NA, TL> f0, f1;
+  gv_load<NM, NA, TL>(f0, src, N, arow, asc, K, it_lo, q);
+  int it = it_lo;
+  for (; it + 2 < it_hi; it += 2) {
+    gv_load<NM, NA, TL>(f1, src, N, arow, asc, K, it + 1, q);
     __builtin_amdgcn_sched_barrier(0);
-    gv_mma<NM, NA, TL>(f[1], acc, src.sel);
+    gv_mma<NM, NA, TL>(f0, acc, src.sel);
+    gv_load<NM, NA, TL>(f0, src, N, arow, asc, K, it + 2, q);
+    __builtin_amdgcn_sched_barrier(0);
+    gv_mma<NM, NA, TL>(f1, acc, src.sel);
+  }
+  if (it + 1 < it_hi) {
+    gv_load<NM, NA, TL>(f1, src, N, arow, asc, K, it + 1, q);
+    __builtin_amdgcn_sched_barrier(0);
+    gv_mma<NM, NA, TL>(f0, acc, src.sel);
+    gv_mma<NM, NA, TL>(f1, acc, src.sel);
+  } else {
+    gv_mma<NM, NA, TL>(f0, acc, src.sel);
   }
 }
 
