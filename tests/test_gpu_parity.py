@@ -98,6 +98,8 @@ def test_identity_experts_closed_form_on_gpu():
     (7, 128, 1024, 8, 1, 64, 8),    # the layer's expert limit, routed in one launch
     (8, 160, 1000, 4, 1, 96, 40),   # near the limit, chunked routing (T*E past one workgroup's LDS)
     (10, 64, 2, 1, 1, 32, 64),      # two experts, top-1, the one-launch routing's token limit
+    (11, 256, 16, 4, 0, 128, 8),    # decode batch without a shared expert
+    (12, 128, 8, 8, 1, 64, 4),      # decode batch routed to every expert
 ])
 def test_random_shapes_both_paths(case):
     seed, hidden, experts, k, shared, inter, tokens = case
