@@ -135,8 +135,13 @@ def main():
     y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    # A step is one pass of the layer; stacked decode runs its layers one after another per step
+    # (call i of the run uses layer i % nl and token batch i % nb).
+    L = wl.layers if wl.layers > 1 else 1
+
     def step(s):
-        layers[s % nl].forward(xs[s % nb], workspace=ws, y=y)
+        for c in range(s * L, (s + 1) * L):
+            layers[c % nl].forward(xs[c % nb], workspace=ws, y=y)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -149,9 +154,9 @@ def main():
     # active experts of every (layer, batch) pair a step can meet (outside the timed region)
     period = int(np.lcm(nl, nb))
     active = {}
-    for s in range(min(period, args.steps)):
-        r = layers[s % nl].route(xs[s % nb], workspace=ws)
-        active[(s % nl, s % nb)] = r["counts"]
+    for c in range(min(period, args.steps * L)):
+        r = layers[c % nl].route(xs[c % nb], workspace=ws)
+        active[(c % nl, c % nb)] = r["counts"]
     torch.cuda.synchronize()
     active = {k: int((v > 0).sum().item()) for k, v in active.items()}
 
@@ -176,10 +181,10 @@ def main():
     moe.timing_enable(False)
 
     e_all, e_gu, e_dn = expert_bytes(wl)
-    groups_per_step = [active[(s % nl, s % nb)] + wl.shared for s in range(args.steps)]
-    groups = float(np.mean(groups_per_step))
-    fp4_bytes_step = groups * e_all
-    flops_step = 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
+    groups_per_call = [active[(c % nl, c % nb)] + wl.shared for c in range(args.steps * L)]
+    groups = float(np.mean(groups_per_call))
+    fp4_bytes_step = L * groups * e_all
+    flops_step = L * 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
     # the dominant kernel and its algorithmic work per launch
     # (gate/up weight bytes of the active groups; gate/up flops).  The grouped GEMM is priced
     # against the roof its arithmetic intensity reaches first: MFMA above the ridge
@@ -231,7 +236,8 @@ def main():
         "fp4_weight_frac_hbm": fp4_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "tflops": flops_step / (ms_per_step * 1e-3) / 1e12,
         "tflops_frac_bf16": flops_step / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "active_groups_per_step": groups,
+        "active_groups_per_call": groups,
+        "layer_calls_per_step": L,
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
@@ -271,9 +277,11 @@ def cpu_baseline(wl, args, synth):
             total_s += time.perf_counter() - t0
         total_t += t_batch
         batches += 1
-    return {"value": total_t / total_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    L = wl.layers if wl.layers > 1 else 1  # a token of the stacked workload passes L layers
+    per_layer = f"; a token passes {L} layers of the same cost" if L > 1 else ""
+    return {"value": total_t / total_s / L, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{batches} batch(es) of {t_batch} tokens of {wl.name} layer 0, "
-                      f"{total_s:.1f} s of oracle time (float64 numpy, one thread)"}
+                      f"{total_s:.1f} s of oracle time (float64 numpy, one thread){per_layer}"}
 
 
 # ---------------------------------------------------------------------------------------
