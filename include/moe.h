@@ -141,8 +141,9 @@ int32_t moe_route(const moe_layer* layer, const uint16_t* x, int32_t tokens,
 
 /* The whole layer: y (fp32, device, [T][H]; must not overlap x or the workspace) for x
  * (bf16 bit patterns, device, [T][H]).  If `route` is not NULL its five buffers receive
- * the routing (as moe_route); if NULL the routing stays in the workspace.  Asynchronous
- * on `stream`; T = 0 is a no-op; no host synchronisation. */
+ * the routing (as moe_route); if NULL no routing output is produced, and a small batch then
+ * builds only the grouping its own expert kernels read (the output is the same bit for bit).
+ * Asynchronous on `stream`; T = 0 is a no-op; no host synchronisation. */
 int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, float* y,
                     const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
                     void* stream);
