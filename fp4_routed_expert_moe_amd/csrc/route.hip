@@ -15,7 +15,7 @@ namespace moe {
 // ------------------------------------------------------------------------------------
 // Small batches: router scores l[t][e] = x[t] . W_r[e] + b[e] and the routing tail in one
 // launch.  Workgroup (i, j) scores experts 4i .. 4i+3 (four waves each) for tokens
-// 8j .. 8j+7 and quantizes an equal slice of the activation blocks when asked; the last
+// 4j .. 4j+3 and quantizes an equal slice of the activation blocks when asked; the last
 // workgroup to finish routes the whole batch.
 // ------------------------------------------------------------------------------------
 constexpr int kTailThreads = 1024;

@@ -21,7 +21,7 @@ namespace moe {
 // order.  Every kernel that scores uses this, so a token's scores depend neither on the batch
 // nor on the kernel.  All of a lane's loads are issued before the first product.
 // ------------------------------------------------------------------------------------
-constexpr int kScoreTT = 8;
+constexpr int kScoreTT = 4;  // tokens per router workgroup (4 measured faster than 8 or 2 at 8 tokens)
 constexpr int kScoreWaves = 4;
 
 // Quarter sums of one wave (wq = wave index in the group), same value on every lane.
