@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
 // 32-value step; result lane l, element i -> token 4*(l/16) + i, expert l % 16.
 // ------------------------------------------------------------------------------------
 constexpr int kRouterGemmTile = 64;
+constexpr int kRouterStagedMaxSlices = 4;
 
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {  // (bf16 of a) | (bf16 of b) << 16
   return (a >> 16) | (b & 0xFFFF0000u);
@@ -122,6 +123,7 @@ __device__ __forceinline__ void split3(const float4& p, const float4& r, bf16x8 
   }
 }
 
+template <bool STAGED>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           const float* __restrict__ bias,
@@ -162,48 +164,119 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
   const int r = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * kRouterGemmTile + (wave & 1) * 32;
   const int e0 = blockIdx.y * kRouterGemmTile + (wave >> 1) * 32;
-  const uint16_t* xa[2];
-  const float* wb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    xa[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 8 * kq;
-    wb[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * H + 8 * kq;
-  }
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // 32-value K steps loaded together
-  for (int k0 = k_lo; k0 < k_hi; k0 += 32 * U) {
-    uint4 xr[U][2];
-    float4 wv[U][2][2];
+  if constexpr (STAGED) {
+    // The tile's 64 tokens and 64 experts pass through LDS 64 K values at a time: x as bf16,
+    // W_r split into its three bf16 terms once per workgroup (each wave reads the half it
+    // needs); the next batch's global loads are in flight while this one runs from LDS.
+    constexpr int KBt = 64, PITCH = KBt + 8;  // bf16 per LDS row (16 bytes of padding)
+    __shared__ __align__(16) __bf16 xs[2][kRouterGemmTile][PITCH];
+    __shared__ __align__(16) __bf16 ws3[2][3][kRouterGemmTile][PITCH];
+    // staging: thread t loads 16 K values of tile row t / 4 at column (t % 4) * 16
+    const int srow = threadIdx.x >> 2, scol = (threadIdx.x & 3) * 16;
+    const uint16_t* xg = x + (size_t)min(blockIdx.x * kRouterGemmTile + srow, T - 1) * H;
+    const float* wg = wr + (size_t)min(blockIdx.y * kRouterGemmTile + srow, E - 1) * H;
+    struct Stage {
+      uint4 x[2];
+      float4 w[4];
+    };
+    auto gload = [&](Stage& st, int k0) {
+      const int kk = min(k0 + scol, k_hi - 16);  // past the slice: valid bytes, never used
+      st.x[0] = *reinterpret_cast<const uint4*>(xg + kk);
+      st.x[1] = *reinterpret_cast<const uint4*>(xg + kk + 8);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + 32 * u;
-      if (k < k_hi) {
+      for (int v = 0; v < 4; ++v) st.w[v] = *reinterpret_cast<const float4*>(wg + kk + 4 * v);
+    };
+    auto lstore = [&](int buf, const Stage& st) {
+      *reinterpret_cast<uint4*>(&xs[buf][srow][scol]) = st.x[0];
+      *reinterpret_cast<uint4*>(&xs[buf][srow][scol + 8]) = st.x[1];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          xr[u][i] = *reinterpret_cast<const uint4*>(xa[i] + k);
-          wv[u][i][0] = *reinterpret_cast<const float4*>(wb[i] + k);
-          wv[u][i][1] = *reinterpret_cast<const float4*>(wb[i] + k + 4);
-        }
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 t3[3];
+        split3(st.w[2 * h], st.w[2 * h + 1], t3);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) *reinterpret_cast<bf16x8*>(&ws3[buf][t][srow][scol + 8 * h]) = t3[t];
       }
-    }
+    };
+    auto compute = [&](int buf, int k0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + 32 * u >= k_hi) break;
-      bf16x8 bt[2][3];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
-#pragma unroll
-      for (int t = 0; t < 3; ++t)
+      for (int u = 0; u < KBt / 32; ++u) {
+        if (k0 + 32 * u >= k_hi) break;
+        bf16x8 xa[2], wb[2][3];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
+          xa[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][(wave & 1) * 32 + 16 * i + r][32 * u + 8 * kq]);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[u][i]), bt[j][t],
-                                                                acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+            wb[j][t] = *reinterpret_cast<const bf16x8*>(&ws3[buf][t][(wave >> 1) * 32 + 16 * j + r][32 * u + 8 * kq]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb[j][t], acc[i][j], 0, 0, 0);
+      }
+    };
+    Stage st;
+    gload(st, k_lo);
+    lstore(0, st);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = k_lo; k0 < k_hi; k0 += KBt) {
+      const bool more = k0 + KBt < k_hi;
+      if (more) gload(st, k0 + KBt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf, k0);
+      if (more) lstore(buf ^ 1, st);
+      __syncthreads();
+      buf ^= 1;
+    }
+  } else {
+    // each wave loads its own 32 tokens and 32 experts, four K steps at a time
+    const uint16_t* xa[2];
+    const float* wb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xa[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 8 * kq;
+      wb[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * H + 8 * kq;
+    }
+    constexpr int U = 4;  // 32-value K steps loaded together
+    for (int k0 = k_lo; k0 < k_hi; k0 += 32 * U) {
+      uint4 xr[U][2];
+      float4 wv[U][2][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + 32 * u;
+        if (k < k_hi) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            xr[u][i] = *reinterpret_cast<const uint4*>(xa[i] + k);
+            wv[u][i][0] = *reinterpret_cast<const float4*>(wb[i] + k);
+            wv[u][i][1] = *reinterpret_cast<const float4*>(wb[i] + k + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + 32 * u >= k_hi) break;
+        bf16x8 bt[2][3];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[u][i]), bt[j][t],
+                                                                  acc[i][j], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -326,8 +399,10 @@ hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* w
   dim3 grid((T + kRouterGemmTile - 1) / kRouterGemmTile, (d.E + kRouterGemmTile - 1) / kRouterGemmTile,
             router_slices(d, T));
   const int tk = timing_begin("router_gemm", s);
-  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, quantize_x ? b.xq : nullptr, b.gmask, T, d.E,
-                                          d.H);
+  // operands through LDS once each workgroup has a long K range (few hidden-axis slices);
+  // with many short slices the loads straight to registers start sooner
+  auto kern = grid.z <= kRouterStagedMaxSlices ? router_gemm_kernel<true> : router_gemm_kernel<false>;
+  kern<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, quantize_x ? b.xq : nullptr, b.gmask, T, d.E, d.H);
   timing_end(tk, s);
   return hipGetLastError();
 }

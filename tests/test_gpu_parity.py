@@ -100,6 +100,8 @@ def test_identity_experts_closed_form_on_gpu():
     (10, 64, 2, 1, 1, 32, 64),      # two experts, top-1, the one-launch routing's token limit
     (11, 256, 16, 4, 0, 128, 8),    # decode batch without a shared expert
     (12, 128, 8, 8, 1, 64, 4),      # decode batch routed to every expert
+    (13, 96, 256, 2, 1, 32, 2048),  # router GEMM through LDS, hidden-axis slices of one 32-value step
+    (14, 224, 256, 3, 1, 64, 2048), # router GEMM through LDS, slices of 32 and 64 values
 ])
 def test_random_shapes_both_paths(case):
     seed, hidden, experts, k, shared, inter, tokens = case
