@@ -345,25 +345,49 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(const float* 
 // Per expert: the prefix over the chunks of its pick counts (16 chunks' masks loaded at a
 // time), then the grouping tables.
 __global__ __launch_bounds__(1024) void route_scan_kernel(CallBufs b, int T, int E, int k, int S, int C) {
-  __shared__ int cnt[1024], offs[1024], act[1024], mt_off[1024];
+  __shared__ int cnt[1024], offs[1024], act[1024], mt_off[1024], part[1024];
   __shared__ GroupScan gs;
-  const int e = threadIdx.x;
-  if (e < E) {
-    const uint64_t* __restrict__ gm = b.gmask;
-    int32_t* __restrict__ cb = b.cbase;
+  // P threads per expert, each over a contiguous range of the chunks: first their row counts,
+  // then (after the counts of the ranges before are known) each chunk's base row
+  const int P = E <= 512 ? 1024 / E : 1;
+  const int e = threadIdx.x % E, p = threadIdx.x / E;
+  const bool on = p < P;
+  const int c_lo = p * C / P, c_hi = (p + 1) * C / P;
+  const uint64_t* __restrict__ gm = b.gmask;
+  int32_t* __restrict__ cb = b.cbase;
+  if (on) {
     int c = 0;
-    for (int ch0 = 0; ch0 < C; ch0 += 16) {
+    for (int ch0 = c_lo; ch0 < c_hi; ch0 += 16) {
       uint64_t mv[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) mv[u] = ch0 + u < C ? gm[(size_t)(ch0 + u) * E + e] : 0ull;
+      for (int u = 0; u < 16; ++u) mv[u] = ch0 + u < c_hi ? gm[(size_t)(ch0 + u) * E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c += __popcll(mv[u]);
+    }
+    part[p * E + e] = c;
+  }
+  __syncthreads();
+  if (on) {
+    int base = 0, total = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = part[q * E + e];
+      base += q < p ? v : 0;
+      total += v;
+    }
+    for (int ch0 = c_lo; ch0 < c_hi; ch0 += 16) {
+      uint64_t mv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mv[u] = ch0 + u < c_hi ? gm[(size_t)(ch0 + u) * E + e] : 0ull;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        if (ch0 + u < C) cb[(size_t)(ch0 + u) * E + e] = c;
-        c += __popcll(mv[u]);
+        if (ch0 + u < c_hi) cb[(size_t)(ch0 + u) * E + e] = base;
+        base += __popcll(mv[u]);
       }
     }
-    cnt[e] = c;
-    offs[e] = c;
+    if (p == 0) {
+      cnt[e] = total;
+      offs[e] = total;
+    }
   }
   __syncthreads();
   if (threadIdx.x < 64) group_scan_wave<true>(offs, act, mt_off, &gs, T, E, S);
