@@ -8,9 +8,7 @@
 
 namespace moe {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 // ---- cross-lane reductions on DPP (no LDS round trips) ------------------------------
@@ -96,34 +94,6 @@ constexpr int kChunk = 64;        // tokens per routing chunk (one bit per token
 constexpr int kGemmBM = 64;       // grouped-GEMM rows per M-tile
 constexpr int kGemmBN = 64;       // grouped-GEMM output columns per workgroup
 
-// e8m0 scale byte -> float32 with bit pattern s << 23 (s = 0 gives +0, s = 255 gives +inf).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
-
-// Eight e2m1 codes (one dword; byte q holds elements 2q and 2q+1) -> four bf16 pairs / four
-// fp32 pairs, each value multiplied by `scale` by the gfx950 scaled FP4 converts.
-__device__ __forceinline__ void fp4x8_to_bf16(uint32_t v, float scale, bf16x2 out[4]) {
-  out[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
-  out[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
-  out[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
-  out[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
-}
-__device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float scale, f32x2 out[4]) {
-  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 0);
-  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 1);
-  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 2);
-  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, 3);
-}
-
-// Eight e2m1 codes -> one bf16x8 MFMA operand (value i from nibble i), times `scale`.
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
-  bf16x2 p[4];
-  fp4x8_to_bf16(v, scale, p);
-  bf16x8 r;
-  r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
-  r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
-  return r;
-}
-
 // ---- exact FP8 (e4m3) term splits for the block-scaled MFMA ------------------------
 // A 32-value block v is written as S * (t0 + t1/16 + t2/256 + ...), each t an e4m3 value, with
 // S = 2^(s-127) a power of two chosen from the block's largest magnitude so that |v/S| < 256
@@ -149,6 +119,11 @@ __device__ __forceinline__ uint32_t fp8_of(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
 }
 __device__ __forceinline__ float f32_of_fp8(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+// 0x7F (e4m3 NaN; OR-ing it into any byte gives a NaN byte) for an infinite or NaN value, else
+// 0.  Non-finite activations stay non-finite through the FP8 terms, as they would in the
+// float products they stand for (an e8m0 scale byte of 255 means +inf).
+constexpr uint32_t kFp8NaN = 0x7Fu;
+__device__ __forceinline__ uint32_t fp8_nan_mask(float v) { return fabsf(v) <= 3.402823466e38f ? 0u : kFp8NaN; }
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -157,11 +132,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// Token of grouped row r: routed rows carry t*k+j in perm; the shared expert's rows
-// (r >= T*k) are the tokens in order.
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Operands of v_mfma_scale_f32_16x16x128_f8f6f4 (probed lane layout, 16x16 output tile):
 // * FP4 operand, lane (n, q) = (lane % 16, lane / 16): the 32 values of K block q of row/column
@@ -185,6 +156,8 @@ __device__ __forceinline__ f32x4 mma_f8f4_sb(const i32x8& a, const i32x8& b, f32
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, SELB, sb);
 }
 
+// Token of grouped row r: routed rows carry t*k+j in perm; the shared expert's rows
+// (r >= T*k) are the tokens in order.
 __device__ __forceinline__ int row_token(const int32_t* perm, int r, int tk, int k) {
   return r < tk ? perm[r] / k : r - tk;
 }
@@ -262,9 +235,9 @@ hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* w
                                 const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
-// The whole layer for a small batch in one launch (decode.hip).  With `route_inside` the
-// launch also scores, quantizes x and routes (route_fused batches); otherwise the routing
-// tables and the FP8 activation terms come from earlier launches on the stream.
+// Decode GEMV kernels (gemv.hip): gate/up + SwiGLU into h, then down + the combine into y.
+// They read the routing tables and the FP8 activation terms earlier launches on the stream
+// wrote.
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b, int T,
                               int max_act, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T, int max_act,

@@ -336,9 +336,10 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
             const size_t r = (size_t)(r0 + lrow);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
+              const uint32_t nanm = fp8_nan_mask(hv[c]);  // non-finite h stays NaN in both terms
               const float v = hv[c] * inv;
-              const uint32_t t0 = fp8_of(v);
-              const uint32_t t1 = fp8_of((v - f32_of_fp8(t0)) * 16.f);
+              const uint32_t t0 = fp8_of(v) | nanm;
+              const uint32_t t1 = fp8_of((v - f32_of_fp8(t0)) * 16.f) | nanm;
               const size_t o = r * N + nb + 16 * c + m;
               h8[o] = (uint8_t)t0;
               h_lo[o] = (uint8_t)t1;

@@ -254,12 +254,13 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
           const size_t r = (size_t)(row0 + c0 + tok_i);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
+            const uint32_t nanm = fp8_nan_mask(hv[c][i]);  // non-finite h stays NaN in every term
             float v = hv[c][i] * inv;
-            const uint32_t t0 = fp8_of(v);
+            const uint32_t t0 = fp8_of(v) | nanm;
             v = (v - f32_of_fp8(t0)) * 16.f;
-            const uint32_t t1 = fp8_of(v);
+            const uint32_t t1 = fp8_of(v) | nanm;
             v = (v - f32_of_fp8(t1)) * 16.f;
-            const uint32_t t2 = fp8_of(v);
+            const uint32_t t2 = fp8_of(v) | nanm;
             const size_t o = r * I + nb + 16 * c + m;
             h8[o] = (uint8_t)t0;
             h8[(size_t)R * I + o] = (uint8_t)t1;

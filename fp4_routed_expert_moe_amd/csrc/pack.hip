@@ -13,14 +13,22 @@
 //
 // Each workgroup transposes a tile of 64 rows x 64 blocks through LDS, reading and writing
 // whole 16-byte chunks with consecutive threads on consecutive addresses.
+//
+// e8m0 edges.  A scale byte s means the float with bit pattern s << 23 ("DeepSeek V4: the
+// CUDA kernels, as a tier rather than an engine", PR #772, the note on the MXFP4 decode), so
+// s = 0 is +0: every value of such a block is 0.  OCP MX reads byte 0 as 2^-127 instead, so
+// the repack writes the 16 code bytes of an s = 0 block as zeros: the block is then exactly 0
+// whichever reading the matrix cores take.  s = 255 (+inf here, NaN under OCP MX) is kept:
+// either reading makes the block's products non-finite, and the kernels carry non-finite
+// intermediate values on as NaN.
 #include "common.h"
 
 namespace moe {
 
 constexpr int kPackTile = 64;
 
-__global__ __launch_bounds__(256) void pack_codes_kernel(const uint4* __restrict__ in, uint4* __restrict__ out,
-                                                         int N, int KB, int ntiles) {
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint4* __restrict__ in, const uint8_t* __restrict__ sc,
+                                                         uint4* __restrict__ out, int N, int KB, int ntiles) {
   __shared__ uint4 tile[kPackTile][kPackTile + 1];
   const int g = blockIdx.x / ntiles;
   const int n0 = (blockIdx.x - g * ntiles) * kPackTile;
@@ -29,7 +37,10 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint4* __restrict
   for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
     const int r = i / kPackTile, c = i % kPackTile;  // c fastest: contiguous chunks of one row
     const int n = n0 + r, kb = kb0 + c;
-    if (n < N && kb < KB) tile[r][c] = in[gin + (size_t)n * KB + kb];
+    if (n < N && kb < KB) {
+      const size_t o = gin + (size_t)n * KB + kb;  // chunk o = block kb of row n; its scale is byte o
+      tile[r][c] = sc[o] ? in[o] : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
@@ -69,8 +80,8 @@ hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_
   const int ntiles = (N + kPackTile - 1) / kPackTile;
   dim3 grid(ntiles * groups, (KB + kPackTile - 1) / kPackTile);
   int tk = timing_begin("pack_codes", s);
-  pack_codes_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4*>(codes_in), reinterpret_cast<uint4*>(codes_out),
-                                         N, KB, ntiles);
+  pack_codes_kernel<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4*>(codes_in), scales_in,
+                                         reinterpret_cast<uint4*>(codes_out), N, KB, ntiles);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

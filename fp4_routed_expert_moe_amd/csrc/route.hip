@@ -91,6 +91,12 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
 // minus its own truncation).  x (bf16) times each term is exact in fp32, so a score is the
 // fp32 dot product up to summation order, which is fixed per (token, expert).  64 tokens x
 // 64 experts per workgroup, 32 x 32 per wave (2 x 2 MFMA tiles, three terms each).
+// Rounding chain of a score: each 32-value step's top-term products go through one MFMA
+// that starts from zero (any internal order: at most 31 roundings of that step's products),
+// and that step's result is added into the running fp32 sum with one VALU add; the two low
+// terms (2^-8 and 2^-16 of the products) accumulate in MFMA chains of their own, added at
+// the end.  So a product passes at most 31 + steps + 1 roundings before the slice's partial
+// score, plus one per slice when the top-k adds the slices and one for the bias.
 // Operand layout: lane l holds row (token or expert) l % 16, K values 8*(l/16) .. +8 of each
 // 32-value step; result lane l, element i -> token 4*(l/16) + i, expert l % 16.
 // ------------------------------------------------------------------------------------
@@ -164,11 +170,23 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
   const int r = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * kRouterGemmTile + (wave & 1) * 32;
   const int e0 = blockIdx.y * kRouterGemmTile + (wave >> 1) * 32;
-  f32x4 acc[2][2];
+  f32x4 acc[2][2], acc_lo[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = acc_lo[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one 32-value step: top term from zero, added into acc; low terms chained in acc_lo
+  auto mma_step = [&](const bf16x8 (&xa)[2], const bf16x8 (&wb)[2][3]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb[j][1], acc_lo[i][j], 0, 0, 0);
+        acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb[j][2], acc_lo[i][j], 0, 0, 0);
+        acc[i][j] += hi;
+      }
+  };
   if constexpr (STAGED) {
     // The tile's 64 tokens and 64 experts pass through LDS 64 K values at a time: x as bf16,
     // W_r split into its three bf16 terms once per workgroup (each wave reads the half it
@@ -215,12 +233,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
           for (int t = 0; t < 3; ++t)
             wb[j][t] = *reinterpret_cast<const bf16x8*>(&ws3[buf][t][(wave >> 1) * 32 + 16 * j + r][32 * u + 8 * kq]);
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wb[j][t], acc[i][j], 0, 0, 0);
+        mma_step(xa, wb);
       }
     };
     Stage st;
@@ -268,14 +281,8 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
         bf16x8 bt[2][3];
 #pragma unroll
         for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[u][i]), bt[j][t],
-                                                                  acc[i][j], 0, 0, 0);
+        const bf16x8 xv[2] = {__builtin_bit_cast(bf16x8, xr[u][0]), __builtin_bit_cast(bf16x8, xr[u][1])};
+        mma_step(xv, bt);
       }
     }
   }
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + 16 * i + 4 * kq + v;
-        if (t < T) logits[(size_t)t * E + e] = acc[i][j][v] + be;
+        if (t < T) logits[(size_t)t * E + e] = (acc[i][j][v] + acc_lo[i][j][v]) + be;
       }
     }
 }

@@ -18,8 +18,13 @@ namespace moe {
 // wave w of the group adds x[h]*w[h] over its quarter of the hidden axis, lane l taking
 // h = w*H/4 + 8l + 512j + i (j ascending, i = 0..7) with fused multiply-adds in that order;
 // the lanes are summed in the fixed DPP order of wave_sum_f32 and the four quarters in wave
-// order.  Every kernel that scores uses this, so a token's scores depend neither on the batch
-// nor on the kernel.  All of a lane's loads are issued before the first product.
+// order.  The one-launch router (batches route_fused takes) scores with this, so there a
+// token's scores do not depend on the batch it comes in.  Larger batches score on the matrix
+// cores (router_gemm_kernel) in another summation order: the same fp32 dot product, not the
+// same bits.  All of a lane's loads are issued before the first product.
+// Rounding chain: a lane's FMAs round once each (8 per 512 values of the quarter), then four
+// DPP adds and three lane-total adds, three quarter adds and the bias: a product passes at
+// most 8*ceil(H/2048) + 11 roundings.
 // ------------------------------------------------------------------------------------
 constexpr int kScoreTT = 4;  // tokens per router workgroup (4 measured faster than 8 or 2 at 8 tokens)
 constexpr int kScoreWaves = 4;
@@ -127,6 +132,12 @@ __device__ __forceinline__ XBlock quantize_x_block(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = (v[j] - f32_of_fp8((th[i] >> (8 * j)) & 0xFFu)) * 16.f;
     tl[i] = pack_fp8x4(r[0], r[1], r[2], r[3]);
+    // a non-finite value (the convert would saturate an infinity) becomes NaN in both terms
+    uint32_t nanm = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nanm |= fp8_nan_mask(v[j]) << (8 * j);
+    th[i] |= nanm;
+    tl[i] |= nanm;
   }
   XBlock b;
   b.hi[0] = make_uint4(th[0], th[1], th[2], th[3]);

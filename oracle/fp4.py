@@ -61,12 +61,10 @@ def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     k = 2 * half_k
     if scales.shape != (n, k // 32) or k % 32:
         raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
-    lo = codes & 0x0F
-    hi = codes >> 4
-    nib = np.empty((n, k), dtype=np.uint8)
-    nib[:, 0::2] = lo
-    nib[:, 1::2] = hi
-    vals = E2M1_VALUES[nib]
+    # byte b -> (value of its low nibble, value of its high nibble): elements 2i and 2i+1
+    byte = np.arange(256)
+    pair = np.stack([E2M1_VALUES[byte & 0x0F], E2M1_VALUES[byte >> 4]], axis=1)   # [256][2]
+    vals = pair[codes].reshape(n, k // 32, 32)   # [N][K/32][32]: block j holds elements 32j..32j+31
     s = E8M0_VALUES[scales]                       # [N][K/32]
     with np.errstate(invalid="ignore"):          # 0 * inf (s=255) is NaN, as in float math
-        return vals * np.repeat(s, 32, axis=1)
+        return (vals * s[:, :, None]).reshape(n, k)

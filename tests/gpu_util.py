@@ -1,6 +1,9 @@
 """Helpers for the GPU parity tests: build layers on the device, run them, compare with the oracle."""
 from __future__ import annotations
 
+import concurrent.futures
+import multiprocessing
+import os
 import sys
 
 import numpy as np
@@ -84,37 +87,84 @@ def kernel_layout_scales(scales):
     return six.transpose(0, 4, 1, 3, 5, 2)              # [g][i][t][m][q][j]
 
 
-def weight_tolerance(x_bits, w_router, bias, idx):
-    """Per-token bound on |w_gpu - w_ref| from the arithmetic (not fitted to results).
+def router_chain(tokens, experts, hidden):
+    """Which router kernel scores a batch of `tokens`, and the longest rounding chain of a score.
 
-    A GPU score is an fp32 sum of the H products x_h * W[e,h] (+ b_e) in some fixed order.  The
-    longest chain of fp32 roundings is the matrix-core router's: one per MFMA step for each of
-    the three bf16 terms of W (3H/32), plus the reduction tail; bound it by n = 2*(3H/32) + 64.
-    Every partial sum is at most S = sum_h |x_h W[e,h]| + |b_e|, so |dl| <= n * u * S (Higham's
-    gamma_n bound), and the oracle's rounding of its float64 score to fp32 adds u * |l|.  A
-    softmax weight moves by at most 2 * max_j |dl_j| (d w_j / d l_i = w_j (delta_ij - w_i)),
-    and the fp32 exp and divide add a few ulps (1e-6 covers them).
+    The library's dispatch rule (route.hip, route_fused / router_slices): batches with
+    T <= 64 and T*E <= 8192 are scored by the one-launch FMA router, larger ones by the
+    matrix-core router cut into `slices` hidden-axis slices.  Chains, in fp32 roundings a
+    product can pass before the score is final:
+    * FMA router: one per FMA of the lane (8 per 512 values of a quarter of H), four DPP adds
+      and three lane-total adds, three quarter adds, the bias: 8*ceil(H/2048) + 11, each a
+      round-to-nearest (unit u = 2^-24).
+    * matrix-core router: the step's MFMA (32 exact products from zero, any internal order:
+      at most 31), one add per 32-value step of the longest slice, the low-term add, one per
+      slice in the top-k's sum, the bias.  Counted at 2u each, which also covers a matrix
+      core that truncates.  The low bf16 terms of W_r (at most 2^-7 of |W_r|) add a chain of
+      31 + 2*steps of their own.
+    """
+    if tokens <= 64 and tokens * experts <= 8192:
+        return dict(kind="fused", n=8 * -(-hidden // 2048) + 11, unit=U32, lo_n=0)
+    tiles = -(-tokens // 64) * -(-experts // 64)
+    ks = min(max(-(-512 // tiles), 1), 16, hidden // 32)
+    steps = -(-(hidden // 32) // ks)
+    return dict(kind="gemm", slices=ks, n=31 + steps + 1 + ks + 1, unit=2 * U32, lo_n=31 + 2 * steps)
+
+
+def weight_tolerance(x_bits, w_router, bias, idx, w_ref=None, tokens_per_call=None):
+    """Bound on |w_gpu - w_ref| for each selected (token, slot), [T][k], from the arithmetic of
+    the router kernel that scored the batch (router_chain), not fitted to results.
+
+    Score error: every product x_h*W[e,h] and the bias pass at most n roundings of relative
+    size `unit`, so |dl_e| <= gamma_n * S_e with S_e = sum_h |x_h W[e,h]| + |b_e| (Higham's
+    bound for any summation order of that height), plus the low-term chain, plus u*|l_e| for
+    the oracle's own rounding of its float64 score to fp32.
+    Weight error: w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) moves by w_j (dl_j - sum_i w_i
+    dl_i) to first order, so |dw_j| <= w_j (|dl_j| + sum_i w_i |dl_i|); the kernel's own fp32
+    exp, sum and divide add w_j (|l_j - l_0| + k + 12) u.
     """
     x = bf16_bits_to_f64(x_bits)
     w = np.asarray(w_router, dtype=np.float64)
-    h = w.shape[1]
-    s = np.abs(x) @ np.abs(w).T                       # [T][E]
+    t_count, hidden = x.shape
+    experts = w.shape[0]
+    idx = np.asarray(idx, dtype=np.int64)
+    k = idx.shape[1]
+    ch = router_chain(tokens_per_call or t_count, experts, hidden)
+    s = np.abs(x) @ np.abs(w).T                        # [T][E]
+    l = x @ w.T
     if bias is not None:
-        s = s + np.abs(np.asarray(bias, dtype=np.float64))
-    n = 2 * (3 * h // 32) + 64
-    dl = np.take_along_axis(s, np.asarray(idx, dtype=np.int64), axis=1).max(axis=1) * (n + 1) * U32
-    return 2.0 * dl + 1e-6                            # [T]
+        bb = np.asarray(bias, dtype=np.float64)
+        s = s + np.abs(bb)
+        l = l + bb
+    n, unit = ch["n"], ch["unit"]
+    gamma = n * unit / (1.0 - n * unit)
+    lo = ch["lo_n"] * unit * 2.0 ** -7 * 1.01
+    dl_all = (gamma + lo + 1e-12) * s + U32 * np.abs(l)
+    dl = np.take_along_axis(dl_all, idx, axis=1)      # [T][k]
+    ls = np.take_along_axis(l, idx, axis=1)
+    if w_ref is None:
+        p = np.exp(ls - ls[:, :1])
+        w_ref = p / p.sum(axis=1, keepdims=True)
+    w_ref = np.asarray(w_ref, dtype=np.float64)
+    first = w_ref * (dl + (w_ref * dl).sum(axis=1, keepdims=True)) * 1.01
+    own = w_ref * (np.abs(ls - ls[:, :1]) + k + 12) * U32
+    return first + own + 1e-9
 
 
-def check_routing(got, ref, x_bits, w_router, bias=None):
+def check_routing(got, ref, x_bits, w_router, bias=None, tokens_per_call=None):
     np.testing.assert_array_equal(got["idx"], ref["idx"])
     np.testing.assert_array_equal(got["counts"], ref["counts"])
     np.testing.assert_array_equal(got["offsets"], ref["offsets"])
     np.testing.assert_array_equal(got["perm"], ref["perm"])
-    tol = weight_tolerance(x_bits, w_router, bias, ref["idx"])
-    err = np.abs(np.asarray(got["weight"], dtype=np.float64) - ref["w"]).max(axis=1)
-    bad = np.nonzero(err > tol)[0]
-    assert bad.size == 0, f"routing weights off for tokens {bad[:8]}: err {err[bad[:8]]} > tol {tol[bad[:8]]}"
+    check_weights(got["weight"], ref, x_bits, w_router, bias, tokens_per_call)
+
+
+def check_weights(weight, ref, x_bits, w_router, bias=None, tokens_per_call=None):
+    tol = weight_tolerance(x_bits, w_router, bias, ref["idx"], ref["w"], tokens_per_call)
+    err = np.abs(np.asarray(weight, dtype=np.float64) - ref["w"])
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (f"routing weights off at (token, slot) {bad[:8].tolist()}: "
+                           f"err {err[tuple(bad[:8].T)]} > tol {tol[tuple(bad[:8].T)]}")
 
 
 def output_error(y, y_ref):
@@ -157,3 +207,74 @@ def check_device_weights(wl, layer, weights, groups):
             c, s = synth.expert_matrix(wl, layer, mat, g)
             assert torch.equal(weights[mat][0][g].cpu(), c), (mat, g)
             assert torch.equal(weights[mat][1][g].cpu(), s), (mat, g)
+
+
+# ---- the oracle on many sampled tokens, in parallel host processes -------------------------
+# The float64 oracle decodes each expert it meets (about 1 s per expert at H=4096, I=2048), so
+# full-size checks run it in worker processes (spawned: the parent has a HIP context), each on
+# a chunk of the sampled tokens whose routed experts overlap.
+_POOL = None
+
+
+def oracle_workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _one_thread():
+    # each worker runs numpy on one core: the pool, not BLAS threads, spreads the work
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    torch.set_num_threads(1)
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = concurrent.futures.ProcessPoolExecutor(oracle_workers(), initializer=_one_thread,
+                                                       mp_context=multiprocessing.get_context("spawn"))
+    return _POOL
+
+
+def _oracle_job(args):
+    wl, layer, x_bits, w_router, bias, top_k, shared = args
+    return oracle.moe_forward(x_bits, w_router, bias, synth.LazyExperts(wl, layer, cache=2), top_k, shared)["y"]
+
+
+def oracle_outputs(jobs):
+    """y of oracle.moe_forward for each job (wl, layer, x_bits, w_router, bias, top_k, shared)."""
+    return list(_pool().map(_oracle_job, jobs))
+
+
+def oracle_sampled(wl, layer, x_bits, w_router, bias, tokens, idx):
+    """Oracle outputs [len(tokens)][H] of the given tokens of one layer call, computed in chunks
+    of tokens grouped by their first expert (so a chunk decodes fewer distinct experts)."""
+    tokens = np.asarray(tokens)
+    order = tokens[np.argsort(np.asarray(idx)[tokens, 0], kind="stable")]
+    n = min(len(order), 2 * oracle_workers())
+    chunks = [c for c in np.array_split(order, n) if len(c)]
+    ys = oracle_outputs([(wl, layer, np.ascontiguousarray(x_bits[c]), w_router, bias, wl.top_k, wl.shared)
+                         for c in chunks])
+    out = {}
+    for c, y in zip(chunks, ys):
+        for t, row in zip(c, y):
+            out[int(t)] = row
+    return np.stack([out[int(t)] for t in tokens])
+
+
+def sample_tokens(got, top_k, spread=48, hot=3, per_hot=8):
+    """Tokens whose outputs a full-size test checks: `spread` evenly over the batch, and in each of
+    the `hot` experts with the most rows, the tokens of its first and last grouped rows, the last
+    row of its first 64-row M-tile, the first row of its last (partial) M-tile, and `per_hot`
+    rows spread in between."""
+    t_count = got["idx"].shape[0]
+    picks = set(np.linspace(0, t_count - 1, min(spread, t_count)).astype(int).tolist())
+    counts, offsets, perm = got["counts"], got["offsets"], got["perm"]
+    for e in np.argsort(-counts, kind="stable")[:hot]:
+        rows = perm[offsets[e]:offsets[e + 1]] // top_k
+        n = len(rows)
+        if n == 0:
+            continue
+        last_tile = 64 * ((n - 1) // 64)
+        at = {0, min(63, n - 1), last_tile, n - 1} | set(np.linspace(0, n - 1, per_hot).astype(int).tolist())
+        picks |= {int(rows[i]) for i in at}
+    return np.array(sorted(picks))

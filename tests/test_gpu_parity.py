@@ -1,7 +1,9 @@
 """GPU parity: the HIP layer against the float64 oracle on the same seeded inputs.
 
-Routing (idx, counts, offsets, perm) must match bit for bit; weights within 2e-6; outputs
-within rel-L2 5e-3 and max|dy| <= 2e-2 * rms(y_ref).
+Routing (idx, counts, offsets, perm) must match bit for bit; weights within the bound that the
+rounding chain of the router kernel that ran gives (gpu_util.weight_tolerance; a bf16-rounded
+router breaks it, tests/test_tolerance_cpu.py); outputs within rel-L2 5e-3 and
+max|dy| <= 2e-2 * rms(y_ref).
 """
 import numpy as np
 import pytest
@@ -11,7 +13,8 @@ import moe_synth as synth
 import oracle
 from helpers import random_experts, screened_tokens, identity_experts
 from gpu_util import (check_device_weights, check_outputs, check_routing, kernel_layout_scales, make_layer,
-                      oracle_routing, pack_weights, require_gpu, run_layer, say, stack_groups, x_to_device)
+                      oracle_routing, oracle_sampled, output_error, pack_weights, require_gpu, run_layer,
+                      sample_tokens, say, stack_groups, x_to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +57,12 @@ def test_pack_is_the_block_transpose(shape):
     rng = np.random.default_rng(n + k)
     codes = rng.integers(0, 256, (g, n, k // 2), dtype=np.uint8)
     scales = rng.integers(0, 256, (g, n, k // 32), dtype=np.uint8)
+    scales[:, 0, 0] = 0
     pc, ps = pack_fp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
     torch.cuda.synchronize()
-    want_c = codes.reshape(g, n, k // 32, 16).transpose(0, 2, 1, 3)
+    # a block whose scale byte is 0 (+0) is all zeros: its 16 code bytes are written as zeros
+    blocks = codes.reshape(g, n, k // 32, 16) * (scales != 0)[..., None]
+    want_c = blocks.transpose(0, 2, 1, 3)
     np.testing.assert_array_equal(pc.cpu().numpy(), want_c)
     np.testing.assert_array_equal(ps.cpu().numpy(), kernel_layout_scales(scales))
 
@@ -128,10 +134,11 @@ def test_every_token_on_one_expert():
 
 
 def test_zero_and_extreme_scales():
-    # s=0 blocks contribute exactly zero; the e8m0 scales are applied exactly by the hardware.
-    # The GEMV path carries x exactly and h with 12 significant bits (three FP8 terms), so it
-    # is held to rel-L2 1e-4 over a wide scale range; the GEMM path rounds h to bf16 (8 bits;
-    # heavier-tailed outputs here), so it gets a narrower range under the standard gate.
+    # s=0 blocks next to non-zero ones, over wide scale ranges (2^-17 .. 2^9).  The GEMV path
+    # carries x exactly and h with 12 significant bits (three FP8 terms), so it is held to
+    # rel-L2 1e-4; the GEMM path rounds h to 8 bits (two terms, bf16's precision), which at the
+    # wide range meets rel-L2 but not the max gate (test_gemm_wide_scale_range_error below), so
+    # it runs the narrower 2^-7 .. 2^3 here under the standard gate.
     for path, lo, hi in (("gemv", 110, 136), ("gemm", 120, 130)):
         groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=lo, scale_hi=hi)
         for g in groups[::2]:
@@ -142,6 +149,91 @@ def test_zero_and_extreme_scales():
             ref = oracle.moe_forward(x, wr, b, groups, 2, 1)["y"]
             d = outs["gemv"]["y"].astype(np.float64) - ref
             assert np.linalg.norm(d) <= 1e-4 * np.linalg.norm(ref)
+
+
+def test_gemm_wide_scale_range_error():
+    # What the 8-bit h of the prefill path does at scales 2^-17 .. 2^9: rel-L2 stays in the gate;
+    # the largest error, relative to rms(y), is reported (heavy-tailed outputs make it the gate
+    # that fails first) and must stay below 5 times the max gate.
+    groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=110, scale_hi=136)
+    ref = oracle.moe_forward(x, wr, b, groups, 2, 1)
+    got = run_layer(make_layer(wr, stack_groups(groups), 2, 1, b, "gemm"), x)
+    check_routing(got, ref, x, wr, b)
+    e = output_error(got["y"], ref["y"])
+    say(f"  gemm at scales 110..136: rel_l2={e['rel_l2']:.3e} max/rms={e['max_over_rms']:.3e} "
+        f"max|y|/rms={e['max_ref'] / e['rms_ref']:.1f}")
+    assert e["rel_l2"] <= 5e-3 and e["max_over_rms"] <= 0.1
+
+
+# ------------------------------------------------------------------------- e8m0 edges
+# An e8m0 byte s is the float with bit pattern s << 23 ("DeepSeek V4: the CUDA kernels, as a tier
+# rather than an engine", PR #772, the note on the MXFP4 decode): s = 0 is +0, s = 255 is +inf.
+
+
+def test_e8m0_zero_scale_blocks_are_exact_zeros():
+    # Every block of every expert at s = 0: all weights are +0, so y is +0 bit for bit.  Then only
+    # the down matrices at s = 0, with gate/up normal: h is large (~1e3), so reading byte 0 as
+    # 2^-127 instead of +0 would leave values around 1e-33 in y; +0 leaves exact zeros.
+    for what in ("all", "down"):
+        groups, wr, b, x = _random_case(21, 256, 8, 2, 1, 128, 24)
+        for g in groups:
+            for mat in (("gate", "up", "down") if what == "all" else ("down",)):
+                g[mat][1][:] = 0
+        ref = oracle.moe_forward(x, wr, b, groups, 2, 1)
+        assert (ref["y"] == 0).all()
+        weights = stack_groups(groups)
+        for path in ("gemv", "gemm"):
+            got = run_layer(make_layer(wr, weights, 2, 1, b, path), x)
+            check_routing(got, ref, x, wr, b)
+            nz = np.count_nonzero(got["y"].view(np.uint32))
+            assert nz == 0, f"{what}/{path}: {nz} outputs are not +0 (max |y| {np.abs(got['y']).max():.3e})"
+
+
+def test_e8m0_255_scale_blocks_are_non_finite_where_the_oracle_is():
+    # One s = 255 (+inf) block in a gate row of routed expert 3 (every output of its tokens turns
+    # non-finite through h) and one in a down row of expert 5 (one output column of its tokens).
+    groups, wr, b, x = _random_case(22, 256, 8, 2, 1, 128, 24)
+    groups[3]["gate"][1][7, 2] = 255
+    groups[5]["down"][1][100, 1] = 255
+    ref = oracle.moe_forward(x, wr, b, groups, 2, 1)
+    bad_ref = ~np.isfinite(ref["y"])
+    assert bad_ref.any() and not bad_ref.all()
+    weights = stack_groups(groups)
+    for path in ("gemv", "gemm"):
+        got = run_layer(make_layer(wr, weights, 2, 1, b, path), x)
+        check_routing(got, ref, x, wr, b)
+        bad = ~np.isfinite(got["y"])
+        mism = np.argwhere(bad != bad_ref)
+        assert mism.size == 0, f"{path}: non-finite positions differ at {mism[:6].tolist()}"
+        ok = ~bad_ref.any(axis=1)                      # tokens with no non-finite output
+        check_outputs(got["y"][ok], ref["y"][ok], f"finite tokens path={path}")
+
+
+# --------------------------------------------------------------- router switch
+
+
+@pytest.mark.parametrize("experts,limit", [(256, 32), (64, 64)])
+def test_router_switch_keeps_routing(experts, limit):
+    # Batches up to `limit` tokens are scored by the one-launch FMA router, one more by the
+    # matrix-core router (T*E > 8192 scores, or T > 64).  Both must route every token exactly as
+    # the oracle does; a token's output differs between the two only by rounding.
+    groups, wr, b, x = _random_case(23 + experts, 512, experts, 4, 1, 256, limit + 1)
+    weights = stack_groups(groups)
+    ref_all = oracle.moe_forward(x, wr, b, groups, 4, 1)
+    for path in ("gemv", "gemm"):
+        layer = make_layer(wr, weights, 4, 1, b, path)
+        big = run_layer(layer, x)
+        small = run_layer(layer, x[:limit])
+        check_routing(big, ref_all, x, wr, b)
+        ref_small = oracle.moe_forward(x[:limit], wr, b, groups, 4, 1)
+        check_routing(small, ref_small, x[:limit], wr, b)
+        np.testing.assert_array_equal(small["idx"], big["idx"][:limit])
+        check_outputs(big["y"], ref_all["y"], f"T={limit + 1} path={path}")
+        check_outputs(small["y"], ref_small["y"], f"T={limit} path={path}")
+        for t in (0, limit // 2, limit - 1):
+            one = run_layer(layer, x[t:t + 1])
+            np.testing.assert_array_equal(one["idx"][0], big["idx"][t])
+            np.testing.assert_array_equal(one["y"][0], small["y"][t])   # same router: same bits
 
 
 def test_single_token_and_batch_equals_single():
@@ -222,7 +314,7 @@ def test_workspace_errors():
 # ------------------------------------------------------------------ full-size workloads
 
 
-def _full_size(name, sample_tokens, layer_index=0, bias=True):
+def _full_size(name, layer_index=0, spread=48):
     wl = synth.WORKLOADS[name]
     say(f"[{name}] generating weights on the GPU")
     weights = synth.layer_weights(wl, layer_index, device="cuda")
@@ -236,30 +328,34 @@ def _full_size(name, sample_tokens, layer_index=0, bias=True):
     got = run_layer(layer, x)
     ref_route = oracle_routing(x, wr, b, wl.top_k)
     check_routing(got, ref_route, x, wr, b)
-    sample = np.linspace(0, x.shape[0] - 1, min(sample_tokens, x.shape[0])).astype(int)
+    sample = sample_tokens(got, wl.top_k, spread=spread)
     say(f"[{name}] oracle on {len(sample)} sampled tokens")
-    ref = oracle.moe_forward(x[sample], wr, b, synth.LazyExperts(wl, layer_index, cache=4), wl.top_k, wl.shared)
-    check_outputs(got["y"][sample], ref["y"], name)
-    return got, layer, x
+    ref_y = oracle_sampled(wl, layer_index, x, wr, b, sample, ref_route["idx"])
+    check_outputs(got["y"][sample], ref_y, name)
+    return got, layer, x, sample
 
 
 def test_decode_batch_full_size():
-    _full_size("decode_t8", 8)
+    _, _, x, sample = _full_size("decode_t8")
+    assert len(sample) == x.shape[0]
 
 
 def test_prefill_512_full_size():
-    _full_size("prefill_t512", 6)
+    _, _, _, sample = _full_size("prefill_t512")
+    assert len(sample) >= 64
 
 
 def test_prefill_4096_zipf_full_size():
-    got, _, _ = _full_size("prefill_t4096_zipf", 6)
+    got, _, _, sample = _full_size("prefill_t4096_zipf")
     assert got["counts"].max() > 0.10 * got["idx"].size
+    assert len(sample) >= 64
 
 
 def test_decode_pro_scale_full_size():
     # DeepSeek V4 Pro scale: hidden 7168 (56 K steps of 128), 384 experts (top-k over 6 keys
-    # per lane), 9 GB of FP4 experts
-    _full_size("decode_pro_t8", 4)
+    # per lane), 9 GB of FP4 experts; every token's output checked
+    _, _, x, sample = _full_size("decode_pro_t8")
+    assert len(sample) == x.shape[0]
 
 
 def test_stacked_decode_16_layers():
@@ -295,7 +391,9 @@ def test_stacked_decode_16_layers():
         ref = oracle_routing(xs[(s, l)], routers[l], None, wl.top_k)
         got = {k: v.cpu().numpy() for k, v in r.items()}
         check_routing(got, ref, xs[(s, l)], routers[l])
-    for (s, l) in [(0, 0), (17, 5), (128, 9), (255, 15)]:
-        ref = oracle.moe_forward(xs[(s, l)], routers[l], None, synth.LazyExperts(wl, l, cache=2), wl.top_k,
-                                 wl.shared)
-        check_outputs(ys[(s, l)].cpu().numpy(), ref["y"], f"stacked step={s} layer={l}")
+    # 16 (step, layer) calls, one per layer, steps spread over the run
+    calls = [(17 * l, l) for l in range(wl.layers)]
+    from gpu_util import oracle_outputs
+    refs = oracle_outputs([(wl, l, xs[(s, l)], routers[l], None, wl.top_k, wl.shared) for s, l in calls])
+    for (s, l), ref in zip(calls, refs):
+        check_outputs(ys[(s, l)].cpu().numpy(), ref, f"stacked step={s} layer={l}")

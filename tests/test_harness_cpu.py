@@ -11,16 +11,19 @@ def test_weight_tolerance_follows_the_summation_bound():
     wl = synth.WORKLOADS["tiny"]
     wr = synth.router_weights(wl)
     x = synth.tokens(wl)
-    idx, _, _ = oracle.select_experts(oracle.router_logits(x, wr, None), wl.top_k)
-    tol = weight_tolerance(x, wr, None, idx)
-    assert tol.shape == (x.shape[0],) and np.isfinite(tol).all() and (tol > 1e-6).all()
-    # doubling the weights doubles the score-magnitude part of the bound
-    tol2 = weight_tolerance(x, 2 * wr, None, idx)
-    np.testing.assert_allclose(tol2 - 1e-6, 2 * (tol - 1e-6), rtol=1e-12)
-    # the bound is n * u * S with n = 2 * (3H/32) + 64 (+1 for the oracle's own rounding)
-    s = np.abs(bf16_bits_to_f64(x)) @ np.abs(wr.astype(np.float64)).T
-    n = 2 * (3 * wl.hidden // 32) + 64 + 1
-    want = 2 * n * U32 * np.take_along_axis(s, idx.astype(np.int64), axis=1).max(axis=1) + 1e-6
+    idx, w_ref, _ = oracle.select_experts(oracle.router_logits(x, wr, None), wl.top_k)
+    tol = weight_tolerance(x, wr, None, idx, w_ref)
+    assert tol.shape == idx.shape and np.isfinite(tol).all() and (tol > 0).all()
+    # the score part: w_j (dl_j + sum_i w_i dl_i) * 1.01 with dl = (gamma_n + 1e-12) S + u |l|
+    xf = bf16_bits_to_f64(x)
+    s = np.abs(xf) @ np.abs(wr.astype(np.float64)).T
+    l = xf @ wr.astype(np.float64).T
+    n = 8 * 1 + 11                                  # one 512-value step per quarter at H=256
+    g = n * U32 / (1 - n * U32)
+    dl = np.take_along_axis((g + 1e-12) * s + U32 * np.abs(l), idx.astype(np.int64), axis=1)
+    ls = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    want = (w_ref * (dl + (w_ref * dl).sum(axis=1, keepdims=True)) * 1.01
+            + w_ref * (np.abs(ls - ls[:, :1]) + wl.top_k + 12) * U32 + 1e-9)
     np.testing.assert_allclose(tol, want, rtol=1e-12)
 
 
