@@ -17,7 +17,8 @@ MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_abi_version", "moe_device_supported", "moe_layer_create", "moe_layer_destroy",
-           "moe_workspace_bytes", "moe_route", "moe_forward", "moe_pack_fp4", "moe_status_string",
+           "moe_workspace_bytes", "moe_route", "moe_forward", "moe_pack_fp4",
+           "moe_status_string",
            "moe_last_error",
            "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 

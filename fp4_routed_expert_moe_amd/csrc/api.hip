@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -196,6 +197,12 @@ int32_t moe_device_supported(int32_t device, char* name, int32_t cap) {
       name[cap - 1] = '\0';
     }
   };
+  // test hook: MOE_FAKE_ARCH names the architecture of every device (no HIP call), so the
+  // host-side paths (create, validation, workspace sizing) can be exercised without a GPU
+  if (const char* fake = getenv("MOE_FAKE_ARCH")) {
+    put(fake);
+    return device >= 0 && strncmp(fake, "gfx950", 6) == 0 && (fake[6] == '\0' || fake[6] == ':');
+  }
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
     (void)hipGetLastError();
@@ -241,7 +248,8 @@ int32_t moe_layer_create(const moe_layer_desc* d, moe_layer** out) {
   char arch[64];
   if (!moe_device_supported(d->device, arch, sizeof(arch)))
     return fail(MOE_ERR_UNSUPPORTED, "device %d is not a supported gfx950 (%s)", d->device, arch);
-  moe_layer* L = new (std::nothrow) moe_layer;
+  // test hook: MOE_FAIL_ALLOC makes the layer's host allocation fail
+  moe_layer* L = getenv("MOE_FAIL_ALLOC") ? nullptr : new (std::nothrow) moe_layer;
   if (!L) return fail(MOE_ERR_ALLOC, "moe_layer_create: out of host memory");
   L->desc = *d;
   L->dims = moe::Dims{d->hidden, d->n_experts, d->top_k, d->n_shared, d->inter, d->n_experts + d->n_shared};

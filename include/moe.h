@@ -110,11 +110,17 @@ int32_t moe_abi_version(void);
 
 /* 1 if HIP device `device` is a gfx950 the library was built for, else 0.  Writes the
  * device's architecture name (or a reason) into name[0..cap-1], NUL-terminated, when
- * name is not NULL and cap > 0. */
+ * name is not NULL and cap > 0.  "feat(v4/cuda): the CUDA tier wired into the DeepSeek V4
+ * engine" (PR #1055, "What it is") checks the architecture before anything else runs; this is
+ * that check for gfx950.  Test hook: when the environment variable MOE_FAKE_ARCH is set, its
+ * value is taken as every device's architecture and no HIP call is made (host-side paths can
+ * then be exercised without a GPU). */
 int32_t moe_device_supported(int32_t device, char* name, int32_t cap);
 
 /* Validate `desc`, check the device, and create a layer.  On success *out is a new layer
- * (destroy with moe_layer_destroy); on failure *out is NULL and nothing is leaked.
+ * (destroy with moe_layer_destroy); on failure *out is NULL and nothing is leaked.  Test hook:
+ * with MOE_FAIL_ALLOC set in the environment the layer's host allocation fails
+ * (MOE_ERR_ALLOC).
  * Enqueues no work.  A layer is immutable after creation: concurrent calls on different
  * streams are safe when each uses its own workspace. */
 int32_t moe_layer_create(const moe_layer_desc* desc, moe_layer** out);

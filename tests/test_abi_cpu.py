@@ -109,3 +109,69 @@ def test_timing_api_without_launches(lib):
     lib.moe_timing_enable(1)
     assert lib.moe_timing_read(None, None, None, 0) == 0
     lib.moe_timing_enable(0)
+
+
+# ---- test hooks and the sanitized host build ---------------------------------------------
+
+
+def _fake_desc(**kw):
+    return _desc(hidden=4096, n_experts=256, top_k=6, n_shared=1, inter=2048, **kw)
+
+
+def test_fake_arch_hook_creates_layers_without_a_gpu(lib, monkeypatch):
+    monkeypatch.setenv("MOE_FAKE_ARCH", "gfx950")
+    buf = ctypes.create_string_buffer(64)
+    assert lib.moe_device_supported(0, buf, 64) == 1 and buf.value == b"gfx950"
+    out = ctypes.c_void_p()
+    desc = _fake_desc()
+    assert lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(out)) == _lib.MOE_OK
+    try:
+        ws = [lib.moe_workspace_bytes(out, t) for t in (1, 8, 512, 4096)]
+        assert all(w % 256 == 0 for w in ws) and ws == sorted(ws)
+    finally:
+        lib.moe_layer_destroy(out)
+    monkeypatch.setenv("MOE_FAKE_ARCH", "gfx942")
+    assert lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(out)) == _lib.MOE_ERR_UNSUPPORTED
+    assert b"gfx942" in lib.moe_last_error()
+
+
+def test_fail_alloc_hook(lib, monkeypatch):
+    monkeypatch.setenv("MOE_FAKE_ARCH", "gfx950")
+    monkeypatch.setenv("MOE_FAIL_ALLOC", "1")
+    out = ctypes.c_void_p(1234)
+    desc = _fake_desc()
+    assert lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(out)) == _lib.MOE_ERR_ALLOC
+    assert out.value is None
+
+
+def test_host_abi_code_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The library's host code (api.hip) built with ASan + UBSan on its host pass only, linked
+    with a C++ driver (abi_host_check.cpp) that walks the ABI's host paths on the CPU; leaks are
+    checked at exit."""
+    import shutil
+    import subprocess
+    from fp4_routed_expert_moe_amd import build
+    llvm = "/opt/rocm/llvm/bin/clang++"
+    if not os.path.exists(llvm):
+        pytest.skip("ROCm clang++ not found")
+    objs = [os.path.join(build.BUILD_DIR, s.replace(".hip", ".o")) for s in build.SOURCES if s != "api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build.build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_o, drv_o, exe = tmp_path / "api.o", tmp_path / "drv.o", tmp_path / "abi_host_check"
+    flags = [f for f in build.HIP_FLAGS if f != "-O3"] + ["-O1", "-g"]
+    build._run([build.hipcc(), *flags, *san, "-c", os.path.join(build.CSRC, "api.hip"), "-o", str(api_o)])
+    host_san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+    build._run([llvm, "-O1", "-g", *host_san, "-I", build.INCLUDE, "-c",
+                os.path.join(ROOT, "tests", "abi_host_check.cpp"), "-o", str(drv_o)])
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(build.hipcc()))), "lib")
+    build._run([llvm, *host_san, str(drv_o), str(api_o), *objs, "-L", rocm_lib, "-lamdhip64",
+                f"-Wl,-rpath,{rocm_lib}", "-o", str(exe)])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    env.pop("MOE_FAKE_ARCH", None)
+    env.pop("MOE_FAIL_ALLOC", None)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi host checks: ok" in r.stdout
+    shutil.rmtree(tmp_path, ignore_errors=True)

@@ -13,7 +13,7 @@ import moe_synth as synth
 import oracle
 from helpers import random_experts, screened_tokens, identity_experts
 from gpu_util import (check_device_weights, check_outputs, check_routing, kernel_layout_scales, make_layer,
-                      oracle_routing, oracle_sampled, output_error, pack_weights, require_gpu, run_layer,
+                      oracle_routing, oracle_sampled, pack_weights, require_gpu, run_layer,
                       sample_tokens, say, stack_groups, x_to_device)
 
 pytestmark = pytest.mark.gpu
@@ -134,35 +134,18 @@ def test_every_token_on_one_expert():
 
 
 def test_zero_and_extreme_scales():
-    # s=0 blocks next to non-zero ones, over wide scale ranges (2^-17 .. 2^9).  The GEMV path
-    # carries x exactly and h with 12 significant bits (three FP8 terms), so it is held to
-    # rel-L2 1e-4; the GEMM path rounds h to 8 bits (two terms, bf16's precision), which at the
-    # wide range meets rel-L2 but not the max gate (test_gemm_wide_scale_range_error below), so
-    # it runs the narrower 2^-7 .. 2^3 here under the standard gate.
-    for path, lo, hi in (("gemv", 110, 136), ("gemm", 120, 130)):
-        groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=lo, scale_hi=hi)
-        for g in groups[::2]:
-            g["gate"][1][:, 0] = 0
-            g["down"][1][5, :] = 0
-        outs = _check_case(groups, wr, b, x, 2, 1, paths=(path,), what=f"scales {lo}..{hi}")
-        if path == "gemv":
-            ref = oracle.moe_forward(x, wr, b, groups, 2, 1)["y"]
-            d = outs["gemv"]["y"].astype(np.float64) - ref
-            assert np.linalg.norm(d) <= 1e-4 * np.linalg.norm(ref)
-
-
-def test_gemm_wide_scale_range_error():
-    # What the 8-bit h of the prefill path does at scales 2^-17 .. 2^9: rel-L2 stays in the gate;
-    # the largest error, relative to rms(y), is reported (heavy-tailed outputs make it the gate
-    # that fails first) and must stay below 5 times the max gate.
+    # s=0 blocks next to non-zero ones, over a wide scale range (2^-17 .. 2^9), on both paths
+    # under the standard gate.  The GEMV path carries x exactly and h with 12 significant bits
+    # (three FP8 terms), so it is also held to rel-L2 1e-4; the GEMM path rounds h to 8 bits
+    # (two terms, bf16's precision).
     groups, wr, b, x = _random_case(9, 256, 8, 2, 1, 128, 24, scale_lo=110, scale_hi=136)
-    ref = oracle.moe_forward(x, wr, b, groups, 2, 1)
-    got = run_layer(make_layer(wr, stack_groups(groups), 2, 1, b, "gemm"), x)
-    check_routing(got, ref, x, wr, b)
-    e = output_error(got["y"], ref["y"])
-    say(f"  gemm at scales 110..136: rel_l2={e['rel_l2']:.3e} max/rms={e['max_over_rms']:.3e} "
-        f"max|y|/rms={e['max_ref'] / e['rms_ref']:.1f}")
-    assert e["rel_l2"] <= 5e-3 and e["max_over_rms"] <= 0.1
+    for g in groups[::2]:
+        g["gate"][1][:, 0] = 0
+        g["down"][1][5, :] = 0
+    outs = _check_case(groups, wr, b, x, 2, 1, what="scales 110..136")
+    ref = oracle.moe_forward(x, wr, b, groups, 2, 1)["y"]
+    d = outs["gemv"]["y"].astype(np.float64) - ref
+    assert np.linalg.norm(d) <= 1e-4 * np.linalg.norm(ref)
 
 
 # ------------------------------------------------------------------------- e8m0 edges
