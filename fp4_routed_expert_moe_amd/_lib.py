@@ -14,10 +14,11 @@ LIB_PATH = os.path.join(HERE, "libmoe_fp4.so")
 MOE_ABI_VERSION = 1
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALLOC = range(6)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_abi_version", "moe_device_supported", "moe_layer_create", "moe_layer_destroy",
-           "moe_workspace_bytes", "moe_route", "moe_forward", "moe_pack_fp4",
+           "moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_noalloc", "moe_pack_fp4",
            "moe_status_string",
            "moe_last_error",
            "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
@@ -78,6 +79,7 @@ def load(path: str = None) -> ctypes.CDLL:
         "moe_workspace_bytes": (U64, [P, I32]),
         "moe_route": (I32, [P, P, I32, ctypes.POINTER(RouteOut), P, U64, P]),
         "moe_forward": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P, U64, P]),
+        "moe_forward_noalloc": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P]),
         "moe_pack_fp4": (I32, [P, P, P, P, I32, I32, I32, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),

@@ -18,9 +18,17 @@ struct moe_layer {
   moe::Dims dims;
 };
 
+// Workspace of moe_forward_noalloc: one array per device (each GPU the library runs on holds
+// its own copy until the process ends).  In host code this name is only a stand-in: the
+// device address comes from hipGetSymbolAddress (scratch_of below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
+// set while moe_forward_noalloc runs: its launches record no timing events (no event objects
+// are created inside it)
+thread_local bool g_no_timing = false;
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -154,7 +162,7 @@ void drain_timing_locked() {
 namespace moe {
 
 int timing_begin(const char* name, hipStream_t s) {
-  if (!g_tenabled) return -1;
+  if (!g_tenabled || g_no_timing) return -1;
   std::lock_guard<std::mutex> lk(g_tmu);
   TimingRec r{name, take_event(), take_event()};
   if (!r.a || !r.b) return -1;
@@ -170,6 +178,42 @@ void timing_end(int token, hipStream_t s) {
 }
 
 }  // namespace moe
+
+// ---- moe_forward without a caller workspace -----------------------------------------
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kScratchDevices];  // device address of `scratch` on each device, once looked up
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// The device address of this device's scratch array (the current device is `dev`).  The first
+// call on a device looks it up and enqueues a kernel on `s` that zeroes the control words at
+// its start (a device array starts zeroed; every completed call leaves them at zero again).
+int32_t scratch_of(int dev, hipStream_t s, void** out) {
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d beyond the %d the library tracks", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    const int words = moe::ctrl_layout(0, 0, 0, 0).words;
+    clear_words_kernel<<<1, 64, 0, s>>>(static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: clearing the scratch control words failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+}  // namespace
 
 // =====================================================================================
 extern "C" {
@@ -348,6 +392,27 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_forward: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
+}
+
+int32_t moe_forward_noalloc(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
+                            void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID, "moe_forward_noalloc: NULL layer");
+  if (T < 0 || T > kMaxTokens)
+    return fail(MOE_ERR_INVALID, "moe_forward_noalloc: tokens=%d out of [0, %d]", T, kMaxTokens);
+  if (T == 0) return MOE_OK;
+  const uint64_t need = carve(L->dims, T, nullptr, nullptr);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward_noalloc: %d tokens need %llu bytes of scratch; the limit is %llu", T,
+                (unsigned long long)need, (unsigned long long)MOE_NOALLOC_SCRATCH_BYTES);
+  DeviceGuard dg(L->desc.device);
+  if (!dg.ok) return fail(MOE_ERR_HIP, "moe_forward_noalloc: hipSetDevice(%d) failed", L->desc.device);
+  void* ws = nullptr;
+  int32_t st = scratch_of(L->desc.device, static_cast<hipStream_t>(stream), &ws);
+  if (st != MOE_OK) return st;
+  g_no_timing = true;
+  st = moe_forward(L, x, T, y, route, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+  g_no_timing = false;
+  return st;
 }
 
 int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,

@@ -157,6 +157,19 @@ class MoeLayer:
                                         _ptr(ws), ws.numel(), _stream_handle(stream)), self.lib)
         return y
 
+    def forward_noalloc(self, x: torch.Tensor, y: torch.Tensor, route: Optional[dict] = None,
+                        stream=None) -> torch.Tensor:
+        """forward with the workspace in the library's per-device scratch array: nothing is
+        allocated, so the caller passes the output too."""
+        t = self._check_x(x)
+        if y.shape != (t, self.hidden) or y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous [{t}][{self.hidden}] float32 CUDA tensor")
+        rs = self._route_struct(route) if route is not None else None
+        _lib.check(self.lib.moe_forward_noalloc(self._h, _ptr(x), t, _ptr(y),
+                                                ctypes.byref(rs) if rs is not None else None,
+                                                _stream_handle(stream)), self.lib)
+        return y
+
     __call__ = forward
 
 

@@ -154,6 +154,23 @@ int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, f
                     const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
                     void* stream);
 
+/* Bytes of the scratch array moe_forward_noalloc uses as its workspace, per device. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same layer, the same kernels and
+ * the same result, bit for bit, with the workspace in a scratch array the library holds, one
+ * per device (MOE_NOALLOC_SCRATCH_BYTES each, kept until the process ends), instead of a
+ * caller-allocated one.  No device memory is allocated or freed.  The first call on a device
+ * looks the array up (hipGetSymbolAddress) and enqueues one small kernel on `stream` that
+ * zeroes its control words.  Calls whose workspace (moe_workspace_bytes) would exceed the
+ * array return MOE_ERR_WORKSPACE before anything is enqueued: at H=4096, E=256, top-6, one
+ * shared expert, I=2048 that allows up to 340 tokens.  Every call on a device shares its
+ * array: calls that overlap on one device (different streams or threads) race; serialise
+ * them.  Kernel timing (moe_timing_*) does not record these calls. */
+int32_t moe_forward_noalloc(const moe_layer* layer, const uint16_t* x, int32_t tokens, float* y,
+                            const moe_route_out* route, void* stream);
+
 /* Repack `groups` FP4 matrices of `rows` x `cols` (cols = reduction axis, multiple of 32)
  * from the checkpoint layout into the kernel layout (device pointers; codes 16-byte aligned,
  * scales_out 4-byte aligned and groups * ceil(cols/128) * ceil(rows/64) * 256 bytes long;

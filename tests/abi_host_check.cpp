@@ -111,6 +111,8 @@ int main(void) {
   CHECK(moe_workspace_bytes(L, 0) == w1);
   CHECK(moe_workspace_bytes(L, -1) == 0 && moe_workspace_bytes(L, (1 << 20) + 1) == 0);
   CHECK(moe_workspace_bytes(NULL, 8) == 0);
+  CHECK(moe_workspace_bytes(L, 340) <= MOE_NOALLOC_SCRATCH_BYTES);
+  CHECK(moe_workspace_bytes(L, 341) > MOE_NOALLOC_SCRATCH_BYTES);
 
   const uint16_t* x = (const uint16_t*)0x100000;
   float* y = (float*)0x200000;
@@ -130,6 +132,11 @@ int main(void) {
   CHECK(moe_route(L, x, 8, NULL, ws, w8, NULL) == MOE_ERR_INVALID);
   CHECK(moe_route(L, x, 8, &r, ws, w8, NULL) == MOE_ERR_INVALID);
   CHECK(moe_route(NULL, x, 8, &r, ws, w8, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_forward_noalloc(L, x, 341, y, NULL, NULL) == MOE_ERR_WORKSPACE);
+  CHECK(strstr(moe_last_error(), "scratch") != NULL);
+  CHECK(moe_forward_noalloc(L, x, -3, y, NULL, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_forward_noalloc(L, x, 0, y, NULL, NULL) == MOE_OK);
+  CHECK(moe_forward_noalloc(NULL, x, 8, y, NULL, NULL) == MOE_ERR_INVALID);
   moe_layer_destroy(L);
   moe_layer_destroy(NULL);
 

@@ -87,6 +87,7 @@ def test_create_null_arguments(lib):
 def test_calls_on_null_layer(lib):
     assert lib.moe_workspace_bytes(None, 8) == 0
     assert lib.moe_forward(None, None, 0, None, None, None, 0, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_forward_noalloc(None, None, 4, None, None, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_route(None, None, 4, None, None, 0, None) == _lib.MOE_ERR_INVALID
     assert b"NULL layer" in lib.moe_last_error()
     lib.moe_layer_destroy(None)
@@ -128,6 +129,11 @@ def test_fake_arch_hook_creates_layers_without_a_gpu(lib, monkeypatch):
     try:
         ws = [lib.moe_workspace_bytes(out, t) for t in (1, 8, 512, 4096)]
         assert all(w % 256 == 0 for w in ws) and ws == sorted(ws)
+        # the no-allocation entry point's limit at these dims, and its rejection (no launch)
+        assert lib.moe_workspace_bytes(out, 340) <= _lib.MOE_NOALLOC_SCRATCH_BYTES
+        assert lib.moe_workspace_bytes(out, 341) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+        assert lib.moe_forward_noalloc(out, 0x100000, 341, 0x200000, None, None) == _lib.MOE_ERR_WORKSPACE
+        assert b"scratch" in lib.moe_last_error()
     finally:
         lib.moe_layer_destroy(out)
     monkeypatch.setenv("MOE_FAKE_ARCH", "gfx942")
