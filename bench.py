@@ -53,7 +53,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_t8")
+    p.add_argument("--workload", default=None,
+                   help="measure only this workload (default: decode_t8 as the headline, plus a 'workloads' "
+                        "object with the prefill and stacked-decode workloads)")
+    p.add_argument("--no-workloads", action="store_true", help="headline only")
+    p.add_argument("--mfma-summary", metavar="DIR", help="summarise a rocprofv3 --pmc run of MFMA counters")
     p.add_argument("--layers", type=int, default=16, help="independent weight sets rotated per step")
     p.add_argument("--batches", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,24 +104,87 @@ def traffic_record(kernel, workload):
     return None
 
 
+EXTRA_WORKLOADS = ("prefill_t512", "prefill_t4096_zipf", "stacked_decode_16l")
+# per extra workload: (steps, warm-up steps, weight sets rotated, token batches rotated).  A
+# prefill call's 3.4 GB of weights is far beyond the 256 MB last-level cache, so two weight sets
+# and four token batches suffice there; the stacked workload is 16 layers by definition.
+EXTRA_SHAPE = {"prefill_t512": (50, 5, 2, 4), "prefill_t4096_zipf": (50, 5, 2, 4),
+               "stacked_decode_16l": (100, 10, 16, 64)}
+
+
+def progress(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         return pmc_summary(args)
+    if args.mfma_summary:
+        return mfma_summary(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    import torch
+
+    import moe_synth as synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    headline = args.workload or "decode_t8"
+    wl = synth.WORKLOADS[headline]
+    res = measure(wl, args.steps, args.warmup, args.layers, args.batches, args.copy_probe_mib)
+    extra = {}
+    if args.workload is None and not args.no_workloads:
+        for name in EXTRA_WORKLOADS:
+            steps, warm, nl, nb = EXTRA_SHAPE[name]
+            r = measure(synth.WORKLOADS[name], steps, warm, nl, nb, 0)
+            extra[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+                                             "fp4_weight_GBps", "fp4_weight_frac_hbm", "tflops",
+                                             "tflops_frac_bf16", "active_groups_per_call", "layer_calls_per_step",
+                                             "roofline", "kernels")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args, synth)
+        progress("cpu baseline done")
+    out = {
+        "metric": "MoE layer tokens/s; decode FP4 weight GB/s & prefill TFLOPS vs MI355X peak",
+        "value": res["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16xfp4->fp32",
+        "dtype_note": ("x bf16 enters the block-scaled matrix cores exactly, as two e4m3 terms; weights e2m1 "
+                       "codes with e8m0 scales as stored; fp32 accumulation and output; SwiGLU h carried as three "
+                       "e4m3 terms (12 bits) in decode, two (8 bits, bf16's precision) in prefill"),
+        "data": "synthetic (seeded; random-init weights at the workload's DeepSeek V4 expert shapes)",
+    }
+    out.update({k: res[k] for k in ("config", "fp4_weight_GBps", "fp4_weight_frac_hbm", "tflops", "tflops_frac_bf16",
+                                    "active_groups_per_call", "layer_calls_per_step", "roofline", "kernels")})
+    out["cpu_baseline"] = cpu
+    if extra:
+        out["workloads"] = extra
+    if args.copy_probe_mib:
+        out["copy_probe_mib"] = args.copy_probe_mib
+    print(json.dumps(out), flush=True)
+
+
+def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
+    """Time `steps` steps of one workload (after `warmup` untimed ones) and its kernels."""
     import numpy as np
     import torch
 
     import moe_synth as synth
     import fp4_routed_expert_moe_amd as moe
 
-    wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    nl = max(1, min(args.layers, wl.layers if wl.layers > 1 else args.layers))
+    nl = max(1, min(layers_rotated, wl.layers if wl.layers > 1 else layers_rotated))
     layers, keep = [], []
     for l in range(nl):
         raw = synth.layer_weights(wl, l, device=dev)          # checkpoint layout
@@ -128,7 +195,9 @@ def main():
         bt = None if b is None else torch.from_numpy(b).to(dev)
         layers.append(moe.MoeLayer(wr, w["gate"], w["up"], w["down"], wl.top_k, wl.shared, bt))
         keep.append((w, wr, bt))
-    nb = args.batches
+    torch.cuda.synchronize()
+    progress(f"{wl.name}: {nl} weight set(s) resident")
+    nb = batches
     xs = torch.stack([torch.from_numpy(synth.tokens(wl, layer=0, step=s).view(np.int16)) for s in range(nb)]).to(dev)
     T = wl.tokens
     ws = layers[0].workspace(T)
@@ -143,8 +212,8 @@ def main():
         for c in range(s * L, (s + 1) * L):
             layers[c % nl].forward(xs[c % nb], workspace=ws, y=y)
 
-    if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    if copy_probe_mib:
+        src = torch.empty(copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
@@ -154,34 +223,35 @@ def main():
     # active experts of every (layer, batch) pair a step can meet (outside the timed region)
     period = int(np.lcm(nl, nb))
     active = {}
-    for c in range(min(period, args.steps * L)):
+    for c in range(min(period, steps * L)):
         r = layers[c % nl].route(xs[c % nb], workspace=ws)
         active[(c % nl, c % nb)] = r["counts"]
     torch.cuda.synchronize()
     active = {k: int((v > 0).sum().item()) for k, v in active.items()}
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    tokens_per_s = args.steps * T / elapsed
+    ms_per_step = 1e3 * elapsed / steps
+    tokens_per_s = steps * T / elapsed
+    progress(f"{wl.name}: {steps} timed steps, {ms_per_step:.4f} ms per step")
 
     # per-kernel HIP-event timing over a second pass of the same steps
     moe.timing_reset()
     moe.timing_enable(True)
-    for s in range(args.steps):
+    for s in range(steps):
         step(s)
     torch.cuda.synchronize()
     kt = moe.timing_read()
     moe.timing_enable(False)
 
     e_all, e_gu, e_dn = expert_bytes(wl)
-    groups_per_call = [active[(c % nl, c % nb)] + wl.shared for c in range(args.steps * L)]
+    groups_per_call = [active[(c % nl, c % nb)] + wl.shared for c in range(steps * L)]
     groups = float(np.mean(groups_per_call))
     fp4_bytes_step = L * groups * e_all
     flops_step = L * 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
@@ -210,25 +280,9 @@ def main():
     roof["algorithmic_per_launch"] = work
     roof["algorithmic_unit"] = "bytes" if bound == "hbm" else "flops"
     roof["algorithmic_bytes_per_launch"] = gu_bytes
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args, synth)
-
     kernels = {k: dict(launches=v[0], avg_us=1e3 * v[1] / max(v[0], 1)) for k, v in kt.items()}
-    out = {
-        "metric": "MoE layer tokens/s; decode FP4 weight GB/s & prefill TFLOPS vs MI355X peak",
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8xfp4->fp32",
-        "data": "synthetic (seeded; random-init weights at the workload's DeepSeek V4 expert shapes)",
+    res = {
+        "value": tokens_per_s, "unit": "tokens/s", "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup,
         "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
                    "shared": wl.shared, "inter": wl.inter, "tokens": T, "layers_rotated": nl,
                    "batches_rotated": nb, "parallelism": "single GPU"},
@@ -240,48 +294,101 @@ def main():
         "layer_calls_per_step": L,
         "roofline": roof,
         "kernels": kernels,
-        "cpu_baseline": cpu,
     }
-    if args.copy_probe_mib:
-        out["copy_probe_mib"] = args.copy_probe_mib
-    print(json.dumps(out), flush=True)
+    del layers, keep, xs, ws, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def _cpu_batch(wl, b, synth):
+    """Token batch `b` of the workload (layer 0) and the expert weights its routing needs."""
+    import oracle
+    t_batch = min(wl.tokens, 8)
+    wr = synth.router_weights(wl, 0)
+    bias = synth.router_bias(wl)
+    x = synth.tokens(wl, layer=0, step=b)[:t_batch]
+    idx, _, _ = oracle.select_experts(oracle.router_logits(x, wr, bias), wl.top_k)
+    needed = sorted(set(idx.reshape(-1).tolist()) | ({wl.experts} if wl.shared else set()))
+    lazy = synth.LazyExperts(wl, 0, cache=len(needed) + 1)
+    return x, wr, bias, {g: lazy[g] for g in needed}
+
+
+class _Pre:
+    def __init__(self, experts):
+        self.experts = experts
+
+    def __getitem__(self, g):
+        return self.experts[g]
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    import torch
+    threadpool_limits(1)
+    torch.set_num_threads(1)
+
+
+def _cpu_job(wl, b):
+    """One all-cores oracle job: prepare batch b's weights (untimed), run the oracle on it with
+    one numpy thread; returns (tokens, start, end) of the oracle run."""
+    import moe_synth as synth
+    import oracle
+    x, wr, bias, experts = _cpu_batch(wl, b, synth)
+    t0 = time.time()
+    oracle.moe_forward(x, wr, bias, _Pre(experts), wl.top_k, wl.shared)
+    return x.shape[0], t0, time.time()
 
 
 def cpu_baseline(wl, args, synth):
-    """The float64 CPU oracle on whole batches of the same workload, one after another, until
-    ``--cpu-seconds`` of oracle time is spent (at least one batch, at most 16).  Weight
-    generation is outside the timed region."""
-    import numpy as np
+    """The float64 CPU oracle on whole batches of the same workload (layer 0, 8 tokens each).
+
+    One thread: batches one after another until half of ``--cpu-seconds`` of oracle time is
+    spent.  All cores: one worker process per core of this process's CPU set (at most 16, the
+    host share of one GPU), each running the oracle on its own batches with one numpy thread,
+    timed from the first oracle start to the last oracle end.  Weight generation is outside
+    both timed regions."""
+    import multiprocessing
+
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    t_batch = min(wl.tokens, 8)
-    wr = synth.router_weights(wl, 0)
-    b = synth.router_bias(wl)
     total_t, total_s, batches = 0, 0.0, 0
-    while batches < 16 and (batches == 0 or total_s < args.cpu_seconds):
-        x = synth.tokens(wl, layer=0, step=batches)[:t_batch]
-        idx, _, _ = oracle.select_experts(oracle.router_logits(x, wr, b), wl.top_k)
-        needed = sorted(set(idx.reshape(-1).tolist()) | ({wl.experts} if wl.shared else set()))
-        lazy = synth.LazyExperts(wl, 0, cache=len(needed) + 1)
-        experts = {g: lazy[g] for g in needed}
-
-        class Pre:
-            def __getitem__(self, g):
-                return experts[g]
-
+    while batches < 16 and (batches == 0 or total_s < args.cpu_seconds / 2):
+        x, wr, bias, experts = _cpu_batch(wl, batches, synth)
         with threadpool_limits(limits=1):          # the oracle as it stands: numpy, one thread
             t0 = time.perf_counter()
-            oracle.moe_forward(x, wr, b, Pre(), wl.top_k, wl.shared)
+            oracle.moe_forward(x, wr, bias, _Pre(experts), wl.top_k, wl.shared)
             total_s += time.perf_counter() - t0
-        total_t += t_batch
+        total_t += x.shape[0]
         batches += 1
+    one = total_t / total_s
+    per_batch_s = total_s / batches
+    progress(f"cpu baseline: one thread {one:.3g} tokens/s over {batches} batch(es)")
+
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, affinity))
+    # batches per worker so the parallel phase lasts about half of --cpu-seconds
+    per_worker = max(1, min(8, int(round(args.cpu_seconds / 2 / per_batch_s))))
+    import concurrent.futures
+    res = []
+    with concurrent.futures.ProcessPoolExecutor(workers, initializer=_cpu_worker_init,
+                                                mp_context=multiprocessing.get_context("spawn")) as pool:
+        futs = [pool.submit(_cpu_job, wl, 100 + j) for j in range(workers * per_worker)]
+        for f in concurrent.futures.as_completed(futs, timeout=300):
+            res.append(f.result())
+            progress(f"cpu baseline: {len(res)} of {len(futs)} all-cores batches done")
+    toks = sum(r[0] for r in res)
+    wall = max(r[2] for r in res) - min(r[1] for r in res)
     L = wl.layers if wl.layers > 1 else 1  # a token of the stacked workload passes L layers
     per_layer = f"; a token passes {L} layers of the same cost" if L > 1 else ""
-    return {"value": total_t / total_s / L, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{batches} batch(es) of {t_batch} tokens of {wl.name} layer 0, "
-                      f"{total_s:.1f} s of oracle time (float64 numpy, one thread){per_layer}"}
+    return {"value": toks / wall / L, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": (f"{workers} worker processes, {per_worker} batch(es) each, of {min(wl.tokens, 8)} tokens of "
+                       f"{wl.name} layer 0, one numpy thread each, {wall:.1f} s wall{per_layer}"),
+            "host_cpus_in_affinity": affinity,
+            "single_thread": {"value": one / L, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{batches} batch(es) one after another, {total_s:.1f} s of oracle time"}}
 
 
 # ---------------------------------------------------------------------------------------
@@ -368,6 +475,46 @@ def pmc_summary(args):
     print("\n`sources` is a digest of the files the kernel is built from; `bench.py` reports `traffic` only "
           "while it matches.\n")
     print("```json\n" + json.dumps(rec, indent=None) + "\n```")
+
+
+def mfma_summary(args):
+    """Per-kernel means of an MFMA counter pass (MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE x SIMDs, and the F8 / F6F4 MFMA op counts, 512 flops each) as markdown."""
+    rows = _read_pmc(args.mfma_summary)
+    run = {}
+    if args.pmc_log:
+        with open(args.pmc_log) as f:
+            for line in f:
+                if line.startswith("{"):
+                    run = json.loads(line)
+    acc = {}
+    for r in rows:
+        n = _short_name(r["Kernel_Name"])
+        if n:
+            acc.setdefault(n, {}).setdefault(r.get("Counter_Name", "value"), []).append(float(r["Counter_Value"]))
+    cfg = run.get("config", {})
+    wl = cfg.get("workload", "?")
+    print(f"# MFMA counters per dispatch: {wl}\n")
+    print("Command (repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n")
+    print("```\n" + (args.pmc_command or "(not recorded)") + "\n```\n")
+    print("| kernel | dispatches | MfmaUtil % | F8 MFMA flops (x512 ops) | F6F4 MFMA flops | "
+          "algorithmic flops / launch |")
+    print("|---|---|---|---|---|---|")
+    recs = {}
+    t, kk, ss, h, i = (cfg.get(k, 0) for k in ("tokens", "top_k", "shared", "hidden", "inter"))
+    alg = {"gemm_gateup": 2.0 * t * (kk + ss) * 2 * h * i, "gemm_down": 2.0 * t * (kk + ss) * h * i}
+    for n in sorted(acc):
+        c = acc[n]
+        mean = {k: sum(v) / len(v) for k, v in c.items()}
+        nd = max(len(v) for v in c.values())
+        util = mean.get("MfmaUtil")
+        f8 = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512
+        f6 = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0) * 512
+        recs[n] = {"dispatches": nd, "mfma_util_pct": util, "f8_flops": f8, "f6f4_flops": f6,
+                   "algorithmic_flops": alg.get(n)}
+        print(f"| {n} | {nd} | {util if util is None else f'{util:.1f}'} | {f8:.4g} | {f6:.4g} | "
+              f"{alg.get(n, float('nan')):.4g} |")
+    print("\n```json\n" + json.dumps({"workload": wl, "kernels": recs}) + "\n```")
 
 
 if __name__ == "__main__":
