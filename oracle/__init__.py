@@ -20,15 +20,17 @@ Each function cites the page passage it follows.  Pages, by title:
   experts are FP4 E2M1 with UE8M0 scales per group of 32; the 16-entry E2M1
   table is 64 bytes; doubled E2M1 values are integers; six experts per token;
   expert shapes 2048x4096 (gate/up) and 4096x2048 (down); fp64-oracle error
-  bounds as the test style.
+  bounds as the test style; dense tensors are FP8 E4M3 with 128x128 block
+  scales (the shared-expert variant, oracle/fp8.py).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force and the printed facts above; none is "parity unpinned".
 """
 from .fp4 import E2M1_VALUES, e2m1_value, e8m0_value, dequant
-from .moe import (router_logits, select_experts, group_rows, silu, expert_ffn,
+from .fp8 import E4M3_VALUES, Fp8Matrix, e4m3_value, dequant_fp8_block
+from .moe import (router_logits, select_experts, group_rows, silu, expert_ffn, dequant_matrix,
                   moe_forward, screen_near_ties)
 
-__all__ = ["E2M1_VALUES", "e2m1_value", "e8m0_value", "dequant", "router_logits",
-           "select_experts", "group_rows", "silu", "expert_ffn", "moe_forward",
-           "screen_near_ties"]
+__all__ = ["E2M1_VALUES", "e2m1_value", "e8m0_value", "dequant", "E4M3_VALUES", "Fp8Matrix",
+           "e4m3_value", "dequant_fp8_block", "router_logits", "select_experts", "group_rows", "silu",
+           "expert_ffn", "dequant_matrix", "moe_forward", "screen_near_ties"]

@@ -34,6 +34,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp4 import dequant
+from .fp8 import Fp8Matrix, dequant_fp8_block
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -93,11 +94,21 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def dequant_matrix(w) -> np.ndarray:
+    """An expert matrix in either stored format, as float64: an FP4 (codes, scales) pair (e2m1 +
+    e8m0 per 32), or an Fp8Matrix (e4m3 + float32 per 128 x 128 block; the V4 dense format of
+    "Add DeepSeek V4 Flash CPU inference with NVMe expert streaming", PR #165, the question on
+    V4 sizes)."""
+    if isinstance(w, Fp8Matrix):
+        return dequant_fp8_block(w.codes, w.scales)
+    return dequant(*w)
+
+
 def expert_ffn(xrows: np.ndarray, weights) -> np.ndarray:
     """SwiGLU expert on float64 rows [n][H]: silu(x Wg^T) * (x Wu^T), then times Wd^T -> [n][H]."""
-    wg = dequant(*weights["gate"])       # [I][H]
-    wu = dequant(*weights["up"])         # [I][H]
-    wd = dequant(*weights["down"])       # [H][I]
+    wg = dequant_matrix(weights["gate"])       # [I][H]
+    wu = dequant_matrix(weights["up"])         # [I][H]
+    wd = dequant_matrix(weights["down"])       # [H][I]
     g = xrows @ wg.T
     u = xrows @ wu.T
     h = silu(g) * u

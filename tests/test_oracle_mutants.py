@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import oracle.fp4 as ofp4
+import oracle.fp8 as ofp8
 import oracle.moe as omoe
 import test_oracle_pins as pins
 
@@ -27,11 +28,12 @@ ORIG = {
     "moe_forward": omoe.moe_forward,
     "silu": omoe.silu,
     "bf16_bits_to_f64": omoe.bf16_bits_to_f64,
+    "dequant_fp8_block": ofp8.dequant_fp8_block,
 }
 
 
 @contextlib.contextmanager
-def patched(name, value, modules=(ofp4, omoe, oracle)):
+def patched(name, value, modules=(ofp4, ofp8, omoe, oracle)):
     """Replace `name` in every oracle namespace that holds it (package re-exports included)."""
     saved = [(m, getattr(m, name)) for m in modules if hasattr(m, name)]
     try:
@@ -107,6 +109,19 @@ def _bf16_shift15(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def _fp8_blocks_of_64(codes, scales):
+    codes = np.asarray(codes, np.uint8)
+    s = np.asarray(scales, np.float32).astype(np.float64)
+    r = np.minimum(np.arange(codes.shape[0]) // 64, s.shape[0] - 1)
+    c = np.minimum(np.arange(codes.shape[1]) // 64, s.shape[1] - 1)
+    return ofp8.E4M3_VALUES[codes] * s[r[:, None], c[None, :]]
+
+
+def _fp8_scales_transposed(codes, scales):
+    s = np.asarray(scales, np.float32)
+    return ORIG["dequant_fp8_block"](codes, s.T if s.shape[0] == s.shape[1] else s[::-1, ::-1])
+
+
 MUTANTS = {
     "nibble order swapped": [("dequant", _dequant_nibbles_swapped)],
     "scale blocks of 16": [("dequant", _dequant_scale_block_16)],
@@ -123,6 +138,10 @@ MUTANTS = {
     "gate and up swapped": [("expert_ffn", _ffn_gate_up_swapped)],
     "shared expert dropped": [("moe_forward", _forward_no_shared)],
     "bf16 decode shifted": [("bf16_bits_to_f64", _bf16_shift15)],
+    "e4m3 exponent bias 8": [("E4M3_VALUES", ofp8.E4M3_VALUES / 2)],
+    "e4m3 subnormals flushed": [("E4M3_VALUES", np.where((np.arange(256) & 0x78) == 0, 0.0, ofp8.E4M3_VALUES))],
+    "fp8 scale blocks of 64": [("dequant_fp8_block", _fp8_blocks_of_64)],
+    "fp8 scale grid transposed": [("dequant_fp8_block", _fp8_scales_transposed)],
 }
 
 

@@ -308,3 +308,83 @@ def test_zipf_bias_makes_hot_experts():
     counts = np.bincount(idx.reshape(-1), minlength=wl.experts)
     assert counts.max() > 0.10 * idx.size
     assert (counts == 0).sum() > 10
+
+
+# ------------------------------------------------------------- FP8 (E4M3, 128 x 128 blocks)
+# "Add DeepSeek V4 Flash CPU inference with NVMe expert streaming" (PR #165, the question on V4
+# sizes): dense tensors are FP8 E4M3 with 128x128 block scales; the shared expert may be stored so.
+
+
+def test_e4m3_closed_form_and_edges():
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        v = oracle.e4m3_value(c)
+        if e == 15 and m == 7:
+            assert math.isnan(v)
+            continue
+        want = (-1) ** s * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+        assert v == want and math.copysign(1, v) == math.copysign(1, want), c
+    vals = oracle.E4M3_VALUES
+    assert vals[0x38] == 1.0 and vals[0xB8] == -1.0
+    assert vals[0x7E] == 448.0 and np.nanmax(vals) == 448.0      # largest finite, no infinity
+    assert vals[0x01] == 2.0 ** -9 and vals[0x08] == 2.0 ** -6    # smallest subnormal, smallest normal
+    assert np.isnan(vals[[0x7F, 0xFF]]).all() and np.isnan(vals).sum() == 2
+    assert math.copysign(1, vals[0x80]) == -1 and vals[0x80] == 0
+    np.testing.assert_array_equal(vals[128:], -vals[:128])
+
+
+def test_e4m3_matches_torch_float8_e4m3fn():
+    # an independent decoder: torch's float8_e4m3fn dtype (the same OCP E4M3 "fn" encoding)
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = oracle.E4M3_VALUES
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(mine[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_block_dequant_hand_worked():
+    lines = list(golden_lines("fp8_block_example.txt"))
+    scales = np.array([float(v) for v in lines[0].split()[1:]], np.float32).reshape(2, 2)
+    codes = np.zeros((130, 256), np.uint8)
+    entries = []
+    for line in lines[1:]:
+        r, c, code, val = line.split("#")[0].split()
+        entries.append((int(r), int(c), int(code, 16), float(val)))
+        codes[int(r), int(c)] = int(code, 16)
+    out = oracle.dequant_fp8_block(codes, scales)
+    for r, c, _, val in entries:
+        assert out[r, c] == val and math.copysign(1, out[r, c]) == math.copysign(1, val), (r, c, out[r, c], val)
+    # every other element is +0 (code 0) whatever its block's scale
+    mask = np.ones_like(codes, bool)
+    for r, c, _, _ in entries:
+        mask[r, c] = False
+    assert (out[mask] == 0).all()
+
+
+def test_fp8_shared_identity_expert_closed_form():
+    # FP4 identity routed experts (as above) with an FP8 shared expert: gate = selector of 1.0,
+    # up = selector of 2.0, down = selector of 1.0, and down's block scale 0.75 (not a power of
+    # two), so the shared expert adds 0.75 * silu(x_i) * 2 x_i for i < I.
+    hidden, inter, experts, k = 128, 64, 6, 2
+    groups, wr, x, sigma = _identity_setup(hidden, inter, experts, k)
+    one, two = 0x38, 0x40
+    g = np.zeros((inter, hidden), np.uint8)
+    u = np.zeros((inter, hidden), np.uint8)
+    d = np.zeros((hidden, inter), np.uint8)
+    for i in range(inter):
+        g[i, i], u[i, i], d[i, i] = one, two, one
+    sg = np.ones((1, 1), np.float32)
+    groups[experts] = dict(gate=oracle.Fp8Matrix(g, sg), up=oracle.Fp8Matrix(u, sg),
+                           down=oracle.Fp8Matrix(d, np.full((1, 1), 0.75, np.float32)))
+    out = oracle.moe_forward(x, wr, None, groups, k, 1)
+    xf = bf16_bits_to_f64(x)
+    for t in range(x.shape[0]):
+        coef = 0.75
+        for j in range(k):
+            coef += out["w"][t, j] * 2.0 ** -sigma[out["idx"][t, j]]
+        for h in range(hidden):
+            v = xf[t, h]
+            want = coef * (v / (1 + math.exp(-v))) * 2 * v if h < inter else 0.0
+            assert abs(out["y"][t, h] - want) <= 1e-13 * (1 + abs(want)), (t, h)
