@@ -18,11 +18,12 @@ What the layer computes, for tokens x[t] (bf16) of width H:
    at the V4 Flash expert shapes 2048x4096 and 4096x2048).
 5. One shared expert runs on every token with weight 1 (PR #1055, "What it
    is": decode fuses routed and shared experts in one MoE stage).
-6. y[t] = y_shared[t] + sum_j w[t,j] * y_{idx[t,j]}[t].
+6. y[t] = y_shared[t] + r * sum_j w[t,j] * y_{idx[t,j]}[t].
 
 Readings where the pages are silent: softmax (not sigmoid) scoring, the
-bias added before both selection and weighting, no routed scale (1.0), plain
-SwiGLU without clamping, silu(z) = z / (1 + exp(-z)).
+bias added before both selection and weighting, a routed scale r that
+multiplies the routed sum only (default 1.0; the shared expert keeps weight 1),
+plain SwiGLU without clamping, silu(z) = z / (1 + exp(-z)).
 
 Precision: everything is float64, except that the top-k *decision* is taken on
 the scores rounded to float32 -- the precision the GPU kernel decides in -- so
@@ -96,11 +97,15 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 def dequant_matrix(w) -> np.ndarray:
     """An expert matrix in either stored format, as float64: an FP4 (codes, scales) pair (e2m1 +
-    e8m0 per 32), or an Fp8Matrix (e4m3 + float32 per 128 x 128 block; the V4 dense format of
+    e8m0 per 32), or FP8 (e4m3 + float32 per 128 x 128 block; the V4 dense format of
     "Add DeepSeek V4 Flash CPU inference with NVMe expert streaming", PR #165, the question on
-    V4 sizes)."""
+    V4 sizes) given as an Fp8Matrix or as the tagged triple ("fp8", codes, scales)."""
     if isinstance(w, Fp8Matrix):
         return dequant_fp8_block(w.codes, w.scales)
+    if len(w) == 3 and isinstance(w[0], str):
+        if w[0] != "fp8":
+            raise ValueError(f"unknown matrix format {w[0]!r}")
+        return dequant_fp8_block(w[1], w[2])
     return dequant(*w)
 
 
@@ -115,9 +120,10 @@ def expert_ffn(xrows: np.ndarray, weights) -> np.ndarray:
     return h @ wd.T
 
 
-def moe_forward(x_bits, w_router, bias, experts, top_k: int, n_shared: int):
+def moe_forward(x_bits, w_router, bias, experts, top_k: int, n_shared: int, routed_scale: float = 1.0):
     """The whole layer.  ``experts[g]`` -> dict(gate=(codes, scales), up=..., down=...);
     groups 0..E-1 are routed experts, group E the shared expert when ``n_shared`` is 1.
+    ``routed_scale`` multiplies the weighted sum of the routed experts' outputs.
 
     Returns a dict with y (float64 [T][H]), logits (float64), l32, idx, w,
     counts, offsets, perm.
@@ -138,6 +144,7 @@ def moe_forward(x_bits, w_router, bias, experts, top_k: int, n_shared: int):
         slot = rows % top_k
         ye = expert_ffn(x[tok], experts[e])
         y[tok] += w[tok, slot][:, None] * ye     # a token meets an expert at most once
+    y *= routed_scale
     if n_shared:
         y += expert_ffn(x, experts[n_exp])
     return dict(y=y, logits=logits, l32=l32, idx=idx, w=w, counts=counts,

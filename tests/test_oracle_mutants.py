@@ -100,8 +100,18 @@ def _ffn_gate_up_swapped(xrows, weights):
     return ORIG["expert_ffn"](xrows, dict(gate=weights["up"], up=weights["gate"], down=weights["down"]))
 
 
-def _forward_no_shared(x_bits, w_router, bias, experts, top_k, n_shared):
-    return ORIG["moe_forward"](x_bits, w_router, bias, experts, top_k, 0)
+def _forward_no_shared(x_bits, w_router, bias, experts, top_k, n_shared, routed_scale=1.0):
+    return ORIG["moe_forward"](x_bits, w_router, bias, experts, top_k, 0, routed_scale)
+
+
+def _forward_scale_ignored(x_bits, w_router, bias, experts, top_k, n_shared, routed_scale=1.0):
+    return ORIG["moe_forward"](x_bits, w_router, bias, experts, top_k, n_shared)
+
+
+def _forward_scale_on_shared_too(x_bits, w_router, bias, experts, top_k, n_shared, routed_scale=1.0):
+    out = ORIG["moe_forward"](x_bits, w_router, bias, experts, top_k, n_shared)
+    out["y"] = out["y"] * routed_scale
+    return out
 
 
 def _bf16_shift15(bits):
@@ -137,6 +147,8 @@ MUTANTS = {
     "router bias ignored": [("router_logits", _router_no_bias)],
     "gate and up swapped": [("expert_ffn", _ffn_gate_up_swapped)],
     "shared expert dropped": [("moe_forward", _forward_no_shared)],
+    "routed scale ignored": [("moe_forward", _forward_scale_ignored)],
+    "routed scale on the shared expert too": [("moe_forward", _forward_scale_on_shared_too)],
     "bf16 decode shifted": [("bf16_bits_to_f64", _bf16_shift15)],
     "e4m3 exponent bias 8": [("E4M3_VALUES", ofp8.E4M3_VALUES / 2)],
     "e4m3 subnormals flushed": [("E4M3_VALUES", np.where((np.arange(256) & 0x78) == 0, 0.0, ofp8.E4M3_VALUES))],

@@ -220,14 +220,23 @@ def _identity_setup(hidden=128, inter=64, experts=6, k=2, tokens=5, seed=0):
 
 
 def test_identity_experts_closed_form():
+    _identity_closed_form(1.0)
+
+
+def test_routed_scale_closed_form():
+    # the routed scale multiplies the routed experts' weighted sum; the shared expert keeps weight 1
+    _identity_closed_form(2.5)
+
+
+def _identity_closed_form(routed_scale):
     hidden, inter, experts, k = 128, 64, 6, 2
     groups, wr, x, sigma = _identity_setup(hidden, inter, experts, k)
-    out = oracle.moe_forward(x, wr, None, groups, k, 1)
+    out = oracle.moe_forward(x, wr, None, groups, k, 1, routed_scale=routed_scale)
     xf = bf16_bits_to_f64(x)
     for t in range(x.shape[0]):
         coef = 2.0 ** -sigma[experts]  # shared expert
         for j in range(k):
-            coef += out["w"][t, j] * 2.0 ** -sigma[out["idx"][t, j]]
+            coef += routed_scale * out["w"][t, j] * 2.0 ** -sigma[out["idx"][t, j]]
         for h in range(hidden):
             v = xf[t, h]
             want = coef * (v / (1 + math.exp(-v))) * 2 * v if h < inter else 0.0
@@ -376,7 +385,7 @@ def test_fp8_shared_identity_expert_closed_form():
     for i in range(inter):
         g[i, i], u[i, i], d[i, i] = one, two, one
     sg = np.ones((1, 1), np.float32)
-    groups[experts] = dict(gate=oracle.Fp8Matrix(g, sg), up=oracle.Fp8Matrix(u, sg),
+    groups[experts] = dict(gate=oracle.Fp8Matrix(g, sg), up=("fp8", u, sg),
                            down=oracle.Fp8Matrix(d, np.full((1, 1), 0.75, np.float32)))
     out = oracle.moe_forward(x, wr, None, groups, k, 1)
     xf = bf16_bits_to_f64(x)
