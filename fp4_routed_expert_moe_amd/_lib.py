@@ -11,7 +11,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp4.so")
 
-MOE_ABI_VERSION = 1
+MOE_ABI_VERSION = 2
+MOE_SHARED_FP8 = 1
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALLOC = range(6)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -19,7 +20,7 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_abi_version", "moe_device_supported", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_noalloc", "moe_pack_fp4",
-           "moe_status_string",
+           "moe_pack_fp8", "moe_status_string",
            "moe_last_error",
            "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 
@@ -34,6 +35,10 @@ class LayerDesc(ctypes.Structure):
         ("inter", ctypes.c_int32),
         ("path", ctypes.c_int32),
         ("device", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("routed_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
         ("w_router", ctypes.c_void_p),
         ("router_bias", ctypes.c_void_p),
         ("gate_codes", ctypes.c_void_p),
@@ -42,6 +47,12 @@ class LayerDesc(ctypes.Structure):
         ("up_scales", ctypes.c_void_p),
         ("down_codes", ctypes.c_void_p),
         ("down_scales", ctypes.c_void_p),
+        ("shared_gate_fp8", ctypes.c_void_p),
+        ("shared_gate_fp8_scales", ctypes.c_void_p),
+        ("shared_up_fp8", ctypes.c_void_p),
+        ("shared_up_fp8_scales", ctypes.c_void_p),
+        ("shared_down_fp8", ctypes.c_void_p),
+        ("shared_down_fp8_scales", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +92,7 @@ def load(path: str = None) -> ctypes.CDLL:
         "moe_forward": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P, U64, P]),
         "moe_forward_noalloc": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P]),
         "moe_pack_fp4": (I32, [P, P, P, P, I32, I32, I32, P]),
+        "moe_pack_fp8": (I32, [P, P, I32, I32, I32, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (I32, [I32]),

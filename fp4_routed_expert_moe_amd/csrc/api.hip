@@ -283,12 +283,35 @@ int32_t moe_layer_create(const moe_layer_desc* d, moe_layer** out) {
     return fail(MOE_ERR_INVALID, "top_k=%d must be in [1, n_experts=%d]", d->top_k, d->n_experts);
   if (d->n_shared != 0 && d->n_shared != 1) return fail(MOE_ERR_INVALID, "n_shared=%d must be 0 or 1", d->n_shared);
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GEMM) return fail(MOE_ERR_INVALID, "path=%d unknown", d->path);
+  if (d->block != 32) return fail(MOE_ERR_INVALID, "block=%d: FP4 scales cover 32 values", d->block);
+  if (d->reserved != 0) return fail(MOE_ERR_INVALID, "reserved=%d must be 0", d->reserved);
+  if (!(d->routed_scale > 0.f) || !(d->routed_scale <= 3.402823466e38f))
+    return fail(MOE_ERR_INVALID, "routed_scale=%g must be finite and > 0", (double)d->routed_scale);
+  if (d->flags & ~(int32_t)MOE_SHARED_FP8) return fail(MOE_ERR_INVALID, "flags=0x%x has unknown bits", d->flags);
+  const bool fp8 = (d->flags & MOE_SHARED_FP8) != 0;
   if (!d->w_router || !d->gate_codes || !d->gate_scales || !d->up_codes || !d->up_scales || !d->down_codes ||
       !d->down_scales)
     return fail(MOE_ERR_INVALID, "moe_layer_create: a weight pointer is NULL");
   if (!aligned16(d->w_router) || !aligned16(d->gate_codes) || !aligned16(d->up_codes) ||
       !aligned16(d->down_codes))
     return fail(MOE_ERR_INVALID, "router weights and code arrays must be 16-byte aligned");
+  const void* f8[6] = {d->shared_gate_fp8, d->shared_gate_fp8_scales, d->shared_up_fp8,
+                       d->shared_up_fp8_scales, d->shared_down_fp8, d->shared_down_fp8_scales};
+  if (fp8) {
+    if (d->n_shared != 1) return fail(MOE_ERR_INVALID, "MOE_SHARED_FP8 needs n_shared = 1");
+    if (d->hidden % 128 || d->inter % 128)
+      return fail(MOE_ERR_INVALID, "MOE_SHARED_FP8: hidden=%d and inter=%d must be multiples of 128", d->hidden,
+                  d->inter);
+    for (int i = 0; i < 6; ++i)
+      if (!f8[i]) return fail(MOE_ERR_INVALID, "MOE_SHARED_FP8: a shared-expert FP8 pointer is NULL");
+    if (!aligned16(d->shared_gate_fp8) || !aligned16(d->shared_up_fp8) || !aligned16(d->shared_down_fp8))
+      return fail(MOE_ERR_INVALID, "FP8 code arrays must be 16-byte aligned");
+    for (int i = 1; i < 6; i += 2)
+      if (reinterpret_cast<uintptr_t>(f8[i]) & 3u) return fail(MOE_ERR_INVALID, "FP8 scales must be 4-byte aligned");
+  } else {
+    for (int i = 0; i < 6; ++i)
+      if (f8[i]) return fail(MOE_ERR_INVALID, "shared-expert FP8 pointers given without MOE_SHARED_FP8");
+  }
   char arch[64];
   if (!moe_device_supported(d->device, arch, sizeof(arch)))
     return fail(MOE_ERR_UNSUPPORTED, "device %d is not a supported gfx950 (%s)", d->device, arch);
@@ -296,7 +319,8 @@ int32_t moe_layer_create(const moe_layer_desc* d, moe_layer** out) {
   moe_layer* L = getenv("MOE_FAIL_ALLOC") ? nullptr : new (std::nothrow) moe_layer;
   if (!L) return fail(MOE_ERR_ALLOC, "moe_layer_create: out of host memory");
   L->desc = *d;
-  L->dims = moe::Dims{d->hidden, d->n_experts, d->top_k, d->n_shared, d->inter, d->n_experts + d->n_shared};
+  L->dims = moe::Dims{d->hidden, d->n_experts, d->top_k, d->n_shared, d->inter, d->n_experts + d->n_shared,
+                      fp8, d->routed_scale};
   *out = L;
   return MOE_OK;
 }
@@ -438,6 +462,23 @@ int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t*
   const hipError_t e = moe::launch_pack(codes_in, scales_in, codes_out, scales_out, groups, rows, cols,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_pack_fp4: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int32_t moe_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int32_t groups, int32_t rows, int32_t cols,
+                     void* stream) {
+  if (!codes_in || !codes_out) return fail(MOE_ERR_INVALID, "moe_pack_fp8: NULL pointer");
+  if (groups < 1 || rows < 1 || cols < 128 || cols % 128)
+    return fail(MOE_ERR_INVALID, "moe_pack_fp8: groups=%d rows=%d cols=%d (cols must be a positive multiple of 128)",
+                groups, rows, cols);
+  if (!aligned16(codes_in) || !aligned16(codes_out))
+    return fail(MOE_ERR_INVALID, "moe_pack_fp8: code arrays must be 16-byte aligned");
+  const size_t n = (size_t)groups * rows * cols;
+  const char* a = reinterpret_cast<const char*>(codes_in);
+  const char* b = reinterpret_cast<const char*>(codes_out);
+  if (a < b + n && b < a + n) return fail(MOE_ERR_INVALID, "moe_pack_fp8: output overlaps input");
+  const hipError_t e = moe::launch_pack_fp8(codes_in, codes_out, groups, rows, cols, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_pack_fp8: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 

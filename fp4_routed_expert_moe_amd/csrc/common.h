@@ -150,6 +150,12 @@ __device__ __forceinline__ i32x8 fp8_operand(const uint4& lo, const uint4& hi) {
 __device__ __forceinline__ f32x4 mma_f8f4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
 }
+// acc += A(fp8, scale sa) x B(fp8 e4m3, scale byte 127 = 1.0): the FP8 shared expert, whose
+// float32 128 x 128 block scales are applied to the product afterwards.  Both operands use the
+// FP8 lane layout above.
+__device__ __forceinline__ f32x4 mma_f8f8(const i32x8& a, const i32x8& b, f32x4 acc, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, 127);
+}
 // The same with B's scale taken from byte SELB of the register sb.
 template <int SELB>
 __device__ __forceinline__ f32x4 mma_f8f4_sb(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
@@ -175,7 +181,10 @@ __host__ __device__ inline size_t scale_slab_bytes(int N, int K) {
 
 struct Dims {
   int H, E, K, S, I, G;  // hidden, experts, top-k, shared, inter, groups = E + S
+  bool fp8_shared;       // the shared expert (group E) is FP8 E4M3 with 128 x 128 block scales
+  float routed_scale;    // multiplies every routed row's routing weight in the combine
 };
+constexpr int kFp8Block = 128;
 
 // Device buffers of one call, carved from the workspace (and the caller's route buffers).
 // Active-group slot of the decode kernels: one 16-byte load gives a workgroup its group, the
@@ -197,7 +206,7 @@ struct CallBufs {
   int32_t* grp_row0;  // [G] first grouped row of group g
   int32_t* grp_rows;  // [G] rows of group g
   GroupRec* grec;     // [G] groups with rows, ascending, shared last; then count-only slots
-  int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles
+  int32_t* info;      // [0] = active groups, [1] = GEMM M-tiles, [2] = routed GEMM M-tiles (the shared ones follow)
   int32_t* mt_group;  // [mt_bound]
   int32_t* mt_row0;   // [mt_bound]
   int32_t* ctrl;      // control words (zero between calls): [0] routing arrival counter
@@ -238,6 +247,9 @@ hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStre
 // Decode GEMV kernels (gemv.hip): gate/up + SwiGLU into h, then down + the combine into y.
 // They read the routing tables and the FP8 activation terms earlier launches on the stream
 // wrote.
+// With d.fp8_shared each of these enqueues the FP4 kernel for the routed groups and then the
+// FP8 kernel for the shared expert (whose down launch also does the combine, after every
+// routed row is in staging).
 hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b, int T,
                               int max_act, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T, int max_act,
@@ -246,6 +258,7 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
                               int T, int mt_bound, hipStream_t s);
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s);
+hipError_t launch_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int groups, int N, int K, hipStream_t s);
 hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
                        int groups, int N, int K, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s);

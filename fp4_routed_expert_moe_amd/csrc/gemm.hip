@@ -21,6 +21,8 @@
 // * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes the M-tiles 8i + x, every
 //   column slice of each in turn: an M-tile's activation rows are fetched into one XCD's L2
 //   only, and with small batches (one M-tile per expert) the XCDs stream different experts.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -53,6 +55,10 @@ struct GemmShape {
 #endif
 using GateUpShape = GemmShape<MOE_GU_SHAPE>;
 using DownShape = GemmShape<MOE_DN_SHAPE>;
+// The FP8 shared expert's kernels: the same tiles at one workgroup per CU (its weight operands
+// are twice the FP4 ones' registers)
+using GateUpShape8 = GemmShape<GateUpShape::NW, GateUpShape::CT, GateUpShape::PU, 1>;
+using DownShape8 = GemmShape<DownShape::NW, DownShape::CT, DownShape::PU, 1>;
 
 template <class SH>
 struct ATile {                    // one K step of the activation tile
@@ -211,24 +217,97 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& 
   }
 }
 
+// ---- the FP8 shared expert's weights (e4m3, float32 scale per 128 x 128 block) ----------
+// Kernel layout [K/128][N][128]; lane (n, q) takes bytes 16q.. and 64+16q.. of its row's
+// 128-value chunk (the FP8 lane layout, the same as the activations').  A wave's CT tiles lie in
+// one 128-row scale block, so one float32 per chunk and matrix scales the wave's products,
+// applied after the chunk's two MFMAs (one per activation term).
+template <class SH, int NM>
+struct BFrag8 {
+  i32x4 c[SH::PU][NM][SH::CT][2];
+  float s[SH::PU][NM];
+};
+template <class SH, int NM>
+struct BSrc8 {
+  __amdgpu_buffer_rsrc_t c[NM];
+  const float* s[NM];  // the wave's row block of each matrix's scales, indexed by chunk
+  int voff;            // column tile 0, chunk 0
+};
+template <class SH, int NM>
+__device__ __forceinline__ void b_fetch(BFrag8<SH, NM>& f, const BSrc8<SH, NM>& bs, int N, int KB, int step, int q) {
+  (void)q;
+#pragma unroll
+  for (int u = 0; u < SH::PU; ++u) {
+    const int chunk = step * SH::PU + u;
+    const bool past = 4 * chunk >= KB;  // the prefetch runs past the last step: read zeros
+    const int so = __builtin_amdgcn_readfirstlane(past ? 0 : chunk * N * 128);
+    const int bias = past ? kOutOfRange : 0;
+#pragma unroll
+    for (int mtx = 0; mtx < NM; ++mtx) {
+#pragma unroll
+      for (int c = 0; c < SH::CT; ++c) {
+        f.c[u][mtx][c][0] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff + bias + 2048 * c, so, 0));
+        f.c[u][mtx][c][1] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff + bias + 2048 * c + 64, so, 0));
+      }
+      f.s[u][mtx] = past ? 0.f : bs.s[mtx][chunk];
+    }
+  }
+}
+template <class SH, int NM>
+__device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>& f, f32x4 (&acc)[NM][4][SH::CT],
+                                       int nsub, int m, int q, int sh) {
+  (void)sh;
+#pragma unroll
+  for (int u = 0; u < SH::PU; ++u) {
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {
+      if (rs >= nsub) break;
+      const int r = 16 * rs + m;
+      const int b = 128 * u + 16 * q;
+      const i32x8 a0 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[0][r][b]),
+                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b + 64]), 0, 1, 2, 3, 4,
+                                               5, 6, 7);
+      const i32x8 a1 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[1][r][b]),
+                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b + 64]), 0, 1, 2, 3, 4,
+                                               5, 6, 7);
+      const int sa = t.s[r][4 * u + q];
+#pragma unroll
+      for (int c = 0; c < SH::CT; ++c)
+#pragma unroll
+        for (int mtx = 0; mtx < NM; ++mtx) {
+          const i32x8 bb = __builtin_shufflevector(f.c[u][mtx][c][0], f.c[u][mtx][c][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          f32x4 p = mma_f8f8(a0, bb, f32x4{0.f, 0.f, 0.f, 0.f}, sa);
+          p = mma_f8f8(a1, bb, p, sa - 4);
+          acc[mtx][rs][c] += p * f.s[u][mtx];
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // GATEUP: h[r][n] = silu(x_t(r) . Wg[n]) * (x_t(r) . Wu[n]) as 2 FP8 terms + e8m0 per 32
 //         (h8 = [2][R][I] bytes then [R][kb_pad(I)] scales).
 // DOWN:   staging[slot(r)][n] = weight(r) * (h_r . Wd[n])  (wts: weight of grouped row r).
 // ------------------------------------------------------------------------------------
-template <bool GATEUP, class SH>
+// FP8: the M-tiles of the FP8 shared expert (info[2] .. info[1]), weights c0p/c1p as FP8 codes
+// and f0p/f1p their float32 block scales.  Otherwise the FP4 M-tiles [0, info[1]), or
+// [0, info[2]) when routed_only (the shared expert is FP8 and has its own launch).
+template <bool GATEUP, class SH, bool FP8 = false>
 __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     ARows a, const uint8_t* __restrict__ c0p, const uint8_t* __restrict__ s0p, const uint8_t* __restrict__ c1p,
-    const uint8_t* __restrict__ s1p, const int32_t* __restrict__ perm, const float* __restrict__ wts,
+    const uint8_t* __restrict__ s1p, const float* __restrict__ f0p, const float* __restrict__ f1p,
+    const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
     const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8,
-    float* __restrict__ staging, int T, int k, int N, int R, int NT) {
+    float* __restrict__ staging, int routed_only, float routed_scale, int T, int k, int N, int R, int NT) {
   constexpr int NM = GATEUP ? 2 : 1;
   __shared__ ATile<SH> tile[2];
   // XCD x (= b % 8) takes the M-tiles mt = 8i + x, all NT column slices of each
   const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-  const int mt = (jj / NT) * 8 + xcd, nt = jj % NT;
-  if (mt >= info[1]) return;
+  const int mt = (jj / NT) * 8 + xcd + (FP8 ? info[2] : 0), nt = jj % NT;
+  if (mt >= (routed_only ? info[2] : info[1])) return;
   // tile metadata is the same for every lane: keep it in scalar registers
   const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
   const int mr0 = __builtin_amdgcn_readfirstlane(mt_row0[mt]);
@@ -252,19 +331,32 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   // results are not stored)
   const int n0 = nt * SH::PN + wave * 16 * SH::CT;
   const uint8_t* codes[2] = {c0p, c1p};
-  const uint8_t* scales[2] = {s0p, s1p};
-  BSrc<SH, NM> bs;
-  const int slab = (int)scale_slab_bytes(N, a.K);
+  using BS = typename std::conditional<FP8, BSrc8<SH, NM>, BSrc<SH, NM>>::type;
+  using BF = typename std::conditional<FP8, BFrag8<SH, NM>, BFrag<SH, NM>>::type;
+  BS bs;
+  if constexpr (FP8) {
+    const float* fsc[2] = {f0p, f1p};
 #pragma unroll
-  for (int mtx = 0; mtx < NM; ++mtx) {
-    bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
-                                                  KB * N * 16, kBufferFlags);
-    bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
-                                                  kBufferFlags);
+    for (int mtx = 0; mtx < NM; ++mtx) {
+      bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)codes[mtx], (short)0, a.K * N, kBufferFlags);
+      // (a wave wholly past N reads the last row block's scales; its results are not stored)
+      bs.s[mtx] = fsc[mtx] + (size_t)min(n0 / kFp8Block, N / kFp8Block - 1) * (a.K / kFp8Block);
+    }
+    bs.voff = (n0 + m) * 128 + 16 * q;
+  } else {
+    const uint8_t* scales[2] = {s0p, s1p};
+    const int slab = (int)scale_slab_bytes(N, a.K);
+#pragma unroll
+    for (int mtx = 0; mtx < NM; ++mtx) {
+      bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
+                                                    KB * N * 16, kBufferFlags);
+      bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
+                                                    kBufferFlags);
+    }
+    bs.voff_c = (q * N + n0 + m) * 16;
+    bs.nt64 = (N + 63) >> 6;
+    bs.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;
   }
-  bs.voff_c = (q * N + n0 + m) * 16;
-  bs.nt64 = (N + 63) >> 6;
-  bs.voff_s = (((n0 >> 6) * 16 + m) * 4 + q) * 4;
   const int sh = 8 * ((n0 >> 4) & 3);  // CT == 2: this wave's tiles are bytes sh/8 and sh/8 + 1
   static_assert(SH::CT == 2 || SH::CT == 4, "a wave's tiles share one scale dword");
   const int nsub = (nrows + 15) >> 4;
@@ -281,21 +373,21 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   // s+2 and the weight operands of step s+2 are in flight, and step s+1's rows (loaded one
   // step earlier) go from registers into the other LDS buffer.
   AStage<SH> ast[2];
-  BFrag<SH, NM> fb[3];
+  BF fb[3];
   // The loads run ahead unconditionally: past the last step the activation rows repeat the
   // last step (cache hits) and the weights read zeros without memory traffic, so no wait
   // in the loop has to assume a missing load.
   const int last = nsteps - 1;
   a_store<SH>(tile[0], a_fetch<SH>(ap, a.K, 0, lp), lr, lp);
-  b_fetch<SH, NM>(fb[0], bs, N, KB, 0, q);
+  b_fetch(fb[0], bs, N, KB, 0, q);
   ast[1] = a_fetch<SH>(ap, a.K, min(1, last), lp);
-  b_fetch<SH, NM>(fb[1], bs, N, KB, 1, q);
+  b_fetch(fb[1], bs, N, KB, 1, q);
   __syncthreads();
-  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BFrag<SH, NM>& fc,
-                  BFrag<SH, NM>& f_far) -> bool {
+  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BF& fc,
+                  BF& f_far) -> bool {
     a_far = a_fetch<SH>(ap, a.K, min(s + 2, last), lp);
-    b_fetch<SH, NM>(f_far, bs, N, KB, s + 2, q);
-    k_step<SH, NM>(tc, fc, acc, nsub, m, q, sh);
+    b_fetch(f_far, bs, N, KB, s + 2, q);
+    k_step(tc, fc, acc, nsub, m, q, sh);
     const bool more = s + 1 < nsteps;
     if (more) a_store<SH>(tn, a_next, lr, lp);
     __syncthreads();
@@ -363,7 +455,7 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
       for (int i = 0; i < 4; ++i) {
         const int rr = r0 + min(16 * rs + 4 * q + i, nrows - 1);
         slot[rs][i] = rr < tk ? perm[rr] : rr;
-        wt[rs][i] = rr < tk ? wts[rr] : 1.0f;
+        wt[rs][i] = rr < tk ? wts[rr] * routed_scale : 1.0f;
       }
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
@@ -389,11 +481,19 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int R = T * (d.K + d.S);
   const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H};
   const int tk = timing_begin("gemm_gateup", s);
-  gemm_f8f4_kernel<true, GateUpShape><<<(mt_bound + 7) / 8 * 8 * NT, GateUpShape::NTH, 0, s>>>(a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales,
-                                                       b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
-                                                       b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, T, d.K, d.I,
-                                                       R, NT);
+  gemm_f8f4_kernel<true, GateUpShape><<<(mt_bound + 7) / 8 * 8 * NT, GateUpShape::NTH, 0, s>>>(
+      a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr, b.perm, b.w, b.info, b.mt_group,
+      b.mt_row0, b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, d.fp8_shared, 1.0f, T, d.K, d.I, R, NT);
   timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !d.fp8_shared) return e;
+  const int mts = (T + kGemmBM - 1) / kGemmBM;  // the shared expert's M-tiles
+  const int tk8 = timing_begin("gemm_gateup_fp8", s);
+  gemm_f8f4_kernel<true, GateUpShape8, true><<<(mts + 7) / 8 * 8 * NT, GateUpShape8::NTH, 0, s>>>(
+      a, w.shared_gate_fp8, nullptr, w.shared_up_fp8, nullptr, w.shared_gate_fp8_scales, w.shared_up_fp8_scales,
+      b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, 0,
+      1.0f, T, d.K, d.I, R, NT);
+  timing_end(tk8, s);
   return hipGetLastError();
 }
 
@@ -404,10 +504,20 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
   const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
   const int tk = timing_begin("gemm_down", s);
-  gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(a, w.down_codes, w.down_scales, w.down_codes, w.down_scales,
-                                                        b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0,
-                                                        b.grp_rows, nullptr, b.staging, T, d.K, d.H, R, NT);
+  gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(
+      a, w.down_codes, w.down_scales, w.down_codes, w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.info,
+      b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr, b.staging, d.fp8_shared, d.routed_scale, T, d.K, d.H,
+      R, NT);
   timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !d.fp8_shared) return e;
+  const int mts = (T + kGemmBM - 1) / kGemmBM;
+  const int tk8 = timing_begin("gemm_down_fp8", s);
+  gemm_f8f4_kernel<false, DownShape8, true><<<(mts + 7) / 8 * 8 * NT, DownShape8::NTH, 0, s>>>(
+      a, w.shared_down_fp8, nullptr, w.shared_down_fp8, nullptr, w.shared_down_fp8_scales,
+      w.shared_down_fp8_scales, b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr,
+      b.staging, 0, d.routed_scale, T, d.K, d.H, R, NT);
+  timing_end(tk8, s);
   return hipGetLastError();
 }
 

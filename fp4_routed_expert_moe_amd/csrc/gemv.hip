@@ -24,6 +24,8 @@
 //   a group are the MFMA's M side, up to 16 per pass: one pass per group in decode.
 // * A token's result depends only on its own activations (fixed K and reduction order), so
 //   batch composition never changes a bit of it.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -139,33 +141,118 @@ __device__ __forceinline__ void gv_mma(const GFrag<NM, NA, TL>& f, f32x4 (&acc)[
     }
   }
 }
+// ---- the FP8 shared expert (e4m3 codes, float32 scale per 128 x 128 block) --------------
+// Kernel layout [K/128][N][128]: the 128 codes of reduction step it of row n are together.  In
+// the FP8 lane layout (common.h) lane (n, q) takes bytes 16q.. and 64+16q.. of its row's step:
+// two 16-byte loads, and across the wave each row's 128 bytes are read once.  A wave's TL tiles
+// (16*TL consecutive rows from a multiple of 16*TL) lie in one 128-row scale block, so one
+// float32 per matrix and step scales the wave's products (applied after the step's MFMAs).
+template <int NM, int NA, int TL>
+struct GFrag8 {
+  i32x4 c[NM][TL][2];
+  float s[NM];
+  i32x4 a[NA][2];
+  int sa;
+};
+template <int NM>
+struct GSrc8 {
+  __amdgpu_buffer_rsrc_t c[NM];
+  const float* s[NM];  // this wave's row block of each matrix's scales: s[mtx][it]
+  int voff;            // tile 0, step 0
+  int sel;             // unused (the FP4 source's byte select)
+};
+template <int NM>
+__device__ __forceinline__ void gsrc8_init(GSrc8<NM>& src, const uint8_t* const* codes, const float* const* scales,
+                                           int K, int N, int n0, int m, int q) {
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx) {
+    src.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)codes[mtx], (short)0, K * N, kBufferFlags);
+    src.s[mtx] = scales[mtx] + (size_t)(n0 / kFp8Block) * (K / kFp8Block);
+  }
+  src.voff = (n0 + m) * 128 + 16 * q;  // rows past N read other rows (or zeros past the end): not stored
+  src.sel = 0;
+}
+template <int NM, int NA, int TL>
+__device__ __forceinline__ void gv_load(GFrag8<NM, NA, TL>& f, const GSrc8<NM>& src, int N, const uint8_t* const* arow,
+                                        const uint8_t* asc, int K, int it, int q) {
+  const int so = __builtin_amdgcn_readfirstlane(it * N * 128);
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx) {
+#pragma unroll
+    for (int j = 0; j < TL; ++j) {
+      f.c[mtx][j][0] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], src.voff + 2048 * j, so, kWeightAux));
+      f.c[mtx][j][1] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(src.c[mtx], src.voff + 2048 * j + 64, so, kWeightAux));
+    }
+    f.s[mtx] = src.s[mtx][it];
+  }
+  const int o1 = it * 128 + 16 * q, o2 = o1 + 64;  // K is a multiple of 128 here
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    f.a[t][0] = *reinterpret_cast<const i32x4*>(arow[t] + o1);
+    f.a[t][1] = *reinterpret_cast<const i32x4*>(arow[t] + o2);
+  }
+  f.sa = asc[4 * it + q];
+}
+template <int NM, int NA, int TL>
+__device__ __forceinline__ void gv_mma(const GFrag8<NM, NA, TL>& f, f32x4 (&acc)[NM][TL], int sel) {
+  (void)sel;
+  i32x8 a[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) a[t] = __builtin_shufflevector(f.a[t][0], f.a[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+  for (int mtx = 0; mtx < NM; ++mtx)
+#pragma unroll
+    for (int j = 0; j < TL; ++j) {
+      const i32x8 b = __builtin_shufflevector(f.c[mtx][j][0], f.c[mtx][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      f32x4 p = mma_f8f8(a[0], b, f32x4{0.f, 0.f, 0.f, 0.f}, f.sa);
+#pragma unroll
+      for (int t = 1; t < NA; ++t) p = mma_f8f8(a[t], b, p, f.sa - 4 * t);
+      acc[mtx][j] += p * f.s[mtx];
+    }
+}
+
+// The fragment and source types of a weight format.
+template <bool FP8, int NM, int NA, int TL>
+struct GvFmt {
+  using Frag = GFrag<NM, NA, TL>;
+  using Src = GSrc<NM>;
+};
+template <int NM, int NA, int TL>
+struct GvFmt<true, NM, NA, TL> {
+  using Frag = GFrag8<NM, NA, TL>;
+  using Src = GSrc8<NM>;
+};
+
 // This wave's K iterations [it_lo, it_hi), the loads of iteration i+1 in flight while
 // iteration i runs on the matrix cores.  The steady-state loop body is one block whose loads
 // are issued before the matrix work (a scheduling barrier keeps them there), so the wait
 // before each step's MFMAs covers only that step's own loads.
-template <int NM, int NA, int TL>
-__device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& src, int N,
+template <int NM, int NA, int TL, class Src>
+__device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const Src& src, int N,
                                         const uint8_t* const* arow, const uint8_t* asc, int K, int it_lo, int it_hi,
                                         int q) {
   if (it_lo >= it_hi) return;
-  GFrag<NM, NA, TL> f0, f1;
-  gv_load<NM, NA, TL>(f0, src, N, arow, asc, K, it_lo, q);
+  using Frag = typename GvFmt<std::is_same<Src, GSrc8<NM>>::value, NM, NA, TL>::Frag;
+  Frag f0, f1;
+  gv_load(f0, src, N, arow, asc, K, it_lo, q);
   int it = it_lo;
   for (; it + 2 < it_hi; it += 2) {
-    gv_load<NM, NA, TL>(f1, src, N, arow, asc, K, it + 1, q);
+    gv_load(f1, src, N, arow, asc, K, it + 1, q);
     __builtin_amdgcn_sched_barrier(0);
-    gv_mma<NM, NA, TL>(f0, acc, src.sel);
-    gv_load<NM, NA, TL>(f0, src, N, arow, asc, K, it + 2, q);
+    gv_mma(f0, acc, src.sel);
+    gv_load(f0, src, N, arow, asc, K, it + 2, q);
     __builtin_amdgcn_sched_barrier(0);
-    gv_mma<NM, NA, TL>(f1, acc, src.sel);
+    gv_mma(f1, acc, src.sel);
   }
   if (it + 1 < it_hi) {
-    gv_load<NM, NA, TL>(f1, src, N, arow, asc, K, it + 1, q);
+    gv_load(f1, src, N, arow, asc, K, it + 1, q);
     __builtin_amdgcn_sched_barrier(0);
-    gv_mma<NM, NA, TL>(f0, acc, src.sel);
-    gv_mma<NM, NA, TL>(f1, acc, src.sel);
+    gv_mma(f0, acc, src.sel);
+    gv_mma(f1, acc, src.sel);
   } else {
-    gv_mma<NM, NA, TL>(f0, acc, src.sel);
+    gv_mma(f0, acc, src.sel);
   }
 }
 
@@ -173,13 +260,18 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const GSrc<NM>& sr
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
 // (h8 = [kHTerms][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
-template <int TL, int SPLIT>
+// FP8: the FP8 shared expert alone (the grid's y dimension is 1; its rows are the T tokens after
+// the T*k routed rows).  Otherwise the FP4 groups of the active-group slots, skipping group
+// `skip_group` (the shared expert when it is FP8; -1 for none); gc/gs/uc/us are then the FP4
+// arrays, else g8/g8s/u8/u8s the FP8 codes and scales.
+template <int TL, int SPLIT, bool FP8>
 __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
-    const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const int32_t* __restrict__ perm,
-    const GroupRec* __restrict__ grec, uint8_t* __restrict__ h8, uint32_t* __restrict__ stage_clear,
-    int T, int k, int H, int I, int R) {
-  {
+    const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const uint8_t* __restrict__ g8,
+    const float* __restrict__ g8s, const uint8_t* __restrict__ u8, const float* __restrict__ u8s,
+    const int32_t* __restrict__ perm, const GroupRec* __restrict__ grec, uint8_t* __restrict__ h8,
+    uint32_t* __restrict__ stage_clear, int skip_group, int T, int k, int H, int I, int R) {
+  if (stage_clear) {
     // clear the staging rows the down kernel fills next (R x H words)
     const size_t n = (size_t)R * H;
     const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x, nwg = (size_t)gridDim.x * gridDim.y;
@@ -188,20 +280,34 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
   }
   static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
   __shared__ f32x4 red[SPLIT][TL][2][64];
-  const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
-  if ((int)blockIdx.y >= rec.w) return;
-  const int g = __builtin_amdgcn_readfirstlane(rec.x);
-  const int row0 = __builtin_amdgcn_readfirstlane(rec.y), rows = __builtin_amdgcn_readfirstlane(rec.z);
+  int g, row0, rows;
+  if constexpr (FP8) {
+    g = -1;
+    row0 = T * k;
+    rows = T;
+  } else {
+    const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
+    if ((int)blockIdx.y >= rec.w || rec.x == skip_group) return;
+    g = __builtin_amdgcn_readfirstlane(rec.x);
+    row0 = __builtin_amdgcn_readfirstlane(rec.y);
+    rows = __builtin_amdgcn_readfirstlane(rec.z);
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * (16 * TL);
   const int KB = H >> 5;
   const int NI = (KB + 3) >> 2;  // K iterations of 4 blocks
   const int it_lo = wave * NI / SPLIT, it_hi = (wave + 1) * NI / SPLIT;
-  const uint8_t* codes[2] = {gc, uc};
-  const uint8_t* scales[2] = {gs, us};
-  GSrc<2> src;
-  gsrc_init<2>(src, codes, scales, g, KB, I, n0, m, q, 0);
+  typename GvFmt<FP8, 2, 2, TL>::Src src;
+  if constexpr (FP8) {
+    const uint8_t* codes[2] = {g8, u8};
+    const float* scales[2] = {g8s, u8s};
+    gsrc8_init<2>(src, codes, scales, H, I, n0, m, q);
+  } else {
+    const uint8_t* codes[2] = {gc, uc};
+    const uint8_t* scales[2] = {gs, us};
+    gsrc_init<2>(src, codes, scales, g, KB, I, n0, m, q, 0);
+  }
   const uint8_t* x_hi = xq;
   const uint8_t* x_lo = xq + (size_t)T * H;
   const uint8_t* x_sc = xq + (size_t)2 * T * H;
@@ -299,32 +405,53 @@ constexpr int kDnBlocks = 1;  // column blocks (of TL tiles) per down workgroup
 constexpr int kDnSplit = MOE_DN_SPLIT;            // waves per down workgroup = reduction-axis slices
 constexpr int kDnThreads = 64 * kDnSplit;
 
-template <int TL>
+// FP8: the FP8 shared expert alone (launched after the FP4 kernel, so every routed row is in
+// staging), each workgroup also combining its tile.  Otherwise the FP4 groups, skipping
+// skip_group.  A routed row's weight is its routing weight times routed_scale.
+template <int TL, bool FP8>
 __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
+    const uint8_t* __restrict__ d8, const float* __restrict__ d8s,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const GroupRec* __restrict__ grec,
-    float* __restrict__ staging, float* __restrict__ y, int T, int k, int S,
+    float* __restrict__ staging, float* __restrict__ y, int skip_group, float routed_scale, int T, int k, int S,
     int H, int I, int R) {
   constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
   // column tiles each wave finishes (waves past the last tile only reduce)
   constexpr int kDnPerWave = kDnBlocks * TL > kDnSplit ? kDnBlocks * TL / kDnSplit : 1;
   static_assert(kDnPerWave * kDnSplit >= kDnBlocks * TL, "down workgroup shape");
   __shared__ f32x4 red[kDnSplit][kDnBlocks][TL][64];
-  const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
-  const int nact = rec.w;
-  if ((int)blockIdx.y >= nact) return;
-  const int g = __builtin_amdgcn_readfirstlane(rec.x);
-  const int row0 = __builtin_amdgcn_readfirstlane(rec.y), rows = __builtin_amdgcn_readfirstlane(rec.z);
+  int g, row0, rows;
+  bool combiner;
+  if constexpr (FP8) {
+    g = -1;
+    row0 = T * k;
+    rows = T;
+    combiner = true;
+  } else {
+    const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
+    const int nslots = rec.w;
+    if ((int)blockIdx.y >= nslots || rec.x == skip_group) return;
+    g = __builtin_amdgcn_readfirstlane(rec.x);
+    row0 = __builtin_amdgcn_readfirstlane(rec.y);
+    rows = __builtin_amdgcn_readfirstlane(rec.z);
+    combiner = (int)blockIdx.y == nslots - 1;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * kDnCols;
   const int KB = I >> 5;
   const int NI = (KB + 3) >> 2;
   const int it_lo = wave * NI / kDnSplit, it_hi = (wave + 1) * NI / kDnSplit;
-  const uint8_t* codes[kDnBlocks] = {dc};
-  const uint8_t* scales[kDnBlocks] = {ds};
-  GSrc<kDnBlocks> src;
-  gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * TL);
+  typename GvFmt<FP8, kDnBlocks, kHTerms, TL>::Src src;
+  if constexpr (FP8) {
+    const uint8_t* codes[kDnBlocks] = {d8};
+    const float* scales[kDnBlocks] = {d8s};
+    gsrc8_init<kDnBlocks>(src, codes, scales, I, H, n0, m, q);
+  } else {
+    const uint8_t* codes[kDnBlocks] = {dc};
+    const uint8_t* scales[kDnBlocks] = {ds};
+    gsrc_init<kDnBlocks>(src, codes, scales, g, KB, H, n0, m, q, 16 * TL);
+  }
   const uint8_t* hs = h8 + (size_t)kHTerms * R * I;
   const int tk = T * k;
   for (int c0 = 0; c0 < rows; c0 += kSkM) {
@@ -337,7 +464,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     for (int i = 0; i < 4; ++i) {
       const int rr = row0 + c0 + min(4 * q + i, nt - 1);
       slot_i[i] = rr < tk ? perm[rr] : rr;
-      wt_i[i] = rr < tk ? row_w[rr] : 1.0f;
+      wt_i[i] = rr < tk ? row_w[rr] * routed_scale : 1.0f;
     }
     const uint8_t* arow[kHTerms] = {h8 + r * I, h8 + (size_t)R * I + r * I
 #if MOE_DEC_HTERMS == 3
@@ -374,7 +501,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   }
   // The last active group's workgroup of the tile adds the tile's rows once they are all
   // there (a word is 0 until its row is written; the others need not wait for their stores).
-  if ((int)blockIdx.y != nact - 1) return;
+  if (!combiner) return;
   // The slots of an output are read 8 at a time with their loads issued together; a word
   // still 0 is polled again on its own.
   const uint32_t* st = reinterpret_cast<const uint32_t*>(staging);
@@ -423,12 +550,21 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const bool narrow = (size_t)max_act * ((d.I + 63) / 64) < kMinGemvGroups;
   const int cols = narrow ? 32 : 64;
   dim3 grid((d.I + cols - 1) / cols, max_act);
+  const int skip = d.fp8_shared ? d.E : -1;
   const int tk = timing_begin("gemv_gateup", s);
-  auto kern = narrow ? gemv_gateup_kernel<2, kSplit> : gemv_gateup_kernel<4, kSplit>;
-  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, b.perm, b.grec,
-                                    static_cast<uint8_t*>(b.h),
-                                    reinterpret_cast<uint32_t*>(b.staging), T, d.K, d.H, d.I, R);
+  auto kern = narrow ? gemv_gateup_kernel<2, kSplit, false> : gemv_gateup_kernel<4, kSplit, false>;
+  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr,
+                                    nullptr, nullptr, b.perm, b.grec, static_cast<uint8_t*>(b.h),
+                                    reinterpret_cast<uint32_t*>(b.staging), skip, T, d.K, d.H, d.I, R);
   timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !d.fp8_shared) return e;
+  // the FP8 shared expert: 32-column tiles (its one group over the whole GPU)
+  const int tk8 = timing_begin("gemv_gateup_fp8", s);
+  gemv_gateup_kernel<2, kSplit, true><<<dim3((d.I + 31) / 32, 1), 64 * kSplit, 0, s>>>(
+      b.xq, nullptr, nullptr, nullptr, nullptr, w.shared_gate_fp8, w.shared_gate_fp8_scales, w.shared_up_fp8,
+      w.shared_up_fp8_scales, b.perm, b.grec, static_cast<uint8_t*>(b.h), nullptr, -1, T, d.K, d.H, d.I, R);
+  timing_end(tk8, s);
   return hipGetLastError();
 }
 
@@ -438,11 +574,20 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   // (narrower down tiles measured slower: a down workgroup's bytes are already few)
   constexpr int kCols = kDnBlocks * 16 * 4;
   dim3 grid((d.H + kCols - 1) / kCols, max_act);
+  const int skip = d.fp8_shared ? d.E : -1;
   const int tk = timing_begin("gemv_down", s);
-  auto kern = gemv_down_kernel<4>;
-  kern<<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes, w.down_scales, b.perm, b.row_w,
-                                   b.grec, b.staging, y, T, d.K, d.S, d.H, d.I, R);
+  gemv_down_kernel<4, false><<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes,
+                                                         w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.grec,
+                                                         b.staging, y, skip, d.routed_scale, T, d.K, d.S, d.H,
+                                                         d.I, R);
   timing_end(tk, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !d.fp8_shared) return e;
+  const int tk8 = timing_begin("gemv_down_fp8", s);
+  gemv_down_kernel<4, true><<<dim3(grid.x, 1), kDnThreads, 0, s>>>(
+      static_cast<const uint8_t*>(b.h), nullptr, nullptr, w.shared_down_fp8, w.shared_down_fp8_scales, b.perm,
+      b.row_w, b.grec, b.staging, y, -1, d.routed_scale, T, d.K, d.S, d.H, d.I, R);
+  timing_end(tk8, s);
   return hipGetLastError();
 }
 

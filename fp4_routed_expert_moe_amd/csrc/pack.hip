@@ -74,6 +74,31 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   out[id] = v;
 }
 
+// FP8 codes [G][N][K] -> [G][K/128][N][128]: the 128-byte chunks of each row transposed, one
+// 16-byte piece per thread (consecutive threads on consecutive output bytes).
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint4* __restrict__ in, uint4* __restrict__ out, int N,
+                                                       int KC, size_t total) {
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;  // output piece
+  if (id >= total) return;
+  const int p = (int)(id & 7);                               // piece of the 128-byte chunk
+  size_t r = id >> 3;
+  const int n = (int)(r % N);
+  r /= N;
+  const int kc = (int)(r % KC);
+  const size_t g = r / KC;
+  out[id] = in[((g * N + n) * KC + kc) * 8 + p];
+}
+
+hipError_t launch_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int groups, int N, int K, hipStream_t s) {
+  const int KC = K / kFp8Block;
+  const size_t total = (size_t)groups * N * KC * 8;
+  const int tk = timing_begin("pack_fp8", s);
+  pack_fp8_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(reinterpret_cast<const uint4*>(codes_in),
+                                                                   reinterpret_cast<uint4*>(codes_out), N, KC, total);
+  timing_end(tk, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
                        int groups, int N, int K, hipStream_t s) {
   const int KB = K / 32;

@@ -422,6 +422,7 @@ __device__ __forceinline__ void write_tables(const CNT& cnt, const int* offs, co
     }
     b.info[0] = gs.nact + S;
     b.info[1] = gs.nmt;
+    b.info[2] = gs.nmt_routed;
   }
 }
 

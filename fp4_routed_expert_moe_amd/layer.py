@@ -55,22 +55,50 @@ def pack_fp4(codes: torch.Tensor, scales: torch.Tensor, stream=None):
     return out_c, out_s
 
 
+def pack_fp8(codes: torch.Tensor, stream=None) -> torch.Tensor:
+    """FP8 E4M3 codes in the checkpoint layout [G][N][K] (uint8) -> the kernel layout
+    [G][K/128][N][128], by the library's pack kernel.  Block scales need no repacking."""
+    lib = _lib.load()
+    g, n, k = codes.shape
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous() or k % 128:
+        raise ValueError("pack_fp8 wants contiguous uint8 CUDA codes [G][N][K] with K a multiple of 128")
+    out = torch.empty((g, k // 128, n, 128), dtype=torch.uint8, device=codes.device)
+    _lib.check(lib.moe_pack_fp8(_ptr(codes), _ptr(out), g, n, k, _stream_handle(stream)), lib)
+    return out
+
+
 class MoeLayer:
     """One routed FP4-expert MoE layer over borrowed device weights.
 
     ``gate``/``up``/``down`` are (codes, scales) uint8 CUDA tensors in the kernel
-    layout: codes [E+S][K/32][N][16], scales ``kernel_scale_shape`` (see ``pack_fp4``);
-    the library keeps only their pointers, so this object holds references to
-    keep them alive.
+    layout: codes [G][K/32][N][16], scales ``kernel_scale_shape`` (see ``pack_fp4``),
+    G = E + S groups.  With ``shared_fp8`` = dict(gate=(codes, scales), up=..., down=...)
+    the shared expert is FP8 E4M3 instead (codes in the kernel layout of ``pack_fp8``,
+    float32 scales [N/128][K/128]) and the FP4 arrays hold the E routed experts only.
+    The library keeps only pointers, so this object holds references to keep them alive.
     """
 
     def __init__(self, w_router: torch.Tensor, gate, up, down, top_k: int, n_shared: int = 1,
-                 router_bias: Optional[torch.Tensor] = None, path: str = "auto"):
+                 router_bias: Optional[torch.Tensor] = None, path: str = "auto", shared_fp8: Optional[dict] = None,
+                 routed_scale: float = 1.0):
         self.lib = _lib.load()
         e, h = w_router.shape
         g, hb, inter, sixteen = gate[0].shape
-        if g != e + n_shared or hb * 32 != h or sixteen != 16:
+        fp4_groups = e if shared_fp8 is not None else e + n_shared
+        if g != fp4_groups or hb * 32 != h or sixteen != 16:
             raise ValueError(f"gate codes {tuple(gate[0].shape)} do not match E={e}, S={n_shared}, H={h}")
+        f8 = {}
+        if shared_fp8 is not None:
+            for name, n, k in (("gate", inter, h), ("up", inter, h), ("down", h, inter)):
+                c, sc = shared_fp8[name]
+                if tuple(c.shape) != (k // 128, n, 128) or c.dtype != torch.uint8 or not c.is_cuda:
+                    raise ValueError(f"shared FP8 {name} codes {tuple(c.shape)}, expected {(k // 128, n, 128)}")
+                if tuple(sc.shape) != (n // 128, k // 128) or sc.dtype != torch.float32 or not sc.is_cuda:
+                    raise ValueError(f"shared FP8 {name} scales {tuple(sc.shape)}, expected {(n // 128, k // 128)}")
+                if not c.is_contiguous() or not sc.is_contiguous():
+                    raise ValueError(f"shared FP8 {name} tensors must be contiguous")
+                f8[f"shared_{name}_fp8"] = _ptr(c)
+                f8[f"shared_{name}_fp8_scales"] = _ptr(sc)
         for name, (c, s), n, k in (("gate", gate, inter, h), ("up", up, inter, h), ("down", down, h, inter)):
             if tuple(c.shape) != (g, k // 32, n, 16) or tuple(s.shape) != kernel_scale_shape(g, n, k):
                 raise ValueError(f"{name} weights: codes {tuple(c.shape)} / scales {tuple(s.shape)}, "
@@ -86,13 +114,14 @@ class MoeLayer:
             raise ValueError("router_bias must be a float32 CUDA tensor of E values")
         self.hidden, self.n_experts, self.top_k, self.n_shared, self.inter = h, e, top_k, n_shared, inter
         self.device = w_router.device
-        self._keep = (w_router, gate, up, down, router_bias)
+        self._keep = (w_router, gate, up, down, router_bias, shared_fp8)
         desc = _lib.LayerDesc(
             abi_version=_lib.MOE_ABI_VERSION, hidden=h, n_experts=e, top_k=top_k, n_shared=n_shared,
-            inter=inter, path=_PATHS[path], device=w_router.device.index or 0,
+            inter=inter, path=_PATHS[path], device=w_router.device.index or 0, block=32,
+            flags=_lib.MOE_SHARED_FP8 if shared_fp8 is not None else 0, routed_scale=routed_scale, reserved=0,
             w_router=_ptr(w_router), router_bias=_ptr(router_bias),
             gate_codes=_ptr(gate[0]), gate_scales=_ptr(gate[1]), up_codes=_ptr(up[0]),
-            up_scales=_ptr(up[1]), down_codes=_ptr(down[0]), down_scales=_ptr(down[1]))
+            up_scales=_ptr(up[1]), down_codes=_ptr(down[0]), down_scales=_ptr(down[1]), **f8)
         handle = ctypes.c_void_p()
         _lib.check(self.lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(handle)), self.lib)
         self._h = handle

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
   MOE_OK = 0,
@@ -73,6 +73,17 @@ enum moe_status {
  * testing, the kill-switch pattern of PR #165's AVX2 series). */
 enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GEMM = 2 };
 
+/* Layer flags. */
+enum moe_flags {
+  /* The shared expert is stored as FP8 E4M3 with a float32 scale per 128 x 128 block, the dense
+   * format of the V4 checkpoints ("Add DeepSeek V4 Flash CPU inference with NVMe expert
+   * streaming", PR #165, the question on V4 sizes: "FP8 E4M3 dense with 128x128 block scales").
+   * Element (n, k) = E4M3(code) * scale[n / 128][k / 128]; E4M3 has 1 sign, 4 exponent (bias 7)
+   * and 3 mantissa bits, subnormals, and NaN at 0x7F / 0xFF.  Requires n_shared = 1 and H, I
+   * multiples of 128; the FP4 arrays then hold the E routed experts only. */
+  MOE_SHARED_FP8 = 1
+};
+
 /* Layer description.  All pointers are device pointers on `device`.  The library BORROWS
  * them: the caller keeps them alive and unchanged until moe_layer_destroy. */
 typedef struct moe_layer_desc {
@@ -84,14 +95,29 @@ typedef struct moe_layer_desc {
   int32_t inter;         /* I: multiple of 32, 32..8192 */
   int32_t path;          /* enum moe_path */
   int32_t device;        /* HIP device ordinal holding the weights */
+  int32_t block;         /* values per FP4 scale along the reduction axis: must be 32 */
+  int32_t flags;         /* enum moe_flags, OR-ed */
+  float routed_scale;    /* the routed experts' sum is multiplied by this (1.0 for V4 Flash);
+                            finite and > 0; the shared expert's weight stays 1 */
+  int32_t reserved;      /* must be 0 */
   const float* w_router;       /* fp32 [E][H] */
   const float* router_bias;    /* fp32 [E], or NULL for no bias */
-  const uint8_t* gate_codes;   /* kernel layout (see above): [E+S][H/32][I][16] */
-  const uint8_t* gate_scales;  /* [E+S][ceil(H/128)][ceil(I/64)][16][4][4] */
-  const uint8_t* up_codes;     /* [E+S][H/32][I][16] */
-  const uint8_t* up_scales;    /* [E+S][ceil(H/128)][ceil(I/64)][16][4][4] */
-  const uint8_t* down_codes;   /* [E+S][I/32][H][16] */
-  const uint8_t* down_scales;  /* [E+S][ceil(I/128)][ceil(H/64)][16][4][4] */
+  /* FP4 experts, kernel layout (see above); G = E + S groups, or E with MOE_SHARED_FP8 */
+  const uint8_t* gate_codes;   /* [G][H/32][I][16] */
+  const uint8_t* gate_scales;  /* [G][ceil(H/128)][ceil(I/64)][16][4][4] */
+  const uint8_t* up_codes;     /* [G][H/32][I][16] */
+  const uint8_t* up_scales;    /* [G][ceil(H/128)][ceil(I/64)][16][4][4] */
+  const uint8_t* down_codes;   /* [G][I/32][H][16] */
+  const uint8_t* down_scales;  /* [G][ceil(I/128)][ceil(H/64)][16][4][4] */
+  /* MOE_SHARED_FP8 only (else NULL): the shared expert in the FP8 kernel layout, codes
+   * [K/128][N][128] (the 128 values of reduction step j of row n together, see moe_pack_fp8)
+   * and float32 scales [N/128][K/128] as stored; gate/up N = I, K = H; down N = H, K = I */
+  const uint8_t* shared_gate_fp8;
+  const float* shared_gate_fp8_scales;
+  const uint8_t* shared_up_fp8;
+  const float* shared_up_fp8_scales;
+  const uint8_t* shared_down_fp8;
+  const float* shared_down_fp8_scales;
 } moe_layer_desc;
 
 /* Routing results (device pointers), written by moe_route / moe_forward. */
@@ -179,6 +205,13 @@ int32_t moe_forward_noalloc(const moe_layer* layer, const uint16_t* x, int32_t t
  * streaming" (PR #165) likewise repacks each expert once into its kernels' interleaved layout. */
 int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out,
                      uint8_t* scales_out, int32_t groups, int32_t rows, int32_t cols, void* stream);
+
+/* Repack `groups` FP8 E4M3 matrices of `rows` x `cols` (cols = reduction axis, multiple of 128)
+ * from the checkpoint layout codes [groups][rows][cols] into the kernel layout
+ * [groups][cols/128][rows][128] (device pointers, 16-byte aligned, not overlapping).  Their
+ * float32 block scales need no repacking.  Asynchronous on `stream` of the current device. */
+int32_t moe_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int32_t groups, int32_t rows, int32_t cols,
+                     void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(int32_t status);

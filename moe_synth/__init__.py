@@ -14,6 +14,11 @@ What is drawn, and from which workload description:
   popularity prior ``b_e = -1.1 * ln(e + 1)`` (expert 0 most popular).
 * Expert weights: e2m1 code bytes uniform on 0..255 (each nibble uniform on
   0..15) and e8m0 scale bytes uniform on {123..127}, i.e. 2^U{-4..0}.
+* A shared expert stored in FP8 (workloads with ``shared_fp8``): E4M3 code
+  bytes uniform on the 254 finite codes (a drawn 0x7F / 0xFF, the two NaN
+  patterns, becomes 0x7E / 0xFE) and one float32 scale per 128 x 128 block,
+  (0.5 + U[0,1)) * 2^-7 with U on a 2^-24 grid, which gives the shared expert
+  about the same root-mean-square weight as the FP4 experts.
 
 Workload shapes follow the DeepSeek V4 Flash expert dimensions quoted on
 "Add DeepSeek V4 Flash CPU inference with NVMe expert streaming" (PR #165:
@@ -56,10 +61,16 @@ class Workload:
     zipf: Optional[float] = None  # router popularity bias exponent
     scale_lo: int = 123  # e8m0 scale byte range (2^-4 .. 2^0)
     scale_hi: int = 127
+    shared_fp8: bool = False  # shared expert in FP8 E4M3 with 128 x 128 block scales
 
     @property
     def groups(self) -> int:
         return self.experts + self.shared
+
+    @property
+    def fp4_groups(self) -> int:
+        """Groups stored in FP4: every group, or the routed experts only when the shared one is FP8."""
+        return self.experts if self.shared_fp8 else self.groups
 
 
 WORKLOADS = {
@@ -71,6 +82,8 @@ WORKLOADS = {
     # DeepSeek V4 Pro scale (hidden 7168, 384 experts, same expert format); intermediate 2048
     # and top-6 are readings (the pages give neither for Pro)
     "decode_pro_t8": Workload("decode_pro_t8", 7168, 384, 6, 1, 2048, 8),
+    # the V4 Flash decode shape with the shared expert kept in the checkpoint's FP8 E4M3 format
+    "decode_t8_fp8shared": Workload("decode_t8_fp8shared", 4096, 256, 6, 1, 2048, 8, shared_fp8=True),
 }
 _WORKLOAD_IDS = {n: i + 1 for i, n in enumerate(WORKLOADS)}
 
@@ -79,6 +92,9 @@ TENSOR_IDS = {
     "gate_codes": 3, "gate_scales": 4,
     "up_codes": 5, "up_scales": 6,
     "down_codes": 7, "down_scales": 8,
+    "gate_fp8_codes": 9, "gate_fp8_scales": 10,
+    "up_fp8_codes": 11, "up_fp8_scales": 12,
+    "down_fp8_codes": 13, "down_fp8_scales": 14,
 }
 MATRICES = ("gate", "up", "down")
 
@@ -97,7 +113,10 @@ def _wl_id(wl: Workload) -> int:
         return _WORKLOAD_IDS[wl.name]
     # custom workloads: fold the name and every field into an id
     h = 0
-    for ch in repr(dataclasses.astuple(wl)).encode():
+    fields = dataclasses.astuple(wl)
+    if not wl.shared_fp8:
+        fields = fields[:-1]    # ids of workloads from before the FP8 field stay as they were
+    for ch in repr(fields).encode():
         h = (h * 1099511628211 + ch) & _MASK64
     return h | (1 << 40)
 
@@ -214,18 +233,41 @@ def expert_matrix(wl, layer: int, mat: str, group: int, device="cpu"):
 
 
 def layer_weights(wl, layer: int, device="cpu"):
-    """All expert matrices of one layer: dict mat -> (codes [G][N][K/2], scales [G][N][K/32])."""
+    """All FP4 expert matrices of one layer: dict mat -> (codes [G][N][K/2], scales [G][N][K/32]),
+    G = ``wl.fp4_groups`` (the shared expert is left out when it is stored in FP8)."""
     wl = workload(wl)
     out = {}
     for mat in MATRICES:
         n, k = matrix_dims(wl, mat)
         kc, ks = _keys(wl, layer, mat)
-        codes = torch.empty((wl.groups, n, k // 2), dtype=torch.uint8, device=device)
-        scales = torch.empty((wl.groups, n, k // 32), dtype=torch.uint8, device=device)
+        codes = torch.empty((wl.fp4_groups, n, k // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((wl.fp4_groups, n, k // 32), dtype=torch.uint8, device=device)
         fill_code_bytes(codes, kc)
         fill_scale_bytes(scales, ks, wl.scale_lo, wl.scale_hi)
         out[mat] = (codes, scales)
     return out
+
+
+def shared_fp8_matrix(wl, layer: int, mat: str, device="cpu"):
+    """The FP8 shared expert's matrix ``mat``: codes [N][K] (uint8 E4M3 bytes, never a NaN
+    pattern) and float32 block scales [ceil(N/128)][ceil(K/128)]."""
+    wl = workload(wl)
+    n, k = matrix_dims(wl, mat)
+    wid = _wl_id(wl)
+    codes = torch.empty((n, k), dtype=torch.uint8, device=device)
+    fill_code_bytes(codes, derive_key(wid, layer, TENSOR_IDS[mat + "_fp8_codes"]))
+    nan = (codes & 0x7F) == 0x7F
+    codes[nan] = codes[nan] - 1
+    nb, kb = -(-n // 128), -(-k // 128)
+    w = splitmix64_words(derive_key(wid, layer, TENSOR_IDS[mat + "_fp8_scales"]), 0, nb * kb, device)
+    u = _srl(w, 40).to(torch.float32) * 2.0 ** -24          # exact: 24-bit integers
+    scales = ((0.5 + u) * 2.0 ** -7).reshape(nb, kb).contiguous()
+    return codes, scales
+
+
+def shared_fp8_weights(wl, layer: int, device="cpu"):
+    """dict mat -> (codes [N][K], scales) of the FP8 shared expert (see ``shared_fp8_matrix``)."""
+    return {mat: shared_fp8_matrix(wl, layer, mat, device) for mat in MATRICES}
 
 
 class LazyExperts:
@@ -246,12 +288,18 @@ class LazyExperts:
         return self.wl.groups
 
     def __getitem__(self, g: int):
+        """FP4 groups as (codes, scales) pairs; with ``shared_fp8`` group E is instead
+        dict mat -> ("fp8", codes [N][K], scales [N/128][K/128]) for the caller to wrap."""
         if g < 0 or g >= self.wl.groups:
             raise IndexError(g)
         if g in self._cache:
             return self._cache[g]
         d = {}
         for mat in MATRICES:
+            if g >= self.wl.fp4_groups:
+                c, s = shared_fp8_matrix(self.wl, self.layer, mat)
+                d[mat] = ("fp8", c.numpy(), s.numpy())
+                continue
             c, s = expert_matrix(self.wl, self.layer, mat, g)
             d[mat] = (c.numpy(), s.numpy())
         self._cache[g] = d

@@ -31,6 +31,10 @@ static moe_layer_desc base_desc(void) {
   d.inter = 2048;
   d.path = MOE_PATH_AUTO;
   d.device = 0;
+  d.block = 32;
+  d.flags = 0;
+  d.routed_scale = 1.0f;
+  d.reserved = 0;
   // never dereferenced on the host: the library only keeps and checks these pointers
   d.w_router = (const float*)0x10000;
   d.gate_codes = (const uint8_t*)0x20000;
@@ -151,6 +155,33 @@ int main(void) {
   CHECK(moe_pack_fp4(ci + 8, si, co, so, 1, 64, 256, NULL) == MOE_ERR_INVALID);
   CHECK(moe_pack_fp4(ci, si, co, so + 2, 1, 64, 256, NULL) == MOE_ERR_INVALID);
   CHECK(moe_pack_fp4(ci, si, (uint8_t*)ci + 16, so, 1, 64, 256, NULL) == MOE_ERR_INVALID);  // overlap
+  CHECK(moe_pack_fp8(NULL, co, 1, 64, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_pack_fp8(ci, co, 1, 64, 96, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_pack_fp8(ci, co + 8, 1, 64, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_pack_fp8(ci, (uint8_t*)ci + 64, 1, 64, 256, NULL) == MOE_ERR_INVALID);  // overlap
+
+  // the FP8 shared expert's descriptor checks, and routed_scale / block / reserved
+  {
+    moe_layer_desc b = base_desc();
+    b.flags = MOE_SHARED_FP8;
+    CHECK(create(&b, &L) == MOE_ERR_INVALID);  // pointers missing
+    b.shared_gate_fp8 = (const uint8_t*)0x80000;
+    b.shared_gate_fp8_scales = (const float*)0x90000;
+    b.shared_up_fp8 = (const uint8_t*)0xa0000;
+    b.shared_up_fp8_scales = (const float*)0xb0000;
+    b.shared_down_fp8 = (const uint8_t*)0xc0000;
+    b.shared_down_fp8_scales = (const float*)0xd0000;
+    CHECK(create(&b, &L) == MOE_OK && L != NULL);
+    moe_layer_destroy(L);
+    b.shared_down_fp8_scales = (const float*)0xd0002;
+    CHECK(create(&b, &L) == MOE_ERR_INVALID);  // misaligned scales
+    b = base_desc();
+    b.routed_scale = -1.0f;
+    CHECK(create(&b, &L) == MOE_ERR_INVALID);
+    b = base_desc();
+    b.block = 64;
+    CHECK(create(&b, &L) == MOE_ERR_INVALID);
+  }
 
   // timing calls with nothing recorded
   CHECK(moe_timing_enable(1) == MOE_OK);

@@ -46,13 +46,30 @@ def pack_weights(weights):
     return {mat: pack_fp4(*weights[mat]) for mat in synth.MATRICES}
 
 
-def make_layer(w_router, weights, top_k, n_shared, bias=None, path="auto", packed=None):
-    """Layer over checkpoint-layout device weights (packed here unless `packed` is given)."""
+def pack_shared_fp8(shared):
+    """FP8 shared expert, dict mat -> (codes [N][K], float32 scales) on the host or the device ->
+    the kernel layout (codes through the library's pack call), as MoeLayer's ``shared_fp8``."""
+    from fp4_routed_expert_moe_amd import pack_fp8
+    out = {}
+    for mat in synth.MATRICES:
+        c, sc = shared[mat]
+        c = torch.as_tensor(np.asarray(c) if not torch.is_tensor(c) else c).cuda().contiguous()
+        sc = torch.as_tensor(np.asarray(sc) if not torch.is_tensor(sc) else sc).cuda().contiguous()
+        out[mat] = (pack_fp8(c[None])[0], sc)
+    return out
+
+
+def make_layer(w_router, weights, top_k, n_shared, bias=None, path="auto", packed=None, shared_fp8=None,
+               routed_scale=1.0):
+    """Layer over checkpoint-layout device weights (packed here unless `packed` is given); with
+    ``shared_fp8`` (see ``pack_shared_fp8``) the FP4 weights hold the routed experts only."""
     from fp4_routed_expert_moe_amd import MoeLayer
     wr = torch.from_numpy(np.ascontiguousarray(w_router, dtype=np.float32)).cuda()
     b = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32)).cuda()
     pk = packed if packed is not None else pack_weights(weights)
-    layer = MoeLayer(wr, pk["gate"], pk["up"], pk["down"], top_k, n_shared, b, path)
+    f8 = None if shared_fp8 is None else pack_shared_fp8(shared_fp8)
+    layer = MoeLayer(wr, pk["gate"], pk["up"], pk["down"], top_k, n_shared, b, path, shared_fp8=f8,
+                     routed_scale=routed_scale)
     return layer
 
 
@@ -236,24 +253,27 @@ def _pool():
 
 
 def _oracle_job(args):
-    wl, layer, x_bits, w_router, bias, top_k, shared = args
-    return oracle.moe_forward(x_bits, w_router, bias, synth.LazyExperts(wl, layer, cache=2), top_k, shared)["y"]
+    wl, layer, x_bits, w_router, bias, top_k, shared = args[:7]
+    routed_scale = args[7] if len(args) > 7 else 1.0
+    return oracle.moe_forward(x_bits, w_router, bias, synth.LazyExperts(wl, layer, cache=2), top_k, shared,
+                              routed_scale)["y"]
 
 
 def oracle_outputs(jobs):
-    """y of oracle.moe_forward for each job (wl, layer, x_bits, w_router, bias, top_k, shared)."""
+    """y of oracle.moe_forward for each job (wl, layer, x_bits, w_router, bias, top_k, shared
+    [, routed_scale]); the experts are the workload's seeded ones."""
     return list(_pool().map(_oracle_job, jobs))
 
 
-def oracle_sampled(wl, layer, x_bits, w_router, bias, tokens, idx):
+def oracle_sampled(wl, layer, x_bits, w_router, bias, tokens, idx, routed_scale=1.0):
     """Oracle outputs [len(tokens)][H] of the given tokens of one layer call, computed in chunks
     of tokens grouped by their first expert (so a chunk decodes fewer distinct experts)."""
     tokens = np.asarray(tokens)
     order = tokens[np.argsort(np.asarray(idx)[tokens, 0], kind="stable")]
     n = min(len(order), 2 * oracle_workers())
     chunks = [c for c in np.array_split(order, n) if len(c)]
-    ys = oracle_outputs([(wl, layer, np.ascontiguousarray(x_bits[c]), w_router, bias, wl.top_k, wl.shared)
-                         for c in chunks])
+    ys = oracle_outputs([(wl, layer, np.ascontiguousarray(x_bits[c]), w_router, bias, wl.top_k, wl.shared,
+                          routed_scale) for c in chunks])
     out = {}
     for c, y in zip(chunks, ys):
         for t, row in zip(c, y):

@@ -77,3 +77,35 @@ def random_experts(rng, hidden, inter, groups, scale_lo=123, scale_hi=127):
                       rng.integers(scale_lo, scale_hi + 1, (n, k // 32), dtype=np.uint8))
         out.append(d)
     return out
+
+
+def random_fp8_shared(rng, hidden, inter, code_hi=0x7E, scale_exp=-7):
+    """A random FP8 shared expert, dict mat -> (codes [N][K] uint8, float32 scales
+    [ceil(N/128)][ceil(K/128)]): codes uniform on the finite E4M3 patterns with magnitude code
+    at most ``code_hi`` (0x7E = 448), scales (0.5 + U) * 2^scale_exp."""
+    out = {}
+    for mat, (n, k) in (("gate", (inter, hidden)), ("up", (inter, hidden)), ("down", (hidden, inter))):
+        mag = rng.integers(0, code_hi + 1, (n, k), dtype=np.uint8)
+        sign = rng.integers(0, 2, (n, k), dtype=np.uint8) << 7
+        sc = ((0.5 + rng.random((-(-n // 128), -(-k // 128)))) * 2.0 ** scale_exp).astype(np.float32)
+        out[mat] = (mag | sign, sc)
+    return out
+
+
+def identity_fp8_shared(hidden, inter, down_scale=0.75):
+    """FP8 shared expert with a closed form: gate = selector of 1.0 (E4M3 0x38), up = selector of
+    2.0 (0x40), down = selector of 1.0 with every down block scale ``down_scale``; it adds
+    down_scale * silu(x_i) * 2 x_i for i < I."""
+    g = np.zeros((inter, hidden), np.uint8)
+    u = np.zeros((inter, hidden), np.uint8)
+    d = np.zeros((hidden, inter), np.uint8)
+    for i in range(inter):
+        g[i, i], u[i, i], d[i, i] = 0x38, 0x40, 0x38
+    one = lambda n, k: np.ones((-(-n // 128), -(-k // 128)), np.float32)
+    return dict(gate=(g, one(inter, hidden)), up=(u, one(inter, hidden)),
+                down=(d, np.full((-(-hidden // 128), -(-inter // 128)), down_scale, np.float32)))
+
+
+def as_oracle_fp8(shared):
+    """dict mat -> (codes, scales) as the oracle's tagged FP8 triples."""
+    return {mat: ("fp8", np.asarray(c), np.asarray(s)) for mat, (c, s) in shared.items()}

@@ -48,7 +48,7 @@ def test_status_strings(lib):
 
 def _desc(**kw):
     base = dict(abi_version=_lib.MOE_ABI_VERSION, hidden=256, n_experts=8, top_k=2, n_shared=1, inter=128,
-                path=0, device=0, w_router=0x10000, router_bias=None, gate_codes=0x20000, gate_scales=0x30000,
+                path=0, device=0, block=32, flags=0, routed_scale=1.0, reserved=0, w_router=0x10000, router_bias=None, gate_codes=0x20000, gate_scales=0x30000,
                 up_codes=0x40000, up_scales=0x50000, down_codes=0x60000, down_scales=0x70000)
     base.update(kw)
     return _lib.LayerDesc(**base)
@@ -68,6 +68,21 @@ def _desc(**kw):
     (dict(gate_codes=None), _lib.MOE_ERR_INVALID),
     (dict(down_codes=0x60004), _lib.MOE_ERR_INVALID),
     (dict(abi_version=99), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(abi_version=1), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(block=16), _lib.MOE_ERR_INVALID),
+    (dict(reserved=1), _lib.MOE_ERR_INVALID),
+    (dict(routed_scale=0.0), _lib.MOE_ERR_INVALID),
+    (dict(routed_scale=float("nan")), _lib.MOE_ERR_INVALID),
+    (dict(routed_scale=float("inf")), _lib.MOE_ERR_INVALID),
+    (dict(flags=2), _lib.MOE_ERR_INVALID),
+    (dict(flags=1), _lib.MOE_ERR_INVALID),                               # FP8 pointers missing
+    (dict(flags=1, n_shared=0, shared_gate_fp8=0x80000, shared_gate_fp8_scales=0x90000, shared_up_fp8=0xa0000,
+          shared_up_fp8_scales=0xb0000, shared_down_fp8=0xc0000, shared_down_fp8_scales=0xd0000),
+     _lib.MOE_ERR_INVALID),                                              # FP8 shared with S = 0
+    (dict(flags=1, inter=96, shared_gate_fp8=0x80000, shared_gate_fp8_scales=0x90000, shared_up_fp8=0xa0000,
+          shared_up_fp8_scales=0xb0000, shared_down_fp8=0xc0000, shared_down_fp8_scales=0xd0000),
+     _lib.MOE_ERR_INVALID),                                              # I not a multiple of 128
+    (dict(shared_up_fp8=0xa0000), _lib.MOE_ERR_INVALID),                 # FP8 pointer without the flag
 ])
 def test_create_rejects_bad_descriptors(lib, bad, status):
     out = ctypes.c_void_p(1234)

@@ -65,3 +65,32 @@ def test_bf16_rounding_is_nearest_even():
     bits = synth.f32_to_bf16_bits(f)
     # 1+2^-8 is a tie -> even (1.0); 1+3*2^-8 is a tie -> even (1+2^-6); 1+2^-7+2^-9 rounds to 1+2^-7
     assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F80, 0xC020, 0x3F81]
+
+
+def test_fp8_shared_expert_draws():
+    wl = synth.custom_workload("fp8_small", 256, 4, 2, 1, 384, 4, shared_fp8=True)
+    assert wl.fp4_groups == 4 and wl.groups == 5
+    w = synth.shared_fp8_weights(wl, 0)
+    for mat, (n, k) in (("gate", (384, 256)), ("up", (384, 256)), ("down", (256, 384))):
+        c, s = w[mat]
+        assert c.shape == (n, k) and c.dtype == torch.uint8
+        assert s.shape == (n // 128, k // 128) and s.dtype == torch.float32
+        assert not ((c & 0x7F) == 0x7F).any()                   # no NaN pattern is drawn
+        assert len(torch.unique(c)) == 254                       # every finite code occurs
+        assert (s >= 2.0 ** -8).all() and (s < 1.5 * 2.0 ** -7).all()
+        c2, s2 = synth.shared_fp8_matrix(wl, 0, mat)
+        assert torch.equal(c, c2) and torch.equal(s, s2)         # deterministic
+    # FP4 arrays hold the routed experts only, with the same bytes a per-group draw gives
+    fp4 = synth.layer_weights(wl, 0)
+    assert fp4["gate"][0].shape[0] == 4
+    c, sc = synth.expert_matrix(wl, 0, "down", 3)
+    assert torch.equal(fp4["down"][0][3], c) and torch.equal(fp4["down"][1][3], sc)
+    g = synth.LazyExperts(wl, 0)[4]
+    assert g["up"][0] == "fp8" and np.array_equal(g["up"][1], w["up"][0].numpy())
+
+
+def test_fp8_flag_leaves_other_workload_ids_alone():
+    a = synth.custom_workload("w", 256, 4, 2, 1, 128, 4)
+    b = synth.custom_workload("w", 256, 4, 2, 1, 128, 4, shared_fp8=True)
+    assert synth._wl_id(a) != synth._wl_id(b)
+    assert synth.WORKLOADS["decode_t8"].fp4_groups == 257
