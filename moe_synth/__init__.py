@@ -9,6 +9,9 @@ What is drawn, and from which workload description:
 
 * Token activations ``x``: N(0, 1) in float32, rounded to bfloat16 with
   round-to-nearest-even and handed over as the raw 16-bit patterns.
+* Chained decode (workloads with ``chained``): the residual-stream input
+  ``h_0`` is N(0, 1) in float32 [T][H]; each layer's RMSNorm weight is
+  1 + 0.1 * N(0, 1) in float32 [H].
 * Router weights ``W_r``: N(0, 0.02^2) in float32, shape [E][H].
 * Router bias: only for the skewed long-prefill workload, a Zipf(1.1)
   popularity prior ``b_e = -1.1 * ln(e + 1)`` (expert 0 most popular).
@@ -62,6 +65,7 @@ class Workload:
     scale_lo: int = 123  # e8m0 scale byte range (2^-4 .. 2^0)
     scale_hi: int = 127
     shared_fp8: bool = False  # shared expert in FP8 E4M3 with 128 x 128 block scales
+    chained: bool = False     # layers joined by the residual stream (RMSNorm between them)
 
     @property
     def groups(self) -> int:
@@ -84,6 +88,9 @@ WORKLOADS = {
     "decode_pro_t8": Workload("decode_pro_t8", 7168, 384, 6, 1, 2048, 8),
     # the V4 Flash decode shape with the shared expert kept in the checkpoint's FP8 E4M3 format
     "decode_t8_fp8shared": Workload("decode_t8_fp8shared", 4096, 256, 6, 1, 2048, 8, shared_fp8=True),
+    # one token through 16 V4 Flash MoE layers, each layer's input the RMSNorm of the residual stream
+    "chained_decode_16l": Workload("chained_decode_16l", 4096, 256, 6, 1, 2048, 1, layers=16, steps=256,
+                                   chained=True),
 }
 _WORKLOAD_IDS = {n: i + 1 for i, n in enumerate(WORKLOADS)}
 
@@ -95,6 +102,7 @@ TENSOR_IDS = {
     "gate_fp8_codes": 9, "gate_fp8_scales": 10,
     "up_fp8_codes": 11, "up_fp8_scales": 12,
     "down_fp8_codes": 13, "down_fp8_scales": 14,
+    "h_in": 15, "norm_weight": 16,
 }
 MATRICES = ("gate", "up", "down")
 
@@ -113,9 +121,10 @@ def _wl_id(wl: Workload) -> int:
         return _WORKLOAD_IDS[wl.name]
     # custom workloads: fold the name and every field into an id
     h = 0
-    fields = dataclasses.astuple(wl)
-    if not wl.shared_fp8:
-        fields = fields[:-1]    # ids of workloads from before the FP8 field stay as they were
+    # fields added later fold in only when set, so earlier workloads keep their ids
+    later = {"shared_fp8", "chained"}
+    fields = tuple(getattr(wl, f.name) for f in dataclasses.fields(wl)
+                   if f.name not in later or getattr(wl, f.name) != f.default)
     for ch in repr(fields).encode():
         h = (h * 1099511628211 + ch) & _MASK64
     return h | (1 << 40)
@@ -348,3 +357,18 @@ def router_bias(wl) -> Optional[np.ndarray]:
     if wl.zipf is None:
         return None
     return (-wl.zipf * np.log(np.arange(1, wl.experts + 1, dtype=np.float64))).astype(np.float32)
+
+
+def residual_input(wl, step: int = 0, count: Optional[int] = None) -> np.ndarray:
+    """Residual-stream input h_0 of a chained workload: ``count`` (default T) rows of N(0, 1), float32 [count][H]."""
+    wl = workload(wl)
+    n = wl.tokens if count is None else count
+    g = _rng(_wl_id(wl), 0, TENSOR_IDS["h_in"], step)
+    return g.standard_normal((n, wl.hidden), dtype=np.float32)
+
+
+def norm_weight(wl, layer: int) -> np.ndarray:
+    """RMSNorm weight of one layer's input: 1 + 0.1 * N(0, 1), float32 [H]."""
+    wl = workload(wl)
+    g = _rng(_wl_id(wl), layer, TENSOR_IDS["norm_weight"])
+    return (1.0 + 0.1 * g.standard_normal(wl.hidden, dtype=np.float64)).astype(np.float32)

@@ -21,7 +21,8 @@ Each function cites the page passage it follows.  Pages, by title:
   table is 64 bytes; doubled E2M1 values are integers; six experts per token;
   expert shapes 2048x4096 (gate/up) and 4096x2048 (down); fp64-oracle error
   bounds as the test style; dense tensors are FP8 E4M3 with 128x128 block
-  scales (the shared-expert variant, oracle/fp8.py).
+  scales (the shared-expert variant, oracle/fp8.py); 43 layers for V4 Flash, run one
+  after another in decode (the chained reading of oracle/chain.py).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force and the printed facts above; none is "parity unpinned".
@@ -30,7 +31,9 @@ from .fp4 import E2M1_VALUES, e2m1_value, e8m0_value, dequant
 from .fp8 import E4M3_VALUES, Fp8Matrix, e4m3_value, dequant_fp8_block
 from .moe import (router_logits, select_experts, group_rows, silu, expert_ffn, dequant_matrix,
                   moe_forward, screen_near_ties)
+from .chain import RMS_EPS, rms_norm, f64_to_bf16_bits, norm_input, chain_forward
 
 __all__ = ["E2M1_VALUES", "e2m1_value", "e8m0_value", "dequant", "E4M3_VALUES", "Fp8Matrix",
            "e4m3_value", "dequant_fp8_block", "router_logits", "select_experts", "group_rows", "silu",
-           "expert_ffn", "dequant_matrix", "moe_forward", "screen_near_ties"]
+           "expert_ffn", "dequant_matrix", "moe_forward", "screen_near_ties", "RMS_EPS", "rms_norm",
+           "f64_to_bf16_bits", "norm_input", "chain_forward"]

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import oracle.fp4 as ofp4
+import oracle.chain as ochain
 import oracle.fp8 as ofp8
 import oracle.moe as omoe
 import test_oracle_pins as pins
@@ -29,11 +30,14 @@ ORIG = {
     "silu": omoe.silu,
     "bf16_bits_to_f64": omoe.bf16_bits_to_f64,
     "dequant_fp8_block": ofp8.dequant_fp8_block,
+    "rms_norm": ochain.rms_norm,
+    "f64_to_bf16_bits": ochain.f64_to_bf16_bits,
+    "chain_forward": ochain.chain_forward,
 }
 
 
 @contextlib.contextmanager
-def patched(name, value, modules=(ofp4, ofp8, omoe, oracle)):
+def patched(name, value, modules=(ofp4, ofp8, omoe, ochain, oracle)):
     """Replace `name` in every oracle namespace that holds it (package re-exports included)."""
     saved = [(m, getattr(m, name)) for m in modules if hasattr(m, name)]
     try:
@@ -132,6 +136,46 @@ def _fp8_scales_transposed(codes, scales):
     return ORIG["dequant_fp8_block"](codes, s.T if s.shape[0] == s.shape[1] else s[::-1, ::-1])
 
 
+def _rms_sum_not_mean(h, gamma, eps=1e-6):
+    h = np.asarray(h, np.float64)
+    return h / np.sqrt(np.sum(h * h, axis=-1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+def _rms_eps_outside(h, gamma, eps=1e-6):
+    h = np.asarray(h, np.float64)
+    return h / (np.sqrt(np.mean(h * h, axis=-1, keepdims=True)) + eps) * np.asarray(gamma, np.float64)
+
+
+def _rms_no_gamma(h, gamma, eps=1e-6):
+    return ORIG["rms_norm"](h, np.ones(np.asarray(h).shape[-1]), eps)
+
+
+def _bf16_truncate(v):
+    b = np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)
+    return b.astype(np.uint16)
+
+
+def _chain_no_residual(h_in, gammas, routers, biases, experts, top_k, n_shared, eps=1e-6, routed_scale=1.0):
+    h = np.asarray(h_in, np.float64)
+    xs, ys, routes = [], [], []
+    for l in range(len(routers)):
+        x = ochain.norm_input(h, gammas[l], eps)
+        out = omoe.moe_forward(x, routers[l], biases[l], experts[l], top_k, n_shared, routed_scale)
+        h = out["y"]                                   # the residual dropped
+        xs.append(x), ys.append(out["y"]), routes.append(out)
+    return dict(x=xs, y=ys, route=routes, h=h)
+
+
+def _chain_gamma_shifted(h_in, gammas, routers, biases, experts, top_k, n_shared, eps=1e-6, routed_scale=1.0):
+    shifted = list(gammas[1:]) + list(gammas[:1])
+    return ORIG["chain_forward"](h_in, shifted, routers, biases, experts, top_k, n_shared, eps, routed_scale)
+
+
+def _chain_norm_skipped(h_in, gammas, routers, biases, experts, top_k, n_shared, eps=1e-6, routed_scale=1.0):
+    with patched("norm_input", lambda h, g, e=1e-6: ochain.f64_to_bf16_bits(np.asarray(h) * np.asarray(g))):
+        return ORIG["chain_forward"](h_in, gammas, routers, biases, experts, top_k, n_shared, eps, routed_scale)
+
+
 MUTANTS = {
     "nibble order swapped": [("dequant", _dequant_nibbles_swapped)],
     "scale blocks of 16": [("dequant", _dequant_scale_block_16)],
@@ -154,6 +198,13 @@ MUTANTS = {
     "e4m3 subnormals flushed": [("E4M3_VALUES", np.where((np.arange(256) & 0x78) == 0, 0.0, ofp8.E4M3_VALUES))],
     "fp8 scale blocks of 64": [("dequant_fp8_block", _fp8_blocks_of_64)],
     "fp8 scale grid transposed": [("dequant_fp8_block", _fp8_scales_transposed)],
+    "rms norm over the sum, not the mean": [("rms_norm", _rms_sum_not_mean)],
+    "rms norm eps outside the root": [("rms_norm", _rms_eps_outside)],
+    "rms norm gamma dropped": [("rms_norm", _rms_no_gamma)],
+    "bf16 rounding truncates": [("f64_to_bf16_bits", _bf16_truncate)],
+    "chain residual dropped": [("chain_forward", _chain_no_residual)],
+    "chain gamma of the next layer": [("chain_forward", _chain_gamma_shifted)],
+    "chain norm skipped": [("chain_forward", _chain_norm_skipped)],
 }
 
 

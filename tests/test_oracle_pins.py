@@ -4,6 +4,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import moe_synth as synth
 import oracle
@@ -397,3 +398,98 @@ def test_fp8_shared_identity_expert_closed_form():
             v = xf[t, h]
             want = coef * (v / (1 + math.exp(-v))) * 2 * v if h < inter else 0.0
             assert abs(out["y"][t, h] - want) <= 1e-13 * (1 + abs(want)), (t, h)
+
+
+# ---------------------------------------------------------------- chained decode (oracle/chain.py)
+# The inter-layer step is a reading (pre-norm residual with RMSNorm, eps 1e-6): the pages run the
+# MoE stage per layer ("feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine", PR #1055,
+# "What it is") without defining the join.  Pins: torch's own conversions and rms_norm, hand-worked
+# values, and closed forms of whole chains.
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(50000) * 3, rng.standard_normal(2000) * 1e-38,
+                        rng.standard_normal(2000) * 1e38]).astype(np.float32)
+    x = np.concatenate([x, np.float32([0.0, -0.0, np.inf, -np.inf, 3.3e38, -3.39e38])])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(x.astype(np.float64)), want)
+
+
+def test_bf16_rounding_hand_cases():
+    cases = [(1.0, 0x3F80), (1 + 2.0 ** -8, 0x3F80),        # tie -> even (down)
+             (1 + 3 * 2.0 ** -8, 0x3F82),                     # tie -> even (up)
+             (1 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),            # just past the tie: float64 decides
+             (255.5, 0x4380),                                 # tie rounds up into the next binade (256)
+             (-2.5, 0xC020), (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002),
+             (float("nan"), 0x7FC0), (2.0 ** 128, 0x7F80)]
+    for v, bits in cases:
+        assert int(oracle.f64_to_bf16_bits(np.float64(v))) == bits, (v, hex(bits))
+
+
+def test_rms_norm_hand_worked():
+    # h = (3, 4): mean of squares 12.5; gamma = (2, 1/2)
+    got = oracle.rms_norm(np.array([[3.0, 4.0]]), np.array([2.0, 0.5]), eps=0.0)
+    np.testing.assert_allclose(got, [[6 / math.sqrt(12.5), 2 / math.sqrt(12.5)]], rtol=1e-15)
+    got = oracle.rms_norm(np.array([[3.0, 4.0]]), np.ones(2), eps=0.5)     # eps inside the root
+    np.testing.assert_allclose(got, [[3 / math.sqrt(13.0), 4 / math.sqrt(13.0)]], rtol=1e-15)
+    assert (oracle.rms_norm(np.zeros((1, 64)), np.ones(64)) == 0).all()     # eps keeps 0 finite
+    c = oracle.rms_norm(np.full((1, 32), -0.25), np.ones(32), eps=oracle.RMS_EPS)
+    np.testing.assert_allclose(c, -0.25 / math.sqrt(0.0625 + 1e-6), rtol=1e-15)
+    assert oracle.RMS_EPS == 1e-6
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((5, 96)) * 1e3
+    g = 1 + 0.1 * rng.standard_normal(96)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(h), (96,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(h, g), want, rtol=1e-14)
+
+
+def _zero_experts(hidden, inter, groups):
+    z = lambda n, k: (np.zeros((n, k // 2), np.uint8), np.full((n, k // 32), 127, np.uint8))
+    return [dict(gate=z(inter, hidden), up=z(inter, hidden), down=z(hidden, inter)) for _ in range(groups)]
+
+
+def test_chain_with_zero_experts_keeps_the_residual():
+    # every expert is zero, so each y_l = 0: h_L = h_0 and x_l = bf16(RMSNorm(h_0) * gamma_l), each
+    # layer with its own gamma
+    rng = np.random.default_rng(13)
+    hidden, inter, e, k, layers = 64, 32, 4, 2, 3
+    h0 = rng.standard_normal((3, hidden))
+    gammas = [1 + 0.1 * rng.standard_normal(hidden) for _ in range(layers)]
+    routers = [(0.1 * rng.standard_normal((e, hidden))).astype(np.float32) for _ in range(layers)]
+    out = oracle.chain_forward(h0, gammas, routers, [None] * layers, [_zero_experts(hidden, inter, e + 1)] * layers,
+                               k, 1)
+    np.testing.assert_array_equal(out["h"], h0)
+    for l in range(layers):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(h0), (hidden,), torch.from_numpy(gammas[l]),
+                                            eps=1e-6).numpy()
+        np.testing.assert_array_equal(out["x"][l], oracle.f64_to_bf16_bits(want))
+        assert (out["y"][l] == 0).all()
+
+
+def test_chain_identity_experts_closed_form():
+    # two layers of identity experts (closed form of each layer as in the single-layer pin): the
+    # residual after layer l is h_l + y_l with y_l[h] = c_l * silu(x_h) * 2 x_h for h < I, 0 above
+    hidden, inter, experts, k = 128, 64, 6, 2
+    groups, wr, _, sigma = _identity_setup(hidden, inter, experts, k)
+    rng = np.random.default_rng(14)
+    h0 = rng.standard_normal((4, hidden))
+    gammas = [np.ones(hidden), 1 + 0.1 * rng.standard_normal(hidden)]
+    out = oracle.chain_forward(h0, gammas, [wr, wr], [None, None], [groups, groups], k, 1)
+    h = h0.copy()
+    for l in range(2):
+        want_x = oracle.f64_to_bf16_bits(torch.nn.functional.rms_norm(
+            torch.from_numpy(h), (hidden,), torch.from_numpy(gammas[l]), eps=1e-6).numpy())
+        np.testing.assert_array_equal(out["x"][l], want_x)
+        xf = bf16_bits_to_f64(want_x)
+        r = out["route"][l]
+        coef = 2.0 ** -sigma[experts] + (r["w"] * 2.0 ** -np.array(sigma)[r["idx"]]).sum(axis=1)
+        y = np.zeros_like(h)
+        v = xf[:, :inter]
+        y[:, :inter] = coef[:, None] * (v / (1 + np.exp(-v))) * 2 * v
+        np.testing.assert_allclose(out["y"][l], y, rtol=1e-13, atol=1e-300)
+        h = h + y
+    np.testing.assert_allclose(out["h"], h, rtol=1e-13)

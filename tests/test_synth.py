@@ -94,3 +94,17 @@ def test_fp8_flag_leaves_other_workload_ids_alone():
     b = synth.custom_workload("w", 256, 4, 2, 1, 128, 4, shared_fp8=True)
     assert synth._wl_id(a) != synth._wl_id(b)
     assert synth.WORKLOADS["decode_t8"].fp4_groups == 257
+
+
+def test_chain_inputs_are_seeded_and_shaped():
+    wl = synth.WORKLOADS["chained_decode_16l"]
+    h = synth.residual_input(wl, step=3)
+    assert h.shape == (1, 4096) and h.dtype == np.float32
+    assert np.array_equal(h, synth.residual_input(wl, step=3))
+    assert not np.array_equal(h, synth.residual_input(wl, step=4))
+    g = synth.norm_weight(wl, 5)
+    assert g.shape == (4096,) and g.dtype == np.float32 and abs(g.mean() - 1) < 0.01 and 0.08 < g.std() < 0.12
+    assert not np.array_equal(g, synth.norm_weight(wl, 6))
+    # workloads without the later fields keep the ids they had before those fields existed
+    a = synth.custom_workload("w", 256, 4, 2, 1, 128, 4)
+    assert synth._wl_id(a) == synth._wl_id(synth.custom_workload("w", 256, 4, 2, 1, 128, 4, chained=False))
