@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_fp4.so")
 
 MOE_ABI_VERSION = 2
 MOE_SHARED_FP8 = 1
+MOE_CHAIN_RESIDUAL = 1
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALLOC = range(6)
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GEMM = range(3)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -20,7 +21,8 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_abi_version", "moe_device_supported", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_noalloc", "moe_pack_fp4",
-           "moe_pack_fp8", "moe_status_string",
+           "moe_pack_fp8", "moe_residual_rmsnorm", "moe_chain_create", "moe_chain_run", "moe_chain_destroy",
+           "moe_status_string",
            "moe_last_error",
            "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
 
@@ -66,6 +68,26 @@ class RouteOut(ctypes.Structure):
     ]
 
 
+class ChainDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("tokens", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("layers", ctypes.POINTER(ctypes.c_void_p)),
+        ("norm_weight", ctypes.POINTER(ctypes.c_void_p)),
+        ("h_in", ctypes.c_void_p),
+        ("h_out", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("routes", ctypes.POINTER(RouteOut)),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
 _lib = None
 
 
@@ -93,6 +115,10 @@ def load(path: str = None) -> ctypes.CDLL:
         "moe_forward_noalloc": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P]),
         "moe_pack_fp4": (I32, [P, P, P, P, I32, I32, I32, P]),
         "moe_pack_fp8": (I32, [P, P, I32, I32, I32, P]),
+        "moe_residual_rmsnorm": (I32, [P, P, P, P, ctypes.c_float, P, I32, I32, P]),
+        "moe_chain_create": (I32, [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]),
+        "moe_chain_run": (I32, [P, P]),
+        "moe_chain_destroy": (None, [P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (I32, [I32]),

@@ -482,6 +482,177 @@ int32_t moe_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int32_t groups
   return MOE_OK;
 }
 
+int32_t moe_residual_rmsnorm(const float* h_src, const float* y, float* h_dst, const float* norm_weight, float eps,
+                             uint16_t* x, int32_t T, int32_t H, void* stream) {
+  if (T < 0 || T > kMaxTokens || H < 4 || H > (1 << 20) || H % 4)
+    return fail(MOE_ERR_INVALID, "moe_residual_rmsnorm: tokens=%d hidden=%d (hidden a multiple of 4)", T, H);
+  if (T == 0) return MOE_OK;
+  if (!h_src) return fail(MOE_ERR_INVALID, "moe_residual_rmsnorm: NULL h_src");
+  if (!y && !x) return fail(MOE_ERR_INVALID, "moe_residual_rmsnorm: neither y nor x given: nothing to do");
+  if (!(eps > 0.f) || !(eps <= 3.402823466e38f))
+    return fail(MOE_ERR_INVALID, "moe_residual_rmsnorm: eps=%g must be finite and > 0", (double)eps);
+  if (!aligned16(h_src) || !aligned16(y) || !aligned16(h_dst) || !aligned16(norm_weight) ||
+      (reinterpret_cast<uintptr_t>(x) & 7u))
+    return fail(MOE_ERR_INVALID, "moe_residual_rmsnorm: float arrays must be 16-byte and x 8-byte aligned");
+  const hipError_t e = moe::launch_residual_rmsnorm(h_src, y, y ? h_dst : nullptr, norm_weight, eps, x, T, H,
+                                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_residual_rmsnorm: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+struct moe_chain {
+  int device = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+// Enqueue the chain's work on s (being captured): for each layer the join step and the layer,
+// then the final residual add.
+int32_t enqueue_chain(const moe_chain_desc* d, const std::vector<moe_route_out>& routes, hipStream_t s) {
+  const moe::Dims& dm = d->layers[0]->dims;
+  const int T = d->tokens, H = dm.H;
+  const size_t plane = (size_t)T * H;
+  const bool residual = d->flags & MOE_CHAIN_RESIDUAL;
+  for (int l = 0; l < d->n_layers; ++l) {
+    uint16_t* x = d->x + l * plane;
+    if (residual) {
+      const float* g = d->norm_weight ? d->norm_weight[l] : nullptr;
+      // layer 0 normalises h_in; layer l > 0 first adds y_{l-1} into the running residual
+      const float* src = l <= 1 ? d->h_in : d->h_out;
+      const float* yp = l == 0 ? nullptr : d->y + (l - 1) * plane;
+      const hipError_t e = moe::launch_residual_rmsnorm(src, yp, l == 0 ? nullptr : d->h_out, g, d->eps, x, T, H, s);
+      if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_chain_create: join launch failed: %s", hipGetErrorString(e));
+    }
+    const int32_t st = moe_forward(d->layers[l], x, T, d->y + l * plane, routes.empty() ? nullptr : &routes[l],
+                                   d->workspace, d->workspace_bytes, s);
+    if (st != MOE_OK) return st;
+  }
+  if (residual) {
+    const int L = d->n_layers;
+    const hipError_t e = moe::launch_residual_rmsnorm(L == 1 ? d->h_in : d->h_out, d->y + (L - 1) * plane,
+                                                      d->h_out, nullptr, d->eps, nullptr, T, H, s);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_chain_create: residual launch failed: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_chain_create(const moe_chain_desc* d, moe_chain** out) {
+  if (!out) return fail(MOE_ERR_INVALID, "moe_chain_create: NULL out");
+  *out = nullptr;
+  if (!d) return fail(MOE_ERR_INVALID, "moe_chain_create: NULL descriptor");
+  if (d->abi_version != MOE_ABI_VERSION)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_chain_create: abi_version %d, library %d", d->abi_version, MOE_ABI_VERSION);
+  if (d->n_layers < 1 || d->n_layers > 1024 || !d->layers)
+    return fail(MOE_ERR_INVALID, "moe_chain_create: n_layers=%d (1..1024) and a layer array are required", d->n_layers);
+  if (d->tokens < 1 || d->tokens > kMaxTokens)
+    return fail(MOE_ERR_INVALID, "moe_chain_create: tokens=%d out of [1, %d]", d->tokens, kMaxTokens);
+  if (d->flags & ~MOE_CHAIN_RESIDUAL) return fail(MOE_ERR_INVALID, "moe_chain_create: unknown flags 0x%x", d->flags);
+  if (d->reserved != 0) return fail(MOE_ERR_INVALID, "moe_chain_create: reserved must be 0");
+  const bool residual = d->flags & MOE_CHAIN_RESIDUAL;
+  for (int l = 0; l < d->n_layers; ++l) {
+    const moe_layer* L = d->layers[l];
+    if (!L) return fail(MOE_ERR_INVALID, "moe_chain_create: layer %d is NULL", l);
+    if (L->dims.H != d->layers[0]->dims.H || L->desc.device != d->layers[0]->desc.device)
+      return fail(MOE_ERR_INVALID, "moe_chain_create: layer %d differs from layer 0 in hidden size or device", l);
+    const uint64_t need = carve(L->dims, d->tokens, nullptr, nullptr);
+    if (!d->workspace || (reinterpret_cast<uintptr_t>(d->workspace) & 255u) || d->workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "moe_chain_create: layer %d needs %llu workspace bytes aligned to 256", l,
+                  (unsigned long long)need);
+    if (residual && d->norm_weight && !aligned16(d->norm_weight[l]))
+      return fail(MOE_ERR_INVALID, "moe_chain_create: norm_weight[%d] must be 16-byte aligned", l);
+    if (d->routes && !route_ok(&d->routes[l]))
+      return fail(MOE_ERR_INVALID, "moe_chain_create: routes[%d] has a NULL buffer", l);
+  }
+  const int H = d->layers[0]->dims.H;
+  const size_t plane = (size_t)d->tokens * H;
+  if (!d->x || !d->y || !aligned16(d->x) || !aligned16(d->y))
+    return fail(MOE_ERR_INVALID, "moe_chain_create: x and y are required and 16-byte aligned");
+  if (overlaps(d->x, plane * 2 * d->n_layers, d->y, plane * 4 * d->n_layers))
+    return fail(MOE_ERR_INVALID, "moe_chain_create: x and y overlap");
+  if (residual) {
+    if (!(d->eps > 0.f) || !(d->eps <= 3.402823466e38f))
+      return fail(MOE_ERR_INVALID, "moe_chain_create: eps=%g must be finite and > 0", (double)d->eps);
+    if (!d->h_in || !d->h_out || !aligned16(d->h_in) || !aligned16(d->h_out))
+      return fail(MOE_ERR_INVALID, "moe_chain_create: h_in and h_out are required and 16-byte aligned");
+    if (overlaps(d->h_in, plane * 4, d->h_out, plane * 4))
+      return fail(MOE_ERR_INVALID, "moe_chain_create: h_in and h_out overlap");
+  } else if (d->h_in || d->h_out || d->norm_weight) {
+    return fail(MOE_ERR_INVALID, "moe_chain_create: h_in, h_out and norm_weight belong to MOE_CHAIN_RESIDUAL");
+  }
+  std::vector<moe_route_out> routes;
+  if (d->routes) routes.assign(d->routes, d->routes + d->n_layers);
+
+  const int dev = d->layers[0]->desc.device;
+  DeviceGuard dg(dev);
+  if (!dg.ok) return fail(MOE_ERR_HIP, "moe_chain_create: hipSetDevice(%d) failed", dev);
+  moe_chain* c = new (std::nothrow) moe_chain;
+  if (!c) return fail(MOE_ERR_ALLOC, "moe_chain_create: out of host memory");
+  c->device = dev;
+  hipStream_t s = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(MOE_ERR_HIP, "moe_chain_create: hipStreamCreate failed: %s", hipGetErrorString(e));
+  }
+  int32_t st = MOE_OK;
+  e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    st = fail(MOE_ERR_HIP, "moe_chain_create: hipStreamBeginCapture failed: %s", hipGetErrorString(e));
+  } else {
+    const bool no_timing = g_no_timing;
+    g_no_timing = true;  // no timing events inside the graph
+    st = enqueue_chain(d, routes, s);
+    g_no_timing = no_timing;
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);  // always ends the capture, also after a failed enqueue
+    c->graph = g;
+    if (st == MOE_OK && e != hipSuccess)
+      st = fail(MOE_ERR_HIP, "moe_chain_create: hipStreamEndCapture failed: %s", hipGetErrorString(e));
+    if (st == MOE_OK) {
+      e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
+      if (e != hipSuccess) st = fail(MOE_ERR_HIP, "moe_chain_create: hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    }
+  }
+  (void)hipStreamDestroy(s);
+  if (st != MOE_OK) {
+    moe_chain_destroy(c);
+    return st;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+int32_t moe_chain_run(const moe_chain* c, void* stream) {
+  if (!c || !c->exec) return fail(MOE_ERR_INVALID, "moe_chain_run: NULL chain");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(MOE_ERR_HIP, "moe_chain_run: hipSetDevice(%d) failed", c->device);
+  const hipError_t e = hipGraphLaunch(c->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_chain_run: hipGraphLaunch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+void moe_chain_destroy(moe_chain* c) {
+  if (!c) return;
+  DeviceGuard dg(c->device);
+  if (c->exec) (void)hipGraphExecDestroy(c->exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  delete c;
+}
+
 int32_t moe_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_tenabled = on != 0;

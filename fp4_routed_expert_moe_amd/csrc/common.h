@@ -259,6 +259,9 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
                             hipStream_t s);
 hipError_t launch_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int groups, int N, int K, hipStream_t s);
+// h_dst = h_src + y (y, h_dst may be NULL), x = bf16(RMSNorm(h) * gamma) (x may be NULL)
+hipError_t launch_residual_rmsnorm(const float* h_src, const float* y, float* h_dst, const float* gamma, float eps,
+                                   uint16_t* x, int T, int H, hipStream_t s);
 hipError_t launch_pack(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out, uint8_t* scales_out,
                        int groups, int N, int K, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const CallBufs& b, float* y, int T, hipStream_t s);

@@ -202,6 +202,99 @@ class MoeLayer:
     __call__ = forward
 
 
+# ---- chained decode ----------------------------------------------------------------------
+
+def _f32_cuda(t, shape, what):
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be a contiguous float32 CUDA tensor of shape {tuple(shape)}")
+
+
+def residual_rmsnorm(h_src: torch.Tensor, y: Optional[torch.Tensor] = None, h_dst: Optional[torch.Tensor] = None,
+                     norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6, x: Optional[torch.Tensor] = None,
+                     stream=None):
+    """The join between two layers (one library call): h_dst = h_src + y when y is given, and
+    x = bf16(RMSNorm(h) * norm_weight) when x is given; returns x."""
+    lib = _lib.load()
+    t, h = h_src.shape
+    _f32_cuda(h_src, (t, h), "h_src")
+    for name, a in (("y", y), ("h_dst", h_dst)):
+        if a is not None:
+            _f32_cuda(a, (t, h), name)
+    if norm_weight is not None:
+        _f32_cuda(norm_weight, (h,), "norm_weight")
+    if x is not None and (x.element_size() != 2 or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != (t, h)):
+        raise ValueError(f"x must be a contiguous [{t}][{h}] 16-bit CUDA tensor")
+    _lib.check(lib.moe_residual_rmsnorm(_ptr(h_src), _ptr(y), _ptr(h_dst), _ptr(norm_weight), eps, _ptr(x), t, h,
+                                        _stream_handle(stream)), lib)
+    return x
+
+
+class MoeChain:
+    """Layers recorded into one HIP graph by the library and replayed by ``run``.
+
+    ``residual=True``: the chained decode -- layer l's input x[l] = bf16(RMSNorm(h_l) * norm_weight[l]),
+    y[l] = layer l (x[l]), h_{l+1} = h_l + y[l], from ``h_in`` to ``h_out``.  ``residual=False``: the
+    layers one after another on the inputs the caller writes into ``x`` (independent calls).  The
+    buffers are allocated here (x [L][T][H] int16 bf16 bits, y [L][T][H] float32, h_in/h_out
+    [T][H] float32) and are the graph's: write inputs into ``h_in`` (or ``x``) in place."""
+
+    def __init__(self, layers, tokens: int, residual: bool = True, norm_weight=None, eps: float = 1e-6,
+                 routes: bool = False):
+        self.lib = _lib.load()
+        if not layers:
+            raise ValueError("a chain needs at least one layer")
+        self.layers = list(layers)
+        h, dev = self.layers[0].hidden, self.layers[0].device
+        n, t = len(self.layers), tokens
+        self.hidden, self.tokens, self.device, self.residual = h, t, dev, residual
+        self.x = torch.zeros((n, t, h), dtype=torch.int16, device=dev)
+        self.y = torch.zeros((n, t, h), dtype=torch.float32, device=dev)
+        self.h_in = torch.zeros((t, h), dtype=torch.float32, device=dev) if residual else None
+        self.h_out = torch.zeros((t, h), dtype=torch.float32, device=dev) if residual else None
+        self.routes = [l.route_buffers(t) for l in self.layers] if routes else None
+        self.workspace = torch.zeros(max(l.workspace_bytes(t) for l in self.layers), dtype=torch.uint8, device=dev)
+        self.norm_weight = list(norm_weight) if norm_weight is not None else None
+        if self.norm_weight is not None:
+            if len(self.norm_weight) != n:
+                raise ValueError("one norm weight per layer")
+            for g in self.norm_weight:
+                if g is not None:
+                    _f32_cuda(g, (h,), "norm weight")
+        lp = (ctypes.c_void_p * n)(*[l._h for l in self.layers])
+        gp = None
+        if self.norm_weight is not None:
+            gp = (ctypes.c_void_p * n)(*[_ptr(g) for g in self.norm_weight])
+        rp = None
+        if self.routes is not None:
+            rp = (_lib.RouteOut * n)(*[MoeLayer._route_struct(r) for r in self.routes])
+        self._arrays = (lp, gp, rp)
+        desc = _lib.ChainDesc(abi_version=_lib.MOE_ABI_VERSION, n_layers=n, tokens=t,
+                              flags=_lib.MOE_CHAIN_RESIDUAL if residual else 0, eps=eps, reserved=0,
+                              layers=ctypes.cast(lp, ctypes.POINTER(ctypes.c_void_p)),
+                              norm_weight=ctypes.cast(gp, ctypes.POINTER(ctypes.c_void_p)) if gp is not None else None,
+                              h_in=_ptr(self.h_in), h_out=_ptr(self.h_out), x=_ptr(self.x), y=_ptr(self.y),
+                              routes=ctypes.cast(rp, ctypes.POINTER(_lib.RouteOut)) if rp is not None else None,
+                              workspace=_ptr(self.workspace), workspace_bytes=self.workspace.numel())
+        torch.cuda.synchronize(dev)        # the zeroed buffers exist before the graph names them
+        h_ = ctypes.c_void_p()
+        _lib.check(self.lib.moe_chain_create(ctypes.byref(desc), ctypes.byref(h_)), self.lib)
+        self._h = h_.value
+
+    def run(self, stream=None):
+        _lib.check(self.lib.moe_chain_run(self._h, _stream_handle(stream)), self.lib)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.moe_chain_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ---- kernel timing ---------------------------------------------------------------------
 
 def timing_enable(on: bool = True):

@@ -213,6 +213,68 @@ int32_t moe_pack_fp4(const uint8_t* codes_in, const uint8_t* scales_in, uint8_t*
 int32_t moe_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int32_t groups, int32_t rows, int32_t cols,
                      void* stream);
 
+/* ---- chained decode -----------------------------------------------------------------
+ * The pages run the MoE stage once per transformer layer in decode ("feat(v4/cuda): the CUDA
+ * tier wired into the DeepSeek V4 engine", PR #1055, "What it is"; V4 Flash has 43 layers,
+ * "Add DeepSeek V4 Flash CPU inference with NVMe expert streaming", PR #165) and leave the
+ * join between layers open.  The library takes the plain pre-norm residual reading, with
+ * attention and hyper-connection mixing left to the caller:
+ *   x_l = bf16(RMSNorm(h_l) * gamma_l),  y_l = MoE_l(x_l),  h_{l+1} = h_l + y_l,
+ *   RMSNorm(v) = v / sqrt(mean(v^2) + eps). */
+
+/* One join step on T rows of width H (device pointers, float4-aligned, H a multiple of 4):
+ *   if y is not NULL:  h_dst = h_src + y   (fp32, one rounding per add; h_dst may equal
+ *                                            h_src, NULL means h_dst is not written)
+ *   if x is not NULL:  x = bf16 round-to-nearest-even of (h * (1/sqrt(mean(h^2) + eps))) *
+ *                      norm_weight, h being h_src (+ y); norm_weight NULL means all ones.
+ * eps must be finite and > 0.  Asynchronous on `stream` of the current device. */
+int32_t moe_residual_rmsnorm(const float* h_src, const float* y, float* h_dst, const float* norm_weight,
+                             float eps, uint16_t* x, int32_t tokens, int32_t hidden, void* stream);
+
+enum moe_chain_flags {
+  /* layers joined by the residual stream and RMSNorm (above); without it the layers run
+   * one after another on inputs the caller wrote into x (a stack of independent calls) */
+  MOE_CHAIN_RESIDUAL = 1
+};
+
+typedef struct moe_chain_desc {
+  int32_t abi_version;              /* MOE_ABI_VERSION */
+  int32_t n_layers;                 /* 1 .. 1024 */
+  int32_t tokens;                   /* T per layer call, >= 1 */
+  int32_t flags;                    /* MOE_CHAIN_RESIDUAL or 0 */
+  float eps;                        /* RMSNorm epsilon (RESIDUAL; finite, > 0) */
+  int32_t reserved;                 /* 0 */
+  const moe_layer* const* layers;   /* host array [n_layers]: same hidden size and device */
+  const float* const* norm_weight;  /* host array [n_layers] of device float32 [H] (an entry may
+                                       be NULL: all ones), or NULL (all ones); RESIDUAL only */
+  const float* h_in;                /* device float32 [T][H]: residual input h_0 (RESIDUAL; read only) */
+  float* h_out;                     /* device float32 [T][H]: residual after the last layer, also
+                                       the running residual (RESIDUAL; must not overlap h_in) */
+  uint16_t* x;                      /* device bf16 [n_layers][T][H]: each layer's input (written
+                                       when RESIDUAL, else read) */
+  float* y;                         /* device float32 [n_layers][T][H]: each layer's output */
+  const moe_route_out* routes;      /* host array [n_layers] (copied at create) or NULL: each
+                                       layer's routing, as moe_forward's route argument */
+  void* workspace;                  /* one workspace for every layer (sequential on one stream) */
+  uint64_t workspace_bytes;         /* >= moe_workspace_bytes(layer, T) for every layer */
+} moe_chain_desc;
+
+typedef struct moe_chain moe_chain;
+
+/* Record the whole chain -- for each layer the join step and moe_forward, and the final
+ * residual add -- into a HIP graph, once, on a stream of the library's own (no work runs).
+ * Every pointer is borrowed and baked into the graph: buffers, weights and layers must stay
+ * alive and in place until moe_chain_destroy.  On failure *out is NULL and nothing leaks. */
+int32_t moe_chain_create(const moe_chain_desc* desc, moe_chain** out);
+
+/* Replay the recorded chain on `stream` (NULL = default stream): one graph launch.  With
+ * RESIDUAL, h_in is only read, so replays with the same h_in give the same results bit for
+ * bit.  Replays that overlap (other streams) race on the buffers and the workspace. */
+int32_t moe_chain_run(const moe_chain* chain, void* stream);
+
+/* Free the graph.  NULL is a no-op; the caller must have synchronised every replay. */
+void moe_chain_destroy(moe_chain* chain);
+
 /* Static text for a status code. */
 const char* moe_status_string(int32_t status);
 

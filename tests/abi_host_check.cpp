@@ -141,6 +141,76 @@ int main(void) {
   CHECK(moe_forward_noalloc(L, x, -3, y, NULL, NULL) == MOE_ERR_INVALID);
   CHECK(moe_forward_noalloc(L, x, 0, y, NULL, NULL) == MOE_OK);
   CHECK(moe_forward_noalloc(NULL, x, 8, y, NULL, NULL) == MOE_ERR_INVALID);
+
+  // the join step: rejected on the host
+  float* h = (float*)0x800000;
+  uint16_t* xo = (uint16_t*)0x900000;
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, 1e-6f, xo, 0, 256, NULL) == MOE_OK);  // T = 0: no-op
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, 1e-6f, xo, -1, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, 1e-6f, xo, 8, 254, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(NULL, y, h, NULL, 1e-6f, xo, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, NULL, h, NULL, 1e-6f, NULL, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, 0.f, xo, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, -1.f, xo, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h + 1, y, h, NULL, 1e-6f, xo, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, y, h, (const float*)0x800008, 1e-6f, xo, 8, 256, NULL) == MOE_ERR_INVALID);
+  CHECK(moe_residual_rmsnorm(h, y, h, NULL, 1e-6f, xo + 1, 8, 256, NULL) == MOE_ERR_INVALID);
+
+  // chain descriptors: every rejection leaves *out NULL and leaks nothing
+  {
+    const moe_layer* layers[2] = {L, L};
+    moe_chain_desc c;
+    memset(&c, 0, sizeof(c));
+    c.abi_version = MOE_ABI_VERSION;
+    c.n_layers = 2;
+    c.tokens = 8;
+    c.flags = MOE_CHAIN_RESIDUAL;
+    c.eps = 1e-6f;
+    c.layers = layers;
+    c.h_in = (const float*)0xa00000;
+    c.h_out = (float*)0xb00000;
+    c.x = (uint16_t*)0xc00000;
+    c.y = (float*)0xd00000;
+    c.workspace = ws;
+    c.workspace_bytes = w8;
+    moe_chain* ch = (moe_chain*)0x1;
+    CHECK(moe_chain_create(NULL, &ch) == MOE_ERR_INVALID && ch == NULL);
+    CHECK(moe_chain_create(&c, NULL) == MOE_ERR_INVALID);
+    struct {
+      void (*edit)(moe_chain_desc*);
+      int status;
+    } bad[] = {
+        {[](moe_chain_desc* b) { b->abi_version = 1; }, MOE_ERR_UNSUPPORTED},
+        {[](moe_chain_desc* b) { b->n_layers = 0; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->tokens = 0; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->flags = 2; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->reserved = 1; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->layers = NULL; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->workspace_bytes -= 1; }, MOE_ERR_WORKSPACE},
+        {[](moe_chain_desc* b) { b->workspace = (char*)b->workspace + 16; }, MOE_ERR_WORKSPACE},
+        {[](moe_chain_desc* b) { b->x = NULL; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->y = (float*)((char*)b->x + 64); }, MOE_ERR_INVALID},  // x, y overlap
+        {[](moe_chain_desc* b) { b->eps = 0.f; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->h_out = (float*)b->h_in + 16; }, MOE_ERR_INVALID},     // h overlap
+        {[](moe_chain_desc* b) { b->h_in = NULL; }, MOE_ERR_INVALID},
+        {[](moe_chain_desc* b) { b->flags = 0; }, MOE_ERR_INVALID},  // h_in given without RESIDUAL
+    };
+    for (size_t i = 0; i < sizeof(bad) / sizeof(bad[0]); ++i) {
+      moe_chain_desc b = c;
+      bad[i].edit(&b);
+      ch = (moe_chain*)0x1;
+      CHECK(moe_chain_create(&b, &ch) == bad[i].status && ch == NULL);
+    }
+    const moe_layer* with_null[2] = {L, NULL};
+    moe_chain_desc b = c;
+    b.layers = with_null;
+    CHECK(moe_chain_create(&b, &ch) == MOE_ERR_INVALID && ch == NULL);
+    // a descriptor that passes every host check reaches the device, which this host lacks
+    ch = (moe_chain*)0x1;
+    CHECK(moe_chain_create(&c, &ch) == MOE_ERR_HIP && ch == NULL);
+    CHECK(moe_chain_run(NULL, NULL) == MOE_ERR_INVALID);
+    moe_chain_destroy(NULL);
+  }
   moe_layer_destroy(L);
   moe_layer_destroy(NULL);
 

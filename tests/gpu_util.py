@@ -298,3 +298,62 @@ def sample_tokens(got, top_k, spread=48, hot=3, per_hot=8):
         at = {0, min(63, n - 1), last_tile, n - 1} | set(np.linspace(0, n - 1, per_hot).astype(int).tolist())
         picks |= {int(rows[i]) for i in at}
     return np.array(sorted(picks))
+
+
+# ---- chained decode -------------------------------------------------------------------------
+NORM_REL = 64 * U32   # relative bound of the join kernel's fp32 RMSNorm value before its bf16 rounding
+
+
+def check_bf16_near(got_bits, ref, rel=NORM_REL, what=""):
+    """Each bf16 pattern in ``got_bits`` must be the round-to-nearest-even of some value within
+    relative distance ``rel`` of the float64 ``ref``: the rounding of ``ref`` itself, or, when
+    ``ref`` lies that close to a rounding boundary, its neighbour across it."""
+    got = np.asarray(got_bits).view(np.uint16)
+    ref = np.asarray(ref, dtype=np.float64)
+    ok = ((got == oracle.f64_to_bf16_bits(ref)) | (got == oracle.f64_to_bf16_bits(ref * (1 - rel)))
+          | (got == oracle.f64_to_bf16_bits(ref * (1 + rel))))
+    bad = np.argwhere(~ok)
+    assert bad.size == 0, (f"{what}: {len(bad)} bf16 values off, first at {bad[:4].tolist()}: "
+                           f"got {got[tuple(bad[:4].T)]}, ref {ref[tuple(bad[:4].T)]}")
+    return int((got != oracle.f64_to_bf16_bits(ref)).sum())   # values on the far side of a boundary
+
+
+def check_routing_screened(got, ref, x_bits, w_router, bias, top_k):
+    """Routing of a computed (not screened) input: tokens whose top-(k+1) float64 scores hold a gap
+    under 1e-4 may order differently at any precision, so only the other tokens' experts and
+    weights are compared; with no such token the whole grouping must match too.  Returns the
+    mask of compared tokens."""
+    near = oracle.screen_near_ties(x_bits, w_router, bias, top_k)
+    keep = ~near
+    if not near.any():
+        check_routing(got, ref, x_bits, w_router, bias)
+        return keep
+    np.testing.assert_array_equal(got["idx"][keep], ref["idx"][keep])
+    tol = weight_tolerance(x_bits, w_router, bias, ref["idx"], ref["w"])
+    assert (np.abs(got["weight"][keep] - ref["w"][keep]) <= tol[keep]).all()
+    assert int(got["counts"].sum()) == got["idx"].size
+    return keep
+
+
+def check_chain_teacher_forced(x_gpu, y_gpu, h_out, routes, h_in, gammas, routers, biases, y_refs, top_k,
+                               eps=1e-6, what="chain"):
+    """Every step of a GPU chain checked on the GPU's own inputs to that step:
+    the residual h_{l+1} = fl32(h_l + y_l) bit for bit (h_L against h_out), each layer input x_l
+    against the float64 RMSNorm of the GPU's h_l (check_bf16_near), each layer's routing of x_l
+    against the oracle's (check_routing_screened), and y_l against ``y_refs[l]``, the oracle layer
+    on the GPU's x_l.  Returns (compared tokens, bf16 values across a boundary)."""
+    h = np.asarray(h_in, dtype=np.float32)
+    compared, across = 0, 0
+    for l in range(len(routers)):
+        ref_x = oracle.rms_norm(h.astype(np.float64), gammas[l], eps)
+        across += check_bf16_near(x_gpu[l], ref_x, what=f"{what} x[{l}]")
+        xb = np.ascontiguousarray(x_gpu[l]).view(np.uint16)
+        keep = np.ones(xb.shape[0], bool)
+        if routes is not None:
+            ref_r = oracle_routing(xb, routers[l], biases[l], top_k)
+            keep = check_routing_screened(routes[l], ref_r, xb, routers[l], biases[l], top_k)
+        check_outputs(y_gpu[l][keep], y_refs[l][keep], f"{what} y[{l}]")
+        compared += int(keep.sum())
+        h = (h + np.asarray(y_gpu[l], dtype=np.float32)).astype(np.float32)   # one fp32 rounding per add
+    np.testing.assert_array_equal(np.asarray(h_out).view(np.uint32), h.view(np.uint32))
+    return compared, across
