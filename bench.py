@@ -58,6 +58,7 @@ def parse():
                         "object with the prefill and stacked-decode workloads)")
     p.add_argument("--no-workloads", action="store_true", help="headline only")
     p.add_argument("--mfma-summary", metavar="DIR", help="summarise a rocprofv3 --pmc run of MFMA counters")
+    p.add_argument("--stats-summary", metavar="DIR", help="summarise a rocprofv3 --kernel-trace --stats run")
     p.add_argument("--layers", type=int, default=16, help="independent weight sets rotated per step")
     p.add_argument("--batches", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,9 +75,21 @@ def parse():
 
 
 def expert_bytes(wl):
+    """Bytes of one FP4 expert: (whole expert, gate+up, down)."""
     h, i = wl.hidden, wl.inter
     per_matrix = i * h // 2 + i * h // 32
-    return 3 * per_matrix, 2 * per_matrix, per_matrix  # whole expert, gate+up, down
+    return 3 * per_matrix, 2 * per_matrix, per_matrix
+
+
+def shared_bytes(wl):
+    """Bytes of the shared expert in its stored format: (whole expert, gate+up, down)."""
+    if not wl.shared:
+        return 0, 0, 0
+    if not wl.shared_fp8:
+        return expert_bytes(wl)
+    h, i = wl.hidden, wl.inter
+    per_matrix = i * h + 4 * (-(-i // 128)) * (-(-h // 128))   # e4m3 codes + float32 block scales
+    return 3 * per_matrix, 2 * per_matrix, per_matrix
 
 
 def sources_digest(kernel):
@@ -104,12 +117,14 @@ def traffic_record(kernel, workload):
     return None
 
 
-EXTRA_WORKLOADS = ("prefill_t512", "prefill_t4096_zipf", "stacked_decode_16l")
+EXTRA_WORKLOADS = ("decode_t8_fp8shared", "prefill_t512", "prefill_t4096_zipf", "stacked_decode_16l",
+                   "chained_decode_16l")
 # per extra workload: (steps, warm-up steps, weight sets rotated, token batches rotated).  A
 # prefill call's 3.4 GB of weights is far beyond the 256 MB last-level cache, so two weight sets
 # and four token batches suffice there; the stacked workload is 16 layers by definition.
-EXTRA_SHAPE = {"prefill_t512": (50, 5, 2, 4), "prefill_t4096_zipf": (50, 5, 2, 4),
-               "stacked_decode_16l": (100, 10, 16, 64)}
+EXTRA_SHAPE = {"decode_t8_fp8shared": (200, 20, 16, 64), "prefill_t512": (50, 5, 2, 4),
+               "prefill_t4096_zipf": (50, 5, 2, 4), "stacked_decode_16l": (100, 10, 16, 64),
+               "chained_decode_16l": (100, 10, 16, 64)}
 
 
 def progress(msg):
@@ -122,6 +137,8 @@ def main():
         return pmc_summary(args)
     if args.mfma_summary:
         return mfma_summary(args)
+    if args.stats_summary:
+        return stats_summary(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path)", file=sys.stderr)
@@ -141,7 +158,7 @@ def main():
             steps, warm, nl, nb = EXTRA_SHAPE[name]
             r = measure(synth.WORKLOADS[name], steps, warm, nl, nb, 0)
             extra[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
-                                             "fp4_weight_GBps", "fp4_weight_frac_hbm", "tflops",
+                                             "weight_GBps", "weight_frac_hbm", "tflops",
                                              "tflops_frac_bf16", "active_groups_per_call", "layer_calls_per_step",
                                              "roofline", "kernels")}
     cpu = None
@@ -165,7 +182,7 @@ def main():
                        "e4m3 terms (12 bits) in decode, two (8 bits, bf16's precision) in prefill"),
         "data": "synthetic (seeded; random-init weights at the workload's DeepSeek V4 expert shapes)",
     }
-    out.update({k: res[k] for k in ("config", "fp4_weight_GBps", "fp4_weight_frac_hbm", "tflops", "tflops_frac_bf16",
+    out.update({k: res[k] for k in ("config", "weight_GBps", "weight_frac_hbm", "tflops", "tflops_frac_bf16",
                                     "active_groups_per_call", "layer_calls_per_step", "roofline", "kernels")})
     out["cpu_baseline"] = cpu
     if extra:
@@ -190,11 +207,16 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
         raw = synth.layer_weights(wl, l, device=dev)          # checkpoint layout
         w = {m: moe.pack_fp4(*raw[m]) for m in synth.MATRICES}  # kernel layout, packed once
         del raw
+        f8 = None
+        if wl.shared_fp8:
+            f8 = {}
+            for m, (c, sc) in synth.shared_fp8_weights(wl, l, device=dev).items():
+                f8[m] = (moe.pack_fp8(c[None])[0], sc)
         wr = torch.from_numpy(synth.router_weights(wl, l)).to(dev)
         b = synth.router_bias(wl)
         bt = None if b is None else torch.from_numpy(b).to(dev)
-        layers.append(moe.MoeLayer(wr, w["gate"], w["up"], w["down"], wl.top_k, wl.shared, bt))
-        keep.append((w, wr, bt))
+        layers.append(moe.MoeLayer(wr, w["gate"], w["up"], w["down"], wl.top_k, wl.shared, bt, shared_fp8=f8))
+        keep.append((w, f8, wr, bt))
     torch.cuda.synchronize()
     progress(f"{wl.name}: {nl} weight set(s) resident")
     nb = batches
@@ -204,13 +226,56 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    # A step is one pass of the layer; stacked decode runs its layers one after another per step
-    # (call i of the run uses layer i % nl and token batch i % nb).
+    # A step is one pass of the layer.  Stacked decode runs its L layers one after another per step
+    # (call i of the run uses layer i % nl and token batch i % nb); chained decode runs them as one
+    # token's residual stream (RMSNorm between layers), from residual input h_0 = batch s % nb.
+    # Both replay the step from a HIP graph the library records (moe_chain_*): one launch per step.
+    # The per-kernel event timing pass runs the same kernels from eager calls (the graph carries
+    # no timing events).
     L = wl.layers if wl.layers > 1 else 1
+    chains, hs, gammas = [], None, None
+    if wl.chained:
+        hs = torch.stack([torch.from_numpy(synth.residual_input(wl, step=s)) for s in range(nb)]).to(dev)
+        gammas = [torch.from_numpy(synth.norm_weight(wl, l)).to(dev) for l in range(nl)]
+        chains.append(moe.MoeChain(layers, T, residual=True, norm_weight=gammas))
+    elif L > 1:
+        period_steps = int(np.lcm(nl, nb)) // L if int(np.lcm(nl, nb)) % L == 0 else None
+        if period_steps is None or nl != L:
+            raise ValueError("stacked decode: the layer/batch rotation must repeat after whole steps")
+        for p in range(period_steps):
+            ch = moe.MoeChain(layers, T, residual=False)
+            for l in range(L):
+                ch.x[l].copy_(xs[(p * L + l) % nb])
+            chains.append(ch)
+        torch.cuda.synchronize()
 
     def step(s):
-        for c in range(s * L, (s + 1) * L):
-            layers[c % nl].forward(xs[c % nb], workspace=ws, y=y)
+        if wl.chained:
+            chains[0].h_in.copy_(hs[s % nb])
+            chains[0].run(torch.cuda.current_stream())
+        elif chains:
+            chains[s % len(chains)].run(torch.cuda.current_stream())
+        else:
+            layers[s % nl].forward(xs[s % nb], workspace=ws, y=y)
+
+    ye = torch.empty((L, T, wl.hidden), dtype=torch.float32, device=dev)
+    xe = torch.empty((L, T, wl.hidden), dtype=torch.int16, device=dev)
+    he = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+
+    def eager_step(s):
+        """The step's kernels from eager library calls (for the per-kernel event timing)."""
+        if not wl.chained:
+            for c in range(s * L, (s + 1) * L):
+                layers[c % nl].forward(xs[c % nb], workspace=ws, y=y)
+            return
+        h0 = hs[s % nb]
+        for l in range(L):
+            if l == 0:
+                moe.residual_rmsnorm(h0, None, None, gammas[0], 1e-6, xe[0])
+            else:
+                moe.residual_rmsnorm(h0 if l == 1 else he, ye[l - 1], he, gammas[l], 1e-6, xe[l])
+            layers[l].forward(xe[l], workspace=ws, y=ye[l])
+        moe.residual_rmsnorm(h0 if L == 1 else he, ye[L - 1], he, None, 1e-6, None)
 
     if copy_probe_mib:
         src = torch.empty(copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -223,9 +288,17 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     # active experts of every (layer, batch) pair a step can meet (outside the timed region)
     period = int(np.lcm(nl, nb))
     active = {}
-    for c in range(min(period, steps * L)):
-        r = layers[c % nl].route(xs[c % nb], workspace=ws)
-        active[(c % nl, c % nb)] = r["counts"]
+    if wl.chained:
+        # the layers' inputs come from the chain itself: route what an eager pass computes
+        for b in range(min(nb, steps)):
+            eager_step(b)
+            for l in range(L):
+                r = layers[l].route(xe[l], workspace=ws)
+                active[(l, b)] = r["counts"]
+    else:
+        for c in range(min(period, steps * L)):
+            r = layers[c % nl].route(xs[c % nb], workspace=ws)
+            active[(c % nl, c % nb)] = r["counts"]
     torch.cuda.synchronize()
     active = {k: int((v > 0).sum().item()) for k, v in active.items()}
 
@@ -245,22 +318,28 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     moe.timing_reset()
     moe.timing_enable(True)
     for s in range(steps):
-        step(s)
+        eager_step(s)
     torch.cuda.synchronize()
     kt = moe.timing_read()
     moe.timing_enable(False)
 
     e_all, e_gu, e_dn = expert_bytes(wl)
-    groups_per_call = [active[(c % nl, c % nb)] + wl.shared for c in range(steps * L)]
-    groups = float(np.mean(groups_per_call))
-    fp4_bytes_step = L * groups * e_all
+    s_all, s_gu, s_dn = shared_bytes(wl)
+    if wl.chained:
+        routed_per_call = [active[(l, s % nb)] for s in range(steps) for l in range(L)]
+    else:
+        routed_per_call = [active[(c % nl, c % nb)] for c in range(steps * L)]
+    routed = float(np.mean(routed_per_call))
+    groups = routed + wl.shared
+    weight_bytes_step = L * (routed * e_all + s_all)   # weight bytes of the active groups
     flops_step = L * 2.0 * T * (wl.top_k + wl.shared) * 3 * wl.hidden * wl.inter
     # the dominant kernel and its algorithmic work per launch
-    # (gate/up weight bytes of the active groups; gate/up flops).  The grouped GEMM is priced
+    # (gate/up weight bytes of the groups it reads; gate/up flops).  The grouped GEMM is priced
     # against the roof its arithmetic intensity reaches first: MFMA above the ridge
-    # (bf16 peak / HBM peak flop per byte), HBM below it.
-    gu_bytes = groups * e_gu
-    gu_flops = 2.0 * T * (wl.top_k + wl.shared) * 2 * wl.hidden * wl.inter
+    # (bf16 peak / HBM peak flop per byte), HBM below it.  An FP8 shared expert has launches of
+    # its own, so the FP4 kernels then read the routed experts only.
+    gu_bytes = routed * e_gu + (0 if wl.shared_fp8 else s_gu)
+    gu_flops = 2.0 * T * (wl.top_k + (0 if wl.shared_fp8 else wl.shared)) * 2 * wl.hidden * wl.inter
     if "gemv_gateup" in kt:
         dom, work, bound = "gemv_gateup", gu_bytes, "hbm"
     elif gu_flops / gu_bytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
@@ -284,10 +363,13 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     res = {
         "value": tokens_per_s, "unit": "tokens/s", "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup,
         "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
-                   "shared": wl.shared, "inter": wl.inter, "tokens": T, "layers_rotated": nl,
-                   "batches_rotated": nb, "parallelism": "single GPU"},
-        "fp4_weight_GBps": fp4_bytes_step / (ms_per_step * 1e-3) / 1e9,
-        "fp4_weight_frac_hbm": fp4_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                   "shared": wl.shared, "shared_format": "fp8_e4m3_128x128" if wl.shared_fp8 else "fp4_e2m1_e8m0_32",
+                   "inter": wl.inter, "tokens": T, "layers_rotated": nl,
+                   "batches_rotated": nb, "parallelism": "single GPU",
+                   "launch": "hip_graph_per_step" if chains else "eager_per_call",
+                   **({"join": "residual + RMSNorm (eps 1e-6) between layers"} if wl.chained else {})},
+        "weight_GBps": weight_bytes_step / (ms_per_step * 1e-3) / 1e9,
+        "weight_frac_hbm": weight_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "tflops": flops_step / (ms_per_step * 1e-3) / 1e12,
         "tflops_frac_bf16": flops_step / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "active_groups_per_call": groups,
@@ -295,7 +377,9 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
         "roofline": roof,
         "kernels": kernels,
     }
-    del layers, keep, xs, ws, y
+    for ch in chains:
+        ch.close()
+    del layers, keep, xs, ws, y, chains
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -515,6 +599,40 @@ def mfma_summary(args):
         print(f"| {n} | {nd} | {util if util is None else f'{util:.1f}'} | {f8:.4g} | {f6:.4g} | "
               f"{alg.get(n, float('nan')):.4g} |")
     print("\n```json\n" + json.dumps({"workload": wl, "kernels": recs}) + "\n```")
+
+
+def stats_summary(args):
+    """The library's kernels from a rocprofv3 --kernel-trace --stats run (k_kernel_stats.csv), and
+    the run's own JSON line, as markdown."""
+    files = glob.glob(os.path.join(args.stats_summary, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.stats_summary}")
+    run = {}
+    if args.pmc_log:
+        with open(args.pmc_log) as f:
+            for line in f:
+                if line.startswith("{"):
+                    run = json.loads(line)
+    cfg = run.get("config", {})
+    print(f"# rocprofv3 kernel stats: {cfg.get('workload', '?')}\n")
+    print("Command (`cd /tmp && export TMPDIR=/tmp` first):\n")
+    print("```\n" + (args.pmc_command or "(not recorded)") + "\n```\n")
+    print("| kernel | calls | average (us) | min (us) | max (us) | total (ms) |")
+    print("|---|---|---|---|---|---|")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Name"].split("(")[0].split("<")[0].strip().split()[-1]
+                     .startswith("moe::")]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0].replace("void ", "").replace("moe::", "").replace("(anonymous namespace)::", "")
+        print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} |")
+    if run:
+        keep = {k: run.get(k) for k in ("value", "unit", "ms_per_step", "steps", "warmup")}
+        keep["kernels_event_timed"] = run.get("kernels")
+        print("\nThe run's own line (steps timed without the profiler's per-dispatch records are faster):\n")
+        print("```json\n" + json.dumps(keep) + "\n```")
 
 
 if __name__ == "__main__":
