@@ -22,6 +22,7 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("moe_abi_version", "moe_device_supported", "moe_layer_create", "moe_layer_destroy",
            "moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_noalloc", "moe_pack_fp4",
            "moe_pack_fp8", "moe_residual_rmsnorm", "moe_chain_create", "moe_chain_run", "moe_chain_destroy",
+           "moe_bank_create", "moe_bank_forward", "moe_bank_stats", "moe_bank_destroy",
            "moe_status_string",
            "moe_last_error",
            "moe_timing_enable", "moe_timing_read", "moe_timing_reset")
@@ -119,6 +120,10 @@ def load(path: str = None) -> ctypes.CDLL:
         "moe_chain_create": (I32, [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]),
         "moe_chain_run": (I32, [P, P]),
         "moe_chain_destroy": (None, [P]),
+        "moe_bank_create": (I32, [P, I32, I32, ctypes.POINTER(P)]),
+        "moe_bank_forward": (I32, [P, P, I32, P, ctypes.POINTER(RouteOut), P, U64, P]),
+        "moe_bank_stats": (I32, [P, ctypes.POINTER(ctypes.c_int64)]),
+        "moe_bank_destroy": (None, [P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (I32, [I32]),

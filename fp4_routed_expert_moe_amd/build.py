@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_fp4.so")
-SOURCES = ("route.hip", "gemv.hip", "gemm.hip", "pack.hip", "chain.hip", "api.hip")
+SOURCES = ("route.hip", "gemv.hip", "gemm.hip", "pack.hip", "chain.hip", "api.hip", "bank.hip")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

@@ -11,19 +11,14 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
-
-struct moe_layer {
-  moe_layer_desc desc;
-  moe::Dims dims;
-};
+#include "api_internal.h"
 
 // Workspace of moe_forward_noalloc: one array per device (each GPU the library runs on holds
 // its own copy until the process ends).  In host code this name is only a stand-in: the
 // device address comes from hipGetSymbolAddress (scratch_of below).
 static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
-namespace {
+namespace moe_api {
 
 thread_local std::string g_last_error;
 // set while moe_forward_noalloc runs: its launches record no timing events (no event objects
@@ -40,10 +35,8 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-constexpr int kMaxTokens = 1 << 20;
 constexpr int kGemvMaxTokens = 32;  // AUTO: GEMV up to this many tokens, grouped GEMM above
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout for T tokens; assigns pointers when base != nullptr.  Returns bytes.
 size_t carve(const moe::Dims& d, int T, char* base, moe::CallBufs* b) {
@@ -103,17 +96,6 @@ int max_active_of(const moe::Dims& d, int T) {
   return (int)(std::min<size_t>(d.E, (size_t)T * d.K) + d.S);
 }
 
-struct DeviceGuard {
-  int old = -1;
-  bool ok = true;
-  explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&old) != hipSuccess) old = -1;
-    if (old != dev) ok = hipSetDevice(dev) == hipSuccess;
-  }
-  ~DeviceGuard() {
-    if (old >= 0) (void)hipSetDevice(old);
-  }
-};
 
 // ---- kernel timing -------------------------------------------------------------------
 struct TimingRec {
@@ -157,7 +139,9 @@ void drain_timing_locked() {
   g_trecs.clear();
 }
 
-}  // namespace
+}  // namespace moe_api
+
+using namespace moe_api;
 
 namespace moe {
 
@@ -214,6 +198,50 @@ int32_t scratch_of(int dev, hipStream_t s, void** out) {
   return MOE_OK;
 }
 }  // namespace
+
+namespace moe_api {
+
+int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void* ws, uint64_t ws_bytes,
+                          const char* what) {
+  if (!L) return fail(MOE_ERR_INVALID, "%s: NULL layer", what);
+  if (T < 0 || T > kMaxTokens) return fail(MOE_ERR_INVALID, "%s: tokens=%d out of [0, %d]", what, T, kMaxTokens);
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_ERR_INVALID, "%s: NULL input", what);
+  if (reinterpret_cast<uintptr_t>(x) & 15u) return fail(MOE_ERR_INVALID, "%s: x must be 16-byte aligned", what);
+  const uint64_t need = carve(L->dims, T, nullptr, nullptr);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %p/%llu bytes, need %llu bytes aligned to 256", what, ws,
+                (unsigned long long)ws_bytes, (unsigned long long)need);
+  return MOE_OK;
+}
+
+// Routing; with `forward` set the routing kernels also write the FP8 activation terms the
+// expert kernels read, and (for the grouped GEMM) its M-tile list.  route_out: the caller
+// reads the routing (idx, weights, counts, offsets, perm), so every table is written.
+int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
+                             bool forward, bool gemm, bool route_out) {
+  const moe::Dims& d = L->dims;
+  const bool lean = forward && !gemm && !route_out;
+  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, forward,
+                                           forward && gemm, lean, s);
+  if (e == hipSuccess && !moe::route_fused(d, T)) e = moe::launch_route_chunked(d, b, T, s);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+void use_route_out(moe::CallBufs& b, const moe_route_out* r) {
+  b.idx = r->idx;
+  b.w = r->weight;
+  b.counts = r->counts;
+  b.offsets = r->offsets;
+  b.perm = r->perm;
+}
+
+bool route_ok(const moe_route_out* r) {
+  return r && r->idx && r->weight && r->counts && r->offsets && r->perm;
+}
+
+}  // namespace moe_api
 
 // =====================================================================================
 extern "C" {
@@ -330,46 +358,6 @@ void moe_layer_destroy(moe_layer* layer) { delete layer; }
 uint64_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens) {
   if (!layer || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
   return carve(layer->dims, std::max(max_tokens, 1), nullptr, nullptr);
-}
-
-static int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void* ws, uint64_t ws_bytes,
-                          const char* what) {
-  if (!L) return fail(MOE_ERR_INVALID, "%s: NULL layer", what);
-  if (T < 0 || T > kMaxTokens) return fail(MOE_ERR_INVALID, "%s: tokens=%d out of [0, %d]", what, T, kMaxTokens);
-  if (T == 0) return MOE_OK;
-  if (!x) return fail(MOE_ERR_INVALID, "%s: NULL input", what);
-  if (reinterpret_cast<uintptr_t>(x) & 15u) return fail(MOE_ERR_INVALID, "%s: x must be 16-byte aligned", what);
-  const uint64_t need = carve(L->dims, T, nullptr, nullptr);
-  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || ws_bytes < need)
-    return fail(MOE_ERR_WORKSPACE, "%s: workspace %p/%llu bytes, need %llu bytes aligned to 256", what, ws,
-                (unsigned long long)ws_bytes, (unsigned long long)need);
-  return MOE_OK;
-}
-
-// Routing; with `forward` set the routing kernels also write the FP8 activation terms the
-// expert kernels read, and (for the grouped GEMM) its M-tile list.  route_out: the caller
-// reads the routing (idx, weights, counts, offsets, perm), so every table is written.
-static int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
-                             bool forward, bool gemm, bool route_out) {
-  const moe::Dims& d = L->dims;
-  const bool lean = forward && !gemm && !route_out;
-  hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, forward,
-                                           forward && gemm, lean, s);
-  if (e == hipSuccess && !moe::route_fused(d, T)) e = moe::launch_route_chunked(d, b, T, s);
-  if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
-  return MOE_OK;
-}
-
-static void use_route_out(moe::CallBufs& b, const moe_route_out* r) {
-  b.idx = r->idx;
-  b.w = r->weight;
-  b.counts = r->counts;
-  b.offsets = r->offsets;
-  b.perm = r->perm;
-}
-
-static bool route_ok(const moe_route_out* r) {
-  return r && r->idx && r->weight && r->counts && r->offsets && r->perm;
 }
 
 int32_t moe_route(const moe_layer* L, const uint16_t* x, int32_t T, const moe_route_out* route, void* ws,

@@ -254,10 +254,13 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
                               int max_act, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, float* y, int T, int max_act,
                             hipStream_t s);
+// slot_of (NULL: every group at its own index): group g's weights sit at index slot_of[g] of
+// w's arrays; the M-tiles of groups with slot_of[g] < 0 are skipped (one expert-bank refill group
+// per launch).  FP4 groups only.
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
-                              int T, int mt_bound, hipStream_t s);
+                              int T, int mt_bound, hipStream_t s, const int32_t* slot_of = nullptr);
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* slot_of = nullptr);
 hipError_t launch_pack_fp8(const uint8_t* codes_in, uint8_t* codes_out, int groups, int N, int K, hipStream_t s);
 // h_dst = h_src + y (y, h_dst may be NULL), x = bf16(RMSNorm(h) * gamma) (x may be NULL)
 hipError_t launch_residual_rmsnorm(const float* h_src, const float* y, float* h_dst, const float* gamma, float eps,

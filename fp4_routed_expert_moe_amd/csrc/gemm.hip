@@ -294,14 +294,18 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
 // FP8: the M-tiles of the FP8 shared expert (info[2] .. info[1]), weights c0p/c1p as FP8 codes
 // and f0p/f1p their float32 block scales.  Otherwise the FP4 M-tiles [0, info[1]), or
 // [0, info[2]) when routed_only (the shared expert is FP8 and has its own launch).
+// slot_of (FP4 only; NULL = every group at its own index): group g's weights are at index
+// slot_of[g] of the weight arrays, and the M-tiles of groups with slot_of[g] < 0 are skipped
+// (an expert bank running one refill group of experts per launch).
 template <bool GATEUP, class SH, bool FP8 = false>
 __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     ARows a, const uint8_t* __restrict__ c0p, const uint8_t* __restrict__ s0p, const uint8_t* __restrict__ c1p,
     const uint8_t* __restrict__ s1p, const float* __restrict__ f0p, const float* __restrict__ f1p,
     const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
-    const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, uint8_t* __restrict__ h8,
-    float* __restrict__ staging, int routed_only, float routed_scale, int T, int k, int N, int R, int NT) {
+    const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, const int32_t* __restrict__ slot_of,
+    uint8_t* __restrict__ h8, float* __restrict__ staging, int routed_only, float routed_scale, int T, int k, int N,
+    int R, int NT) {
   constexpr int NM = GATEUP ? 2 : 1;
   __shared__ ATile<SH> tile[2];
   // XCD x (= b % 8) takes the M-tiles mt = 8i + x, all NT column slices of each
@@ -310,6 +314,8 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   if (mt >= (routed_only ? info[2] : info[1])) return;
   // tile metadata is the same for every lane: keep it in scalar registers
   const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
+  const int gw = slot_of ? __builtin_amdgcn_readfirstlane(slot_of[g]) : g;  // weight index of the group
+  if (gw < 0) return;
   const int mr0 = __builtin_amdgcn_readfirstlane(mt_row0[mt]);
   const int r0 = __builtin_amdgcn_readfirstlane(grp_row0[g]) + mr0;  // first grouped row of the tile
   const int nrows = min(kPM, __builtin_amdgcn_readfirstlane(grp_rows[g]) - mr0);
@@ -348,9 +354,9 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     const int slab = (int)scale_slab_bytes(N, a.K);
 #pragma unroll
     for (int mtx = 0; mtx < NM; ++mtx) {
-      bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)g * KB * N * 16), (short)0,
+      bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)gw * KB * N * 16), (short)0,
                                                     KB * N * 16, kBufferFlags);
-      bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)g * slab), (short)0, slab,
+      bs.s[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(scales[mtx] + (size_t)gw * slab), (short)0, slab,
                                                     kBufferFlags);
     }
     bs.voff_c = (q * N + n0 + m) * 16;
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
-                              int T, int mt_bound, hipStream_t s) {
+                              int T, int mt_bound, hipStream_t s, const int32_t* slot_of) {
   (void)x;
   const int NT = (d.I + GateUpShape::PN - 1) / GateUpShape::PN;
   const int R = T * (d.K + d.S);
@@ -483,7 +489,8 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int tk = timing_begin("gemm_gateup", s);
   gemm_f8f4_kernel<true, GateUpShape><<<(mt_bound + 7) / 8 * 8 * NT, GateUpShape::NTH, 0, s>>>(
       a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr, b.perm, b.w, b.info, b.mt_group,
-      b.mt_row0, b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, d.fp8_shared, 1.0f, T, d.K, d.I, R, NT);
+      b.mt_row0, b.grp_row0, b.grp_rows, slot_of, static_cast<uint8_t*>(b.h), nullptr, d.fp8_shared, 1.0f, T, d.K,
+      d.I, R, NT);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.fp8_shared) return e;
@@ -491,14 +498,14 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int tk8 = timing_begin("gemm_gateup_fp8", s);
   gemm_f8f4_kernel<true, GateUpShape8, true><<<(mts + 7) / 8 * 8 * NT, GateUpShape8::NTH, 0, s>>>(
       a, w.shared_gate_fp8, nullptr, w.shared_up_fp8, nullptr, w.shared_gate_fp8_scales, w.shared_up_fp8_scales,
-      b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, static_cast<uint8_t*>(b.h), nullptr, 0,
-      1.0f, T, d.K, d.I, R, NT);
+      b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr, static_cast<uint8_t*>(b.h),
+      nullptr, 0, 1.0f, T, d.K, d.I, R, NT);
   timing_end(tk8, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBufs& b, int T, int mt_bound,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* slot_of) {
   const int NT = (d.H + DownShape::PN - 1) / DownShape::PN;
   const int R = T * (d.K + d.S);
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
@@ -506,8 +513,8 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const int tk = timing_begin("gemm_down", s);
   gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(
       a, w.down_codes, w.down_scales, w.down_codes, w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.info,
-      b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr, b.staging, d.fp8_shared, d.routed_scale, T, d.K, d.H,
-      R, NT);
+      b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, slot_of, nullptr, b.staging, d.fp8_shared, d.routed_scale, T,
+      d.K, d.H, R, NT);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.fp8_shared) return e;
@@ -516,7 +523,7 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   gemm_f8f4_kernel<false, DownShape8, true><<<(mts + 7) / 8 * 8 * NT, DownShape8::NTH, 0, s>>>(
       a, w.shared_down_fp8, nullptr, w.shared_down_fp8, nullptr, w.shared_down_fp8_scales,
       w.shared_down_fp8_scales, b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr,
-      b.staging, 0, d.routed_scale, T, d.K, d.H, R, NT);
+      nullptr, b.staging, 0, d.routed_scale, T, d.K, d.H, R, NT);
   timing_end(tk8, s);
   return hipGetLastError();
 }

@@ -80,7 +80,7 @@ class MoeLayer:
 
     def __init__(self, w_router: torch.Tensor, gate, up, down, top_k: int, n_shared: int = 1,
                  router_bias: Optional[torch.Tensor] = None, path: str = "auto", shared_fp8: Optional[dict] = None,
-                 routed_scale: float = 1.0):
+                 routed_scale: float = 1.0, host_weights: bool = False):
         self.lib = _lib.load()
         e, h = w_router.shape
         g, hb, inter, sixteen = gate[0].shape
@@ -103,8 +103,12 @@ class MoeLayer:
             if tuple(c.shape) != (g, k // 32, n, 16) or tuple(s.shape) != kernel_scale_shape(g, n, k):
                 raise ValueError(f"{name} weights: codes {tuple(c.shape)} / scales {tuple(s.shape)}, "
                                  f"expected {(g, k // 32, n, 16)} / {(g, k // 32, n)} (kernel layout)")
-            if c.dtype != torch.uint8 or s.dtype != torch.uint8 or not c.is_cuda or not s.is_cuda:
-                raise ValueError(f"{name} weights must be uint8 CUDA tensors")
+            if c.dtype != torch.uint8 or s.dtype != torch.uint8:
+                raise ValueError(f"{name} weights must be uint8 tensors")
+            if host_weights and not (c.is_pinned() and s.is_pinned()):
+                raise ValueError(f"{name} weights must be pinned host tensors (host_weights=True: an expert bank)")
+            if not host_weights and not (c.is_cuda and s.is_cuda):
+                raise ValueError(f"{name} weights must be CUDA tensors")
             if not c.is_contiguous() or not s.is_contiguous():
                 raise ValueError(f"{name} weights must be contiguous")
         if w_router.dtype != torch.float32 or not w_router.is_cuda or not w_router.is_contiguous():
@@ -200,6 +204,50 @@ class MoeLayer:
         return y
 
     __call__ = forward
+
+
+# ---- partial-residency expert bank --------------------------------------------------------
+
+class MoeBank:
+    """HBM expert slots filled on demand from a layer whose FP4 weights are pinned host tensors
+    (``MoeLayer(..., host_weights=True)``): ``forward`` routes on the device, waits for the
+    routing counts, uploads the missing active experts in refill groups of ``group`` and runs the
+    grouped-GEMM expert kernels of each refill group as soon as its uploads are in."""
+
+    def __init__(self, layer: "MoeLayer", n_slots: int, group: int):
+        self.lib = _lib.load()
+        self.layer = layer
+        h = ctypes.c_void_p()
+        _lib.check(self.lib.moe_bank_create(layer._h, n_slots, group, ctypes.byref(h)), self.lib)
+        self._h = h.value
+
+    def forward(self, x: torch.Tensor, workspace: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                route: Optional[dict] = None, stream=None) -> torch.Tensor:
+        L = self.layer
+        t = L._check_x(x)
+        if y is None:
+            y = torch.empty((t, L.hidden), dtype=torch.float32, device=L.device)
+        ws = workspace if workspace is not None else L.workspace(t)
+        rs = L._route_struct(route) if route is not None else None
+        _lib.check(self.lib.moe_bank_forward(self._h, _ptr(x), t, _ptr(y), ctypes.byref(rs) if rs is not None else None,
+                                             _ptr(ws), ws.numel(), _stream_handle(stream)), self.lib)
+        return y
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * 5)()
+        _lib.check(self.lib.moe_bank_stats(self._h, out), self.lib)
+        return dict(calls=out[0], resident_hits=out[1], uploads=out[2], bytes_uploaded=out[3], refill_groups=out[4])
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.moe_bank_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---- chained decode ----------------------------------------------------------------------

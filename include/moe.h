@@ -275,6 +275,49 @@ int32_t moe_chain_run(const moe_chain* chain, void* stream);
 /* Free the graph.  NULL is a no-op; the caller must have synchronised every replay. */
 void moe_chain_destroy(moe_chain* chain);
 
+/* ---- partial-residency expert bank --------------------------------------------------
+ * For expert sets larger than the HBM set aside for them.  The pages' prefill MoE routes on
+ * the device, then refills a transient per-layer VRAM expert bank route-aware, in groups the
+ * size of its slots, from page-locked host slabs, with the lookups of group g+1 overlapping the
+ * uploads of group g ("feat(v4/cuda): the CUDA tier wired into the DeepSeek V4 engine", PR
+ * #1055, "What it is", the Prefill MoE item; the decode tier keeps a VRAM-sized FP4 expert
+ * mirror cache, refilled in place).  Here a bank is n_slots expert slots in HBM, each holding one
+ * group's gate, up and down codes and scales in the kernel layout, filled from the layer's FP4
+ * arrays, which live in page-locked host memory. */
+typedef struct moe_bank moe_bank;
+
+/* A bank for `layer`: a layer created by moe_layer_create whose six FP4 weight pointers are
+ * page-locked host memory (hipHostMalloc) in the kernel layout ([G][...] as moe_pack_fp4 writes
+ * it), with its router weights on the device and no FP8 shared expert.  Allocates n_slots
+ * expert slots in HBM (n_slots >= 2 * group; one slot is the bytes of one group of all six
+ * arrays), a copy stream (default priority), events and small page-locked tables; `group`
+ * (>= 1) is the number of experts per refill group.  The bank borrows the layer, which must
+ * outlive it.  On failure *out is NULL and nothing leaks. */
+int32_t moe_bank_create(const moe_layer* layer, int32_t n_slots, int32_t group, moe_bank** out);
+
+/* The layer's forward with its experts served from the bank.  Routing runs on `stream`; the
+ * calling thread then waits for the routing counts (the refill is route-aware, so this call
+ * blocks until routing is done), takes the groups with rows (shared expert included) resident
+ * ones first, and splits them into refill groups of up to `group` experts.  The experts of
+ * refill group i that are not resident are uploaded on the bank's copy stream (into free slots,
+ * least recently used ones, or slots of refill groups two or more back, after their kernels);
+ * the grouped-GEMM expert kernels of refill group i run on `stream` once its uploads are in,
+ * while group i+1 uploads; the combine runs after the last group.  Slots keep their experts
+ * between calls.  The result equals moe_forward on the same layer with MOE_PATH_GEMM and
+ * resident weights, bit for bit.  Returns with the expert work enqueued on `stream`.  Calls on
+ * one bank must not overlap; `workspace` is as for moe_forward. */
+int32_t moe_bank_forward(moe_bank* bank, const uint16_t* x, int32_t tokens, float* y,
+                         const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
+                         void* stream);
+
+/* Counters since creation: [0] calls, [1] experts found resident, [2] experts uploaded,
+ * [3] bytes uploaded, [4] refill groups run. */
+int32_t moe_bank_stats(const moe_bank* bank, int64_t* out5);
+
+/* Free the bank's slots, stream, events and tables (never the layer).  NULL is a no-op; the
+ * caller must have synchronised the streams of its calls. */
+void moe_bank_destroy(moe_bank* bank);
+
 /* Static text for a status code. */
 const char* moe_status_string(int32_t status);
 

@@ -211,6 +211,23 @@ int main(void) {
     CHECK(moe_chain_run(NULL, NULL) == MOE_ERR_INVALID);
     moe_chain_destroy(NULL);
   }
+
+  // expert bank: argument checks on the host; a well-formed request reaches the device
+  {
+    moe_bank* bk = (moe_bank*)0x1;
+    CHECK(moe_bank_create(L, 4, 2, NULL) == MOE_ERR_INVALID);
+    CHECK(moe_bank_create(NULL, 4, 2, &bk) == MOE_ERR_INVALID && bk == NULL);
+    bk = (moe_bank*)0x1;
+    CHECK(moe_bank_create(L, 3, 2, &bk) == MOE_ERR_INVALID && bk == NULL);  // fewer than 2 * group slots
+    bk = (moe_bank*)0x1;
+    CHECK(moe_bank_create(L, 4, 0, &bk) == MOE_ERR_INVALID && bk == NULL);
+    bk = (moe_bank*)0x1;
+    CHECK(moe_bank_create(L, 4, 2, &bk) == MOE_ERR_HIP && bk == NULL);      // no device on this host
+    CHECK(moe_bank_forward(NULL, x, 8, y, NULL, ws, w8, NULL) == MOE_ERR_INVALID);
+    int64_t st5[5];
+    CHECK(moe_bank_stats(NULL, st5) == MOE_ERR_INVALID);
+    moe_bank_destroy(NULL);
+  }
   moe_layer_destroy(L);
   moe_layer_destroy(NULL);
 
