@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=None,
                    help="measure only this workload (default: decode_t8 as the headline, plus a 'workloads' "
-                        "object with the prefill and stacked-decode workloads)")
+                        "object with the other workloads, the expert-bank one included)")
     p.add_argument("--no-workloads", action="store_true", help="headline only")
     p.add_argument("--mfma-summary", metavar="DIR", help="summarise a rocprofv3 --pmc run of MFMA counters")
     p.add_argument("--stats-summary", metavar="DIR", help="summarise a rocprofv3 --kernel-trace --stats run")
@@ -127,6 +127,13 @@ EXTRA_SHAPE = {"decode_t8_fp8shared": (200, 20, 16, 64), "prefill_t512": (50, 5,
                "chained_decode_16l": (100, 10, 16, 64)}
 
 
+# Partial-residency expert bank workloads: the named layer workload with its experts in pinned host
+# memory, served through an HBM bank of n_slots expert slots refilled `group` experts at a time.
+# name -> (layer workload, steps, warm-up steps, n_slots, group, token batches rotated)
+BANK_WORKLOADS = {"prefill_t512_bank64": ("prefill_t512", 10, 2, 64, 16, 4)}
+PCIE_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction (the MI355X host link)
+
+
 def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -149,6 +156,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in BANK_WORKLOADS:
+        print(json.dumps(measure_bank(args.workload)), flush=True)
+        return
     headline = args.workload or "decode_t8"
     wl = synth.WORKLOADS[headline]
     res = measure(wl, args.steps, args.warmup, args.layers, args.batches, args.copy_probe_mib)
@@ -161,6 +171,8 @@ def main():
                                              "weight_GBps", "weight_frac_hbm", "tflops",
                                              "tflops_frac_bf16", "active_groups_per_call", "layer_calls_per_step",
                                              "roofline", "kernels")}
+        for name in BANK_WORKLOADS:
+            extra[name] = measure_bank(name)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args, synth)
@@ -382,6 +394,70 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     del layers, keep, xs, ws, y, chains
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return res
+
+
+def measure_bank(name):
+    """Time whole layer calls served through a partial-residency expert bank (uploads included)."""
+    import numpy as np
+    import torch
+
+    import moe_synth as synth
+    import fp4_routed_expert_moe_amd as moe
+
+    base, steps, warmup, n_slots, group, nb = BANK_WORKLOADS[name]
+    wl = synth.WORKLOADS[base]
+    dev = torch.device("cuda:0")
+    raw = synth.layer_weights(wl, 0, device=dev)
+    host = {}
+    for m in synth.MATRICES:
+        c, sc = moe.pack_fp4(*raw[m])
+        hc = torch.empty(c.shape, dtype=torch.uint8, pin_memory=True)
+        hs = torch.empty(sc.shape, dtype=torch.uint8, pin_memory=True)
+        hc.copy_(c)
+        hs.copy_(sc)
+        host[m] = (hc, hs)
+    torch.cuda.synchronize()
+    del raw, c, sc
+    torch.cuda.empty_cache()
+    wr = torch.from_numpy(synth.router_weights(wl, 0)).to(dev)
+    b = synth.router_bias(wl)
+    bt = None if b is None else torch.from_numpy(b).to(dev)
+    layer = moe.MoeLayer(wr, host["gate"], host["up"], host["down"], wl.top_k, wl.shared, bt, "gemm",
+                         host_weights=True)
+    bank = moe.MoeBank(layer, n_slots, group)
+    xs = torch.stack([torch.from_numpy(synth.tokens(wl, layer=0, step=s).view(np.int16)) for s in range(nb)]).to(dev)
+    T = wl.tokens
+    ws = layer.workspace(T)
+    y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    progress(f"{name}: {sum(t.numel() for p in host.values() for t in p) / 1e9:.2f} GB of experts in pinned host "
+             f"memory, bank of {n_slots} slots")
+    for s in range(warmup):
+        bank.forward(xs[s % nb], workspace=ws, y=y)
+    torch.cuda.synchronize()
+    st0 = bank.stats()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        bank.forward(xs[s % nb], workspace=ws, y=y)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st1 = bank.stats()
+    up_bytes = st1["bytes_uploaded"] - st0["bytes_uploaded"]
+    ms = 1e3 * elapsed / steps
+    progress(f"{name}: {steps} timed steps, {ms:.3f} ms per step")
+    res = {"value": steps * T / elapsed, "unit": "tokens/s", "ms_per_step": ms, "steps": steps, "warmup": warmup,
+           "config": {"workload": name, "layer_workload": base, "tokens": T, "bank_slots": n_slots,
+                      "refill_group": group, "expert_bytes_host": sum(t.numel() for p in host.values() for t in p),
+                      "bank_bytes": n_slots * sum(t[0].numel() for p in host.values() for t in p),
+                      "launch": "moe_bank_forward per call (blocks on the routing counts)"},
+           "h2d_GBps": up_bytes / elapsed / 1e9, "h2d_frac_pcie": up_bytes / elapsed / 1e9 / PCIE_PEAK_GBPS,
+           "uploads_per_call": (st1["uploads"] - st0["uploads"]) / steps,
+           "resident_hits_per_call": (st1["resident_hits"] - st0["resident_hits"]) / steps,
+           "refill_groups_per_call": (st1["refill_groups"] - st0["refill_groups"]) / steps,
+           "bound": "pcie (uploads of the experts not resident)"}
+    bank.close()
+    del layer, host, xs, ws, y
+    torch.cuda.synchronize()
     return res
 
 

@@ -5,9 +5,9 @@
 // bank in groups the size of its slots from page-locked host slabs, the lookups of group g+1
 // overlapping the uploads of group g ("feat(v4/cuda): the CUDA tier wired into the DeepSeek V4
 // engine", PR #1055, "What it is", the Prefill MoE item).  Here the lookups are host-side slot
-// decisions, the uploads are DMA copies on a copy stream of the bank's own, and the expert
+// decisions, the uploads are DMA copies on copy streams of the bank's own, and the expert
 // kernels are the grouped GEMM's, which take a group -> slot table and skip the M-tiles of
-// groups outside the current refill group.  A slot reused within a call waits (on the copy
+// groups outside the current refill group.  A slot reused within a call waits (on its copy
 // stream) for the kernels of the refill group that last read it.
 #include <algorithm>
 #include <new>
@@ -19,6 +19,12 @@ using namespace moe_api;
 
 namespace {
 constexpr int kArrays = 6;  // gate codes, gate scales, up codes, up scales, down codes, down scales
+// Copy streams the uploads rotate over, expert by expert: one stream's copies run on one DMA
+// engine at a time, several keep more engines busy.
+#ifndef MOE_BANK_COPY_STREAMS
+#define MOE_BANK_COPY_STREAMS 4
+#endif
+constexpr int kCopies = MOE_BANK_COPY_STREAMS;
 }
 
 struct moe_bank {
@@ -28,8 +34,8 @@ struct moe_bank {
   size_t bytes[kArrays] = {};        // one group of each array
   uint8_t* slots[kArrays] = {};      // device [n_slots][bytes[i]]
   const uint8_t* host[kArrays] = {};
-  hipStream_t copy = nullptr;
-  std::vector<hipEvent_t> ev_up, ev_done;
+  hipStream_t copy[kCopies] = {};
+  std::vector<hipEvent_t> ev_up, ev_done;  // ev_up: [max_groups][kCopies]
   hipEvent_t ev_end = nullptr;       // after the last call's combine
   bool called = false;
   int32_t* counts_host = nullptr;    // page-locked [E]
@@ -53,7 +59,8 @@ void release(moe_bank* k) {
   for (auto e : k->ev_done)
     if (e) (void)hipEventDestroy(e);
   if (k->ev_end) (void)hipEventDestroy(k->ev_end);
-  if (k->copy) (void)hipStreamDestroy(k->copy);
+  for (auto c : k->copy)
+    if (c) (void)hipStreamDestroy(c);
   if (k->counts_host) (void)hipHostFree(k->counts_host);
   if (k->tables_host) (void)hipHostFree(k->tables_host);
   if (k->tables_dev) (void)hipFree(k->tables_dev);
@@ -106,13 +113,13 @@ int32_t moe_bank_create(const moe_layer* layer, int32_t n_slots, int32_t group, 
     k->host[i] = host[i];
     e = hipMalloc(reinterpret_cast<void**>(&k->slots[i]), k->bytes[i] * n_slots);
   }
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&k->copy, hipStreamNonBlocking);
-  k->ev_up.assign(k->max_groups, nullptr);
+  for (int c = 0; c < kCopies && e == hipSuccess; ++c) e = hipStreamCreateWithFlags(&k->copy[c], hipStreamNonBlocking);
+  k->ev_up.assign((size_t)k->max_groups * kCopies, nullptr);
   k->ev_done.assign(k->max_groups, nullptr);
-  for (int i = 0; i < k->max_groups && e == hipSuccess; ++i) {
+  for (size_t i = 0; i < k->ev_up.size() && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&k->ev_up[i], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&k->ev_done[i], hipEventDisableTiming);
-  }
+  for (int i = 0; i < k->max_groups && e == hipSuccess; ++i)
+    e = hipEventCreateWithFlags(&k->ev_done[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&k->ev_end, hipEventDisableTiming);
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&k->counts_host), (size_t)d.E * 4, hipHostMallocDefault);
   const size_t tbytes = (size_t)k->max_groups * d.G * 4;
@@ -190,7 +197,7 @@ int32_t moe_bank_forward(moe_bank* k, const uint16_t* x, int32_t T, float* y, co
     const int lo = rg * k->group, hi = std::min((int)need.size(), lo + k->group);
     int32_t* table = k->tables_host + (size_t)rg * d.G;
     std::fill(table, table + d.G, -1);
-    bool uploads = false;
+    bool uploads[kCopies] = {};
     for (int j = lo; j < hi; ++j) {
       const int g = need[j];
       int slot = k->group_slot[g];
@@ -210,8 +217,9 @@ int32_t moe_bank_forward(moe_bank* k, const uint16_t* x, int32_t T, float* y, co
         }
         if (best < 0) return hip_fail(hipErrorUnknown, "no slot free for a refill group");
         slot = best;
+        const int cs = (int)(k->stats[2] % kCopies);  // the copy stream of this upload
         if (slot_rg[slot] >= 0) {
-          e = hipStreamWaitEvent(k->copy, k->ev_done[slot_rg[slot]], 0);
+          e = hipStreamWaitEvent(k->copy[cs], k->ev_done[slot_rg[slot]], 0);
           if (e != hipSuccess) return hip_fail(e, "ordering a slot reuse");
         }
         if (k->slot_group[slot] >= 0) k->group_slot[k->slot_group[slot]] = -1;
@@ -219,19 +227,21 @@ int32_t moe_bank_forward(moe_bank* k, const uint16_t* x, int32_t T, float* y, co
         k->group_slot[g] = slot;
         for (int i = 0; i < kArrays && e == hipSuccess; ++i)
           e = hipMemcpyAsync(k->slots[i] + (size_t)slot * k->bytes[i], k->host[i] + (size_t)g * k->bytes[i],
-                             k->bytes[i], hipMemcpyHostToDevice, k->copy);
+                             k->bytes[i], hipMemcpyHostToDevice, k->copy[cs]);
         if (e != hipSuccess) return hip_fail(e, "uploading an expert");
         ++k->stats[2];
         for (int i = 0; i < kArrays; ++i) k->stats[3] += (int64_t)k->bytes[i];
-        uploads = true;
+        uploads[cs] = true;
       }
       table[g] = slot;
       slot_rg[slot] = rg;
       k->slot_tick[slot] = ++k->tick;
     }
-    if (uploads) {
-      e = hipEventRecord(k->ev_up[rg], k->copy);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s, k->ev_up[rg], 0);
+    for (int c = 0; c < kCopies; ++c) {
+      if (!uploads[c]) continue;
+      hipEvent_t ev = k->ev_up[(size_t)rg * kCopies + c];
+      e = hipEventRecord(ev, k->copy[c]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, ev, 0);
       if (e != hipSuccess) return hip_fail(e, "ordering the kernels after their uploads");
     }
     int32_t* tdev = k->tables_dev + (size_t)rg * d.G;

@@ -290,7 +290,7 @@ typedef struct moe_bank moe_bank;
  * page-locked host memory (hipHostMalloc) in the kernel layout ([G][...] as moe_pack_fp4 writes
  * it), with its router weights on the device and no FP8 shared expert.  Allocates n_slots
  * expert slots in HBM (n_slots >= 2 * group; one slot is the bytes of one group of all six
- * arrays), a copy stream (default priority), events and small page-locked tables; `group`
+ * arrays), four copy streams (default priority), events and small page-locked tables; `group`
  * (>= 1) is the number of experts per refill group.  The bank borrows the layer, which must
  * outlive it.  On failure *out is NULL and nothing leaks. */
 int32_t moe_bank_create(const moe_layer* layer, int32_t n_slots, int32_t group, moe_bank** out);
@@ -299,8 +299,9 @@ int32_t moe_bank_create(const moe_layer* layer, int32_t n_slots, int32_t group, 
  * calling thread then waits for the routing counts (the refill is route-aware, so this call
  * blocks until routing is done), takes the groups with rows (shared expert included) resident
  * ones first, and splits them into refill groups of up to `group` experts.  The experts of
- * refill group i that are not resident are uploaded on the bank's copy stream (into free slots,
- * least recently used ones, or slots of refill groups two or more back, after their kernels);
+ * refill group i that are not resident are uploaded on the bank's copy streams, expert by
+ * expert in turn (into free slots, least recently used ones, or slots of refill groups two or
+ * more back, after their kernels);
  * the grouped-GEMM expert kernels of refill group i run on `stream` once its uploads are in,
  * while group i+1 uploads; the combine runs after the last group.  Slots keep their experts
  * between calls.  The result equals moe_forward on the same layer with MOE_PATH_GEMM and
@@ -314,7 +315,7 @@ int32_t moe_bank_forward(moe_bank* bank, const uint16_t* x, int32_t tokens, floa
  * [3] bytes uploaded, [4] refill groups run. */
 int32_t moe_bank_stats(const moe_bank* bank, int64_t* out5);
 
-/* Free the bank's slots, stream, events and tables (never the layer).  NULL is a no-op; the
+/* Free the bank's slots, streams, events and tables (never the layer).  NULL is a no-op; the
  * caller must have synchronised the streams of its calls. */
 void moe_bank_destroy(moe_bank* bank);
 
