@@ -403,13 +403,18 @@ constexpr int kDnBlocks = 1;  // column blocks (of TL tiles) per down workgroup
 #define MOE_DN_SPLIT 4
 #endif
 constexpr int kDnSplit = MOE_DN_SPLIT;            // waves per down workgroup = reduction-axis slices
-constexpr int kDnThreads = 64 * kDnSplit;
+// The FP8 shared expert is one group over the whole GPU: its column tiles alone give 64
+// workgroups at H or I = 4096 or 2048, so its kernels split the reduction axis over more waves.
+#ifndef MOE_FP8_SPLIT
+#define MOE_FP8_SPLIT 8
+#endif
+constexpr int kFp8Split = MOE_FP8_SPLIT;
 
 // FP8: the FP8 shared expert alone (launched after the FP4 kernel, so every routed row is in
 // staging), each workgroup also combining its tile.  Otherwise the FP4 groups, skipping
 // skip_group.  A routed row's weight is its routing weight times routed_scale.
-template <int TL, bool FP8>
-__global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
+template <int TL, bool FP8, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_down_kernel(
     const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
     const uint8_t* __restrict__ d8, const float* __restrict__ d8s,
     const int32_t* __restrict__ perm, const float* __restrict__ row_w, const GroupRec* __restrict__ grec,
@@ -417,9 +422,9 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
     int H, int I, int R) {
   constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
   // column tiles each wave finishes (waves past the last tile only reduce)
-  constexpr int kDnPerWave = kDnBlocks * TL > kDnSplit ? kDnBlocks * TL / kDnSplit : 1;
-  static_assert(kDnPerWave * kDnSplit >= kDnBlocks * TL, "down workgroup shape");
-  __shared__ f32x4 red[kDnSplit][kDnBlocks][TL][64];
+  constexpr int kDnPerWave = kDnBlocks * TL > SPLIT ? kDnBlocks * TL / SPLIT : 1;
+  static_assert(kDnPerWave * SPLIT >= kDnBlocks * TL, "down workgroup shape");
+  __shared__ f32x4 red[SPLIT][kDnBlocks][TL][64];
   int g, row0, rows;
   bool combiner;
   if constexpr (FP8) {
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   const int n0 = blockIdx.x * kDnCols;
   const int KB = I >> 5;
   const int NI = (KB + 3) >> 2;
-  const int it_lo = wave * NI / kDnSplit, it_hi = (wave + 1) * NI / kDnSplit;
+  const int it_lo = wave * NI / SPLIT, it_hi = (wave + 1) * NI / SPLIT;
   typename GvFmt<FP8, kDnBlocks, kHTerms, TL>::Src src;
   if constexpr (FP8) {
     const uint8_t* codes[kDnBlocks] = {d8};
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
       if (jj >= kDnBlocks * TL) break;
       f32x4 sum = red[0][c][j][lane];
 #pragma unroll
-      for (int w = 1; w < kDnSplit; ++w) sum += red[w][c][j][lane];
+      for (int w = 1; w < SPLIT; ++w) sum += red[w][c][j][lane];
       const int n = n0 + 16 * jj + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // lane (n, q) holds rows 4q .. 4q+3 of the pass
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(kDnThreads, 8 / kDnSplit) void gemv_down_kernel(
   // still 0 is polled again on its own.
   const uint32_t* st = reinterpret_cast<const uint32_t*>(staging);
   const int ns = k + S;
-  for (int i = threadIdx.x; i < T * kDnCols; i += kDnThreads) {
+  for (int i = threadIdx.x; i < T * kDnCols; i += (64 * SPLIT)) {
     const int t = i / kDnCols, n = n0 + i % kDnCols;
     if (n >= H) continue;
     float sacc = 0.f;
@@ -561,7 +566,7 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   if (e != hipSuccess || !d.fp8_shared) return e;
   // the FP8 shared expert: 32-column tiles (its one group over the whole GPU)
   const int tk8 = timing_begin("gemv_gateup_fp8", s);
-  gemv_gateup_kernel<2, kSplit, true><<<dim3((d.I + 31) / 32, 1), 64 * kSplit, 0, s>>>(
+  gemv_gateup_kernel<2, kFp8Split, true><<<dim3((d.I + 31) / 32, 1), 64 * kFp8Split, 0, s>>>(
       b.xq, nullptr, nullptr, nullptr, nullptr, w.shared_gate_fp8, w.shared_gate_fp8_scales, w.shared_up_fp8,
       w.shared_up_fp8_scales, b.perm, b.grec, static_cast<uint8_t*>(b.h), nullptr, -1, T, d.K, d.H, d.I, R);
   timing_end(tk8, s);
@@ -576,7 +581,7 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   dim3 grid((d.H + kCols - 1) / kCols, max_act);
   const int skip = d.fp8_shared ? d.E : -1;
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<4, false><<<grid, kDnThreads, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes,
+  gemv_down_kernel<4, false, kDnSplit><<<grid, 64 * kDnSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes,
                                                          w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.grec,
                                                          b.staging, y, skip, d.routed_scale, T, d.K, d.S, d.H,
                                                          d.I, R);
@@ -584,7 +589,8 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.fp8_shared) return e;
   const int tk8 = timing_begin("gemv_down_fp8", s);
-  gemv_down_kernel<4, true><<<dim3(grid.x, 1), kDnThreads, 0, s>>>(
+  // the FP8 shared expert: 32-column tiles (its one group over the whole GPU)
+  gemv_down_kernel<2, true, kFp8Split><<<dim3((d.H + 31) / 32, 1), 64 * kFp8Split, 0, s>>>(
       static_cast<const uint8_t*>(b.h), nullptr, nullptr, w.shared_down_fp8, w.shared_down_fp8_scales, b.perm,
       b.row_w, b.grec, b.staging, y, -1, d.routed_scale, T, d.K, d.S, d.H, d.I, R);
   timing_end(tk8, s);
