@@ -30,7 +30,7 @@ def _t(a):
 # ------------------------------------------------------------------------------- the join step
 
 
-@pytest.mark.parametrize("tokens,hidden", [(1, 4096), (5, 96), (8, 7168), (3, 4)])
+@pytest.mark.parametrize("tokens,hidden", [(1, 4096), (5, 96), (8, 7168), (3, 4), (2, 8196)])
 def test_residual_rmsnorm_step(tokens, hidden):
     from fp4_routed_expert_moe_amd import residual_rmsnorm
     rng = np.random.default_rng(tokens * 1000 + hidden)
