@@ -348,16 +348,18 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     # the dominant kernel and its algorithmic work per launch
     # (gate/up weight bytes of the groups it reads; gate/up flops).  The grouped GEMM is priced
     # against the roof its arithmetic intensity reaches first: MFMA above the ridge
-    # (bf16 peak / HBM peak flop per byte), HBM below it.  An FP8 shared expert has launches of
-    # its own, so the FP4 kernels then read the routed experts only.
-    gu_bytes = routed * e_gu + (0 if wl.shared_fp8 else s_gu)
+    # (bf16 peak / HBM peak flop per byte), HBM below it.  The decode gate/up launch reads the
+    # shared expert in either format (an FP8 one as extra tiles of the same launch); the grouped
+    # GEMM gives an FP8 shared expert launches of its own.
+    gu_bytes = routed * e_gu + s_gu
+    gu_bytes_gemm = routed * e_gu + (0 if wl.shared_fp8 else s_gu)
     gu_flops = 2.0 * T * (wl.top_k + (0 if wl.shared_fp8 else wl.shared)) * 2 * wl.hidden * wl.inter
     if "gemv_gateup" in kt:
         dom, work, bound = "gemv_gateup", gu_bytes, "hbm"
-    elif gu_flops / gu_bytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+    elif gu_flops / gu_bytes_gemm >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         dom, work, bound = "gemm_gateup", gu_flops, "mfma"
     else:
-        dom, work, bound = "gemm_gateup", gu_bytes, "hbm"
+        dom, work, bound = "gemm_gateup", gu_bytes_gemm, "hbm"
     launches, total_ms = kt.get(dom, (0, 0.0))
     avg_s = total_ms * 1e-3 / launches if launches else float("nan")
     if bound == "hbm":
@@ -370,7 +372,7 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     roof["avg_launch_us"] = avg_s * 1e6
     roof["algorithmic_per_launch"] = work
     roof["algorithmic_unit"] = "bytes" if bound == "hbm" else "flops"
-    roof["algorithmic_bytes_per_launch"] = gu_bytes
+    roof["algorithmic_bytes_per_launch"] = gu_bytes if dom == "gemv_gateup" else gu_bytes_gemm
     kernels = {k: dict(launches=v[0], avg_us=1e3 * v[1] / max(v[0], 1)) for k, v in kt.items()}
     res = {
         "value": tokens_per_s, "unit": "tokens/s", "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup,

@@ -260,41 +260,34 @@ __device__ __forceinline__ void gv_pass(f32x4 (&acc)[NM][TL], const Src& src, in
 // gate/up:  h[row][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), written as 3 FP8 terms + scales
 // (h8 = [kHTerms][rows][I] bytes, hs = [rows][kb_pad(I)] e8m0).
 // ------------------------------------------------------------------------------------
-// FP8: the FP8 shared expert alone (the grid's y dimension is 1; its rows are the T tokens after
-// the T*k routed rows).  Otherwise the FP4 groups of the active-group slots, skipping group
-// `skip_group` (the shared expert when it is FP8; -1 for none); gc/gs/uc/us are then the FP4
-// arrays, else g8/g8s/u8/u8s the FP8 codes and scales.
+// One tile: column tile bx of active-group slot `slot` (FP4), or column tile bx of the FP8
+// shared expert (slot unused).  red: the workgroup's LDS reduction buffer.
+#define GATEUP_ARGS                                                                                         \
+  const uint8_t *__restrict__ xq, const uint8_t *__restrict__ gc, const uint8_t *__restrict__ gs,           \
+      const uint8_t *__restrict__ uc, const uint8_t *__restrict__ us, const uint8_t *__restrict__ g8,       \
+      const float *__restrict__ g8s, const uint8_t *__restrict__ u8, const float *__restrict__ u8s,         \
+      const int32_t *__restrict__ perm, const GroupRec *__restrict__ grec, uint8_t *__restrict__ h8,        \
+      uint32_t *__restrict__ stage_clear, int skip_group, int T, int k, int H, int I, int R
+#define GATEUP_PASS xq, gc, gs, uc, us, g8, g8s, u8, u8s, perm, grec, h8, stage_clear, skip_group, T, k, H, I, R
 template <int TL, int SPLIT, bool FP8>
-__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ gc, const uint8_t* __restrict__ gs,
-    const uint8_t* __restrict__ uc, const uint8_t* __restrict__ us, const uint8_t* __restrict__ g8,
-    const float* __restrict__ g8s, const uint8_t* __restrict__ u8, const float* __restrict__ u8s,
-    const int32_t* __restrict__ perm, const GroupRec* __restrict__ grec, uint8_t* __restrict__ h8,
-    uint32_t* __restrict__ stage_clear, int skip_group, int T, int k, int H, int I, int R) {
-  if (stage_clear) {
-    // clear the staging rows the down kernel fills next (R x H words)
-    const size_t n = (size_t)R * H;
-    const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x, nwg = (size_t)gridDim.x * gridDim.y;
-    for (size_t i = (wg * (64 * SPLIT) + threadIdx.x) * 4; i < n; i += nwg * (64 * SPLIT) * 4)
-      *reinterpret_cast<uint4*>(stage_clear + i) = make_uint4(0u, 0u, 0u, 0u);
-  }
+__device__ __forceinline__ void gateup_tile(f32x4 (*red)[TL][2][64], int bx, int slot, GATEUP_ARGS) {
+  (void)stage_clear;
   static_assert(TL == 2 || TL == 4, "h's FP8 blocks are 32 columns: a workgroup finishes whole blocks");
-  __shared__ f32x4 red[SPLIT][TL][2][64];
   int g, row0, rows;
   if constexpr (FP8) {
     g = -1;
     row0 = T * k;
     rows = T;
   } else {
-    const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
-    if ((int)blockIdx.y >= rec.w || rec.x == skip_group) return;
+    const int4 rec = *reinterpret_cast<const int4*>(grec + slot);
+    if (slot >= rec.w || rec.x == skip_group) return;
     g = __builtin_amdgcn_readfirstlane(rec.x);
     row0 = __builtin_amdgcn_readfirstlane(rec.y);
     rows = __builtin_amdgcn_readfirstlane(rec.z);
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * (16 * TL);
+  const int n0 = bx * (16 * TL);
   const int KB = H >> 5;
   const int NI = (KB + 3) >> 2;  // K iterations of 4 blocks
   const int it_lo = wave * NI / SPLIT, it_hi = (wave + 1) * NI / SPLIT;
@@ -384,6 +377,42 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_g
   }
 }
 
+// The staging rows the down kernel fills next (R x H words) start at zero: every workgroup
+// of the gate/up launch clears a grid-stride share.
+template <int NTH>
+__device__ __forceinline__ void clear_stage(uint32_t* stage_clear, int R, int H) {
+  if (!stage_clear) return;
+  const size_t n = (size_t)R * H;
+  const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x, nwg = (size_t)gridDim.x * gridDim.y;
+  for (size_t i = (wg * NTH + threadIdx.x) * 4; i < n; i += nwg * NTH * 4)
+    *reinterpret_cast<uint4*>(stage_clear + i) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// FP8: the FP8 shared expert alone (the grid's y dimension is 1; its rows are the T tokens after
+// the T*k routed rows).  Otherwise the FP4 groups of the active-group slots, skipping group
+// `skip_group` (the shared expert when it is FP8; -1 for none).
+template <int TL, int SPLIT, bool FP8>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_kernel(GATEUP_ARGS) {
+  clear_stage<64 * SPLIT>(stage_clear, R, H);
+  __shared__ f32x4 red[SPLIT][TL][2][64];
+  gateup_tile<TL, SPLIT, FP8>(red, blockIdx.x, blockIdx.y, GATEUP_PASS);
+}
+
+// The FP4 groups and an FP8 shared expert in one launch: the first TL/2 rows of the grid are the
+// FP8 expert's 32-column tiles (dispatched first, so they overlap the FP4 tiles), the rest the
+// FP4 active-group slots (skip_group = the shared expert's FP4 slot).
+template <int TL, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_gateup_mixed_kernel(GATEUP_ARGS) {
+  clear_stage<64 * SPLIT>(stage_clear, R, H);
+  __shared__ f32x4 red[SPLIT][TL][2][64];
+  constexpr int n8 = TL / 2;
+  if ((int)blockIdx.y < n8)
+    gateup_tile<2, SPLIT, true>(reinterpret_cast<f32x4(*)[2][2][64]>(red), blockIdx.y * gridDim.x + blockIdx.x, 0,
+                                GATEUP_PASS);
+  else
+    gateup_tile<TL, SPLIT, false>(red, blockIdx.x, blockIdx.y - n8, GATEUP_PASS);
+}
+
 // ------------------------------------------------------------------------------------
 // down:  staging[slot(r)][n] = weight(r) * (h_r . Wd[n]),  h_r from its 3 FP8 terms, and
 // y[t][n] = staging[shared slot of t][n] + sum_j staging[t*k + j][n].
@@ -403,47 +432,42 @@ constexpr int kDnBlocks = 1;  // column blocks (of TL tiles) per down workgroup
 #define MOE_DN_SPLIT 4
 #endif
 constexpr int kDnSplit = MOE_DN_SPLIT;            // waves per down workgroup = reduction-axis slices
-// The FP8 shared expert is one group over the whole GPU: its column tiles alone give 64
-// workgroups at H or I = 4096 or 2048, so its kernels split the reduction axis over more waves.
-#ifndef MOE_FP8_SPLIT
-#define MOE_FP8_SPLIT 8
-#endif
-constexpr int kFp8Split = MOE_FP8_SPLIT;
 
-// FP8: the FP8 shared expert alone (launched after the FP4 kernel, so every routed row is in
-// staging), each workgroup also combining its tile.  Otherwise the FP4 groups, skipping
-// skip_group.  A routed row's weight is its routing weight times routed_scale.
+// One tile: column tile bx of active-group slot `slot` (FP4), or column tile bx of the FP8 shared
+// expert.  comb: which tiles add the call's rows -- for FP4, the slot `comb` places from the
+// end (1: the last slot; 2: the last routed slot, when the shared expert's slot is skipped);
+// for FP8, every tile when comb != 0.  red: the workgroup's LDS reduction buffer.
+#define DOWN_ARGS                                                                                           \
+  const uint8_t *__restrict__ h8, const uint8_t *__restrict__ dc, const uint8_t *__restrict__ ds,           \
+      const uint8_t *__restrict__ d8, const float *__restrict__ d8s, const int32_t *__restrict__ perm,      \
+      const float *__restrict__ row_w, const GroupRec *__restrict__ grec, float *__restrict__ staging,       \
+      float *__restrict__ y, int skip_group, float routed_scale, int T, int k, int S, int H, int I, int R
+#define DOWN_PASS h8, dc, ds, d8, d8s, perm, row_w, grec, staging, y, skip_group, routed_scale, T, k, S, H, I, R
 template <int TL, bool FP8, int SPLIT>
-__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_down_kernel(
-    const uint8_t* __restrict__ h8, const uint8_t* __restrict__ dc, const uint8_t* __restrict__ ds,
-    const uint8_t* __restrict__ d8, const float* __restrict__ d8s,
-    const int32_t* __restrict__ perm, const float* __restrict__ row_w, const GroupRec* __restrict__ grec,
-    float* __restrict__ staging, float* __restrict__ y, int skip_group, float routed_scale, int T, int k, int S,
-    int H, int I, int R) {
+__device__ __forceinline__ void down_tile(f32x4 (*red)[kDnBlocks][TL][64], int bx, int slot, int comb, DOWN_ARGS) {
   constexpr int kDnCols = kDnBlocks * 16 * TL;  // output columns per workgroup
   // column tiles each wave finishes (waves past the last tile only reduce)
   constexpr int kDnPerWave = kDnBlocks * TL > SPLIT ? kDnBlocks * TL / SPLIT : 1;
   static_assert(kDnPerWave * SPLIT >= kDnBlocks * TL, "down workgroup shape");
-  __shared__ f32x4 red[SPLIT][kDnBlocks][TL][64];
   int g, row0, rows;
   bool combiner;
   if constexpr (FP8) {
     g = -1;
     row0 = T * k;
     rows = T;
-    combiner = true;
+    combiner = comb != 0;
   } else {
-    const int4 rec = *reinterpret_cast<const int4*>(grec + blockIdx.y);
+    const int4 rec = *reinterpret_cast<const int4*>(grec + slot);
     const int nslots = rec.w;
-    if ((int)blockIdx.y >= nslots || rec.x == skip_group) return;
+    if (slot >= nslots || rec.x == skip_group) return;
     g = __builtin_amdgcn_readfirstlane(rec.x);
     row0 = __builtin_amdgcn_readfirstlane(rec.y);
     rows = __builtin_amdgcn_readfirstlane(rec.z);
-    combiner = (int)blockIdx.y == nslots - 1;
+    combiner = slot == nslots - comb;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * kDnCols;
+  const int n0 = bx * kDnCols;
   const int KB = I >> 5;
   const int NI = (KB + 3) >> 2;
   const int it_lo = wave * NI / SPLIT, it_hi = (wave + 1) * NI / SPLIT;
@@ -543,6 +567,30 @@ __global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_d
   }
 }
 
+// FP8: the FP8 shared expert alone (launched after the FP4 kernel, so every routed row is in
+// staging), each workgroup also combining its tile.  Otherwise the FP4 groups, skipping
+// skip_group, the last slot's workgroups combining.  A routed row's weight is its routing
+// weight times routed_scale.
+template <int TL, bool FP8, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_down_kernel(DOWN_ARGS) {
+  __shared__ f32x4 red[SPLIT][kDnBlocks][TL][64];
+  down_tile<TL, FP8, SPLIT>(red, blockIdx.x, blockIdx.y, 1, DOWN_PASS);
+}
+
+// The FP4 groups and an FP8 shared expert in one launch: the first TL/2 rows of the grid are the
+// FP8 expert's 32-column tiles (dispatched first), the rest the FP4 active-group slots, whose last
+// routed slot combines (the shared expert's FP4 slot is skip_group, the last slot).
+template <int TL, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT, SPLIT <= 4 ? 8 / SPLIT : 1) void gemv_down_mixed_kernel(DOWN_ARGS) {
+  __shared__ f32x4 red[SPLIT][kDnBlocks][TL][64];
+  constexpr int n8 = TL / 2;
+  if ((int)blockIdx.y < n8)
+    down_tile<2, true, SPLIT>(reinterpret_cast<f32x4(*)[kDnBlocks][2][64]>(red), blockIdx.y * gridDim.x + blockIdx.x,
+                              0, 0, DOWN_PASS);
+  else
+    down_tile<TL, false, SPLIT>(red, blockIdx.x, blockIdx.y - n8, 2, DOWN_PASS);
+}
+
 // ------------------------------------------------------------------------------------
 // Few active groups (small batches) get narrower column tiles per workgroup, so the grid
 // still covers the GPU several times over.
@@ -554,22 +602,23 @@ hipError_t launch_gemv_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int R = T * (d.K + d.S);
   const bool narrow = (size_t)max_act * ((d.I + 63) / 64) < kMinGemvGroups;
   const int cols = narrow ? 32 : 64;
-  dim3 grid((d.I + cols - 1) / cols, max_act);
-  const int skip = d.fp8_shared ? d.E : -1;
   const int tk = timing_begin("gemv_gateup", s);
-  auto kern = narrow ? gemv_gateup_kernel<2, kSplit, false> : gemv_gateup_kernel<4, kSplit, false>;
-  kern<<<grid, 64 * kSplit, 0, s>>>(b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr,
-                                    nullptr, nullptr, b.perm, b.grec, static_cast<uint8_t*>(b.h),
-                                    reinterpret_cast<uint32_t*>(b.staging), skip, T, d.K, d.H, d.I, R);
+  uint32_t* clear = reinterpret_cast<uint32_t*>(b.staging);
+  uint8_t* h = static_cast<uint8_t*>(b.h);
+  if (!d.fp8_shared) {
+    auto kern = narrow ? gemv_gateup_kernel<2, kSplit, false> : gemv_gateup_kernel<4, kSplit, false>;
+    kern<<<dim3((d.I + cols - 1) / cols, max_act), 64 * kSplit, 0, s>>>(
+        b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr, nullptr, nullptr, b.perm,
+        b.grec, h, clear, -1, T, d.K, d.H, d.I, R);
+  } else {
+    // the FP8 shared expert's 32-column tiles (cols/32 grid rows) ahead of the FP4 slots, whose
+    // shared-expert slot is skipped
+    auto kern = narrow ? gemv_gateup_mixed_kernel<2, kSplit> : gemv_gateup_mixed_kernel<4, kSplit>;
+    kern<<<dim3(d.I / cols, max_act + cols / 32), 64 * kSplit, 0, s>>>(
+        b.xq, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, w.shared_gate_fp8, w.shared_gate_fp8_scales,
+        w.shared_up_fp8, w.shared_up_fp8_scales, b.perm, b.grec, h, clear, d.E, T, d.K, d.H, d.I, R);
+  }
   timing_end(tk, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !d.fp8_shared) return e;
-  // the FP8 shared expert: 32-column tiles (its one group over the whole GPU)
-  const int tk8 = timing_begin("gemv_gateup_fp8", s);
-  gemv_gateup_kernel<2, kFp8Split, true><<<dim3((d.I + 31) / 32, 1), 64 * kFp8Split, 0, s>>>(
-      b.xq, nullptr, nullptr, nullptr, nullptr, w.shared_gate_fp8, w.shared_gate_fp8_scales, w.shared_up_fp8,
-      w.shared_up_fp8_scales, b.perm, b.grec, static_cast<uint8_t*>(b.h), nullptr, -1, T, d.K, d.H, d.I, R);
-  timing_end(tk8, s);
   return hipGetLastError();
 }
 
@@ -578,22 +627,20 @@ hipError_t launch_gemv_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const int R = T * (d.K + d.S);
   // (narrower down tiles measured slower: a down workgroup's bytes are already few)
   constexpr int kCols = kDnBlocks * 16 * 4;
-  dim3 grid((d.H + kCols - 1) / kCols, max_act);
-  const int skip = d.fp8_shared ? d.E : -1;
   const int tk = timing_begin("gemv_down", s);
-  gemv_down_kernel<4, false, kDnSplit><<<grid, 64 * kDnSplit, 0, s>>>(static_cast<const uint8_t*>(b.h), w.down_codes,
-                                                         w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.grec,
-                                                         b.staging, y, skip, d.routed_scale, T, d.K, d.S, d.H,
-                                                         d.I, R);
+  const uint8_t* h = static_cast<const uint8_t*>(b.h);
+  if (!d.fp8_shared) {
+    gemv_down_kernel<4, false, kDnSplit><<<dim3((d.H + kCols - 1) / kCols, max_act), 64 * kDnSplit, 0, s>>>(
+        h, w.down_codes, w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.grec, b.staging, y, -1, d.routed_scale,
+        T, d.K, d.S, d.H, d.I, R);
+  } else {
+    // the FP8 shared expert's 32-column tiles (two grid rows) ahead of the FP4 slots; the last
+    // routed slot's workgroups combine
+    gemv_down_mixed_kernel<4, kDnSplit><<<dim3(d.H / kCols, max_act + 2), 64 * kDnSplit, 0, s>>>(
+        h, w.down_codes, w.down_scales, w.shared_down_fp8, w.shared_down_fp8_scales, b.perm, b.row_w, b.grec,
+        b.staging, y, d.E, d.routed_scale, T, d.K, d.S, d.H, d.I, R);
+  }
   timing_end(tk, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !d.fp8_shared) return e;
-  const int tk8 = timing_begin("gemv_down_fp8", s);
-  // the FP8 shared expert: 32-column tiles (its one group over the whole GPU)
-  gemv_down_kernel<2, true, kFp8Split><<<dim3((d.H + 31) / 32, 1), 64 * kFp8Split, 0, s>>>(
-      static_cast<const uint8_t*>(b.h), nullptr, nullptr, w.shared_down_fp8, w.shared_down_fp8_scales, b.perm,
-      b.row_w, b.grec, b.staging, y, -1, d.routed_scale, T, d.K, d.S, d.H, d.I, R);
-  timing_end(tk8, s);
   return hipGetLastError();
 }
 
