@@ -219,11 +219,11 @@ int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void* ws, u
 // expert kernels read, and (for the grouped GEMM) its M-tile list.  route_out: the caller
 // reads the routing (idx, weights, counts, offsets, perm), so every table is written.
 int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
-                             bool forward, bool gemm, bool route_out) {
+                             bool forward, bool gemm, bool route_out, const moe::JoinArgs* join) {
   const moe::Dims& d = L->dims;
   const bool lean = forward && !gemm && !route_out;
   hipError_t e = moe::launch_router_logits(d, x, L->desc.w_router, L->desc.router_bias, b, T, forward,
-                                           forward && gemm, lean, s);
+                                           forward && gemm, lean, s, join);
   if (e == hipSuccess && !moe::route_fused(d, T)) e = moe::launch_route_chunked(d, b, T, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -375,6 +375,15 @@ int32_t moe_route(const moe_layer* L, const uint16_t* x, int32_t T, const moe_ro
 
 int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
                     void* ws, uint64_t ws_bytes, void* stream) {
+  return forward_impl(L, x, T, y, route, ws, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+}  // extern "C"
+
+namespace moe_api {
+
+int32_t forward_impl(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
+                     void* ws, uint64_t ws_bytes, hipStream_t s, const moe::JoinArgs* join) {
   int32_t st = check_call(L, x, T, ws, ws_bytes, "moe_forward");
   if (st != MOE_OK || T == 0) return st;
   if (!y) return fail(MOE_ERR_INVALID, "moe_forward: NULL output");
@@ -386,10 +395,9 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   moe::CallBufs b;
   carve(d, T, static_cast<char*>(ws), &b);
   if (route) use_route_out(b, route);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool gemv = L->desc.path == MOE_PATH_GEMV || (L->desc.path == MOE_PATH_AUTO && T <= kGemvMaxTokens);
   hipError_t e;
-  st = enqueue_route(L, x, T, b, s, true, !gemv, route != nullptr);
+  st = enqueue_route(L, x, T, b, s, true, !gemv, route != nullptr, join);
   if (st != MOE_OK) return st;
   if (gemv) {
     // the down kernel also adds each token's rows into y
@@ -405,6 +413,10 @@ int32_t moe_forward(const moe_layer* L, const uint16_t* x, int32_t T, float* y, 
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_forward: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
+
+}  // namespace moe_api
+
+extern "C" {
 
 int32_t moe_forward_noalloc(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
                             void* stream) {
@@ -507,16 +519,23 @@ int32_t enqueue_chain(const moe_chain_desc* d, const std::vector<moe_route_out>&
   const bool residual = d->flags & MOE_CHAIN_RESIDUAL;
   for (int l = 0; l < d->n_layers; ++l) {
     uint16_t* x = d->x + l * plane;
+    moe::JoinArgs join{};
+    bool fused = false;
     if (residual) {
       const float* g = d->norm_weight ? d->norm_weight[l] : nullptr;
       // layer 0 normalises h_in; layer l > 0 first adds y_{l-1} into the running residual
       const float* src = l <= 1 ? d->h_in : d->h_out;
       const float* yp = l == 0 ? nullptr : d->y + (l - 1) * plane;
-      const hipError_t e = moe::launch_residual_rmsnorm(src, yp, l == 0 ? nullptr : d->h_out, g, d->eps, x, T, H, s);
-      if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_chain_create: join launch failed: %s", hipGetErrorString(e));
+      join = moe::JoinArgs{src, yp, l == 0 ? nullptr : d->h_out, g, d->eps};
+      // small batches: the layer's routing launch does the join itself (the same arithmetic)
+      fused = moe::join_fused(d->layers[l]->dims, T);
+      if (!fused) {
+        const hipError_t e = moe::launch_residual_rmsnorm(src, yp, join.h_dst, g, d->eps, x, T, H, s);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "moe_chain_create: join launch failed: %s", hipGetErrorString(e));
+      }
     }
-    const int32_t st = moe_forward(d->layers[l], x, T, d->y + l * plane, routes.empty() ? nullptr : &routes[l],
-                                   d->workspace, d->workspace_bytes, s);
+    const int32_t st = forward_impl(d->layers[l], x, T, d->y + l * plane, routes.empty() ? nullptr : &routes[l],
+                                    d->workspace, d->workspace_bytes, s, fused ? &join : nullptr);
     if (st != MOE_OK) return st;
   }
   if (residual) {

@@ -27,7 +27,11 @@ int32_t check_call(const moe_layer* L, const uint16_t* x, int32_t T, void* ws, u
 // Routing launches; `forward` also writes the FP8 activation terms, `gemm` the M-tile list,
 // `route_out` every routing table.
 int32_t enqueue_route(const moe_layer* L, const uint16_t* x, int32_t T, moe::CallBufs& b, hipStream_t s,
-                      bool forward, bool gemm, bool route_out);
+                      bool forward, bool gemm, bool route_out, const moe::JoinArgs* join = nullptr);
+// moe_forward with, optionally, the chained decode's join done by the routing launch (x is
+// then written from the residual; moe::join_fused must hold).
+int32_t forward_impl(const moe_layer* L, const uint16_t* x, int32_t T, float* y, const moe_route_out* route,
+                     void* ws, uint64_t ws_bytes, hipStream_t s, const moe::JoinArgs* join);
 void use_route_out(moe::CallBufs& b, const moe_route_out* r);
 bool route_ok(const moe_route_out* r);
 

@@ -235,13 +235,28 @@ inline int router_slices(const Dims& d, int T) {
   ks = ks < 1 ? 1 : (ks > kRouterMaxSlices ? kRouterMaxSlices : ks);
   return ks < d.H / 32 ? ks : d.H / 32;
 }
+// The chained decode's join (h = h_src + y, x = bf16(RMSNorm(h) * gamma)) done by the routing
+// launch of the next layer, for batches route_fused takes and at most kJoinMaxT tokens: every
+// router workgroup normalises the rows itself (the same steps as the join kernel) and writes x;
+// the last one writes h_dst.
+struct JoinArgs {
+  const float* h_src;  // residual before the join [T][H]
+  const float* y;      // previous layer's output [T][H], or NULL (the first layer)
+  float* h_dst;        // residual after the join (may equal h_src), or NULL
+  const float* gamma;  // RMSNorm weight [H], or NULL (ones)
+  float eps;
+};
+constexpr int kJoinMaxT = 16;
+inline bool join_fused(const Dims& d, int T) { return route_fused(d, T) && T <= kJoinMaxT && d.H <= 8192; }
+
 // Router scores (and, for batches route_fused takes, the whole routing in the same launch).
 // quantize_x: also write the FP8 activation terms; mtiles: also the grouped GEMM's M-tile
 // list; lean: the caller only runs the decode kernels and reads no routing output, so with
 // at most kLeanMaxPicks picks only their tables are built.
 constexpr int kLeanMaxPicks = 64;
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s);
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s,
+                                const JoinArgs* join = nullptr);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
 // Decode GEMV kernels (gemv.hip): gate/up + SwiGLU into h, then down + the combine into y.

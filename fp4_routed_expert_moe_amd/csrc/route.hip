@@ -8,6 +8,7 @@
 // in the workspace, left at zero again) runs top-k, the grouping tables and the scatter.
 // Larger batches score on the matrix cores, then use a per-chunk top-k kernel, a
 // one-workgroup scan and a per-chunk scatter.
+#include "join_dev.h"
 #include "route_dev.h"
 
 namespace moe {
@@ -27,19 +28,42 @@ using RouterTail = TailLayout<1024, kTailScores>;
 // publishing their scores, so the split never delays the routing); kRouteMTiles = also build
 // the grouped GEMM's M-tile list; kRouteLean = only the tables the decode kernels read (at
 // most 64 picks).
-constexpr int kRouteQuantize = 1, kRouteMTiles = 2, kRouteLean = 4;
+// kRouteJoin = first form x from the chained decode's residual (JoinArgs) into the x buffer.
+constexpr int kRouteQuantize = 1, kRouteMTiles = 2, kRouteLean = 4, kRouteJoin = 8;
 
-__global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __restrict__ x,
+// x is not __restrict__: with kRouteJoin this launch writes it before reading it.
+__global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* x,
                                                              const float* __restrict__ wr,
                                                              const float* __restrict__ bias, CallBufs b, int T,
-                                                             int E, int H, int K, int S, int flags) {
+                                                             int E, int H, int K, int S, int flags, JoinArgs join) {
   __shared__ __align__(16) char lds[RouterTail::kBytes];
-  const int t0 = blockIdx.y * kScoreTT;
-  const int nt = min(kScoreTT, T - t0);
   const int wave = threadIdx.x >> 6;
-  __shared__ float part[kRouterEPB][kScoreWaves * kScoreTT];
   const int grp = wave / kScoreWaves;
   const int e = blockIdx.x * kRouterEPB + grp;
+  if (flags & kRouteJoin) {
+    // every workgroup forms all T rows of x itself (identical values), four rows at a time,
+    // 256 threads a row, the join kernel's steps; x is then read back as usual
+    static_assert(kTailThreads == 4 * kJoinThreads, "four join rows per pass");
+    __shared__ float jpart[4][4];
+    const int jr = threadIdx.x / kJoinThreads, tid = threadIdx.x % kJoinThreads;
+    uint16_t* xo = const_cast<uint16_t*>(x);
+    for (int tb = 0; tb < T; tb += 4) {
+      const int t = tb + jr;
+      JoinRow r;
+      float ss = 0.f;
+      if (t < T) {
+        join_load(r, join.h_src + (size_t)t * H, join.y ? join.y + (size_t)t * H : nullptr, nullptr, H, tid);
+        ss = join_wave_sum(r.ss);
+      }
+      if ((threadIdx.x & 63) == 0) jpart[jr][tid >> 6] = ss;
+      __syncthreads();
+      if (t < T) join_store_x(r, join_inv(jpart[jr], H, join.eps), join.gamma, xo + (size_t)t * H, H, tid);
+      __syncthreads();
+    }
+  }
+  const int t0 = blockIdx.y * kScoreTT;
+  const int nt = min(kScoreTT, T - t0);
+  __shared__ float part[kRouterEPB][kScoreWaves * kScoreTT];
   score_expert(x, wr, bias, b.logits, t0, nt, e, e < E, E, H, part[grp]);
   // the x split: slice `part` of `parts` of all T*KB blocks
   auto quantize = [&](int slice, int parts) {
@@ -81,6 +105,25 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* __
   else
     route_tail<kTailThreads, 16, 1024, kTailScores, false>(b, T, E, K, S, lds);
   if (threadIdx.x == 0) reset_counter(counter);
+  if ((flags & kRouteJoin) && join.h_dst) {
+    // the residual after the join: every other workgroup has read h_src (it arrived), so an
+    // in-place update is safe; fp32 adds, as in the join kernel
+    const size_t n4 = (size_t)T * H / 4;
+    const float4* hs = reinterpret_cast<const float4*>(join.h_src);
+    const float4* ys = reinterpret_cast<const float4*>(join.y);
+    float4* hd = reinterpret_cast<float4*>(join.h_dst);
+    for (size_t i = threadIdx.x; i < n4; i += kTailThreads) {
+      float4 v = hs[i];
+      if (ys) {
+        const float4 d = ys[i];
+        v.x += d.x;
+        v.y += d.y;
+        v.z += d.z;
+        v.w += d.w;
+      }
+      hd[i] = v;
+    }
+  }
   if ((flags & kRouteQuantize) && total == 1) quantize(0, 1);
 }
 
@@ -417,13 +460,16 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
-                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s) {
+                                const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s,
+                                const JoinArgs* join) {
+  if (join && !join_fused(d, T)) return hipErrorInvalidValue;  // the caller runs the join kernel instead
   if (route_fused(d, T)) {
     dim3 grid((d.E + kRouterEPB - 1) / kRouterEPB, (T + kScoreTT - 1) / kScoreTT);
     const int tk = timing_begin("router_route", s);
     const int flags = (quantize_x ? kRouteQuantize : 0) | (mtiles ? kRouteMTiles : 0) |
-                      (lean && !mtiles && T * d.K <= kLeanMaxPicks ? kRouteLean : 0);
-    router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, flags);
+                      (lean && !mtiles && T * d.K <= kLeanMaxPicks ? kRouteLean : 0) | (join ? kRouteJoin : 0);
+    router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, flags,
+                                                join ? *join : JoinArgs{nullptr, nullptr, nullptr, nullptr, 0.f});
     timing_end(tk, s);
     return hipGetLastError();
   }

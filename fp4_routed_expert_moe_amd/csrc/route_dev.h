@@ -30,8 +30,8 @@ constexpr int kScoreTT = 4;  // tokens per router workgroup (4 measured faster t
 constexpr int kScoreWaves = 4;
 
 // Quarter sums of one wave (wq = wave index in the group), same value on every lane.
-__device__ __forceinline__ void score_quarter(const uint16_t* __restrict__ x, int nt, const float* __restrict__ w,
-                                              int H, int wq, float (&out)[kScoreTT]) {
+__device__ __forceinline__ void score_quarter(const uint16_t* x, int nt, const float* __restrict__ w, int H, int wq,
+                                              float (&out)[kScoreTT]) {
   const int lane = threadIdx.x & 63;
   const int hq = H / kScoreWaves;  // H % 32 == 0: a multiple of 8
   const int h_end = (wq + 1) * hq;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void score_quarter(const uint16_t* __restrict__ x, in
 // Called by every thread of the block; the group of waves [4g, 4g+4) handles expert e (valid
 // false: the group only takes part in the barrier).  part: kScoreWaves * kScoreTT floats of
 // LDS per group.
-__device__ __forceinline__ void score_expert(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+__device__ __forceinline__ void score_expert(const uint16_t* x, const float* __restrict__ wr,
                                             const float* __restrict__ bias, float* logits, int t0, int nt, int e,
                                             bool valid, int E, int H, float* part) {
   const int wq = (threadIdx.x >> 6) % kScoreWaves, lane = threadIdx.x & 63;
