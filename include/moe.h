@@ -264,7 +264,7 @@ typedef struct moe_chain moe_chain;
 /* Record the whole chain -- for each layer the join step and moe_forward, and the final
  * residual add -- into a HIP graph, once, on a stream of the library's own (no work runs).
  * With RESIDUAL, T <= 16 and H <= 8192 the join runs inside the layer's routing launch, with
- * the same arithmetic as moe_residual_rmsnorm (same x and h bits); otherwise as its own kernel. */
+ * the same arithmetic as moe_residual_rmsnorm (same x and h bits); otherwise as its own kernel.
  * Every pointer is borrowed and baked into the graph: buffers, weights and layers must stay
  * alive and in place until moe_chain_destroy.  On failure *out is NULL and nothing leaks. */
 int32_t moe_chain_create(const moe_chain_desc* desc, moe_chain** out);
