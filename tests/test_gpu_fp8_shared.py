@@ -66,6 +66,7 @@ def _check_fp8(groups, shared, wr, b, x, top_k, routed_scale=1.0, paths=("gemv",
     (24, 1024, 64, 8, 512, 33, 0.5),
     (25, 128, 4, 2, 128, 1, 1.0),        # one token, one block
     (26, 256, 16, 4, 256, 700, 1.7),     # eleven 64-row tiles of the shared expert in the GEMM path
+    (27, 256, 8, 2, 256, 2080, 1.0),     # ~520 rows an expert and 33 FP8 shared M-tiles
 ])
 def test_fp8_shared_random_shapes_both_paths(case):
     seed, hidden, experts, k, inter, tokens, rs = case

@@ -108,6 +108,8 @@ def test_identity_experts_closed_form_on_gpu():
     (12, 128, 8, 8, 1, 64, 4),      # decode batch routed to every expert
     (13, 96, 256, 2, 1, 32, 2048),  # router GEMM through LDS, hidden-axis slices of one 32-value step
     (14, 224, 256, 3, 1, 64, 2048), # router GEMM through LDS, slices of 32 and 64 values
+    (15, 320, 8, 3, 1, 160, 2100),  # ~790 rows an expert: a dozen M-tiles each, ragged last tiles, K tails
+    (16, 256, 12, 5, 0, 288, 2049), # no shared expert; a group's last M-tile short
 ])
 def test_random_shapes_both_paths(case):
     seed, hidden, experts, k, shared, inter, tokens = case
