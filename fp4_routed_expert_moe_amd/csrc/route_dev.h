@@ -215,13 +215,9 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int k, uint16
       key[q] = a > b ? a : b;
       key[q + 1] = a > b ? b : a;
     }
-  int selE[Q];
-  float selV[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    selE[q] = 0;
-    selV[q] = 0.f;
-  }
+  // Each pick is wave-uniform: lane 0 records it in sel_e / sel_w (the score for now) as soon
+  // as it is known, and the softmax below reads the picks back.
+  const bool lead = lane == 0;
   float vtop = 0.f;
   for (int j = 0; j < k; ++j) {
     const uint32_t mhi = (uint32_t)(key[0] >> 32), mlo = (uint32_t)key[0];
@@ -240,23 +236,24 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int k, uint16
       for (int q = 0; q + 1 < Q; ++q) key[q] = key[q + 1];
       key[Q - 1] = 0ull;
     }
-    const bool rec = (j & 63) == lane;
-    const int qj = j >> 6;
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (q == qj) {
-        selE[q] = rec ? e : selE[q];
-        selV[q] = rec ? v : selV[q];
-      }
+    if (lead) {
+      sel_e[j] = (uint16_t)e;
+      sel_w[j] = v;
+    }
   }
+  // softmax over the picks: lane l takes picks l, l + 64, ... (the same order of sums as
+  // before the picks moved through LDS)
+  int selE[Q];
   float p[Q];
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int j = lane + 64 * q;
     p[q] = 0.f;
+    selE[q] = 0;
     if (j < k) {
-      p[q] = expf(selV[q] - vtop);
+      selE[q] = sel_e[j];
+      p[q] = expf(sel_w[j] - vtop);
       s += p[q];
     }
   }
@@ -265,7 +262,6 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int k, uint16
   for (int q = 0; q < Q; ++q) {
     const int j = lane + 64 * q;
     if (j < k) {
-      sel_e[j] = (uint16_t)selE[q];
       sel_w[j] = p[q] / s;
       atomicOr(reinterpret_cast<unsigned long long*>(&mask[selE[q]]), 1ull << tbit);
     }
@@ -439,8 +435,13 @@ __device__ __forceinline__ void lean_tables(const uint16_t* sel_e, const float* 
   const int np = T * K;  // <= 64
   const bool live = lane < np;
   const int key = live ? (int)sel_e[lane] * 64 + lane / K : 0x7FFFFFFF;
+  // the lanes' keys eight at a time (lanes past np hold 0x7FFFFFFF, above every live key, so a
+  // whole last group of eight counts right)
   int rank = 0;
-  for (int j = 0; j < np; ++j) rank += __builtin_amdgcn_readlane(key, j) < key;
+  for (int j0 = 0; j0 < np; j0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += __builtin_amdgcn_readlane(key, j0 + u) < key;
+  }
   if (!live) rank = lane;  // the rest keep their places: the ranks stay a permutation
   if (live) {
     b.perm[rank] = lane;
