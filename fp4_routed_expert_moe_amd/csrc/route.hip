@@ -173,7 +173,7 @@ __device__ __forceinline__ void split3(const float4& p, const float4& r, bf16x8 
 }
 
 template <bool STAGED>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits, uint8_t* __restrict__ xq,
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 #pragma unroll
       for (int v = 0; v < 4; ++v) st.w[v] = *reinterpret_cast<const float4*>(wg + kk + 4 * v);
     };
-    auto lstore = [&](int buf, const Stage& st) {
+    auto lstore = [&](int buf, const Stage st) {  // by value: a reference to either stage spilled it
       *reinterpret_cast<uint4*>(&xs[buf][srow][scol]) = st.x[0];
       *reinterpret_cast<uint4*>(&xs[buf][srow][scol + 8]) = st.x[1];
 #pragma unroll
@@ -279,19 +279,28 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
         mma_step(xa, wb);
       }
     };
-    Stage st;
-    gload(st, k_lo);
-    lstore(0, st);
+    // Global loads run two batches ahead: while batch k0 runs from LDS, batch k0 + KBt waits in
+    // registers for the other LDS buffer and batch k0 + 2 KBt is in flight.
+    Stage sa, sb;
+    gload(sa, k_lo);
+    if (k_lo + KBt < k_hi) gload(sb, k_lo + KBt);
+    lstore(0, sa);
     __syncthreads();
-    int buf = 0;
-    for (int k0 = k_lo; k0 < k_hi; k0 += KBt) {
-      const bool more = k0 + KBt < k_hi;
-      if (more) gload(st, k0 + KBt);
+    // two batches a round: LDS buffer 0 holds batch k0 and sb batch k0 + KBt (sa is free), then
+    // buffer 1 holds k0 + KBt and sa k0 + 2 KBt
+    for (int k0 = k_lo; k0 < k_hi; k0 += 2 * KBt) {
+      if (k0 + 2 * KBt < k_hi) gload(sa, k0 + 2 * KBt);
       __builtin_amdgcn_sched_barrier(0);
-      compute(buf, k0);
-      if (more) lstore(buf ^ 1, st);
+      compute(0, k0);
+      if (k0 + KBt >= k_hi) break;
+      lstore(1, sb);
       __syncthreads();
-      buf ^= 1;
+      if (k0 + 3 * KBt < k_hi) gload(sb, k0 + 3 * KBt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, k0 + KBt);
+      if (k0 + 2 * KBt >= k_hi) break;
+      lstore(0, sa);
+      __syncthreads();
     }
   } else {
     // each wave loads its own 32 tokens and 32 experts, four K steps at a time
