@@ -144,7 +144,6 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* x,
 // 32-value step; result lane l, element i -> token 4*(l/16) + i, expert l % 16.
 // ------------------------------------------------------------------------------------
 constexpr int kRouterGemmTile = 64;
-constexpr int kRouterStagedMaxSlices = 4;
 
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {  // (bf16 of a) | (bf16 of b) << 16
   return (a >> 16) | (b & 0xFFFF0000u);
@@ -172,7 +171,6 @@ __device__ __forceinline__ void split3(const float4& p, const float4& r, bf16x8 
   }
 }
 
-template <bool STAGED>
 __global__ __launch_bounds__(256, 2) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           const float* __restrict__ bias,
@@ -230,113 +228,76 @@ __global__ __launch_bounds__(256, 2) void router_gemm_kernel(const uint16_t* __r
         acc[i][j] += hi;
       }
   };
-  if constexpr (STAGED) {
-    // The tile's 64 tokens and 64 experts pass through LDS 64 K values at a time: x as bf16,
-    // W_r split into its three bf16 terms once per workgroup (each wave reads the half it
-    // needs); the next batch's global loads are in flight while this one runs from LDS.
-    constexpr int KBt = 64, PITCH = KBt + 8;  // bf16 per LDS row (16 bytes of padding)
-    __shared__ __align__(16) __bf16 xs[2][kRouterGemmTile][PITCH];
-    __shared__ __align__(16) __bf16 ws3[2][3][kRouterGemmTile][PITCH];
-    // staging: thread t loads 16 K values of tile row t / 4 at column (t % 4) * 16
-    const int srow = threadIdx.x >> 2, scol = (threadIdx.x & 3) * 16;
-    const uint16_t* xg = x + (size_t)min(blockIdx.x * kRouterGemmTile + srow, T - 1) * H;
-    const float* wg = wr + (size_t)min(blockIdx.y * kRouterGemmTile + srow, E - 1) * H;
-    struct Stage {
-      uint4 x[2];
-      float4 w[4];
-    };
-    auto gload = [&](Stage& st, int k0) {
-      const int kk = min(k0 + scol, k_hi - 16);  // past the slice: valid bytes, never used
-      st.x[0] = *reinterpret_cast<const uint4*>(xg + kk);
-      st.x[1] = *reinterpret_cast<const uint4*>(xg + kk + 8);
+  // The tile's 64 tokens and 64 experts pass through LDS 64 K values at a time: x as bf16,
+  // W_r split into its three bf16 terms once per workgroup (each wave reads the half it
+  // needs); the next batch's global loads are in flight while this one runs from LDS.
+  constexpr int KBt = 64, PITCH = KBt + 8;  // bf16 per LDS row (16 bytes of padding)
+  __shared__ __align__(16) __bf16 xs[2][kRouterGemmTile][PITCH];
+  __shared__ __align__(16) __bf16 ws3[2][3][kRouterGemmTile][PITCH];
+  // staging: thread t loads 16 K values of tile row t / 4 at column (t % 4) * 16
+  const int srow = threadIdx.x >> 2, scol = (threadIdx.x & 3) * 16;
+  const uint16_t* xg = x + (size_t)min(blockIdx.x * kRouterGemmTile + srow, T - 1) * H;
+  const float* wg = wr + (size_t)min(blockIdx.y * kRouterGemmTile + srow, E - 1) * H;
+  struct Stage {
+    uint4 x[2];
+    float4 w[4];
+  };
+  auto gload = [&](Stage& st, int k0) {
+    const int kk = min(k0 + scol, k_hi - 16);  // past the slice: valid bytes, never used
+    st.x[0] = *reinterpret_cast<const uint4*>(xg + kk);
+    st.x[1] = *reinterpret_cast<const uint4*>(xg + kk + 8);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) st.w[v] = *reinterpret_cast<const float4*>(wg + kk + 4 * v);
-    };
-    auto lstore = [&](int buf, const Stage st) {  // by value: a reference to either stage spilled it
-      *reinterpret_cast<uint4*>(&xs[buf][srow][scol]) = st.x[0];
-      *reinterpret_cast<uint4*>(&xs[buf][srow][scol + 8]) = st.x[1];
+    for (int v = 0; v < 4; ++v) st.w[v] = *reinterpret_cast<const float4*>(wg + kk + 4 * v);
+  };
+  auto lstore = [&](int buf, const Stage st) {  // by value: a reference to either stage spilled it
+    *reinterpret_cast<uint4*>(&xs[buf][srow][scol]) = st.x[0];
+    *reinterpret_cast<uint4*>(&xs[buf][srow][scol + 8]) = st.x[1];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 t3[3];
-        split3(st.w[2 * h], st.w[2 * h + 1], t3);
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 t3[3];
+      split3(st.w[2 * h], st.w[2 * h + 1], t3);
 #pragma unroll
-        for (int t = 0; t < 3; ++t) *reinterpret_cast<bf16x8*>(&ws3[buf][t][srow][scol + 8 * h]) = t3[t];
-      }
-    };
-    auto compute = [&](int buf, int k0) {
+      for (int t = 0; t < 3; ++t) *reinterpret_cast<bf16x8*>(&ws3[buf][t][srow][scol + 8 * h]) = t3[t];
+    }
+  };
+  auto compute = [&](int buf, int k0) {
 #pragma unroll
-      for (int u = 0; u < KBt / 32; ++u) {
-        if (k0 + 32 * u >= k_hi) break;
-        bf16x8 xa[2], wb[2][3];
+    for (int u = 0; u < KBt / 32; ++u) {
+      if (k0 + 32 * u >= k_hi) break;
+      bf16x8 xa[2], wb[2][3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          xa[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][(wave & 1) * 32 + 16 * i + r][32 * u + 8 * kq]);
+      for (int i = 0; i < 2; ++i)
+        xa[i] = *reinterpret_cast<const bf16x8*>(&xs[buf][(wave & 1) * 32 + 16 * i + r][32 * u + 8 * kq]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int t = 0; t < 3; ++t)
-            wb[j][t] = *reinterpret_cast<const bf16x8*>(&ws3[buf][t][(wave >> 1) * 32 + 16 * j + r][32 * u + 8 * kq]);
-        mma_step(xa, wb);
-      }
-    };
-    // Global loads run two batches ahead: while batch k0 runs from LDS, batch k0 + KBt waits in
-    // registers for the other LDS buffer and batch k0 + 2 KBt is in flight.
-    Stage sa, sb;
-    gload(sa, k_lo);
-    if (k_lo + KBt < k_hi) gload(sb, k_lo + KBt);
+        for (int t = 0; t < 3; ++t)
+          wb[j][t] = *reinterpret_cast<const bf16x8*>(&ws3[buf][t][(wave >> 1) * 32 + 16 * j + r][32 * u + 8 * kq]);
+      mma_step(xa, wb);
+    }
+  };
+  // Global loads run two batches ahead: while batch k0 runs from LDS, batch k0 + KBt waits in
+  // registers for the other LDS buffer and batch k0 + 2 KBt is in flight.
+  Stage sa, sb;
+  gload(sa, k_lo);
+  if (k_lo + KBt < k_hi) gload(sb, k_lo + KBt);
+  lstore(0, sa);
+  __syncthreads();
+  // two batches a round: LDS buffer 0 holds batch k0 and sb batch k0 + KBt (sa is free), then
+  // buffer 1 holds k0 + KBt and sa k0 + 2 KBt
+  for (int k0 = k_lo; k0 < k_hi; k0 += 2 * KBt) {
+    if (k0 + 2 * KBt < k_hi) gload(sa, k0 + 2 * KBt);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, k0);
+    if (k0 + KBt >= k_hi) break;
+    lstore(1, sb);
+    __syncthreads();
+    if (k0 + 3 * KBt < k_hi) gload(sb, k0 + 3 * KBt);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, k0 + KBt);
+    if (k0 + 2 * KBt >= k_hi) break;
     lstore(0, sa);
     __syncthreads();
-    // two batches a round: LDS buffer 0 holds batch k0 and sb batch k0 + KBt (sa is free), then
-    // buffer 1 holds k0 + KBt and sa k0 + 2 KBt
-    for (int k0 = k_lo; k0 < k_hi; k0 += 2 * KBt) {
-      if (k0 + 2 * KBt < k_hi) gload(sa, k0 + 2 * KBt);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0, k0);
-      if (k0 + KBt >= k_hi) break;
-      lstore(1, sb);
-      __syncthreads();
-      if (k0 + 3 * KBt < k_hi) gload(sb, k0 + 3 * KBt);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1, k0 + KBt);
-      if (k0 + 2 * KBt >= k_hi) break;
-      lstore(0, sa);
-      __syncthreads();
-    }
-  } else {
-    // each wave loads its own 32 tokens and 32 experts, four K steps at a time
-    const uint16_t* xa[2];
-    const float* wb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xa[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 8 * kq;
-      wb[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * H + 8 * kq;
-    }
-    constexpr int U = 4;  // 32-value K steps loaded together
-    for (int k0 = k_lo; k0 < k_hi; k0 += 32 * U) {
-      uint4 xr[U][2];
-      float4 wv[U][2][2];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + 32 * u;
-        if (k < k_hi) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            xr[u][i] = *reinterpret_cast<const uint4*>(xa[i] + k);
-            wv[u][i][0] = *reinterpret_cast<const float4*>(wb[i] + k);
-            wv[u][i][1] = *reinterpret_cast<const float4*>(wb[i] + k + 4);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k0 + 32 * u >= k_hi) break;
-        bf16x8 bt[2][3];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) split3(wv[u][j][0], wv[u][j][1], bt[j]);
-        const bf16x8 xv[2] = {__builtin_bit_cast(bf16x8, xr[u][0]), __builtin_bit_cast(bf16x8, xr[u][1])};
-        mma_step(xv, bt);
-      }
-    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -485,10 +446,7 @@ hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* w
   dim3 grid((T + kRouterGemmTile - 1) / kRouterGemmTile, (d.E + kRouterGemmTile - 1) / kRouterGemmTile,
             router_slices(d, T));
   const int tk = timing_begin("router_gemm", s);
-  // operands through LDS once each workgroup has a long K range (few hidden-axis slices);
-  // with many short slices the loads straight to registers start sooner
-  auto kern = grid.z <= kRouterStagedMaxSlices ? router_gemm_kernel<true> : router_gemm_kernel<false>;
-  kern<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, quantize_x ? b.xq : nullptr, b.gmask, T, d.E, d.H);
+  router_gemm_kernel<<<grid, 256, 0, s>>>(x, wr, bias, b.logits, quantize_x ? b.xq : nullptr, b.gmask, T, d.E, d.H);
   timing_end(tk, s);
   return hipGetLastError();
 }
