@@ -700,10 +700,11 @@ def stats_summary(args):
     rows = []
     for f in files:
         with open(f) as fh:
-            rows += [r for r in csv.DictReader(fh) if r["Name"].split("(")[0].split("<")[0].strip().split()[-1]
+            rows += [r for r in csv.DictReader(fh)
+                     if r["Name"].replace("(anonymous namespace)::", "").split("(")[0].split("<")[0].strip().split()[-1]
                      .startswith("moe::")]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0].replace("void ", "").replace("moe::", "").replace("(anonymous namespace)::", "")
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("moe::", "")
         print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
               f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} |")
     if run:
