@@ -254,9 +254,16 @@ inline bool join_fused(const Dims& d, int T) { return route_fused(d, T) && T <= 
 // list; lean: the caller only runs the decode kernels and reads no routing output, so with
 // at most kLeanMaxPicks picks only their tables are built.
 constexpr int kLeanMaxPicks = 64;
+// Byte ranges the routing launch reads ahead (one word per 128-byte line) once its workgroups
+// have published their scores, so that the lines are in the memory-side cache when the expert
+// kernels stream them: the always-active shared expert's weights.
+struct Warm {
+  const uint8_t* p[6];
+  uint32_t bytes[6];
+};
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s,
-                                const JoinArgs* join = nullptr);
+                                const JoinArgs* join = nullptr, const Warm* warm = nullptr);
 hipError_t launch_route_chunked(const Dims& d, const CallBufs& b, int T, hipStream_t s);
 
 // Decode GEMV kernels (gemv.hip): gate/up + SwiGLU into h, then down + the combine into y.

@@ -29,13 +29,33 @@ using RouterTail = TailLayout<1024, kTailScores>;
 // the grouped GEMM's M-tile list; kRouteLean = only the tables the decode kernels read (at
 // most 64 picks).
 // kRouteJoin = first form x from the chained decode's residual (JoinArgs) into the x buffer.
-constexpr int kRouteQuantize = 1, kRouteMTiles = 2, kRouteLean = 4, kRouteJoin = 8;
+// kRouteWarm = the workgroups that are not last then read one word of every 128-byte line of
+// the Warm ranges, one slice each.
+constexpr int kRouteQuantize = 1, kRouteMTiles = 2, kRouteLean = 4, kRouteJoin = 8, kRouteWarm = 16;
+
+// Slice `part` of `parts` of the lines of the Warm ranges: one 4-byte load per line, kept
+// live only through an empty asm statement.
+__device__ __forceinline__ void warm_lines(const Warm& w, int part, int parts) {
+  size_t total = 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) total += w.bytes[i] >> 7;
+  const size_t per = (total + parts - 1) / parts, lo = (size_t)part * per, hi = min(total, lo + per);
+  float acc = 0.f;
+  for (size_t l = lo + threadIdx.x; l < hi; l += kTailThreads) {
+    size_t r = l;
+    int i = 0;
+    while (i < 5 && r >= (w.bytes[i] >> 7)) r -= w.bytes[i++] >> 7;
+    acc += *reinterpret_cast<const float*>(w.p[i] + (r << 7));
+  }
+  asm volatile("" ::"v"(acc));
+}
 
 // x is not __restrict__: with kRouteJoin this launch writes it before reading it.
 __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* x,
                                                              const float* __restrict__ wr,
                                                              const float* __restrict__ bias, CallBufs b, int T,
-                                                             int E, int H, int K, int S, int flags, JoinArgs join) {
+                                                             int E, int H, int K, int S, int flags, JoinArgs join,
+                                                             Warm warm) {
   __shared__ __align__(16) char lds[RouterTail::kBytes];
   const int wave = threadIdx.x >> 6;
   const int grp = wave / kScoreWaves;
@@ -96,6 +116,7 @@ __global__ __launch_bounds__(kTailThreads) void router_kernel(const uint16_t* x,
   __syncthreads();
   if (ticket < total - 1) {
     if (flags & kRouteQuantize) quantize(ticket, total - 1);
+    if (flags & kRouteWarm) warm_lines(warm, ticket, total - 1);
     return;
   }
   if (flags & kRouteLean)
@@ -431,15 +452,17 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(CallBufs b, int T, in
 // ------------------------------------------------------------------------------------
 hipError_t launch_router_logits(const Dims& d, const uint16_t* x, const float* wr, const float* bias,
                                 const CallBufs& b, int T, bool quantize_x, bool mtiles, bool lean, hipStream_t s,
-                                const JoinArgs* join) {
+                                const JoinArgs* join, const Warm* warm) {
   if (join && !join_fused(d, T)) return hipErrorInvalidValue;  // the caller runs the join kernel instead
   if (route_fused(d, T)) {
     dim3 grid((d.E + kRouterEPB - 1) / kRouterEPB, (T + kScoreTT - 1) / kScoreTT);
     const int tk = timing_begin("router_route", s);
     const int flags = (quantize_x ? kRouteQuantize : 0) | (mtiles ? kRouteMTiles : 0) |
-                      (lean && !mtiles && T * d.K <= kLeanMaxPicks ? kRouteLean : 0) | (join ? kRouteJoin : 0);
+                      (lean && !mtiles && T * d.K <= kLeanMaxPicks ? kRouteLean : 0) | (join ? kRouteJoin : 0) |
+                      (warm && grid.x * grid.y > 1 ? kRouteWarm : 0);
     router_kernel<<<grid, kTailThreads, 0, s>>>(x, wr, bias, b, T, d.E, d.H, d.K, d.S, flags,
-                                                join ? *join : JoinArgs{nullptr, nullptr, nullptr, nullptr, 0.f});
+                                                join ? *join : JoinArgs{nullptr, nullptr, nullptr, nullptr, 0.f},
+                                                warm ? *warm : Warm{});
     timing_end(tk, s);
     return hipGetLastError();
   }
