@@ -118,13 +118,15 @@ def traffic_record(kernel, workload):
 
 
 EXTRA_WORKLOADS = ("decode_t8_fp8shared", "prefill_t512", "prefill_t4096_zipf", "stacked_decode_16l",
-                   "chained_decode_16l")
+                   "chained_decode_16l", "decode_pro_t8", "prefill_pro_t512")
 # per extra workload: (steps, warm-up steps, weight sets rotated, token batches rotated).  A
 # prefill call's 3.4 GB of weights is far beyond the 256 MB last-level cache, so two weight sets
 # and four token batches suffice there; the stacked workload is 16 layers by definition.
 EXTRA_SHAPE = {"decode_t8_fp8shared": (200, 20, 16, 64), "prefill_t512": (50, 5, 2, 4),
                "prefill_t4096_zipf": (50, 5, 2, 4), "stacked_decode_16l": (100, 10, 16, 64),
-               "chained_decode_16l": (100, 10, 16, 64)}
+               "chained_decode_16l": (100, 10, 16, 64),
+               # V4 Pro scale: 8.9 GB of experts per layer, so six weight sets (53 GB) for decode
+               "decode_pro_t8": (200, 20, 6, 64), "prefill_pro_t512": (50, 5, 2, 4)}
 
 
 # Partial-residency expert bank workloads: the named layer workload with its experts in pinned host

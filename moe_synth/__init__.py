@@ -91,6 +91,8 @@ WORKLOADS = {
     # one token through 16 V4 Flash MoE layers, each layer's input the RMSNorm of the residual stream
     "chained_decode_16l": Workload("chained_decode_16l", 4096, 256, 6, 1, 2048, 1, layers=16, steps=256,
                                    chained=True),
+    # a 512-token prefill chunk at the V4 Pro scale (same readings as decode_pro_t8)
+    "prefill_pro_t512": Workload("prefill_pro_t512", 7168, 384, 6, 1, 2048, 512),
 }
 _WORKLOAD_IDS = {n: i + 1 for i, n in enumerate(WORKLOADS)}
 

@@ -343,6 +343,14 @@ def test_decode_pro_scale_full_size():
     assert len(sample) == x.shape[0]
 
 
+def test_prefill_pro_scale_full_size():
+    # V4 Pro scale through the grouped GEMM: 512 tokens, hidden 7168, 384 experts (router GEMM over
+    # six 64-expert tiles, top-k over 8 keys per lane); outputs of 16 spread tokens plus the
+    # first, last and M-tile-boundary rows of the three busiest experts
+    got, _, x, sample = _full_size("prefill_pro_t512", spread=16)
+    assert len(sample) >= 16 and got["counts"].sum() == x.shape[0] * 6
+
+
 def test_stacked_decode_16_layers():
     wl = synth.WORKLOADS["stacked_decode_16l"]
     layers, routers = [], []
