@@ -175,7 +175,11 @@ int32_t moe_route(const moe_layer* layer, const uint16_t* x, int32_t tokens,
  * (bf16 bit patterns, device, [T][H]).  If `route` is not NULL its five buffers receive
  * the routing (as moe_route); if NULL no routing output is produced, and a small batch then
  * builds only the grouping its own expert kernels read (the output is the same bit for bit).
- * Asynchronous on `stream`; T = 0 is a no-op; no host synchronisation. */
+ * Asynchronous on `stream`; T = 0 is a no-op; no host synchronisation.  Device-side failures
+ * are not reported by the return value: a fault surfaces at the caller's next synchronisation,
+ * and the small-batch combine, which waits for the other workgroups' rows with a bounded poll
+ * (every one of them is dispatched before the combining workgroup, so the bound is never
+ * reached in a launch that runs), would leave NaN in the outputs it gave up on. */
 int32_t moe_forward(const moe_layer* layer, const uint16_t* x, int32_t tokens, float* y,
                     const moe_route_out* route, void* workspace, uint64_t workspace_bytes,
                     void* stream);
