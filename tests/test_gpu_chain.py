@@ -101,7 +101,8 @@ def _small_chain(seed, n_layers, hidden=256, experts=8, top_k=2, inter=128, shar
     return layers, refs, gammas
 
 
-@pytest.mark.parametrize("n_layers,tokens", [(1, 3), (3, 5), (4, 40)])
+# 16 tokens: the largest batch whose join runs inside the routing launch; 17: the join kernel
+@pytest.mark.parametrize("n_layers,tokens", [(1, 3), (3, 5), (2, 16), (2, 17), (4, 40)])
 def test_small_chain_teacher_forced(n_layers, tokens):
     from fp4_routed_expert_moe_amd import MoeChain
     layers, refs, gammas = _small_chain(20 + n_layers, n_layers)
