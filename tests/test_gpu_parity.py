@@ -110,6 +110,8 @@ def test_identity_experts_closed_form_on_gpu():
     (14, 224, 256, 3, 1, 64, 2048), # router GEMM through LDS, slices of 32 and 64 values
     (15, 320, 8, 3, 1, 160, 2100),  # ~790 rows an expert: a dozen M-tiles each, ragged last tiles, K tails
     (16, 256, 12, 5, 0, 288, 2049), # no shared expert; a group's last M-tile short
+    (17, 64, 1, 1, 1, 32, 5),       # a single routed expert (every weight 1.0)
+    (18, 160, 3, 3, 1, 96, 130),    # k = E = 3 through the router GEMM, H and I not multiples of 128
 ])
 def test_random_shapes_both_paths(case):
     seed, hidden, experts, k, shared, inter, tokens = case
