@@ -169,7 +169,8 @@ def main():
         for name in EXTRA_WORKLOADS:
             steps, warm, nl, nb = EXTRA_SHAPE[name]
             r = measure(synth.WORKLOADS[name], steps, warm, nl, nb, 0)
-            extra[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+            extra[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "step_us_events", "steps", "warmup",
+                                             "config",
                                              "weight_GBps", "weight_frac_hbm", "tflops",
                                              "tflops_frac_bf16", "active_groups_per_call", "layer_calls_per_step",
                                              "roofline", "kernels")}
@@ -196,7 +197,8 @@ def main():
                        "e4m3 terms (12 bits) in decode, two (8 bits, bf16's precision) in prefill"),
         "data": "synthetic (seeded; random-init weights at the workload's DeepSeek V4 expert shapes)",
     }
-    out.update({k: res[k] for k in ("config", "weight_GBps", "weight_frac_hbm", "tflops", "tflops_frac_bf16",
+    out.update({k: res[k] for k in ("step_us_events", "config", "weight_GBps", "weight_frac_hbm", "tflops",
+                                    "tflops_frac_bf16",
                                     "active_groups_per_call", "layer_calls_per_step", "roofline", "kernels")})
     out["cpu_baseline"] = cpu
     if extra:
@@ -328,6 +330,19 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     tokens_per_s = steps * T / elapsed
     progress(f"{wl.name}: {steps} timed steps, {ms_per_step:.4f} ms per step")
 
+    # the spread of single steps: HIP events around each of up to 100 more steps on the launch
+    # stream (outside the timed region above)
+    n_ev = min(steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(steps + i)
+        e1.record()
+    torch.cuda.synchronize()
+    step_us = np.array([1e3 * e0.elapsed_time(e1) for e0, e1 in evs])
+    step_pct = {"p10": float(np.percentile(step_us, 10)), "p50": float(np.percentile(step_us, 50)),
+                "p90": float(np.percentile(step_us, 90)), "steps": n_ev}
+
     # per-kernel HIP-event timing over a second pass of the same steps
     moe.timing_reset()
     moe.timing_enable(True)
@@ -378,6 +393,7 @@ def measure(wl, steps, warmup, layers_rotated, batches, copy_probe_mib):
     kernels = {k: dict(launches=v[0], avg_us=1e3 * v[1] / max(v[0], 1)) for k, v in kt.items()}
     res = {
         "value": tokens_per_s, "unit": "tokens/s", "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup,
+        "step_us_events": step_pct,
         "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
                    "shared": wl.shared, "shared_format": "fp8_e4m3_128x128" if wl.shared_fp8 else "fp4_e2m1_e8m0_32",
                    "inter": wl.inter, "tokens": T, "layers_rotated": nl,
