@@ -18,6 +18,10 @@
 //   The activation tile of each 128-value K step is staged in LDS (double-buffered) and read
 //   by all waves; 16-row subtiles past the group's last row are skipped.  Loads run two
 //   steps ahead of the matrix work, and two workgroups share a CU.
+// * LDS rows are 128 bytes with their 16-byte chunks permuted by row (chunk c of row r sits
+//   at c ^ (r & 7)): both the staging stores (four threads per row, two chunks each) and the
+//   matrix-operand reads (16 rows, one chunk each) then hit distinct banks, where an unpermuted
+//   160-byte pitch left the stores with two-way conflicts.
 // * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes the M-tiles 8i + x, every
 //   column slice of each in turn: an M-tile's activation rows are fetched into one XCD's L2
 //   only, and with small batches (one M-tile per expert) the XCDs stream different experts.
@@ -42,7 +46,7 @@ struct GemmShape {
   static constexpr int OCC = OCC_;
   static constexpr int PK = 128 * PU;      // K values per step
   static constexpr int PKB = PK / 32;      // K blocks per step
-  static constexpr int ALD = PK + 32;      // LDS row pitch of the activation tile (bytes; +32 measured faster than +16)
+  static constexpr int ALD = PK;           // LDS row pitch of the activation tile (bytes; chunks swizzled)
   static constexpr int CH = 128 / TPR / 16;  // 16-byte chunks per thread, term and K chunk
   static constexpr int PN = NW * CT * 16;    // output columns per workgroup
   static_assert(TPR == 4 || TPR == 8, "workgroup shape");
@@ -120,11 +124,11 @@ template <class SH>
 __device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int r, int p) {
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
-    const int b = 128 * u + 16 * SH::CH * p;
 #pragma unroll
     for (int j = 0; j < SH::CH; ++j) {
-      *reinterpret_cast<i32x4*>(&t.v[0][r][b + 16 * j]) = st.c[u][0][j];
-      *reinterpret_cast<i32x4*>(&t.v[1][r][b + 16 * j]) = st.c[u][1][j];
+      const int b = 128 * u + 16 * ((SH::CH * p + j) ^ (r & 7));
+      *reinterpret_cast<i32x4*>(&t.v[0][r][b]) = st.c[u][0][j];
+      *reinterpret_cast<i32x4*>(&t.v[1][r][b]) = st.c[u][1][j];
     }
     if (p < 4) t.s[r][4 * u + p] = (uint8_t)st.s[u];
   }
@@ -188,14 +192,20 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& 
     for (int mtx = 0; mtx < NM; ++mtx) sb[mtx] = SH::CT == 4 ? f.s[u][mtx] : (int)((uint32_t)f.s[u][mtx] >> sh);
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
-      if (rs >= nsub) break;
+      // Down (one matrix): each subtile's LDS reads just before its matrix work.  Gate/up:
+      // the reads of all subtiles first (the compiler hoists them out of this form), which
+      // measured faster for its eight products per subtile.
+      if (rs >= nsub) {
+        if constexpr (NM == 1) continue;
+        else break;
+      }
       const int r = 16 * rs + m;
-      const int b = 128 * u + 16 * q;
+      const int b = 128 * u + 16 * (q ^ (m & 7)), b2 = b ^ 64;  // (r & 7 == m & 7)
       const i32x8 a0 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[0][r][b]),
-                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b + 64]), 0, 1, 2, 3, 4,
+                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b2]), 0, 1, 2, 3, 4,
                                                5, 6, 7);
       const i32x8 a1 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[1][r][b]),
-                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b + 64]), 0, 1, 2, 3, 4,
+                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b2]), 0, 1, 2, 3, 4,
                                                5, 6, 7);
       const int sa = t.s[r][4 * u + q];
 #pragma unroll
@@ -265,12 +275,12 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
       const int r = 16 * rs + m;
-      const int b = 128 * u + 16 * q;
+      const int b = 128 * u + 16 * (q ^ (m & 7)), b2 = b ^ 64;  // (r & 7 == m & 7)
       const i32x8 a0 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[0][r][b]),
-                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b + 64]), 0, 1, 2, 3, 4,
+                                               *reinterpret_cast<const i32x4*>(&t.v[0][r][b2]), 0, 1, 2, 3, 4,
                                                5, 6, 7);
       const i32x8 a1 = __builtin_shufflevector(*reinterpret_cast<const i32x4*>(&t.v[1][r][b]),
-                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b + 64]), 0, 1, 2, 3, 4,
+                                               *reinterpret_cast<const i32x4*>(&t.v[1][r][b2]), 0, 1, 2, 3, 4,
                                                5, 6, 7);
       const int sa = t.s[r][4 * u + q];
 #pragma unroll
