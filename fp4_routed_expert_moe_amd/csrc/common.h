@@ -92,7 +92,6 @@ inline CtrlLayout ctrl_layout(int H, int E, int S, int I) {
 constexpr int kWave = 64;
 constexpr int kChunk = 64;        // tokens per routing chunk (one bit per token in a 64-bit mask)
 constexpr int kGemmBM = 64;       // grouped-GEMM rows per M-tile
-constexpr int kGemmBN = 64;       // grouped-GEMM output columns per workgroup
 
 // ---- exact FP8 (e4m3) term splits for the block-scaled MFMA ------------------------
 // A 32-value block v is written as S * (t0 + t1/16 + t2/256 + ...), each t an e4m3 value, with

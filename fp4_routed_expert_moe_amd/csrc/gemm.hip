@@ -12,16 +12,19 @@
 //   (about 8 significant bits, the precision of bf16) written by the gate/up epilogue.  One
 //   MFMA per term, all accumulating in fp32.
 // * A workgroup takes one M-tile (64 grouped rows of one group, from the device-built M-tile
-//   list) and a slice of output columns.  Each wave owns a column slice of all 64 rows: 64 columns
-//   (4 x 4 16x16 tiles) in the down kernel, 32 columns for gate and up at once in the gate/up
-//   kernel (eight waves), so SwiGLU stays in registers.
-//   The activation tile of each 128-value K step is staged in LDS (double-buffered) and read
-//   by all waves; 16-row subtiles past the group's last row are skipped.  Loads run two
-//   steps ahead of the matrix work, and two workgroups share a CU.
-// * LDS rows are 128 bytes with their 16-byte chunks permuted by row (chunk c of row r sits
-//   at c ^ (r & 7)): both the staging stores (four threads per row, two chunks each) and the
-//   matrix-operand reads (16 rows, one chunk each) then hit distinct banks, where an unpermuted
-//   160-byte pitch left the stores with two-way conflicts.
+//   list) and a slice of output columns; four waves each own a column slice of all 64 rows:
+//   64 columns (4 16x16 tiles) in the down kernel; 32 or 64 columns of gate and of up at once
+//   in the gate/up kernel (so SwiGLU stays in registers), the wider slice when the groups are
+//   large enough to keep the matrix cores busy (it halves the LDS reads per MFMA but has one
+//   weight step in flight instead of two).  16-row subtiles past the group's last row are
+//   skipped.
+// * The activation tile of each 128-value K step goes straight from memory into LDS (buffer
+//   loads with the LDS flag, no registers), three buffers deep: while step s runs on the
+//   matrix cores, step s+2's tile streams in.  LDS rows are 128 bytes with their 16-byte
+//   chunks permuted by row (chunk c of row r sits at c ^ (r & 7)), which keeps the matrix-
+//   operand reads (16 rows, one chunk each) free of bank conflicts.  Each step ends with one
+//   barrier, preceded by a wait for this wave's loads of the next tile only (counted in
+//   vector-memory instructions, not a full drain).
 // * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes the M-tiles 8i + x, every
 //   column slice of each in turn: an M-tile's activation rows are fetched into one XCD's L2
 //   only, and with small batches (one M-tile per expert) the XCDs stream different experts.
@@ -35,34 +38,33 @@ constexpr int kPM = kGemmBM;      // rows per M-tile (64)
 
 // Per-kernel shape: NW waves of CT 16-column tiles each (PN = NW * CT * 16 columns per
 // workgroup); PU = 128-value MFMA K chunks per step; OCC = workgroups per CU the register
-// budget targets.
-template <int NW_, int CT_, int PU_, int OCC_>
+// budget targets; BS = weight-operand register stages (their loads run BS - 1 steps ahead).
+template <int NW_, int CT_, int PU_, int OCC_, int BS_>
 struct GemmShape {
   static constexpr int NW = NW_;
   static constexpr int CT = CT_;
   static constexpr int NTH = 64 * NW;      // threads
-  static constexpr int TPR = NTH / kPM;    // threads staging one activation row
   static constexpr int PU = PU_;
   static constexpr int OCC = OCC_;
+  static constexpr int BS = BS_;
   static constexpr int PK = 128 * PU;      // K values per step
   static constexpr int PKB = PK / 32;      // K blocks per step
-  static constexpr int ALD = PK;           // LDS row pitch of the activation tile (bytes; chunks swizzled)
-  static constexpr int CH = 128 / TPR / 16;  // 16-byte chunks per thread, term and K chunk
-  static constexpr int PN = NW * CT * 16;    // output columns per workgroup
-  static_assert(TPR == 4 || TPR == 8, "workgroup shape");
+  static constexpr int ALD = PK;           // LDS row pitch of the activation tile (bytes; chunks permuted)
+  static constexpr int PN = NW * CT * 16;  // output columns per workgroup
 };
-#ifndef MOE_GU_SHAPE
-#define MOE_GU_SHAPE 4, 2, 1, 2
-#endif
-#ifndef MOE_DN_SHAPE
-#define MOE_DN_SHAPE 4, 4, 1, 2
-#endif
-using GateUpShape = GemmShape<MOE_GU_SHAPE>;
-using DownShape = GemmShape<MOE_DN_SHAPE>;
+using GateUpShape = GemmShape<4, 2, 1, 2, 3>;      // 32 columns of gate and of up per wave
+using GateUpWideShape = GemmShape<4, 4, 1, 2, 2>;  // 64 columns of each (256 VGPRs, no spill)
+using DownShape = GemmShape<4, 4, 1, 3, 3>;        // three workgroups per CU (164 VGPRs)
 // The FP8 shared expert's kernels: the same tiles at one workgroup per CU (its weight operands
 // are twice the FP4 ones' registers)
-using GateUpShape8 = GemmShape<GateUpShape::NW, GateUpShape::CT, GateUpShape::PU, 1>;
-using DownShape8 = GemmShape<DownShape::NW, DownShape::CT, DownShape::PU, 1>;
+using GateUpShape8 = GemmShape<4, 2, 1, 1, 3>;
+using DownShape8 = GemmShape<4, 4, 1, 1, 3>;
+// Gate/up takes the wide column slices from this many grouped rows per group on average (the
+// measured crossing point at H 4096, I 2048 lies between 30 and 45 rows per group).
+constexpr int kWideRowsPerGroup = 40;
+inline bool gateup_wide(const Dims& d, int T) {
+  return (long long)T * (d.K + d.S) >= (long long)kWideRowsPerGroup * d.G;
+}
 
 template <class SH>
 struct ATile {                    // one K step of the activation tile
@@ -76,62 +78,50 @@ struct ARows {
   const uint8_t* lo;
   const uint8_t* sc;
   int K;
+  int rows;
 };
 
-// Activation K blocks past the end of K (only in the last step when K % PK != 0) read a valid
-// part of the row instead, with scale byte 4; the weights there read as zero codes with scale
-// byte 0, so every such product is 0, and term 1's scale (byte - 4) stays >= 0.
-constexpr uint32_t kTailScaleA = 4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Thread t stages bytes [p*B, p*B + B) (B = 128/TPR, p = t % TPR) of each 128-value chunk u of
-// a K step of tile row t/TPR, both terms, and threads p < 4 the scale of K block 4u + p.
-// Rows past the group's end stage a copy of the tile's first row (their results are dropped).
-template <class SH>
-struct AStage {
-  i32x4 c[SH::PU][2][SH::CH];
-  uint32_t s[SH::PU];
+// The activation tile is loaded straight into LDS (buffer loads with the LDS flag): one such
+// load fills 1 KB, lane l writing bytes 16l..16l+15, i.e. 8 tile rows of one term, lane l
+// covering physical chunk l % 8 of row l / 8.  Wave w fills rows 16w..16w+15 of both terms;
+// since physical chunk p of row r holds logical chunk p ^ (r & 7), lane l fetches logical
+// chunk (l % 8) ^ (l / 8) of its rows 16w + l/8 and 16w + 8 + l/8.  Wave 0 also loads the 64
+// rows' scale dwords of the step (lane l: row l).  Chunks past K in the last step (K % 128
+// != 0) read the row's last 16 bytes instead; the scale rows are padded to whole steps with
+// byte 127 and the weights there read as zero codes, so those products are 0.
+struct ADma {
+  __amdgpu_buffer_rsrc_t hi, lo, sc;
+  int ra, rb;   // byte offsets of this lane's two rows in a term plane
+  int rs;       // wave 0: byte offset of row `lane`'s scales
+  int lc16;     // 16 * logical chunk
 };
-struct APtr {
-  const uint8_t* hi;   // this thread's bytes of its row at K step 0
-  const uint8_t* lo;
-  const uint8_t* sc;   // scale of block p at step 0
-};
 template <class SH>
-__device__ __forceinline__ AStage<SH> a_fetch(const APtr& ap, int K, int step, int p) {
-  AStage<SH> st;
-  const int KB = K >> 5;
-  const bool tail = (step + 1) * SH::PK > K;  // uniform
-#pragma unroll
-  for (int u = 0; u < SH::PU; ++u) {
-    int off = step * SH::PK + 128 * u;  // chunk start (uniform); this thread adds 16*CH*p
-    int blk = step * SH::PKB + 4 * u;   // first block of the chunk (uniform); this thread's is blk + p
-    bool sok = true;
-    if (tail) {
-      if (off + 16 * SH::CH * p >= K) off = K - 16 * SH::CH * (p + 1);  // a valid part of the row
-      sok = blk + p < KB;
-      if (!sok) blk = KB - 1 - p;
-    }
-#pragma unroll
-    for (int j = 0; j < SH::CH; ++j) {
-      st.c[u][0][j] = *reinterpret_cast<const i32x4*>(ap.hi + off + 16 * j);
-      st.c[u][1][j] = *reinterpret_cast<const i32x4*>(ap.lo + off + 16 * j);
-    }
-    st.s[u] = p < 4 ? (sok ? (uint32_t)ap.sc[blk] : kTailScaleA) : 127u;
-  }
-  return st;
+__device__ __forceinline__ void a_dma(ATile<SH>& t, const ADma& d, int K, int step, int wave) {
+  int off = 128 * step + d.lc16;
+  if (off >= K) off = K - 16;
+  lds_u8* base = (lds_u8*)(&t);
+  lds_u8* p0 = base + 2048 * wave;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.hi, p0, 16, d.ra + off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.hi, p0 + 1024, 16, d.rb + off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.lo, p0 + kPM * 128, 16, d.ra + off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.lo, p0 + kPM * 128 + 1024, 16, d.rb + off, 0, 0, 0);
+  if (wave == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.sc, base + 2 * kPM * 128, 4, d.rs + 4 * step, 0, 0, 0);
 }
-template <class SH>
-__device__ __forceinline__ void a_store(ATile<SH>& t, const AStage<SH>& st, int r, int p) {
-#pragma unroll
-  for (int u = 0; u < SH::PU; ++u) {
-#pragma unroll
-    for (int j = 0; j < SH::CH; ++j) {
-      const int b = 128 * u + 16 * ((SH::CH * p + j) ^ (r & 7));
-      *reinterpret_cast<i32x4*>(&t.v[0][r][b]) = st.c[u][0][j];
-      *reinterpret_cast<i32x4*>(&t.v[1][r][b]) = st.c[u][1][j];
-    }
-    if (p < 4) t.s[r][4 * u + p] = (uint8_t)st.s[u];
-  }
+// Keeps the compiler from moving memory accesses across this point: the waits below count
+// vector-memory instructions in issue order.  (The weight pointers reach the kernel without
+// __restrict__ for the same reason: loads the compiler may treat as reading invariant memory
+// can be moved across such a point.)
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
+// Wait until this wave's tile loads issued before the last kNewer vector-memory instructions
+// are done, and for its LDS reads, then meet the other waves: the tile those loads filled is
+// then complete for every wave, and every wave's reads of the tile being refilled next are over.
+template <int kNewer>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(kNewer < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kNewer) : "memory");
 }
 
 // Weight operands of one wave for one K step: PU chunks x NM matrices x CT column tiles.
@@ -196,7 +186,7 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag<SH, NM>& 
       // the reads of all subtiles first (the compiler hoists them out of this form), which
       // measured faster for its eight products per subtile.
       if (rs >= nsub) {
-        if constexpr (NM == 1) continue;
+        if constexpr (NM == 1 || SH::CT == 4) continue;
         else break;
       }
       const int r = 16 * rs + m;
@@ -309,15 +299,16 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
 // (an expert bank running one refill group of experts per launch).
 template <bool GATEUP, class SH, bool FP8 = false>
 __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
-    ARows a, const uint8_t* __restrict__ c0p, const uint8_t* __restrict__ s0p, const uint8_t* __restrict__ c1p,
-    const uint8_t* __restrict__ s1p, const float* __restrict__ f0p, const float* __restrict__ f1p,
+    ARows a, const uint8_t* c0p, const uint8_t* s0p, const uint8_t* c1p, const uint8_t* s1p,
+    const float* __restrict__ f0p, const float* __restrict__ f1p,
     const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
     const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, const int32_t* __restrict__ slot_of,
     uint8_t* __restrict__ h8, float* __restrict__ staging, int routed_only, float routed_scale, int T, int k, int N,
     int R, int NT) {
   constexpr int NM = GATEUP ? 2 : 1;
-  __shared__ ATile<SH> tile[2];
+  static_assert(SH::PU == 1 && SH::NW == 4, "tile loads: 4 waves x 16 rows, one 128-value chunk per step");
+  __shared__ ATile<SH> tile[3];
   // XCD x (= b % 8) takes the M-tiles mt = 8i + x, all NT column slices of each
   const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
   const int mt = (jj / NT) * 8 + xcd + (FP8 ? info[2] : 0), nt = jj % NT;
@@ -335,13 +326,25 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   const int KB = a.K >> 5;
   const int nsteps = (a.K + SH::PK - 1) / SH::PK;
 
-  // the activation row this thread stages (rows past the group repeat the tile's first row)
-  const int lr = tid / SH::TPR, lp = tid % SH::TPR;
-  const int srow = GATEUP ? row_token(perm, r0 + min(lr, nrows - 1) * (lr < nrows), tk, k) : r0 + lr * (lr < nrows);
-  APtr ap;
-  ap.hi = a.hi + (size_t)srow * a.K + 16 * SH::CH * lp;
-  ap.lo = a.lo + (size_t)srow * a.K + 16 * SH::CH * lp;
-  ap.sc = a.sc + (size_t)srow * kb_pad(a.K) + lp;
+  // this lane's tile rows for the loads (rows past the group repeat the tile's first row)
+  ADma ad;
+  {
+    auto srow_of = [&](int lr) {
+      const int gr = r0 + (lr < nrows ? lr : 0);
+      return GATEUP ? row_token(perm, gr, tk, k) : gr;
+    };
+    const int la = 16 * wave + (lane >> 3);
+    ad.ra = srow_of(la) * a.K;
+    ad.rb = srow_of(la + 8) * a.K;
+    ad.rs = wave == 0 ? srow_of(lane) * kb_pad(a.K) : 0;
+    ad.lc16 = 16 * ((lane & 7) ^ (lane >> 3));
+    // (sizes through readfirstlane: the descriptors must stay in scalar registers)
+    const int plane = __builtin_amdgcn_readfirstlane(a.rows * a.K);
+    const int scb = __builtin_amdgcn_readfirstlane(a.rows * kb_pad(a.K));
+    ad.hi = __builtin_amdgcn_make_buffer_rsrc((void*)a.hi, (short)0, plane, kBufferFlags);
+    ad.lo = __builtin_amdgcn_make_buffer_rsrc((void*)a.lo, (short)0, plane, kBufferFlags);
+    ad.sc = __builtin_amdgcn_make_buffer_rsrc((void*)a.sc, (short)0, scb, kBufferFlags);
+  }
 
   // this wave's weight columns (columns past N read other bytes of the group or zeros; their
   // results are not stored)
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     bs.voff = (n0 + m) * 128 + 16 * q;
   } else {
     const uint8_t* scales[2] = {s0p, s1p};
-    const int slab = (int)scale_slab_bytes(N, a.K);
+    const int slab = __builtin_amdgcn_readfirstlane((int)scale_slab_bytes(N, a.K));
 #pragma unroll
     for (int mtx = 0; mtx < NM; ++mtx) {
       bs.c[mtx] = __builtin_amdgcn_make_buffer_rsrc((void*)(codes[mtx] + (size_t)gw * KB * N * 16), (short)0,
@@ -385,38 +388,57 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
 #pragma unroll
       for (int c = 0; c < SH::CT; ++c) acc[mtx][rs][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Three-deep pipeline: while step s runs on the matrix cores, the activation rows of step
-  // s+2 and the weight operands of step s+2 are in flight, and step s+1's rows (loaded one
-  // step earlier) go from registers into the other LDS buffer.
-  AStage<SH> ast[2];
-  BF fb[3];
-  // The loads run ahead unconditionally: past the last step the activation rows repeat the
-  // last step (cache hits) and the weights read zeros without memory traffic, so no wait
-  // in the loop has to assume a missing load.
+  // Pipeline: while step s runs on the matrix cores, the activation tile of step s+2 streams
+  // into the third LDS buffer and the weight operands of step s+BS-1 into registers.  Per
+  // step a wave issues 4 tile loads (wave 0: 5), then NB weight loads (FP4: NM * (CT + 1);
+  // FP8 more), so the tile of step s+1 is complete once at most 2 NB + 4 newer loads are
+  // outstanding (wave 0 waits for one more than it needs).
+  constexpr int kBS = SH::BS;
+  static_assert(kBS == 2 || kBS == 3, "weight stages");
+  constexpr int NB = NM * (SH::CT + 1);
+  constexpr int kNewer = 2 * NB + 4;
+  BF fb[kBS];
+  // The loads run ahead unconditionally: past the last step the tile loads repeat the last
+  // step (cache hits) and the weights read zeros without memory traffic.
   const int last = nsteps - 1;
-  a_store<SH>(tile[0], a_fetch<SH>(ap, a.K, 0, lp), lr, lp);
+  a_dma<SH>(tile[0], ad, a.K, 0, wave);
+  mem_order();
   b_fetch(fb[0], bs, N, KB, 0, q);
-  ast[1] = a_fetch<SH>(ap, a.K, min(1, last), lp);
-  b_fetch(fb[1], bs, N, KB, 1, q);
-  __syncthreads();
-  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& tn, AStage<SH>& a_next, AStage<SH>& a_far, BF& fc,
-                  BF& f_far) -> bool {
-    a_far = a_fetch<SH>(ap, a.K, min(s + 2, last), lp);
-    b_fetch(f_far, bs, N, KB, s + 2, q);
-    k_step(tc, fc, acc, nsub, m, q, sh);
-    const bool more = s + 1 < nsteps;
-    if (more) a_store<SH>(tn, a_next, lr, lp);
-    __syncthreads();
-    return more;
-  };
-  for (int s = 0; s < nsteps; s += 6) {
-    if (!step(s + 0, tile[0], tile[1], ast[1], ast[0], fb[0], fb[2])) break;
-    if (!step(s + 1, tile[1], tile[0], ast[0], ast[1], fb[1], fb[0])) break;
-    if (!step(s + 2, tile[0], tile[1], ast[1], ast[0], fb[2], fb[1])) break;
-    if (!step(s + 3, tile[1], tile[0], ast[0], ast[1], fb[0], fb[2])) break;
-    if (!step(s + 4, tile[0], tile[1], ast[1], ast[0], fb[1], fb[0])) break;
-    if (!step(s + 5, tile[1], tile[0], ast[0], ast[1], fb[2], fb[1])) break;
+  mem_order();
+  a_dma<SH>(tile[1], ad, a.K, min(1, last), wave);
+  if constexpr (kBS == 3) {
+    mem_order();
+    b_fetch(fb[1], bs, N, KB, 1, q);
+    tile_barrier<kNewer>();
+  } else {
+    tile_barrier<NB + 4>();
   }
+  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& t_far, BF& fc, BF& f_far) -> bool {
+    a_dma<SH>(t_far, ad, a.K, min(s + 2, last), wave);
+    mem_order();
+    b_fetch(f_far, bs, N, KB, s + kBS - 1, q);
+    k_step(tc, fc, acc, nsub, m, q, sh);
+    tile_barrier<kNewer>();
+    return s + 1 < nsteps;
+  };
+  if constexpr (kBS == 3) {
+    for (int s = 0; s < nsteps; s += 3) {
+      if (!step(s + 0, tile[0], tile[2], fb[0], fb[2])) break;
+      if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
+      if (!step(s + 2, tile[2], tile[1], fb[2], fb[1])) break;
+    }
+  } else {
+    for (int s = 0; s < nsteps; s += 6) {
+      if (!step(s + 0, tile[0], tile[2], fb[0], fb[1])) break;
+      if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
+      if (!step(s + 2, tile[2], tile[1], fb[0], fb[1])) break;
+      if (!step(s + 3, tile[0], tile[2], fb[1], fb[0])) break;
+      if (!step(s + 4, tile[1], tile[0], fb[0], fb[1])) break;
+      if (!step(s + 5, tile[2], tile[1], fb[1], fb[0])) break;
+    }
+  }
+  // no tile load may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue ----
   if constexpr (GATEUP) {
@@ -490,20 +512,31 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
-                              int T, int mt_bound, hipStream_t s, const int32_t* slot_of) {
-  (void)x;
-  const int NT = (d.I + GateUpShape::PN - 1) / GateUpShape::PN;
+template <class SH>
+static void gateup_fp4(const Dims& d, const moe_layer_desc& w, const CallBufs& b, const ARows& a, int T,
+                       int mt_bound, hipStream_t s, const int32_t* slot_of) {
+  const int NT = (d.I + SH::PN - 1) / SH::PN;
   const int R = T * (d.K + d.S);
-  const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H};
-  const int tk = timing_begin("gemm_gateup", s);
-  gemm_f8f4_kernel<true, GateUpShape><<<(mt_bound + 7) / 8 * 8 * NT, GateUpShape::NTH, 0, s>>>(
+  gemm_f8f4_kernel<true, SH><<<(mt_bound + 7) / 8 * 8 * NT, SH::NTH, 0, s>>>(
       a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr, b.perm, b.w, b.info, b.mt_group,
       b.mt_row0, b.grp_row0, b.grp_rows, slot_of, static_cast<uint8_t*>(b.h), nullptr, d.fp8_shared, 1.0f, T, d.K,
       d.I, R, NT);
+}
+
+hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
+                              int T, int mt_bound, hipStream_t s, const int32_t* slot_of) {
+  (void)x;
+  const ARows a{b.xq, b.xq + (size_t)T * d.H, b.xq + (size_t)2 * T * d.H, d.H, T};
+  const int tk = timing_begin("gemm_gateup", s);
+  if (gateup_wide(d, T))
+    gateup_fp4<GateUpWideShape>(d, w, b, a, T, mt_bound, s, slot_of);
+  else
+    gateup_fp4<GateUpShape>(d, w, b, a, T, mt_bound, s, slot_of);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.fp8_shared) return e;
+  const int NT = (d.I + GateUpShape8::PN - 1) / GateUpShape8::PN;
+  const int R = T * (d.K + d.S);
   const int mts = (T + kGemmBM - 1) / kGemmBM;  // the shared expert's M-tiles
   const int tk8 = timing_begin("gemm_gateup_fp8", s);
   gemm_f8f4_kernel<true, GateUpShape8, true><<<(mts + 7) / 8 * 8 * NT, GateUpShape8::NTH, 0, s>>>(
@@ -519,7 +552,7 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const int NT = (d.H + DownShape::PN - 1) / DownShape::PN;
   const int R = T * (d.K + d.S);
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
-  const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I};
+  const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I, R};
   const int tk = timing_begin("gemm_down", s);
   gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(
       a, w.down_codes, w.down_scales, w.down_codes, w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.info,
