@@ -286,6 +286,33 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
   }
 }
 
+// DPP moves within a lane quad / a 16-lane row (every lane active).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+// max of v over the 16 lanes of this lane's row
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_mov<kRowHalfMirror>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp_mov<kRowMirror>(__float_as_uint(v))));
+}
+// 4 x 4 byte transpose within a lane quad: lane u of the quad holds byte i = element (i, u)
+// and gets byte c = element (u, c).  Two exchange steps: bytes with the neighbour lane, then
+// 16-bit halves with the lane two over.
+__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t w, int u) {
+  const uint32_t p = dpp_mov<kQuadXor1>(w);
+  const uint32_t n = (u & 1) ? (((p >> 8) & 0x00FF00FFu) | (w & 0xFF00FF00u))
+                             : ((w & 0x00FF00FFu) | ((p & 0x00FF00FFu) << 8));
+  const uint32_t p2 = dpp_mov<kQuadXor2>(n);
+  return (u & 2) ? ((p2 >> 16) | (n & 0xFFFF0000u)) : ((n & 0xFFFFu) | (p2 << 16));
+}
+
 // ------------------------------------------------------------------------------------
 // GATEUP: h[r][n] = silu(x_t(r) . Wg[n]) * (x_t(r) . Wu[n]) as 2 FP8 terms + e8m0 per 32
 //         (h8 = [2][R][I] bytes then [R][kb_pad(I)] scales).
@@ -442,46 +469,77 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
 
   // ---- epilogue ----
   if constexpr (GATEUP) {
-    uint8_t* h_lo = h8 + (size_t)R * N;
+    // h leaves through LDS in 16-byte row chunks.  A lane holds column m of rows 4q..4q+3
+    // of each 16x16 tile; it packs those four bytes into a dword, a byte transpose within the
+    // lane quad turns that into columns 4(m/4)..+3 of row 4q + m%4, and those dwords go to an
+    // LDS copy of the workgroup's h rows.  The tile buffers are free once every wave's last
+    // tile loads have landed and every wave is past its last barrier.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    constexpr int EPL = SH::PN + 16;  // LDS row pitch of the staged h (bytes; +16: no bank conflicts)
+    static_assert(2 * kPM * EPL <= (int)sizeof(tile), "staged h fits the tile buffers");
+    uint8_t* hl = reinterpret_cast<uint8_t*>(&tile[0]);
     uint8_t* hs = h8 + (size_t)2 * R * N;
+    const int u = m & 3;
+    const int lds0 = (4 * q + u) * EPL + wave * 16 * SH::CT + 4 * (m >> 2);  // this lane's dword, subtile 0
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
 #pragma unroll
       for (int p = 0; p < SH::CT / 2; ++p) {  // 32-column block = column tiles 2p, 2p+1
         const int nb = n0 + 32 * p;
+        float hv[4][2];  // [row 4q + i][tile]
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) hv[i][c] = silu(acc[0][rs][2 * p + c][i]) * acc[1][rs][2 * p + c][i];
+        float inv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int lrow = 16 * rs + 4 * q + i;
-          float hv[2];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) hv[c] = silu(acc[0][rs][2 * p + c][i]) * acc[1][rs][2 * p + c][i];
           // lanes with the same q hold the same row: |h| max over the block's 32 columns
-          float amax = fmaxf(fabsf(hv[0]), fabsf(hv[1]));
-#pragma unroll
-          for (int msk = 1; msk < 16; msk <<= 1) amax = fmaxf(amax, __shfl_xor(amax, msk, 64));
-          const int sc = fp8_block_scale(amax);
-          const float inv = fp8_inv_scale(sc);
-          if (lrow < nrows && nb < N) {
+          const int sc = fp8_block_scale(row16_max(fmaxf(fabsf(hv[i][0]), fabsf(hv[i][1]))));
+          inv[i] = fp8_inv_scale(sc);
+          const int lrow = 16 * rs + 4 * q + i;
+          if (m == 0 && lrow < nrows && nb < N) {
             const size_t r = (size_t)(r0 + lrow);
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const uint32_t nanm = fp8_nan_mask(hv[c]);  // non-finite h stays NaN in both terms
-              const float v = hv[c] * inv;
-              const uint32_t t0 = fp8_of(v) | nanm;
-              const uint32_t t1 = fp8_of((v - f32_of_fp8(t0)) * 16.f) | nanm;
-              const size_t o = r * N + nb + 16 * c + m;
-              h8[o] = (uint8_t)t0;
-              h_lo[o] = (uint8_t)t1;
-            }
-            if (m == 0) {
-              hs[r * kb_pad(N) + (nb >> 5)] = (uint8_t)sc;
-              if ((nb >> 5) == (N >> 5) - 1)  // pad bytes of the row
-                for (int j = N >> 5; j < kb_pad(N); ++j) hs[r * kb_pad(N) + j] = (uint8_t)127;
-            }
+            hs[r * kb_pad(N) + (nb >> 5)] = (uint8_t)sc;
+            if ((nb >> 5) == (N >> 5) - 1)  // pad bytes of the row
+              for (int j = N >> 5; j < kb_pad(N); ++j) hs[r * kb_pad(N) + j] = (uint8_t)127;
           }
         }
+        uint32_t w[2][2];  // [term][tile]: byte i = row 4q + i
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = hv[i][c] * inv[i];
+          const uint32_t t0 = pack_fp8x4(v[0], v[1], v[2], v[3]);
+          const uint32_t t1 = pack_fp8x4((v[0] - __builtin_amdgcn_cvt_f32_fp8((int)t0, 0)) * 16.f,
+                                         (v[1] - __builtin_amdgcn_cvt_f32_fp8((int)t0, 1)) * 16.f,
+                                         (v[2] - __builtin_amdgcn_cvt_f32_fp8((int)t0, 2)) * 16.f,
+                                         (v[3] - __builtin_amdgcn_cvt_f32_fp8((int)t0, 3)) * 16.f);
+          uint32_t nanm = 0;  // non-finite h stays NaN in both terms
+#pragma unroll
+          for (int i = 0; i < 4; ++i) nanm |= fp8_nan_mask(hv[i][c]) << (8 * i);
+          w[0][c] = t0 | nanm;
+          w[1][c] = t1 | nanm;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            *reinterpret_cast<uint32_t*>(hl + t * kPM * EPL + lds0 + 16 * rs * EPL + 16 * (2 * p + c)) =
+                quad_byte_transpose(w[t][c], u);
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    constexpr int CPR = SH::PN / 16;  // 16-byte chunks per staged row
+#pragma unroll
+    for (int k = tid; k < 2 * kPM * CPR; k += SH::NTH) {
+      const int t = k / (kPM * CPR), row = (k / CPR) % kPM, ch = k % CPR;
+      const int col = nt * SH::PN + 16 * ch;
+      if (row < nrows && col < N)
+        *reinterpret_cast<i32x4*>(h8 + (size_t)t * R * N + (size_t)(r0 + row) * N + col) =
+            *reinterpret_cast<const i32x4*>(hl + t * kPM * EPL + row * EPL + 16 * ch);
     }
   } else {
     // staging slot and routing weight of the 16 rows this lane finishes (all loads first)
