@@ -146,8 +146,8 @@ constexpr int kBufferFlags = 0x00020000;  // raw byte-addressed buffer, 32-bit d
 // past K move their per-lane offsets past the descriptor's range: they read zeros and touch
 // no memory.  (The scalar offset is not relied on for the range check.)
 constexpr int kOutOfRange = 1 << 30;
-template <class SH, int NM>
-__device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<SH, NM>& bs, int N, int KB, int step, int q) {
+template <int AUX, class SH, int NM>
+__device__ __forceinline__ void b_fetch_aux(BFrag<SH, NM>& f, const BSrc<SH, NM>& bs, int N, int KB, int step, int q) {
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
     const int chunk = step * SH::PU + u;  // 128-value K chunk (uniform; kept in scalar registers)
@@ -164,11 +164,15 @@ __device__ __forceinline__ void b_fetch(BFrag<SH, NM>& f, const BSrc<SH, NM>& bs
 #pragma unroll
       for (int c = 0; c < SH::CT; ++c)
         f.c[u][mtx][c] =
-            __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + bias_c + 256 * c, so_c, 0));
-      f.s[u][mtx] = __builtin_amdgcn_raw_buffer_load_b32(bs.s[mtx], bs.voff_s + bias_s, so_s, 0);
+            __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(bs.c[mtx], bs.voff_c + bias_c + 256 * c, so_c, AUX));
+      f.s[u][mtx] = __builtin_amdgcn_raw_buffer_load_b32(bs.s[mtx], bs.voff_s + bias_s, so_s, AUX);
     }
   }
 }
+// A group of one M-tile reads each weight byte once per column slice: those loads go through
+// as nontemporal (they would only push out lines that other tiles reuse); a group of several
+// M-tiles reads its weights once per M-tile and keeps them cached.
+constexpr int kStreamAux = 2;  // nontemporal
 
 // One K step: acc[mtx][rs][c] += A(rs) x B(mtx, c) for both FP8 terms, rs < nsub.  sh: the
 // bit offset of this wave's first tile in its scale dword (0 or 16 when CT == 2).
@@ -233,8 +237,9 @@ struct BSrc8 {
   const float* s[NM];  // the wave's row block of each matrix's scales, indexed by chunk
   int voff;            // column tile 0, chunk 0
 };
-template <class SH, int NM>
-__device__ __forceinline__ void b_fetch(BFrag8<SH, NM>& f, const BSrc8<SH, NM>& bs, int N, int KB, int step, int q) {
+template <int AUX, class SH, int NM>
+__device__ __forceinline__ void b_fetch_aux(BFrag8<SH, NM>& f, const BSrc8<SH, NM>& bs, int N, int KB, int step,
+                                            int q) {  // (the FP8 shared expert spans many M-tiles: cached)
   (void)q;
 #pragma unroll
   for (int u = 0; u < SH::PU; ++u) {
@@ -346,7 +351,8 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   if (gw < 0) return;
   const int mr0 = __builtin_amdgcn_readfirstlane(mt_row0[mt]);
   const int r0 = __builtin_amdgcn_readfirstlane(grp_row0[g]) + mr0;  // first grouped row of the tile
-  const int nrows = min(kPM, __builtin_amdgcn_readfirstlane(grp_rows[g]) - mr0);
+  const int grp_rows_g = __builtin_amdgcn_readfirstlane(grp_rows[g]);
+  const int nrows = min(kPM, grp_rows_g - mr0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, q = lane >> 4;
   const int tk = T * k;
@@ -424,46 +430,55 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   static_assert(kBS == 2 || kBS == 3, "weight stages");
   constexpr int NB = NM * (SH::CT + 1);
   constexpr int kNewer = 2 * NB + 4;
-  BF fb[kBS];
-  // The loads run ahead unconditionally: past the last step the tile loads repeat the last
-  // step (cache hits) and the weights read zeros without memory traffic.
-  const int last = nsteps - 1;
-  a_dma<SH>(tile[0], ad, a.K, 0, wave);
-  mem_order();
-  b_fetch(fb[0], bs, N, KB, 0, q);
-  mem_order();
-  a_dma<SH>(tile[1], ad, a.K, min(1, last), wave);
-  if constexpr (kBS == 3) {
+  // The main loop exists twice, once per weight-load policy, chosen per workgroup (a branch
+  // inside the loop would make the compiler's waits before the MFMAs drain the loads in flight).
+  auto pipeline = [&](auto policy) {
+    constexpr int AUX = decltype(policy)::value;
+    BF fb[kBS];
+    // The loads run ahead unconditionally: past the last step the tile loads repeat the last
+    // step (cache hits) and the weights read zeros without memory traffic.
+    const int last = nsteps - 1;
+    a_dma<SH>(tile[0], ad, a.K, 0, wave);
     mem_order();
-    b_fetch(fb[1], bs, N, KB, 1, q);
-    tile_barrier<kNewer>();
-  } else {
-    tile_barrier<NB + 4>();
-  }
-  auto step = [&](int s, ATile<SH>& tc, ATile<SH>& t_far, BF& fc, BF& f_far) -> bool {
-    a_dma<SH>(t_far, ad, a.K, min(s + 2, last), wave);
+    b_fetch_aux<AUX>(fb[0], bs, N, KB, 0, q);
     mem_order();
-    b_fetch(f_far, bs, N, KB, s + kBS - 1, q);
-    k_step(tc, fc, acc, nsub, m, q, sh);
-    tile_barrier<kNewer>();
-    return s + 1 < nsteps;
+    a_dma<SH>(tile[1], ad, a.K, min(1, last), wave);
+    if constexpr (kBS == 3) {
+      mem_order();
+      b_fetch_aux<AUX>(fb[1], bs, N, KB, 1, q);
+      tile_barrier<kNewer>();
+    } else {
+      tile_barrier<NB + 4>();
+    }
+    auto step = [&](int s, ATile<SH>& tc, ATile<SH>& t_far, BF& fc, BF& f_far) -> bool {
+      a_dma<SH>(t_far, ad, a.K, min(s + 2, last), wave);
+      mem_order();
+      b_fetch_aux<AUX>(f_far, bs, N, KB, s + kBS - 1, q);
+      k_step(tc, fc, acc, nsub, m, q, sh);
+      tile_barrier<kNewer>();
+      return s + 1 < nsteps;
+    };
+    if constexpr (kBS == 3) {
+      for (int s = 0; s < nsteps; s += 3) {
+        if (!step(s + 0, tile[0], tile[2], fb[0], fb[2])) break;
+        if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
+        if (!step(s + 2, tile[2], tile[1], fb[2], fb[1])) break;
+      }
+    } else {
+      for (int s = 0; s < nsteps; s += 6) {
+        if (!step(s + 0, tile[0], tile[2], fb[0], fb[1])) break;
+        if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
+        if (!step(s + 2, tile[2], tile[1], fb[0], fb[1])) break;
+        if (!step(s + 3, tile[0], tile[2], fb[1], fb[0])) break;
+        if (!step(s + 4, tile[1], tile[0], fb[0], fb[1])) break;
+        if (!step(s + 5, tile[2], tile[1], fb[1], fb[0])) break;
+      }
+    }
   };
-  if constexpr (kBS == 3) {
-    for (int s = 0; s < nsteps; s += 3) {
-      if (!step(s + 0, tile[0], tile[2], fb[0], fb[2])) break;
-      if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
-      if (!step(s + 2, tile[2], tile[1], fb[2], fb[1])) break;
-    }
-  } else {
-    for (int s = 0; s < nsteps; s += 6) {
-      if (!step(s + 0, tile[0], tile[2], fb[0], fb[1])) break;
-      if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
-      if (!step(s + 2, tile[2], tile[1], fb[0], fb[1])) break;
-      if (!step(s + 3, tile[0], tile[2], fb[1], fb[0])) break;
-      if (!step(s + 4, tile[1], tile[0], fb[0], fb[1])) break;
-      if (!step(s + 5, tile[2], tile[1], fb[1], fb[0])) break;
-    }
-  }
+  if (!FP8 && mr0 == 0 && nrows == grp_rows_g)
+    pipeline(std::integral_constant<int, kStreamAux>{});
+  else
+    pipeline(std::integral_constant<int, 0>{});
   // no tile load may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

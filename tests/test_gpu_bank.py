@@ -125,6 +125,24 @@ def test_bank_shapes_and_varying_batches(n_slots, group):
     assert st["calls"] == 4 and st["uploads"] + st["resident_hits"] > 0
 
 
+def test_bank_with_wide_gateup_slices():
+    # 300 tokens over 8 experts + shared (100 grouped rows a group) take the gate/up kernel's
+    # 256-column slices (I = 384: the second slice runs past I); 40 tokens take the 128-column
+    # ones.  Both through a 4-slot bank with refills, bitwise against the resident layer.
+    from fp4_routed_expert_moe_amd import MoeBank
+    groups, wr = _case(66, 256, 8, 2, 384)
+    resident, hosted = _pair(wr, pack_weights(stack_groups(groups)), 2, 1)
+    bank = MoeBank(hosted, n_slots=4, group=2)
+    wl = synth.custom_workload("bank4", 256, 8, 2, 1, 384, 300)
+    x = screened_tokens(wl, wr, None)
+    for t in (300, 40):
+        got = _run_both(resident, bank, x[:t])
+        ref = oracle.moe_forward(x[:t], wr, None, groups, 2, 1)
+        check_routing(got, ref, x[:t], wr)
+        check_outputs(got["y"], ref["y"], f"bank, {t} tokens, vs oracle")
+    assert bank.stats()["calls"] == 2
+
+
 def test_bank_rejects_device_weights_and_small_banks():
     from fp4_routed_expert_moe_amd import MoeBank, MoeError
     groups, wr = _case(64, 256, 8, 2, 128)
