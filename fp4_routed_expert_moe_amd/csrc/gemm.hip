@@ -318,6 +318,32 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t w, int u) {
   return (u & 2) ? ((p2 >> 16) | (n & 0xFFFF0000u)) : ((n & 0xFFFFu) | (p2 << 16));
 }
 
+// 4 x 4 transpose of dwords within a lane quad: lane u holds v[i] = element (i, u) and gets
+// v[c] = element (u, c).  Two exchange steps: elements with the neighbour lane, then pairs of
+// elements with the lane two over.
+__device__ __forceinline__ void quad_transpose4(float (&v)[4], int u) {
+  const bool odd = u & 1;
+  const float r0 = __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(odd ? v[0] : v[1])));
+  const float r1 = __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(odd ? v[2] : v[3])));
+  if (odd) {
+    v[0] = r0;
+    v[2] = r1;
+  } else {
+    v[1] = r0;
+    v[3] = r1;
+  }
+  const bool upper = u & 2;
+  const float s0 = __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(upper ? v[0] : v[2])));
+  const float s1 = __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(upper ? v[1] : v[3])));
+  if (upper) {
+    v[0] = s0;
+    v[1] = s1;
+  } else {
+    v[2] = s0;
+    v[3] = s1;
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // GATEUP: h[r][n] = silu(x_t(r) . Wg[n]) * (x_t(r) . Wu[n]) as 2 FP8 terms + e8m0 per 32
 //         (h8 = [2][R][I] bytes then [R][kb_pad(I)] scales).
@@ -557,28 +583,30 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
             *reinterpret_cast<const i32x4*>(hl + t * kPM * EPL + row * EPL + 16 * ch);
     }
   } else {
-    // staging slot and routing weight of the 16 rows this lane finishes (all loads first)
-    int slot[4][4];
-    float wt[4][4];
+    // A 4 x 4 transpose within the lane quad turns column m of rows 4q..4q+3 into columns
+    // 4(m/4)..+3 of row 4q + m%4: one 16-byte store per tile and row.  The staging slot and
+    // routing weight of the four rows this lane stores, all loads first.
+    const int u = m & 3;
+    int slot[4];
+    float wt[4];
 #pragma unroll
-    for (int rs = 0; rs < 4; ++rs)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = r0 + min(16 * rs + 4 * q + i, nrows - 1);
-        slot[rs][i] = rr < tk ? perm[rr] : rr;
-        wt[rs][i] = rr < tk ? wts[rr] * routed_scale : 1.0f;
-      }
+    for (int rs = 0; rs < 4; ++rs) {
+      const int rr = r0 + min(16 * rs + 4 * q + u, nrows - 1);
+      slot[rs] = rr < tk ? perm[rr] : rr;
+      wt[rs] = rr < tk ? wts[rr] * routed_scale : 1.0f;
+    }
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs) {
       if (rs >= nsub) break;
+      const bool row_ok = 16 * rs + 4 * q + u < nrows;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (16 * rs + 4 * q + i >= nrows) continue;
-#pragma unroll
-        for (int c = 0; c < SH::CT; ++c) {
-          const int n = n0 + 16 * c + m;
-          if (n < N) staging[(size_t)slot[rs][i] * N + n] = acc[0][rs][c][i] * wt[rs][i];
-        }
+      for (int c = 0; c < SH::CT; ++c) {
+        float v[4] = {acc[0][rs][c][0], acc[0][rs][c][1], acc[0][rs][c][2], acc[0][rs][c][3]};
+        quad_transpose4(v, u);
+        const int n = n0 + 16 * c + 4 * (m >> 2);
+        if (row_ok && n < N)
+          *reinterpret_cast<float4*>(&staging[(size_t)slot[rs] * N + n]) =
+              make_float4(v[0] * wt[rs], v[1] * wt[rs], v[2] * wt[rs], v[3] * wt[rs]);
       }
     }
   }
