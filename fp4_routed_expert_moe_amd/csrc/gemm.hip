@@ -291,22 +291,6 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
   }
 }
 
-// DPP moves within a lane quad / a 16-lane row (every lane active).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-// max of v over the 16 lanes of this lane's row
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_mov<kRowHalfMirror>(__float_as_uint(v))));
-  return fmaxf(v, __uint_as_float(dpp_mov<kRowMirror>(__float_as_uint(v))));
-}
 // 4 x 4 byte transpose within a lane quad: lane u of the quad holds byte i = element (i, u)
 // and gets byte c = element (u, c).  Two exchange steps: bytes with the neighbour lane, then
 // 16-bit halves with the lane two over.

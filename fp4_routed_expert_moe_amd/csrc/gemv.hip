@@ -343,10 +343,7 @@ __device__ __forceinline__ void gateup_tile(f32x4 (*red)[TL][2][64], int bx, int
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // lanes with the same q hold the same 4 tokens: reduce |h| over the 32 columns
-        float a = fmaxf(fabsf(hv[0][i]), fabsf(hv[1][i]));
-#pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) a = fmaxf(a, __shfl_xor(a, msk, 64));
-        const int sc = fp8_block_scale(a);
+        const int sc = fp8_block_scale(row16_max(fmaxf(fabsf(hv[0][i]), fabsf(hv[1][i]))));
         const float inv = fp8_inv_scale(sc);
         const int tok_i = 4 * q + i;
         if (nb < I && tok_i < nt) {

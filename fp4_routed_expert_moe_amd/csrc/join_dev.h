@@ -62,11 +62,7 @@ __device__ __forceinline__ void join_load(JoinRow& r, const float* h_src, const 
   r.ss = ss;
 }
 
-__device__ __forceinline__ float join_wave_sum(float ss) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) ss += __shfl_xor(ss, m, 64);
-  return ss;
-}
+__device__ __forceinline__ float join_wave_sum(float ss) { return wave64_sum(ss); }
 
 // 1 / sqrt(mean + eps) from the four waves' sums p[0..3] of a row.
 __device__ __forceinline__ float join_inv(const float* p, int H, float eps) {
