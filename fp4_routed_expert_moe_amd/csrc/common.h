@@ -133,36 +133,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// DPP moves within a lane quad or a 16-lane row (every lane of the wave active).  They run on
-// the VALU, where a cross-lane shuffle through LDS (ds_bpermute) costs a round trip each.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+// More DPP controls for the helpers below (every lane of the wave active).
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
 constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within each row
 // max of v over the 16 lanes of this lane's row (every lane gets it)
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_mov<kRowHalfMirror>(__float_as_uint(v))));
-  return fmaxf(v, __uint_as_float(dpp_mov<kRowMirror>(__float_as_uint(v))));
-}
-// sum of v over the wave, the same bits in every lane: a butterfly within each 16-lane row
-// (partners add the same two values, so every lane of a row ends with the same sum), then the
-// four row sums in a fixed order.
-__device__ __forceinline__ float wave64_sum(float v) {
-  v += __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_mov<kRowHalfMirror>(__float_as_uint(v)));
-  v += __uint_as_float(dpp_mov<kRowMirror>(__float_as_uint(v)));
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
+  v = fmaxf(v, __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kRowHalfMirror>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp_u32<kRowMirror>(__float_as_uint(v))));
 }
 
 // Operands of v_mfma_scale_f32_16x16x128_f8f6f4 (probed lane layout, 16x16 output tile):

@@ -295,10 +295,10 @@ __device__ __forceinline__ void k_step(const ATile<SH>& t, const BFrag8<SH, NM>&
 // and gets byte c = element (u, c).  Two exchange steps: bytes with the neighbour lane, then
 // 16-bit halves with the lane two over.
 __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t w, int u) {
-  const uint32_t p = dpp_mov<kQuadXor1>(w);
+  const uint32_t p = dpp_u32<kQuadXor1>(w);
   const uint32_t n = (u & 1) ? (((p >> 8) & 0x00FF00FFu) | (w & 0xFF00FF00u))
                              : ((w & 0x00FF00FFu) | ((p & 0x00FF00FFu) << 8));
-  const uint32_t p2 = dpp_mov<kQuadXor2>(n);
+  const uint32_t p2 = dpp_u32<kQuadXor2>(n);
   return (u & 2) ? ((p2 >> 16) | (n & 0xFFFF0000u)) : ((n & 0xFFFFu) | (p2 << 16));
 }
 
@@ -307,8 +307,8 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t w, int u) {
 // elements with the lane two over.
 __device__ __forceinline__ void quad_transpose4(float (&v)[4], int u) {
   const bool odd = u & 1;
-  const float r0 = __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(odd ? v[0] : v[1])));
-  const float r1 = __uint_as_float(dpp_mov<kQuadXor1>(__float_as_uint(odd ? v[2] : v[3])));
+  const float r0 = __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(odd ? v[0] : v[1])));
+  const float r1 = __uint_as_float(dpp_u32<kQuadXor1>(__float_as_uint(odd ? v[2] : v[3])));
   if (odd) {
     v[0] = r0;
     v[2] = r1;
@@ -317,8 +317,8 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int u) {
     v[3] = r1;
   }
   const bool upper = u & 2;
-  const float s0 = __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(upper ? v[0] : v[2])));
-  const float s1 = __uint_as_float(dpp_mov<kQuadXor2>(__float_as_uint(upper ? v[1] : v[3])));
+  const float s0 = __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(upper ? v[0] : v[2])));
+  const float s1 = __uint_as_float(dpp_u32<kQuadXor2>(__float_as_uint(upper ? v[1] : v[3])));
   if (upper) {
     v[0] = s0;
     v[1] = s1;

@@ -62,7 +62,7 @@ __device__ __forceinline__ void join_load(JoinRow& r, const float* h_src, const 
   r.ss = ss;
 }
 
-__device__ __forceinline__ float join_wave_sum(float ss) { return wave64_sum(ss); }
+__device__ __forceinline__ float join_wave_sum(float ss) { return wave_sum_f32(ss); }
 
 // 1 / sqrt(mean + eps) from the four waves' sums p[0..3] of a row.
 __device__ __forceinline__ float join_inv(const float* p, int H, float eps) {
