@@ -25,9 +25,11 @@
 //   operand reads (16 rows, one chunk each) free of bank conflicts.  Each step ends with one
 //   barrier, preceded by a wait for this wave's loads of the next tile only (counted in
 //   vector-memory instructions, not a full drain).
-// * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes the M-tiles 8i + x, every
-//   column slice of each in turn: an M-tile's activation rows are fetched into one XCD's L2
-//   only, and with small batches (one M-tile per expert) the XCDs stream different experts.
+// * Workgroups reach the 8 XCDs round-robin (b % 8).  XCD x takes every 8th M-tile (or, for
+//   large groups, every 8th run of two consecutive M-tiles, so that a group of two tiles reads
+//   its weights into one XCD's L2), every column slice of each in turn: an M-tile's activation
+//   rows are fetched into one XCD's L2 only, and with small batches (one M-tile per expert)
+//   the XCDs stream different experts.
 #include <type_traits>
 
 #include "common.h"
@@ -65,6 +67,14 @@ constexpr int kWideRowsPerGroup = 40;
 inline bool gateup_wide(const Dims& d, int T) {
   return (long long)T * (d.K + d.S) >= (long long)kWideRowsPerGroup * d.G;
 }
+// Workgroups meet the XCDs in runs of M-tiles: 2 (a group of two M-tiles, common at these
+// sizes, then reads its weights into one XCD's L2) when the groups are as large as for the wide
+// slices, else 1 (round-robin; a hot expert's tiles spread over all XCDs).  Measured at H 4096,
+// I 2048: runs of 2 take 4096 uniform tokens from 1.75 to 1.60 ms per step and 4096 zipf tokens
+// from 1.63 to 1.61, and cost about 1% at 512 uniform tokens; runs of 4 or a contiguous eighth
+// per XCD did no better.
+inline int tile_run_log2(const Dims& d, int T) { return gateup_wide(d, T) ? 1 : 0; }
+inline int tile_grid(int tiles, int rl, int NT) { return (tiles + (8 << rl) - 1) / (8 << rl) * (8 << rl) * NT; }
 
 template <class SH>
 struct ATile {                    // one K step of the activation tile
@@ -347,13 +357,14 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     const int32_t* __restrict__ info, const int32_t* __restrict__ mt_group, const int32_t* __restrict__ mt_row0,
     const int32_t* __restrict__ grp_row0, const int32_t* __restrict__ grp_rows, const int32_t* __restrict__ slot_of,
     uint8_t* __restrict__ h8, float* __restrict__ staging, int routed_only, float routed_scale, int T, int k, int N,
-    int R, int NT) {
+    int R, int NT, int rl) {
   constexpr int NM = GATEUP ? 2 : 1;
   static_assert(SH::PU == 1 && SH::NW == 4, "tile loads: 4 waves x 16 rows, one 128-value chunk per step");
   __shared__ ATile<SH> tile[3];
-  // XCD x (= b % 8) takes the M-tiles mt = 8i + x, all NT column slices of each
-  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-  const int mt = (jj / NT) * 8 + xcd + (FP8 ? info[2] : 0), nt = jj % NT;
+  // XCD x (= b % 8) takes runs of 2^rl consecutive M-tiles, every 8th run, all NT column slices
+  // of each (the grid holds a whole number of runs per XCD)
+  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3, it = jj / NT;
+  const int mt = ((((it >> rl) << 3) + xcd) << rl) + (it & ((1 << rl) - 1)) + (FP8 ? info[2] : 0), nt = jj % NT;
   if (mt >= (routed_only ? info[2] : info[1])) return;
   // tile metadata is the same for every lane: keep it in scalar registers
   const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
@@ -602,10 +613,11 @@ static void gateup_fp4(const Dims& d, const moe_layer_desc& w, const CallBufs& b
                        int mt_bound, hipStream_t s, const int32_t* slot_of) {
   const int NT = (d.I + SH::PN - 1) / SH::PN;
   const int R = T * (d.K + d.S);
-  gemm_f8f4_kernel<true, SH><<<(mt_bound + 7) / 8 * 8 * NT, SH::NTH, 0, s>>>(
+  const int rl = tile_run_log2(d, T);
+  gemm_f8f4_kernel<true, SH><<<tile_grid(mt_bound, rl, NT), SH::NTH, 0, s>>>(
       a, w.gate_codes, w.gate_scales, w.up_codes, w.up_scales, nullptr, nullptr, b.perm, b.w, b.info, b.mt_group,
       b.mt_row0, b.grp_row0, b.grp_rows, slot_of, static_cast<uint8_t*>(b.h), nullptr, d.fp8_shared, 1.0f, T, d.K,
-      d.I, R, NT);
+      d.I, R, NT, rl);
 }
 
 hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint16_t* x, const CallBufs& b,
@@ -624,10 +636,10 @@ hipError_t launch_gemm_gateup(const Dims& d, const moe_layer_desc& w, const uint
   const int R = T * (d.K + d.S);
   const int mts = (T + kGemmBM - 1) / kGemmBM;  // the shared expert's M-tiles
   const int tk8 = timing_begin("gemm_gateup_fp8", s);
-  gemm_f8f4_kernel<true, GateUpShape8, true><<<(mts + 7) / 8 * 8 * NT, GateUpShape8::NTH, 0, s>>>(
+  gemm_f8f4_kernel<true, GateUpShape8, true><<<tile_grid(mts, 0, NT), GateUpShape8::NTH, 0, s>>>(
       a, w.shared_gate_fp8, nullptr, w.shared_up_fp8, nullptr, w.shared_gate_fp8_scales, w.shared_up_fp8_scales,
       b.perm, b.w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr, static_cast<uint8_t*>(b.h),
-      nullptr, 0, 1.0f, T, d.K, d.I, R, NT);
+      nullptr, 0, 1.0f, T, d.K, d.I, R, NT, 0);
   timing_end(tk8, s);
   return hipGetLastError();
 }
@@ -639,19 +651,20 @@ hipError_t launch_gemm_down(const Dims& d, const moe_layer_desc& w, const CallBu
   const uint8_t* h8 = static_cast<const uint8_t*>(b.h);
   const ARows a{h8, h8 + (size_t)R * d.I, h8 + (size_t)2 * R * d.I, d.I, R};
   const int tk = timing_begin("gemm_down", s);
-  gemm_f8f4_kernel<false, DownShape><<<(mt_bound + 7) / 8 * 8 * NT, DownShape::NTH, 0, s>>>(
+  const int rl = tile_run_log2(d, T);
+  gemm_f8f4_kernel<false, DownShape><<<tile_grid(mt_bound, rl, NT), DownShape::NTH, 0, s>>>(
       a, w.down_codes, w.down_scales, w.down_codes, w.down_scales, nullptr, nullptr, b.perm, b.row_w, b.info,
       b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, slot_of, nullptr, b.staging, d.fp8_shared, d.routed_scale, T,
-      d.K, d.H, R, NT);
+      d.K, d.H, R, NT, rl);
   timing_end(tk, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !d.fp8_shared) return e;
   const int mts = (T + kGemmBM - 1) / kGemmBM;
   const int tk8 = timing_begin("gemm_down_fp8", s);
-  gemm_f8f4_kernel<false, DownShape8, true><<<(mts + 7) / 8 * 8 * NT, DownShape8::NTH, 0, s>>>(
+  gemm_f8f4_kernel<false, DownShape8, true><<<tile_grid(mts, 0, NT), DownShape8::NTH, 0, s>>>(
       a, w.shared_down_fp8, nullptr, w.shared_down_fp8, nullptr, w.shared_down_fp8_scales,
       w.shared_down_fp8_scales, b.perm, b.row_w, b.info, b.mt_group, b.mt_row0, b.grp_row0, b.grp_rows, nullptr,
-      nullptr, b.staging, 0, d.routed_scale, T, d.K, d.H, R, NT);
+      nullptr, b.staging, 0, d.routed_scale, T, d.K, d.H, R, NT, 0);
   timing_end(tk8, s);
   return hipGetLastError();
 }
