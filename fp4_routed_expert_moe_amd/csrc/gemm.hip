@@ -445,8 +445,9 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   // Pipeline: while step s runs on the matrix cores, the activation tile of step s+2 streams
   // into the third LDS buffer and the weight operands of step s+BS-1 into registers.  Per
   // step a wave issues 4 tile loads (wave 0: 5), then NB weight loads (FP4: NM * (CT + 1);
-  // FP8 more), so the tile of step s+1 is complete once at most 2 NB + 4 newer loads are
-  // outstanding (wave 0 waits for one more than it needs).
+  // FP8 more), so the tile of step s+1, issued in step s-1, is complete once at most
+  // 2 NB + 4 newer loads are outstanding (wave 0 waits for one more than it needs).
+  // tests/test_gemm_wait_counts_cpu.py checks these counts against the compiled order.
   constexpr int kBS = SH::BS;
   static_assert(kBS == 2 || kBS == 3, "weight stages");
   constexpr int NB = NM * (SH::CT + 1);
@@ -471,28 +472,35 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
     } else {
       tile_barrier<NB + 4>();
     }
-    auto step = [&](int s, ATile<SH>& tc, ATile<SH>& t_far, BF& fc, BF& f_far) -> bool {
+    auto step = [&](int s, ATile<SH>& tc, ATile<SH>& t_far, BF& fc, BF& f_far, auto newer) -> bool {
       a_dma<SH>(t_far, ad, a.K, min(s + 2, last), wave);
       mem_order();
       b_fetch_aux<AUX>(f_far, bs, N, KB, s + kBS - 1, q);
       k_step(tc, fc, acc, nsub, m, q, sh);
-      tile_barrier<kNewer>();
+      tile_barrier<decltype(newer)::value>();
       return s + 1 < nsteps;
     };
+    const std::integral_constant<int, kNewer> steady;
     if constexpr (kBS == 3) {
       for (int s = 0; s < nsteps; s += 3) {
-        if (!step(s + 0, tile[0], tile[2], fb[0], fb[2])) break;
-        if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
-        if (!step(s + 2, tile[2], tile[1], fb[2], fb[1])) break;
+        if (!step(s + 0, tile[0], tile[2], fb[0], fb[2], steady)) break;
+        if (!step(s + 1, tile[1], tile[0], fb[1], fb[0], steady)) break;
+        if (!step(s + 2, tile[2], tile[1], fb[2], fb[1], steady)) break;
       }
     } else {
-      for (int s = 0; s < nsteps; s += 6) {
-        if (!step(s + 0, tile[0], tile[2], fb[0], fb[1])) break;
-        if (!step(s + 1, tile[1], tile[0], fb[1], fb[0])) break;
-        if (!step(s + 2, tile[2], tile[1], fb[0], fb[1])) break;
-        if (!step(s + 3, tile[0], tile[2], fb[1], fb[0])) break;
-        if (!step(s + 4, tile[1], tile[0], fb[0], fb[1])) break;
-        if (!step(s + 5, tile[2], tile[1], fb[1], fb[0])) break;
+      // With one weight stage the prologue ends with step 1's tile loads, so at the end of
+      // step 0 only that step's NB + 4 loads are newer: step 0 waits with that count, the
+      // following steps (whose next tile came one step earlier, before NB + 4 + NB loads)
+      // with 2 NB + 4.
+      if (step(0, tile[0], tile[2], fb[0], fb[1], std::integral_constant<int, NB + 4>{})) {
+        for (int s = 1; s < nsteps; s += 6) {
+          if (!step(s + 0, tile[1], tile[0], fb[1], fb[0], steady)) break;
+          if (!step(s + 1, tile[2], tile[1], fb[0], fb[1], steady)) break;
+          if (!step(s + 2, tile[0], tile[2], fb[1], fb[0], steady)) break;
+          if (!step(s + 3, tile[1], tile[0], fb[0], fb[1], steady)) break;
+          if (!step(s + 4, tile[2], tile[1], fb[1], fb[0], steady)) break;
+          if (!step(s + 5, tile[0], tile[2], fb[0], fb[1], steady)) break;
+        }
       }
     }
   };
