@@ -29,7 +29,9 @@
 //   large groups, every 8th run of two consecutive M-tiles, so that a group of two tiles reads
 //   its weights into one XCD's L2), every column slice of each in turn: an M-tile's activation
 //   rows are fetched into one XCD's L2 only, and with small batches (one M-tile per expert)
-//   the XCDs stream different experts.
+//   the XCDs stream different experts.  Blocks of 8 runs come alternately from the front and
+//   the back of the tile list, so that skewed batches run their many-tile groups (matrix-core
+//   bound) beside their one-tile groups (weight-stream bound).
 #include <type_traits>
 
 #include "common.h"
@@ -362,10 +364,18 @@ __global__ __launch_bounds__(SH::NTH, SH::OCC) void gemm_f8f4_kernel(
   static_assert(SH::PU == 1 && SH::NW == 4, "tile loads: 4 waves x 16 rows, one 128-value chunk per step");
   __shared__ ATile<SH> tile[3];
   // XCD x (= b % 8) takes runs of 2^rl consecutive M-tiles, every 8th run, all NT column slices
-  // of each (the grid holds a whole number of runs per XCD)
-  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3, it = jj / NT;
-  const int mt = ((((it >> rl) << 3) + xcd) << rl) + (it & ((1 << rl) - 1)) + (FP8 ? info[2] : 0), nt = jj % NT;
-  if (mt >= (routed_only ? info[2] : info[1])) return;
+  // of each (the grid holds a whole number of runs per XCD).  The blocks of 8 runs are taken
+  // alternately from the front and, backwards, from the back of the launch's tile list, so that
+  // the tiles of large groups (matrix-core bound, their weights shared through the caches) run
+  // beside those of one-tile groups (bound by their weight stream) instead of before them.
+  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3, it = jj / NT, nt = jj % NT;
+  const int base = FP8 ? info[2] : 0, n_mt = (routed_only ? info[2] : info[1]) - base;
+  const int nblk = (n_mt + (8 << rl) - 1) >> (rl + 3), blk = it >> rl;
+  if (blk >= nblk) return;
+  const int blk_f = (blk & 1) ? nblk - 1 - (blk >> 1) : (blk >> 1);
+  const int mt_l = (((blk_f << 3) + xcd) << rl) + (it & ((1 << rl) - 1));
+  if (mt_l >= n_mt) return;
+  const int mt = base + mt_l;
   // tile metadata is the same for every lane: keep it in scalar registers
   const int g = __builtin_amdgcn_readfirstlane(mt_group[mt]);
   const int gw = slot_of ? __builtin_amdgcn_readfirstlane(slot_of[g]) : g;  // weight index of the group
