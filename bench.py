@@ -149,7 +149,7 @@ def main():
     if args.stats_summary:
         return stats_summary(args)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
